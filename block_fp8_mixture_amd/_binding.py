@@ -1,0 +1,324 @@
+"""ctypes marshalling for libmoefp8.so. No arithmetic of the layer lives here."""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmoefp8.so"
+
+SCALE_FMTS = {"fp32": 0, "pow2": 1, "ue8m0": 2}
+ACTS = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_clamp_after_silu": 2}
+# Row-tile geometry of the grouped GEMM (mirrors the header's macros), used to
+# interpret the tiles_visited counter.
+GEMM_TILES = {"stream_tile_m": 16, "stream_max_rows": 64, "tiled_tile_m": 128, "col_tile": 128}
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "capacity too small",
+           4: "HIP runtime error"}
+
+_lock = threading.Lock()
+_lib = None
+
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({status})")
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("topk", _i32),
+                ("t_cap", _i32), ("align_rows", _i32), ("row_cap", _i32),
+                ("scale_fmt", ctypes.c_int), ("act", ctypes.c_int), ("clamp_limit", _f32)]
+
+
+class _Tensors(ctypes.Structure):
+    _fields_ = [("x", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("t_live_dev", _vp),
+                ("w1", _vp), ("w1_scales", _vp), ("w2", _vp), ("w2_scales", _vp),
+                ("out", _vp)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("expert_counts", ctypes.c_size_t), ("expert_offsets", ctypes.c_size_t),
+                ("row_to_pair", ctypes.c_size_t), ("pair_to_row", ctypes.c_size_t),
+                ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t), ("c1", ctypes.c_size_t),
+                ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t), ("y", ctypes.c_size_t),
+                ("total", ctypes.c_size_t), ("row_cap", _i32)]
+
+
+_SIGNATURES = {
+    "moe_min_row_cap": (_i32, [_i32, _i32, _i32, _i32]),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_align": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "moe_act_quant": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp, _vp,
+                                            _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
+                                            _vp]),
+    "moe_silu_mul_quant": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, ctypes.c_int, _f32,
+                                          ctypes.c_int, _vp, _vp, _vp]),
+    "moe_topk_combine": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]),
+    "moe_workspace_plan": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Layout)]),
+    "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Problem)]),
+    "moe_forward": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
+                                   ctypes.c_size_t, _vp]),
+}
+
+
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libmoefp8.so from the package directory (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise ImportError(f"{path} is not built; run python -m block_fp8_mixture_amd.build")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return t
+
+
+def _fmt(fmt):
+    if fmt not in SCALE_FMTS:
+        raise ValueError(f"scale format must be one of {list(SCALE_FMTS)}")
+    return SCALE_FMTS[fmt]
+
+
+def _scale_dtype(fmt):
+    return torch.uint8 if fmt == "ue8m0" else torch.float32
+
+
+def _live(t_live):
+    if t_live is None:
+        return None
+    return _ptr(_need(t_live, "t_live", torch.int32))
+
+
+def _bf16_view(t, name):
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return _need(t, name, torch.int16)
+
+
+def moe_min_row_cap(t_cap, topk, num_experts, align_rows):
+    return int(load_library().moe_min_row_cap(t_cap, topk, num_experts, align_rows))
+
+
+def moe_status_string(status):
+    return load_library().moe_status_string(status).decode()
+
+
+def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, out=None):
+    """Routing alignment. Returns dict(counts, offsets, row_to_pair, pair_to_row)."""
+    lib = load_library()
+    ids = _need(topk_ids, "topk_ids", torch.int32, ndim=2)
+    t_cap, topk = ids.shape
+    if row_cap is None:
+        row_cap = moe_min_row_cap(t_cap, topk, num_experts, align_rows)
+    dev = ids.device
+    if out is None:
+        out = {
+            "counts": torch.empty(num_experts, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+            "row_to_pair": torch.empty(max(row_cap, 1), dtype=torch.int32, device=dev),
+            "pair_to_row": torch.empty(max(t_cap * topk, 1), dtype=torch.int32, device=dev),
+        }
+    for k in ("counts", "offsets", "row_to_pair", "pair_to_row"):
+        _need(out[k], k, torch.int32)
+    st = lib.moe_align(_ptr(ids), t_cap, _live(t_live), topk, num_experts, align_rows, row_cap,
+                       _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_to_pair"]),
+                       _ptr(out["pair_to_row"]), _stream())
+    _check("moe_align", st)
+    return out
+
+
+def moe_act_quant(x, fmt="fp32", t_live=None, xq=None, xs=None):
+    """Per-token 1x128 quantization. Returns (xq uint8 [t_cap, H], xs [H/128, t_cap])."""
+    lib = load_library()
+    xb = _bf16_view(x, "x")
+    t_cap, hidden = xb.shape
+    if xq is None:
+        xq = torch.empty((t_cap, hidden), dtype=torch.uint8, device=xb.device)
+    if xs is None:
+        xs = torch.empty((hidden // 128, t_cap), dtype=_scale_dtype(fmt), device=xb.device)
+    _need(xq, "xq", torch.uint8)
+    _need(xs, "xs", _scale_dtype(fmt))
+    st = lib.moe_act_quant(_ptr(xb), t_cap, _live(t_live), hidden, _fmt(fmt), _ptr(xq), _ptr(xs),
+                           _stream())
+    _check("moe_act_quant", st)
+    return xq, xs
+
+
+def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap,
+                         a_row_map=None, a_row_div=1, max_rows_per_expert=0, out=None,
+                         tiles_visited=None):
+    """Grouped FP8 GEMM over live rows. ``w`` is uint8 [E, N, K]; returns BF16 bits
+    (int16) [row_cap, N]."""
+    lib = load_library()
+    _need(a, "a", torch.uint8, ndim=2)
+    _need(a_scales, "a_scales", _scale_dtype(fmt), ndim=2)
+    _need(w, "w", torch.uint8, ndim=3)
+    _need(w_scales, "w_scales", torch.float32, ndim=3)
+    _need(counts, "counts", torch.int32)
+    _need(offsets, "offsets", torch.int32)
+    num_experts, n, k = w.shape
+    if a.shape[1] != k:
+        raise ValueError("a and w disagree on K")
+    a_rows = a_scales.shape[1]
+    if out is None:
+        out = torch.empty((max(row_cap, 1), n), dtype=torch.int16, device=a.device)
+    _bf16_view(out, "out")
+    if a_row_map is not None:
+        _need(a_row_map, "a_row_map", torch.int32)
+    if tiles_visited is not None:
+        _need(tiles_visited, "tiles_visited", torch.int32)
+    st = lib.moe_grouped_gemm_fp8(_ptr(a), _ptr(a_scales), _fmt(fmt), a_rows, _ptr(a_row_map),
+                                  a_row_div, _ptr(w), _ptr(w_scales), _ptr(counts),
+                                  _ptr(offsets), num_experts, row_cap, max_rows_per_expert, n, k,
+                                  _ptr(out), _ptr(tiles_visited), _stream())
+    _check("moe_grouped_gemm_fp8", st)
+    return out
+
+
+def moe_silu_mul_quant(gate_up, counts, offsets, act="swiglu", clamp_limit=float("inf"),
+                       fmt="fp32", hq=None, hs=None):
+    """SiLU(gate)*up + 1x128 FP8 quantization of live rows.
+    Returns (hq uint8 [row_cap, I], hs [I/128, row_cap])."""
+    lib = load_library()
+    gu = _bf16_view(gate_up, "gate_up")
+    row_cap, two_i = gu.shape
+    inter = two_i // 2
+    num_experts = counts.shape[0]
+    if hq is None:
+        hq = torch.empty((row_cap, inter), dtype=torch.uint8, device=gu.device)
+    if hs is None:
+        hs = torch.empty((inter // 128, row_cap), dtype=_scale_dtype(fmt), device=gu.device)
+    _need(hq, "hq", torch.uint8)
+    _need(hs, "hs", _scale_dtype(fmt))
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {list(ACTS)}")
+    st = lib.moe_silu_mul_quant(_ptr(gu), inter, _ptr(counts), _ptr(offsets), num_experts,
+                                row_cap, ACTS[act], float(clamp_limit), _fmt(fmt), _ptr(hq),
+                                _ptr(hs), _stream())
+    _check("moe_silu_mul_quant", st)
+    return hq, hs
+
+
+def moe_topk_combine(y, pair_to_row, topk_w, t_live=None, out=None):
+    """Top-k weighted sum of expert rows. Returns BF16 bits (int16) [t_cap, H]."""
+    lib = load_library()
+    yb = _bf16_view(y, "y")
+    row_cap, hidden = yb.shape
+    _need(pair_to_row, "pair_to_row", torch.int32)
+    w = _need(topk_w, "topk_w", torch.float32, ndim=2)
+    t_cap, topk = w.shape
+    if out is None:
+        out = torch.empty((t_cap, hidden), dtype=torch.int16, device=yb.device)
+    ob = _bf16_view(out, "out")
+    st = lib.moe_topk_combine(_ptr(yb), row_cap, _ptr(pair_to_row), _ptr(w), t_cap, _live(t_live),
+                              topk, hidden, _ptr(ob), _stream())
+    _check("moe_topk_combine", st)
+    return out
+
+
+def _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act, clamp_limit):
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {list(ACTS)}")
+    return _Problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap or 0, _fmt(fmt),
+                    ACTS[act], float(clamp_limit))
+
+
+def moe_workspace_plan(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
+                       fmt="fp32", act="swiglu", clamp_limit=float("inf")):
+    """Byte offsets of every intermediate in the forward workspace (dict)."""
+    lib = load_library()
+    prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
+                    clamp_limit)
+    lay = _Layout()
+    _check("moe_workspace_plan", lib.moe_workspace_plan(ctypes.byref(prob), ctypes.byref(lay)))
+    return {name: getattr(lay, name) for name, _ in _Layout._fields_}
+
+
+def moe_workspace_bytes(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
+                        fmt="fp32", act="swiglu", clamp_limit=float("inf")):
+    lib = load_library()
+    prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
+                    clamp_limit)
+    return int(lib.moe_workspace_bytes(ctypes.byref(prob)))
+
+
+def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", act="swiglu",
+                clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None, out=None,
+                workspace=None):
+    """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8)."""
+    lib = load_library()
+    xb = _bf16_view(x, "x")
+    t_cap, hidden = xb.shape
+    _need(topk_ids, "topk_ids", torch.int32, ndim=2)
+    _need(topk_w, "topk_w", torch.float32, ndim=2)
+    _need(w1, "w1", torch.uint8, ndim=3)
+    _need(w1_scales, "w1_scales", torch.float32, ndim=3)
+    _need(w2, "w2", torch.uint8, ndim=3)
+    _need(w2_scales, "w2_scales", torch.float32, ndim=3)
+    num_experts, two_i, h1 = w1.shape
+    topk = topk_ids.shape[1]
+    if h1 != hidden or tuple(w2.shape) != (num_experts, hidden, two_i // 2):
+        raise ValueError("weight shapes disagree with x")
+    prob = _problem(num_experts, hidden, two_i // 2, topk, t_cap, align_rows, row_cap, fmt, act,
+                    clamp_limit)
+    need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
+    if need == 0:
+        lay = _Layout()
+        _check("moe_workspace_plan", lib.moe_workspace_plan(ctypes.byref(prob), ctypes.byref(lay)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xb.device)
+    _need(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((t_cap, hidden), dtype=torch.int16, device=xb.device)
+    ob = _bf16_view(out, "out")
+    tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
+                    _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
+    st = lib.moe_forward(ctypes.byref(prob), ctypes.byref(tens), _ptr(workspace),
+                         workspace.numel(), _stream())
+    _check("moe_forward", st)
+    return out, workspace

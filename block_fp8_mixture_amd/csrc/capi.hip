@@ -1,0 +1,282 @@
+// C ABI of libmoefp8: host-side validation, workspace planning and the
+// launch sequence of the expert layer. Nothing here allocates or
+// synchronizes; every argument is checked before the first HIP call, so an
+// invalid request returns an error with nothing enqueued.
+#include <atomic>
+#include <climits>
+
+#include "../../include/moe_fp8.h"
+#include "kernels.h"
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace moe
+
+namespace {
+
+constexpr int kMaxTopk = 64;
+
+bool fmt_ok(int f) { return f == MOE_SCALE_FP32 || f == MOE_SCALE_FP32_POW2 || f == MOE_SCALE_UE8M0; }
+bool act_ok(int a) {
+  return a == MOE_ACT_SWIGLU || a == MOE_ACT_SWIGLU_CLAMP || a == MOE_ACT_SWIGLU_CLAMP_AFTER_SILU;
+}
+bool dim128(int32_t d) { return d > 0 && d % 128 == 0; }
+size_t scale_bytes(int fmt) { return fmt == MOE_SCALE_UE8M0 ? 1 : 4; }
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int64_t min_row_cap64(int64_t t_cap, int64_t topk, int64_t num_experts, int64_t align_rows) {
+  const int64_t pairs = t_cap * topk;
+  return pairs + (num_experts < pairs ? num_experts : pairs) * (align_rows - 1);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_min_row_cap(int32_t t_cap, int32_t topk, int32_t num_experts, int32_t align_rows) {
+  if (t_cap < 0 || topk < 1 || num_experts < 1 || align_rows < 1) return -1;
+  const int64_t v = min_row_cap64(t_cap, topk, num_experts, align_rows);
+  return v > INT32_MAX ? -1 : static_cast<int32_t>(v);
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_CAPACITY: return "capacity too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
+                     int32_t topk, int32_t num_experts, int32_t align_rows, int32_t row_cap,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_pair,
+                     int32_t* pair_to_row, void* stream) {
+  if (t_cap < 0 || topk < 1 || topk > kMaxTopk || num_experts < 1 || align_rows < 1 || row_cap < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(t_cap) * topk > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (t_cap > 0 && (!topk_ids || !row_to_pair || !pair_to_row)) return MOE_ERR_INVALID_ARG;
+  if (row_cap < min_row_cap64(t_cap, topk, num_experts, align_rows)) return MOE_ERR_CAPACITY;
+  return from_hip(moe::launch_align(topk_ids, t_cap, t_live_dev, topk, num_experts, align_rows,
+                                    expert_counts, expert_offsets, row_to_pair, pair_to_row,
+                                    as_stream(stream)));
+}
+
+moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live_dev,
+                         int32_t hidden, moe_scale_fmt fmt, uint8_t* xq, void* xs, void* stream) {
+  if (t_cap < 0 || !dim128(hidden) || !fmt_ok(fmt)) return MOE_ERR_INVALID_ARG;
+  if (t_cap > 0 && (!x || !xq || !xs)) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(t_cap) * (hidden / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (t_cap == 0) return MOE_OK;
+  return from_hip(moe::launch_act_quant(x, t_cap, t_live_dev, hidden, fmt, xq, xs,
+                                        as_stream(stream)));
+}
+
+static moe_status gemm_checked(const moe::GemmArgs& g, void* stream) {
+  if (!dim128(g.n) || !dim128(g.k) || !fmt_ok(g.fmt) || g.a_rows < 0 || g.a_row_div < 1 ||
+      g.num_experts < 1 || g.row_cap < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (g.num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!g.counts || !g.offsets || !g.w || !g.w_scales) return MOE_ERR_INVALID_ARG;
+  if (g.row_cap > 0 && (!g.c || !g.a || !g.a_scales)) return MOE_ERR_INVALID_ARG;
+  if (g.row_cap == 0) return MOE_OK;
+  return from_hip(moe::launch_grouped_gemm(g, as_stream(stream)));
+}
+
+moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                const uint8_t* w, const float* w_scales,
+                                const int32_t* expert_counts, const int32_t* expert_offsets,
+                                int32_t num_experts, int32_t row_cap, int32_t max_rows_per_expert,
+                                int32_t n, int32_t k, uint16_t* c, int32_t* tiles_visited,
+                                void* stream) {
+  if (max_rows_per_expert < 0) return MOE_ERR_INVALID_ARG;
+  moe::GemmArgs g;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.fmt = fmt;
+  g.a_rows = a_rows;
+  g.a_row_map = a_row_map;
+  g.a_row_div = a_row_div;
+  g.w = w;
+  g.w_scales = w_scales;
+  g.counts = expert_counts;
+  g.offsets = expert_offsets;
+  g.num_experts = num_experts;
+  g.row_cap = row_cap;
+  g.max_rows_per_expert =
+      (max_rows_per_expert == 0 || max_rows_per_expert > row_cap) ? row_cap : max_rows_per_expert;
+  g.max_live_experts = row_cap < num_experts ? row_cap : num_experts;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  g.tiles_visited = tiles_visited;
+  return gemm_checked(g, stream);
+}
+
+moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
+                              const int32_t* expert_counts, const int32_t* expert_offsets,
+                              int32_t num_experts, int32_t row_cap, moe_act act,
+                              float clamp_limit, moe_scale_fmt fmt, uint8_t* hq, void* hs,
+                              void* stream) {
+  if (!dim128(inter) || num_experts < 1 || row_cap < 0 || !fmt_ok(fmt) || !act_ok(act))
+    return MOE_ERR_INVALID_ARG;
+  if (act != MOE_ACT_SWIGLU && !(clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (row_cap > 0 && (!gate_up || !hq || !hs)) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(row_cap) * (inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (row_cap == 0) return MOE_OK;
+  return from_hip(moe::launch_silu_mul_quant(gate_up, inter, expert_counts, expert_offsets,
+                                             num_experts, row_cap, act, clamp_limit, fmt, hq,
+                                             hs, as_stream(stream)));
+}
+
+moe_status moe_topk_combine(const uint16_t* y, int32_t row_cap, const int32_t* pair_to_row,
+                            const float* topk_w, int32_t t_cap, const int32_t* t_live_dev,
+                            int32_t topk, int32_t hidden, uint16_t* out, void* stream) {
+  if (row_cap < 0 || t_cap < 0 || topk < 1 || topk > kMaxTopk || !dim128(hidden))
+    return MOE_ERR_INVALID_ARG;
+  if (t_cap > 0 && (!pair_to_row || !topk_w || !out || (row_cap > 0 && !y)))
+    return MOE_ERR_INVALID_ARG;
+  if (t_cap == 0) return MOE_OK;
+  return from_hip(moe::launch_topk_combine(y, row_cap, pair_to_row, topk_w, t_cap, t_live_dev,
+                                           topk, hidden, out, as_stream(stream)));
+}
+
+moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
+  if (!p || !L) return MOE_ERR_INVALID_ARG;
+  if (p->num_experts < 1 || !dim128(p->hidden) || !dim128(p->inter) || p->topk < 1 ||
+      p->topk > kMaxTopk || p->t_cap < 0 || p->align_rows < 1 || p->row_cap < 0 ||
+      !fmt_ok(p->scale_fmt) || !act_ok(p->act))
+    return MOE_ERR_INVALID_ARG;
+  if (p->act != MOE_ACT_SWIGLU && !(p->clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (p->num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  const int64_t need = min_row_cap64(p->t_cap, p->topk, p->num_experts, p->align_rows);
+  if (need > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
+  const int64_t rc = p->row_cap == 0 ? need : p->row_cap;
+  if (rc < need) return MOE_ERR_CAPACITY;
+  const size_t E = p->num_experts, H = p->hidden, I = p->inter, T = p->t_cap;
+  const size_t R = static_cast<size_t>(rc), P = T * p->topk, sb = scale_bytes(p->scale_fmt);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->expert_counts = take(E * 4);
+  L->expert_offsets = take((E + 1) * 4);
+  L->row_to_pair = take(R * 4);
+  L->pair_to_row = take(P * 4);
+  L->xq = take(T * H);
+  L->xs = take((H / 128) * T * sb);
+  L->c1 = take(R * 2 * I * 2);
+  L->hq = take(R * I);
+  L->hs = take((I / 128) * R * sb);
+  L->y = take(R * H * 2);
+  L->total = off;
+  L->row_cap = static_cast<int32_t>(rc);
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_problem* p) {
+  moe_workspace_layout L;
+  return moe_workspace_plan(p, &L) == MOE_OK ? L.total : 0;
+}
+
+moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  moe_workspace_layout L;
+  const moe_status st = moe_workspace_plan(p, &L);
+  if (st != MOE_OK) return st;
+  if (!t || !workspace) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
+  if (p->t_cap > 0 && (!t->x || !t->topk_ids || !t->topk_w || !t->w1 || !t->w1_scales ||
+                       !t->w2 || !t->w2_scales || !t->out))
+    return MOE_ERR_INVALID_ARG;
+  if (p->t_cap == 0) return MOE_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* counts = reinterpret_cast<int32_t*>(ws + L.expert_counts);
+  auto* offsets = reinterpret_cast<int32_t*>(ws + L.expert_offsets);
+  auto* r2p = reinterpret_cast<int32_t*>(ws + L.row_to_pair);
+  auto* p2r = reinterpret_cast<int32_t*>(ws + L.pair_to_row);
+  auto* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  void* xs = ws + L.xs;
+  auto* c1 = reinterpret_cast<uint16_t*>(ws + L.c1);
+  auto* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+  void* hs = ws + L.hs;
+  auto* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  const hipStream_t s = as_stream(stream);
+  const int R = L.row_cap;
+  const int64_t pairs64 = static_cast<int64_t>(p->t_cap) * p->topk;
+  const int pairs = static_cast<int>(pairs64);
+
+  hipError_t e = moe::launch_align(t->topk_ids, p->t_cap, t->t_live_dev, p->topk,
+                                   p->num_experts, p->align_rows, counts, offsets, r2p, p2r, s);
+  if (e == hipSuccess)
+    e = moe::launch_act_quant(t->x, p->t_cap, t->t_live_dev, p->hidden, p->scale_fmt, xq, xs, s);
+
+  moe::GemmArgs g;
+  g.fmt = p->scale_fmt;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.num_experts = p->num_experts;
+  g.row_cap = R;
+  g.max_rows_per_expert = pairs < R ? pairs : R;
+  g.max_live_experts = pairs < p->num_experts ? pairs : p->num_experts;
+  g.tiles_visited = nullptr;
+  if (e == hipSuccess) {  // FC1: A rows gathered from the token-major quantized activations
+    g.a = xq;
+    g.a_scales = xs;
+    g.a_rows = p->t_cap;
+    g.a_row_map = r2p;
+    g.a_row_div = p->topk;
+    g.w = t->w1;
+    g.w_scales = t->w1_scales;
+    g.n = 2 * p->inter;
+    g.k = p->hidden;
+    g.c = c1;
+    e = moe::launch_grouped_gemm(g, s);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_silu_mul_quant(c1, p->inter, counts, offsets, p->num_experts, R, p->act,
+                                   p->clamp_limit, p->scale_fmt, hq, hs, s);
+  if (e == hipSuccess) {  // FC2
+    g.a = hq;
+    g.a_scales = hs;
+    g.a_rows = R;
+    g.a_row_map = nullptr;
+    g.a_row_div = 1;
+    g.w = t->w2;
+    g.w_scales = t->w2_scales;
+    g.n = p->hidden;
+    g.k = p->inter;
+    g.c = y;
+    e = moe::launch_grouped_gemm(g, s);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_topk_combine(y, R, p2r, t->topk_w, p->t_cap, t->t_live_dev, p->topk,
+                                 p->hidden, t->out, s);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,268 @@
+/*
+ * moe_fp8.h -- C ABI of the block-scaled FP8 mixture-of-experts expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (vLLM PR #59128 "Skip padded work in block-FP8 DeepGemmExperts",
+ * Purpose and SM100-on-B200 sections; TensorRT-LLM PR #21250 "Triton
+ * FP8-activation MoE for decode-sized batches on Hopper", description):
+ *
+ *   moe_align          top-k routing -> per-expert contiguous rows, prefix-sum endpoints
+ *   moe_act_quant      BF16 tokens -> FP8 E4M3 codes + one scale per 1x128 group
+ *   moe_grouped_gemm_fp8  FP8 x FP8 grouped GEMM with 128x128 fp32 weight block
+ *                      scales, visiting only tiles that hold live rows
+ *   moe_silu_mul_quant SiLU(gate) * up, quantized to FP8 the same way (FC2 input)
+ *   moe_topk_combine   top-k weighted sum of the expert outputs back to tokens, BF16
+ *   moe_forward        all of the above on one stream
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device (or managed) memory owned by the
+ *   caller. The library never allocates, frees or synchronizes; all work is
+ *   enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *   call returns without waiting. Every call is capturable into a HIP graph.
+ * - Arguments are validated on the host before anything is enqueued. On any
+ *   error nothing is launched and nothing is written. A launch failure
+ *   reported by the HIP runtime returns MOE_ERR_HIP.
+ * - Matrices are row-major and densely packed unless stated otherwise.
+ *   BF16 values are passed as uint16_t bit patterns; FP8 values are OCP E4M3
+ *   ("E4M3FN": bias 7, max 448, no infinities) bytes.
+ * - Activation scales are stored group-major: scale of row r, 128-wide group
+ *   g lives at index g * ld + r, where ld is the row capacity of that buffer.
+ *   MOE_SCALE_FP32 and MOE_SCALE_FP32_POW2 store float; MOE_SCALE_UE8M0
+ *   stores one uint8_t biased exponent (scale = 2^(byte - 127)).
+ * - The live token count may live on the device (`t_live_dev`, one int32),
+ *   so a captured graph can replay with a different count. It is clamped to
+ *   [0, t_cap]; NULL means t_cap.
+ * - "Untouched": rows past the last expert endpoint, pad rows inside an
+ *   expert segment (except row_to_pair, which marks them -1), and output rows
+ *   of tokens t >= t_live are never written (vLLM PR #59128, SM100 on B200:
+ *   untouched gaps; SM90 on H200: unused output capacity left untouched).
+ */
+#ifndef MOE_FP8_H_
+#define MOE_FP8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* bad size, null pointer, unknown enum value */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_CAPACITY = 3,    /* row_cap (or a workspace) too small */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported an error */
+} moe_status;
+
+/* Activation scale formats (vLLM PR #59128, Purpose: packed UE8M0 on one
+ * architecture, plain or power-of-two-rounded fp32 on the other; vLLM PR
+ * #65794, Overview). Power-of-two rounding rounds up. */
+typedef enum {
+  MOE_SCALE_FP32 = 0,
+  MOE_SCALE_FP32_POW2 = 1,
+  MOE_SCALE_UE8M0 = 2
+} moe_scale_fmt;
+
+/* Gated activations (TensorRT-LLM PR #21250, Test Coverage: no clamp, clamp,
+ * clamp after SiLU; vLLM PR #65794, Details: clamp_limit). With limit L:
+ *   SWIGLU                   y = silu(g) * u
+ *   SWIGLU_CLAMP             y = silu(min(g, L)) * clamp(u, -L, L)
+ *   SWIGLU_CLAMP_AFTER_SILU  y = min(silu(g), L) * clamp(u, -L, L)          */
+typedef enum {
+  MOE_ACT_SWIGLU = 0,
+  MOE_ACT_SWIGLU_CLAMP = 1,
+  MOE_ACT_SWIGLU_CLAMP_AFTER_SILU = 2
+} moe_act;
+
+/* Smallest row capacity that holds any routing of t_cap tokens with top-k:
+ * every pair plus (align_rows - 1) pad rows for each expert that can be in
+ * use. Returns -1 if the arguments are invalid or the value overflows int32. */
+int32_t moe_min_row_cap(int32_t t_cap, int32_t topk, int32_t num_experts, int32_t align_rows);
+
+/* Routing alignment (vLLM PR #59128, Purpose: a shared permutation helper
+ * produces the expert endpoints both GEMMs and the activation quantization
+ * consume; TensorRT-LLM PR #21250, sequence diagram: padded expert blocks and
+ * sorted token ids; review comment on expert parallelism: ids outside the
+ * local range are dropped).
+ *
+ *   topk_ids      device int32 [t_cap, topk]; ids outside [0, num_experts)
+ *                 are dropped (their pair maps to row -1)
+ *   t_live_dev    device int32 scalar or NULL (see conventions)
+ *   align_rows    >= 1; each expert's row count is rounded up to a multiple
+ *   row_cap       rows available; must be >= moe_min_row_cap(...)
+ * Outputs (device int32):
+ *   expert_counts [num_experts]      live pairs per expert
+ *   expert_offsets[num_experts + 1]  exclusive prefix sum of the rounded-up
+ *                                    counts; segment e = [off[e], off[e+1])
+ *   row_to_pair   [row_cap]  pair index p = t*topk + k of each live row, in
+ *                            ascending p within a segment; -1 on pad rows;
+ *                            rows >= off[E] untouched
+ *   pair_to_row   [t_cap*topk]  row of each pair of a live token, -1 when
+ *                            dropped; entries of tokens >= t_live untouched
+ * Errors: INVALID_ARG (sizes, null pointers), CAPACITY (row_cap too small). */
+moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
+                     int32_t topk, int32_t num_experts, int32_t align_rows, int32_t row_cap,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_pair,
+                     int32_t* pair_to_row, void* stream);
+
+/* Per-1x128 FP8 E4M3 activation quantization of the live tokens (vLLM PR
+ * #65794, Details: scale = max(amax / 448, 1 / (448 * 512)), then x / scale,
+ * both IEEE float32 divisions, round to nearest even, saturating at 448;
+ * TensorRT-LLM PR #21250, description: per-1x128 activation quantization).
+ * Tokens are quantized once each; the FC1 GEMM gathers them through
+ * row_to_pair, so routed copies are never materialized.
+ *
+ *   x     device BF16 [t_cap, hidden]
+ *   xq    device uint8 [t_cap, hidden]; rows t >= t_live untouched
+ *   xs    device scales [hidden/128][t_cap] (float or uint8, per `fmt`)
+ * Errors: INVALID_ARG (hidden not a positive multiple of 128, null pointers,
+ * unknown fmt). */
+moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live_dev,
+                         int32_t hidden, moe_scale_fmt fmt, uint8_t* xq, void* xs,
+                         void* stream);
+
+/* Grouped FP8 x FP8 GEMM with per-block scales, over the live rows of every
+ * expert segment only (vLLM PR #59128, Purpose and SM90-on-H200: both grouped
+ * GEMMs skip unused whole tiles through the prefix-sum endpoints; TensorRT-LLM
+ * PR #21250, description: FP8 x FP8 GEMMs with 128x128 weight scales whose
+ * grid covers only the expert blocks the batch occupies).
+ *
+ * For every expert e and live row r in [off[e], off[e] + counts[e]):
+ *   C[r, n] = bf16( sum_kb sa[kb, ar] * ws[e, n/128, kb] * sum_{j<128} A[ar, kb*128+j] * W[e, n, kb*128+j] )
+ * with ar = a_row_map ? a_row_map[r] / a_row_div : r, accumulated in fp32
+ * and rounded to nearest even BF16.
+ *
+ *   a           device uint8 [a_rows, k]
+ *   a_scales    device [k/128][a_rows] in format `fmt`
+ *   a_row_map   device int32 [row_cap] or NULL (identity); entries read only
+ *               for live rows; must satisfy 0 <= a_row_map[r]/a_row_div < a_rows
+ *   w           device uint8 [num_experts, n, k]; w_scales float [num_experts, n/128, k/128]
+ *   expert_counts/expert_offsets  as produced by moe_align (device)
+ *   max_rows_per_expert  host-side bound on any counts[e] (0 = row_cap); it
+ *               only selects which kernels are launched, never the result
+ *   c           device BF16 [row_cap, n]; only live rows written
+ *   tiles_visited  device int32 or NULL; when given, the number of
+ *               (row tile, column tile) pairs computed is ADDED to it
+ * Errors: INVALID_ARG (n or k not positive multiples of 128, null pointers,
+ * a_row_div < 1, unknown fmt). */
+moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                const uint8_t* w, const float* w_scales,
+                                const int32_t* expert_counts, const int32_t* expert_offsets,
+                                int32_t num_experts, int32_t row_cap, int32_t max_rows_per_expert,
+                                int32_t n, int32_t k, uint16_t* c, int32_t* tiles_visited,
+                                void* stream);
+
+/* Row-tile heights of the two GEMM kernels, for interpreting tiles_visited:
+ * experts with at most MOE_GEMM_STREAM_MAX_ROWS live rows are computed by
+ * the weight-streaming kernel in row tiles of MOE_GEMM_STREAM_TILE_M, larger
+ * ones by the MFMA-tiled kernel in row tiles of MOE_GEMM_TILED_TILE_M; column
+ * tiles are MOE_GEMM_COL_TILE wide in both. */
+#define MOE_GEMM_STREAM_TILE_M 16
+#define MOE_GEMM_STREAM_MAX_ROWS 64
+#define MOE_GEMM_TILED_TILE_M 128
+#define MOE_GEMM_COL_TILE 128
+
+/* Fused SiLU(gate) * up + 1x128 FP8 quantization of the FC2 input, over live
+ * rows only (vLLM PR #59128, Purpose: the fused activation quantization
+ * consumes the live expert endpoints; vLLM PR #65794, Details: fp32
+ * SiLU * up without an intermediate BF16 rounding, then the quantization
+ * rule above, with use_ue8m0 and clamp_limit options).
+ * Gate is columns [0, inter) of each row, up is [inter, 2*inter). SiLU and
+ * the product are evaluated in double precision and rounded once to float.
+ *
+ *   gate_up  device BF16 [row_cap, 2*inter]
+ *   hq       device uint8 [row_cap, inter]; hs device [inter/128][row_cap]
+ *   clamp_limit  used by the clamp variants; must be > 0 there
+ * Errors: INVALID_ARG. */
+moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
+                              const int32_t* expert_counts, const int32_t* expert_offsets,
+                              int32_t num_experts, int32_t row_cap, moe_act act,
+                              float clamp_limit, moe_scale_fmt fmt, uint8_t* hq, void* hs,
+                              void* stream);
+
+/* Top-k weighted unpermute/sum (TensorRT-LLM PR #21250, rounding-fix commit:
+ * the routing weights scale the BF16 expert outputs in fp32 in the top-k sum,
+ * not the FC2 accumulators). For each live token t:
+ *   out[t, :] = bf16( sum over k ascending with pair_to_row[t*topk+k] in
+ *                     [0, row_cap) of topk_w[t, k] * y[row, :] )
+ * accumulated in fp32; a token with no valid pair gets zeros.
+ *
+ *   y        device BF16 [row_cap, hidden]; pair_to_row device int32 [t_cap*topk]
+ *   topk_w   device float [t_cap, topk]
+ *   out      device BF16 [t_cap, hidden]; rows t >= t_live untouched
+ * Errors: INVALID_ARG. */
+moe_status moe_topk_combine(const uint16_t* y, int32_t row_cap, const int32_t* pair_to_row,
+                            const float* topk_w, int32_t t_cap, const int32_t* t_live_dev,
+                            int32_t topk, int32_t hidden, uint16_t* out, void* stream);
+
+/* ---- whole layer ---------------------------------------------------------- */
+
+typedef struct {
+  int32_t num_experts;
+  int32_t hidden;       /* H, multiple of 128 */
+  int32_t inter;        /* I, multiple of 128 */
+  int32_t topk;
+  int32_t t_cap;        /* token capacity */
+  int32_t align_rows;   /* per-expert row alignment, >= 1 */
+  int32_t row_cap;      /* 0 = moe_min_row_cap(t_cap, topk, num_experts, align_rows) */
+  moe_scale_fmt scale_fmt;
+  moe_act act;
+  float clamp_limit;
+} moe_problem;
+
+typedef struct {
+  const uint16_t* x;          /* BF16 [t_cap, H] */
+  const int32_t* topk_ids;    /* [t_cap, topk] */
+  const float* topk_w;        /* [t_cap, topk] */
+  const int32_t* t_live_dev;  /* scalar or NULL */
+  const uint8_t* w1;          /* [E, 2I, H]: gate rows [0, I), up rows [I, 2I) */
+  const float* w1_scales;     /* [E, 2I/128, H/128] */
+  const uint8_t* w2;          /* [E, H, I] */
+  const float* w2_scales;     /* [E, H/128, I/128] */
+  uint16_t* out;              /* BF16 [t_cap, H]; rows >= t_live untouched */
+} moe_tensors;
+
+/* Byte offsets of the intermediates inside the forward workspace (each
+ * 256-byte aligned), so callers and tests can inspect them. */
+typedef struct {
+  size_t expert_counts;  /* int32 [E] */
+  size_t expert_offsets; /* int32 [E+1] */
+  size_t row_to_pair;    /* int32 [row_cap] */
+  size_t pair_to_row;    /* int32 [t_cap*topk] */
+  size_t xq;             /* uint8 [t_cap, H] */
+  size_t xs;             /* scales [H/128][t_cap] */
+  size_t c1;             /* BF16 [row_cap, 2I] */
+  size_t hq;             /* uint8 [row_cap, I] */
+  size_t hs;             /* scales [I/128][row_cap] */
+  size_t y;              /* BF16 [row_cap, H] */
+  size_t total;          /* bytes required */
+  int32_t row_cap;       /* effective row capacity */
+} moe_workspace_layout;
+
+/* Fills `layout` for problem `p`. Errors: INVALID_ARG, CAPACITY. */
+moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* layout);
+
+/* Bytes of workspace moe_forward needs for `p` (0 if `p` is invalid). */
+size_t moe_workspace_bytes(const moe_problem* p);
+
+/* The whole expert layer: align -> act_quant -> FC1 -> silu_mul_quant -> FC2
+ * -> topk_combine, enqueued on one stream with no host synchronization
+ * (vLLM PR #59128, SM100 on B200: the full-expert benchmark scope; the layer
+ * replays inside a captured graph with the token count on the device).
+ * `workspace` is device memory of at least moe_workspace_bytes(p) bytes, laid
+ * out as moe_workspace_plan describes; its prior contents do not matter.
+ * Errors: INVALID_ARG, CAPACITY (workspace or row_cap too small), HIP. */
+moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H_ */

@@ -1,0 +1,289 @@
+"""End-to-end parity of moe_forward on the five workloads, plus the layer's
+invariants: graph replay with changing routing and live count, poisoned
+workspaces, untouched capacity, and independence from alignment/capacity.
+
+Checks per run:
+* alignment and per-token FP8 codes/scales read back from the workspace are
+  bit-exact against the oracle on every live pair/token;
+* each later stage is checked on sampled live rows against the oracle applied
+  to the GPU's own inputs to that stage (bit-exact for silu_mul_quant,
+  tolerance for the GEMMs and the combine);
+* the final output of sampled tokens is within tolerance of the oracle's
+  dense per-token evaluation of the whole layer.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_amd as moe
+import oracle
+import synth
+from tests.gpu_helpers import (POISON_BF16, POISON_U8, assert_bf16_close, dev, device_weights,
+                               down, host_weights, say, up)
+
+pytestmark = pytest.mark.gpu
+
+INF = float("inf")
+
+
+def _ws_view(ws, lay, name, dtype, shape):
+    nbytes = int(np.prod(shape)) * np.dtype(dtype).itemsize
+    raw = ws[lay[name]:lay[name] + nbytes].cpu().numpy()
+    return raw.view(dtype).reshape(shape)
+
+
+def _sample(n, k, seed):
+    if n <= k:
+        return np.arange(n)
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], g.choice(n, k - 2, replace=False)]))
+
+
+def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_tok=8,
+                  n_rows=16):
+    cfg = synth.get(name)
+    say(f"forward {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act} lim={lim}")
+    E, H, I, K, A = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, cfg.align_rows
+    x, ids, w = synth.make_workload(cfg, t_cap, variant)
+    (w1q, w1s), (w2q, w2s) = host_weights(name)
+    d_w1q, d_w1s, d_w2q, d_w2s = device_weights(name)
+    lim32 = float(np.float32(lim))
+    out = torch.full((t_cap, H), POISON_BF16, dtype=torch.int16, device=dev())
+    row_cap = cfg.row_cap or 0
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32)
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    moe.moe_forward(up(x), up(ids), up(w), d_w1q, d_w1s, d_w2q, d_w2s, fmt, act, lim32, A,
+                    row_cap, t_live=up(np.array([t_live], np.int32)), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    R = lay["row_cap"]
+    sdt = np.uint8 if fmt == "ue8m0" else np.float32
+
+    # alignment: bit-exact
+    al = oracle.align(ids, t_live, E, A)
+    counts = _ws_view(ws, lay, "expert_counts", np.int32, (E,))
+    offsets = _ws_view(ws, lay, "expert_offsets", np.int32, (E + 1,))
+    r2p = _ws_view(ws, lay, "row_to_pair", np.int32, (R,))
+    p2r = _ws_view(ws, lay, "pair_to_row", np.int32, (t_cap * K,))
+    assert np.array_equal(counts, al["counts"]) and np.array_equal(offsets, al["offsets"])
+    total = int(offsets[-1])
+    assert np.array_equal(r2p[:total], al["row_to_pair"])
+    assert np.array_equal(p2r[:t_live * K], al["pair_to_row"])
+
+    # per-token activation quantization: bit-exact
+    xq = _ws_view(ws, lay, "xq", np.uint8, (t_cap, H))
+    xs = _ws_view(ws, lay, "xs", sdt, (H // 128, t_cap))
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    assert np.array_equal(xq[:t_live], rq)
+    assert np.array_equal(np.ascontiguousarray(xs[:, :t_live]).view(np.uint8),
+                          np.ascontiguousarray(rs).view(np.uint8))
+
+    c1 = _ws_view(ws, lay, "c1", np.uint16, (R, 2 * I))
+    hq = _ws_view(ws, lay, "hq", np.uint8, (R, I))
+    hs = _ws_view(ws, lay, "hs", sdt, (I // 128, R))
+    y = _ws_view(ws, lay, "y", np.uint16, (R, H))
+    sa_x = oracle.scales_to_f64(xs, fmt)
+    sa_h = oracle.scales_to_f64(hs, fmt)
+    g = np.random.default_rng(1)
+    live_experts = np.flatnonzero(al["counts"] > 0)
+    for e in g.permutation(live_experts)[:3]:
+        seg = np.arange(al["offsets"][e], al["offsets"][e] + al["counts"][e])
+        rows = seg[_sample(len(seg), n_rows, int(e))]
+        tok = al["row_to_pair"][rows] // K
+        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e])
+        assert_bf16_close(c1[rows], ref_c1, f"FC1 expert {e}")
+        rhq, rhs = oracle.silu_mul_quant(c1[rows], fmt, act, lim32)
+        assert np.array_equal(hq[rows], rhq)
+        assert np.array_equal(np.ascontiguousarray(hs[:, rows]).view(np.uint8),
+                              np.ascontiguousarray(rhs).view(np.uint8))
+        ref_y = oracle.moe.gemm_rows(hq[rows], sa_h[:, rows], w2q[e], w2s[e])
+        assert_bf16_close(y[rows], ref_y, f"FC2 expert {e}")
+
+    got = down(out)
+    assert np.all(got[t_live:] == POISON_BF16), "rows of tokens past the live count were written"
+    toks = _sample(t_live, n_tok, 2)
+    if len(toks):
+        # combine of the GPU's own expert outputs
+        p2r_s = p2r[:t_live * K].reshape(t_live, K)[toks].reshape(-1)
+        ref_comb = oracle.combine(y, p2r_s, w[toks], len(toks), H)
+        assert_bf16_close(got[toks], ref_comb, "combine")
+        # whole layer against the dense per-token oracle
+        ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, t_live, fmt, act, lim32,
+                                   tokens=toks)
+        err = assert_bf16_close(got[toks], ref, "layer")
+        say(f"  layer max err / max|ref| = {err:.3e}")
+    return got, ws, lay
+
+
+CONFIG_RUNS = [
+    ("tiny", 8, 8, "fp32", "swiglu", INF),
+    ("tiny", 8, 5, "ue8m0", "swiglu", INF),
+    ("tiny", 8, 8, "pow2", "swiglu_clamp", 0.25),
+    ("decode", 1, 1, "fp32", "swiglu", INF),
+    ("decode", 4, 4, "fp32", "swiglu", INF),
+    ("decode", 4, 4, "fp32", "swiglu_clamp", 7.0),
+    ("decode", 4, 4, "fp32", "swiglu_clamp_after_silu", 7.0),
+    ("padded", 512, 16, "ue8m0", "swiglu", INF),
+    ("padded", 512, 16, "fp32", "swiglu", INF),
+    ("full", 4096, 4096, "fp32", "swiglu", INF),
+    ("full", 4096, 4096, "ue8m0", "swiglu", INF),
+    ("sweep", 1, 1, "fp32", "swiglu", INF),
+    ("sweep", 8, 8, "pow2", "swiglu", INF),
+    ("sweep", 64, 64, "fp32", "swiglu", INF),
+    ("sweep", 256, 256, "pow2", "swiglu", INF),
+    ("sweep", 1024, 1024, "fp32", "swiglu", INF),
+    ("sweep", 4096, 4096, "fp32", "swiglu", INF),
+    ("sweep", 4096, 4096, "pow2", "swiglu", INF),
+]
+
+
+@pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim", CONFIG_RUNS)
+def test_forward_matches_oracle(name, t_cap, t_live, fmt, act, lim):
+    run_and_check(name, t_cap, t_live, fmt, act, lim)
+
+
+def test_forward_forced_clamp_on_decode_shape():
+    """Inputs scaled so that the FC1 outputs exceed the limit of 7.0."""
+    cfg = synth.get("decode")
+    x = synth.make_tokens(cfg, 4, scale=8.0)
+    ids, w = synth.make_routing(cfg, 4)
+    (w1q, w1s), (w2q, w2s) = host_weights("decode")
+    d = device_weights("decode")
+    out, _ = moe.moe_forward(up(x), up(ids), up(w), *d, "fp32", "swiglu_clamp", 7.0, 16)
+    torch.cuda.synchronize()
+    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), cfg.num_experts, 4, "fp32",
+                               "swiglu_clamp", 7.0)
+    plain = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), cfg.num_experts, 4, "fp32")
+    assert not np.array_equal(ref, plain)
+    assert_bf16_close(down(out), ref, "forced clamp")
+
+
+def _forward(x, ids, w, name, fmt="fp32", align=16, row_cap=0, t_live=None, ws_fill=None):
+    cfg = synth.get(name)
+    d = device_weights(name)
+    ws = None
+    if ws_fill is not None:
+        n = moe.moe_workspace_bytes(cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, x.shape[0],
+                                    align, row_cap, fmt)
+        ws = torch.full((n,), ws_fill, dtype=torch.uint8, device=dev())
+    out, _ = moe.moe_forward(up(x), up(ids), up(w), *d, fmt, "swiglu", INF, align, row_cap,
+                             t_live=None if t_live is None else up(np.array([t_live], np.int32)),
+                             workspace=ws)
+    torch.cuda.synchronize()
+    return down(out)
+
+
+def test_output_independent_of_alignment_capacity_and_poison():
+    cfg = synth.get("padded")
+    x, ids, w = synth.make_workload(cfg, 512, 3)
+    base = _forward(x, ids, w, "padded", t_live=16)[:16]
+    for align, extra in [(1, 0), (64, 0), (16, 4000)]:
+        rc = moe.moe_min_row_cap(512, 8, 32, align) + extra
+        got = _forward(x, ids, w, "padded", align=align, row_cap=rc, t_live=16)[:16]
+        assert np.array_equal(got, base), (align, extra)
+    for fill in (0x00, 0xFF, 0x7F):
+        assert np.array_equal(_forward(x, ids, w, "padded", t_live=16, ws_fill=fill)[:16], base)
+
+
+def test_output_independent_of_token_order():
+    cfg = synth.get("decode")
+    x, ids, w = synth.make_workload(cfg, 4, 5)
+    base = _forward(x, ids, w, "decode")
+    perm = np.array([2, 0, 3, 1])
+    got = _forward(x[perm], ids[perm], w[perm], "decode")
+    assert np.array_equal(got, base[perm])
+
+
+def test_dropped_ids_and_empty_routing():
+    cfg = synth.get("tiny")
+    x, ids, w = synth.make_workload(cfg, 8, 6)
+    ids2 = ids.copy()
+    ids2[::2, 0] = -1
+    ids2[1, :] = cfg.num_experts  # every pair of token 1 dropped
+    (w1q, w1s), (w2q, w2s) = host_weights("tiny")
+    got = _forward(x, ids2, w, "tiny")
+    ref = oracle.token_forward(x, ids2, w, (w1q, w1s), (w2q, w2s), 4, 8, "fp32")
+    assert np.all(got[1] == 0)
+    assert_bf16_close(got, ref, "dropped ids")
+    out = torch.full((8, cfg.hidden), POISON_BF16, dtype=torch.int16, device=dev())
+    moe.moe_forward(up(x), up(ids), up(w), *device_weights("tiny"), t_live=up(np.array([0], np.int32)),
+                    out=out)
+    torch.cuda.synchronize()
+    assert np.all(down(out) == POISON_BF16)
+
+
+def test_graph_replay_with_changing_routing_and_live_count():
+    """Capture the layer once; replay it with new routing, tokens and live
+    counts written into the captured buffers (vLLM PR #59128, SM100 on B200:
+    graph replay with changing routing, one live row, empty routing and a
+    device token count)."""
+    name = "decode"
+    cfg = synth.get(name)
+    t_cap = 32
+    (w1q, w1s), (w2q, w2s) = host_weights(name)
+    d = device_weights(name)
+    x0, ids0, w0 = synth.make_workload(cfg, t_cap, 10)
+    sx, sids, sw = up(x0), up(ids0), up(w0)
+    st = up(np.array([t_cap], np.int32))
+    out = torch.zeros((t_cap, cfg.hidden), dtype=torch.int16, device=dev())
+    nbytes = moe.moe_workspace_bytes(cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, t_cap, 16)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside capture
+        moe.moe_forward(sx, sids, sw, *d, t_live=st, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe.moe_forward(sx, sids, sw, *d, t_live=st, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for variant, t_live in [(11, 32), (12, 7), (13, 1), (14, 0), (15, 20)]:
+        say(f"  replay variant={variant} t_live={t_live}")
+        x, ids, w = synth.make_workload(cfg, t_cap, variant)
+        sx.copy_(up(x))
+        sids.copy_(up(ids))
+        sw.copy_(up(w))
+        st.fill_(t_live)
+        out.fill_(POISON_BF16)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = down(out)
+        assert np.all(got[t_live:] == POISON_BF16)
+        if t_live:
+            ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), cfg.num_experts,
+                                       t_live, "fp32")
+            assert_bf16_close(got[:t_live], ref, f"replay {variant}")
+            eager = _forward(x, ids, w, name, t_live=t_live)
+            assert np.array_equal(eager[:t_live], got[:t_live])
+
+
+def test_padded_tiles_are_skipped():
+    """On the 512-capacity / 16-live workload the FC1 GEMM visits exactly the
+    tiles that hold live rows, far fewer than the capacity holds."""
+    name = "padded"
+    cfg = synth.get(name)
+    x, ids, w = synth.make_workload(cfg, 512)
+    _, ws, lay = run_and_check(name, 512, 16, "fp32", n_tok=4, n_rows=8)
+    R, E, H, I = lay["row_cap"], cfg.num_experts, cfg.hidden, cfg.inter
+    d_w1q, d_w1s, _, _ = device_weights(name)
+
+    def view(nm, dt, n):
+        return ws[lay[nm]:lay[nm] + n * np.dtype(dt).itemsize].view(
+            torch.int32 if dt == np.int32 else torch.uint8)
+    counts = view("expert_counts", np.int32, E)
+    offsets = view("expert_offsets", np.int32, E + 1)
+    r2p = view("row_to_pair", np.int32, R)
+    xq = ws[lay["xq"]:lay["xq"] + 512 * H].view(512, H)
+    xs = ws[lay["xs"]:lay["xs"] + (H // 128) * 512 * 4].view(torch.float32).view(H // 128, 512)
+    c = torch.empty((R, 2 * I), dtype=torch.int16, device=dev())
+    tiles = torch.zeros(1, dtype=torch.int32, device=dev())
+    moe.moe_grouped_gemm_fp8(xq, xs, "fp32", d_w1q, d_w1s, counts, offsets, R, a_row_map=r2p,
+                             a_row_div=cfg.topk, out=c, tiles_visited=tiles)
+    torch.cuda.synchronize()
+    cnt = down(counts)
+    live_tiles = sum(-(-int(v) // 16) for v in cnt if v > 0) * (2 * I // 128)
+    capacity_tiles = -(-R // 16) * (2 * I // 128)
+    assert int(tiles.item()) == live_tiles
+    assert live_tiles * 4 < capacity_tiles

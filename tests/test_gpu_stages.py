@@ -1,0 +1,326 @@
+"""Stage-isolated parity of the HIP kernels against the CPU oracle.
+
+Bit-exact: alignment indices and endpoints, FP8 codes and scales (act_quant,
+silu_mul_quant fed identical BF16 inputs), GEMM outputs on the exactly
+representable special case. Tolerance (|err| <= 1e-2 * max|ref| + 2 BF16
+ulp): general GEMM and combine outputs. Every test also checks that rows the
+layer must leave alone keep their poison.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_fp8_mixture_amd as moe
+import oracle
+import synth
+from tests.gpu_helpers import (POISON_BF16, POISON_I32, POISON_U8, assert_bf16_close, dev, down,
+                               say, up)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(shape, value, dtype):
+    return torch.full(shape, value, dtype=dtype, device=dev())
+
+
+def _t_live(n):
+    return up(np.array([n], np.int32))
+
+
+def _f32_bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------ align
+
+ALIGN_CASES = [
+    # t_cap, t_live, K, E, A, seed, id_lo, id_hi
+    (8, 8, 2, 4, 16, 0, 0, 4),
+    (8, 5, 2, 4, 1, 1, 0, 4),
+    (16, 16, 8, 72, 16, 2, 0, 72),     # 128 pairs
+    (24, 24, 8, 72, 16, 3, 0, 72),     # 192 pairs
+    (7, 7, 3, 5, 4, 4, -2, 7),         # invalid ids dropped
+    (9, 9, 3, 3, 2, 5, 0, 2),          # an empty expert, duplicate ids
+    (4, 0, 8, 288, 16, 6, 0, 288),     # empty routing
+    (512, 16, 8, 32, 16, 7, 0, 32),
+    (4096, 4096, 8, 32, 16, 8, 0, 32),
+    (1000, 999, 8, 1024, 7, 9, 0, 1024),
+    (4096, 4096, 8, 256, 16, 10, 0, 3),  # three experts own every pair
+    (1500, 1500, 1, 1, 1, 11, 0, 1),
+]
+
+
+def _check_align(ids, t_cap, t_live, k, e, a):
+    ref = oracle.align(ids, t_live, e, a)
+    row_cap = moe.moe_min_row_cap(t_cap, k, e, a) + 5
+    out = {
+        "counts": _full((e,), POISON_I32, torch.int32),
+        "offsets": _full((e + 1,), POISON_I32, torch.int32),
+        "row_to_pair": _full((row_cap,), POISON_I32, torch.int32),
+        "pair_to_row": _full((max(t_cap * k, 1),), POISON_I32, torch.int32),
+    }
+    moe.moe_align(up(ids), e, a, row_cap, t_live=_t_live(t_live), out=out)
+    torch.cuda.synchronize()
+    got = {key: down(v) for key, v in out.items()}
+    assert np.array_equal(got["counts"], ref["counts"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    total = int(ref["offsets"][-1])
+    assert np.array_equal(got["row_to_pair"][:total], ref["row_to_pair"])
+    assert np.all(got["row_to_pair"][total:] == POISON_I32)
+    p = t_live * k
+    assert np.array_equal(got["pair_to_row"][:p], ref["pair_to_row"])
+    assert np.all(got["pair_to_row"][p:] == POISON_I32)
+
+
+@pytest.mark.parametrize("t_cap,t_live,k,e,a,seed,lo,hi", ALIGN_CASES)
+def test_align_bit_exact(t_cap, t_live, k, e, a, seed, lo, hi):
+    say(f"align t_cap={t_cap} t_live={t_live} K={k} E={e} A={a}")
+    ids = np.random.default_rng(seed).integers(lo, hi, (t_cap, k)).astype(np.int32)
+    _check_align(ids, t_cap, t_live, k, e, a)
+
+
+@pytest.mark.parametrize("name,t_cap,t_live", [("tiny", 8, 8), ("decode", 1, 1), ("decode", 4, 4),
+                                               ("padded", 512, 16), ("full", 4096, 4096),
+                                               ("sweep", 64, 64), ("sweep", 4096, 4096)])
+def test_align_workload_routing(name, t_cap, t_live):
+    say(f"align workload {name} t_cap={t_cap} t_live={t_live}")
+    cfg = synth.get(name)
+    ids, _ = synth.make_routing(cfg, t_cap)
+    _check_align(ids, t_cap, t_live, cfg.topk, cfg.num_experts, cfg.align_rows)
+
+
+# ------------------------------------------------------------------ act_quant
+
+
+def _tokens(kind, t_cap, h, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((t_cap, h))
+    if kind == "mixed":
+        groups = x.reshape(t_cap, h // 128, 128)
+        groups *= 10.0 ** g.uniform(-8, 3, (t_cap, h // 128, 1))
+        groups[:, ::7, :] = 0.0                                   # all-zero groups
+        groups[:, 1::11, :] *= 1e-4                               # floor active
+        # groups with amax 448 and values on E4M3 midpoints (scale exactly 1)
+        mids = oracle.e4m3_decode(np.arange(126, dtype=np.uint8))
+        mids = (mids + oracle.e4m3_decode(np.arange(1, 127, dtype=np.uint8))) / 2
+        sel = groups[:, 2::9, :]
+        sel[...] = g.choice(np.concatenate([mids, -mids]), sel.shape)
+        sel[..., 0] = 448.0
+        groups[:, 2::9, :] = sel
+        x = groups.reshape(t_cap, h)
+    bits = oracle.bf16_from_f64(x)
+    if kind == "mixed":
+        bits[:, 5::13] = 0x8000  # negative zeros
+    return bits
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "pow2", "ue8m0"])
+@pytest.mark.parametrize("t_cap,t_live,h,seed,kind", [
+    (8, 8, 256, 0, "normal"), (37, 30, 4096, 1, "mixed"), (512, 16, 7168, 2, "normal"),
+    (300, 300, 6144, 3, "mixed"), (5, 0, 128, 4, "normal")])
+def test_act_quant_bit_exact(fmt, t_cap, t_live, h, seed, kind):
+    say(f"act_quant fmt={fmt} t_cap={t_cap} t_live={t_live} H={h} {kind}")
+    x = _tokens(kind, t_cap, h, seed)
+    sdt = torch.uint8 if fmt == "ue8m0" else torch.float32
+    xq = _full((t_cap, h), POISON_U8, torch.uint8)
+    xs = _full((h // 128, t_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
+    moe.moe_act_quant(up(x), fmt, t_live=_t_live(t_live), xq=xq, xs=xs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    gq, gs = down(xq), down(xs)
+    assert np.array_equal(gq[:t_live], rq)
+    assert np.all(gq[t_live:] == POISON_U8)
+    if fmt == "ue8m0":
+        assert np.array_equal(gs[:, :t_live], rs)
+        assert np.all(gs[:, t_live:] == POISON_U8)
+    else:
+        assert np.array_equal(_f32_bits(gs[:, :t_live]), _f32_bits(rs))
+        assert np.all(np.isnan(gs[:, t_live:]))
+
+
+# ------------------------------------------------------------------ silu_mul_quant
+
+
+def _segments(g, e, max_rows, align, zero_frac=0.3):
+    counts = g.integers(1, max_rows + 1, e)
+    counts[g.random(e) < zero_frac] = 0
+    offsets = np.concatenate([[0], np.cumsum(-(-counts // align) * align)]).astype(np.int32)
+    return counts.astype(np.int32), offsets
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "pow2", "ue8m0"])
+@pytest.mark.parametrize("act,lim,amp", [("swiglu", float("inf"), 2.0), ("swiglu_clamp", 7.0, 8.0),
+                                         ("swiglu_clamp_after_silu", 7.0, 8.0),
+                                         ("swiglu_clamp", 0.5, 1.0),
+                                         ("swiglu_clamp_after_silu", 0.5, 1.0)])
+@pytest.mark.parametrize("inter,e,seed", [(128, 4, 0), (512, 288, 1), (2048, 32, 2)])
+def test_silu_mul_quant_bit_exact(fmt, act, lim, amp, inter, e, seed):
+    say(f"silu_mul_quant fmt={fmt} act={act} lim={lim} I={inter} E={e}")
+    g = np.random.default_rng(seed)
+    counts, offsets = _segments(g, e, 40, 16)
+    row_cap = int(offsets[-1]) + 16
+    gu = oracle.bf16_from_f64(g.standard_normal((row_cap, 2 * inter)) * amp)
+    live = np.zeros(row_cap, bool)
+    for i in range(e):
+        live[offsets[i]:offsets[i] + counts[i]] = True
+    gu[~live] = POISON_BF16  # never read
+    sdt = torch.uint8 if fmt == "ue8m0" else torch.float32
+    hq = _full((row_cap, inter), POISON_U8, torch.uint8)
+    hs = _full((inter // 128, row_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
+    lim32 = float(np.float32(lim))
+    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32)
+    gq, gs = down(hq), down(hs)
+    assert np.array_equal(gq[live], rq)
+    assert np.all(gq[~live] == POISON_U8)
+    if fmt == "ue8m0":
+        assert np.array_equal(gs[:, live], rs)
+        assert np.all(gs[:, ~live] == POISON_U8)
+    else:
+        assert np.array_equal(_f32_bits(gs[:, live]), _f32_bits(rs))
+        assert np.all(np.isnan(gs[:, ~live]))
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+EXACT_CODES = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], np.uint8)  # 0, +-.5, +-1, +-2
+
+
+def _gemm_case(seed, e, n, k, counts, exact, fmt, gather_k=0):
+    g = np.random.default_rng(seed)
+    counts = np.asarray(counts, np.int32)
+    offsets = np.concatenate([[0], np.cumsum(-(-counts // 16) * 16)]).astype(np.int32)
+    row_cap = int(offsets[-1]) + 32
+    kb = k // 128
+    if exact:
+        w = g.choice(EXACT_CODES, (e, n, k))
+        ws = g.choice(np.array([0.5, 1.0, 2.0], np.float32), (e, n // 128, kb))
+    else:
+        w = np.empty((e, n, k), np.uint8)
+        ws = np.empty((e, n // 128, kb), np.float32)
+        for i in range(e):
+            w[i], ws[i] = synth.quantize_weight_blocks((g.standard_normal((n, k)) * 0.02).astype(np.float32))
+    if gather_k:
+        a_rows = max(int(counts.sum()) // gather_k + 3, 4)
+        row_map = np.full(row_cap, POISON_I32, np.int32)
+        for i in range(e):
+            row_map[offsets[i]:offsets[i] + counts[i]] = g.integers(0, a_rows * gather_k, counts[i])
+        div = gather_k
+    else:
+        a_rows, row_map, div = row_cap, None, 1
+    if exact:
+        a = g.choice(EXACT_CODES, (a_rows, k))
+        p2 = g.integers(-1, 2, (kb, a_rows))
+        a_sc = np.ldexp(1.0, p2).astype(np.float32)
+        if fmt == "ue8m0":
+            a_sc = (p2 + 127).astype(np.uint8)
+    else:
+        x = g.standard_normal((a_rows, k)).astype(np.float32)
+        a, a_sc = oracle.quantize_groups(x, fmt)
+    return dict(w=w, ws=ws, a=a, a_sc=a_sc, counts=counts, offsets=offsets, row_cap=row_cap,
+                row_map=row_map, div=div, n=n, k=k, fmt=fmt)
+
+
+def _run_gemm(c):
+    out = _full((c["row_cap"], c["n"]), POISON_BF16, torch.int16)
+    tiles = torch.zeros(1, dtype=torch.int32, device=dev())
+    moe.moe_grouped_gemm_fp8(up(c["a"]), up(c["a_sc"]), c["fmt"], up(c["w"]), up(c["ws"]),
+                             up(c["counts"]), up(c["offsets"]), c["row_cap"],
+                             a_row_map=None if c["row_map"] is None else up(c["row_map"]),
+                             a_row_div=c["div"], out=out, tiles_visited=tiles)
+    torch.cuda.synchronize()
+    return down(out), int(tiles.item())
+
+
+def _expected_tiles(counts, n):
+    t = 0
+    for cnt in counts:
+        if 0 < cnt <= moe.GEMM_TILES["stream_max_rows"]:
+            t += -(-cnt // moe.GEMM_TILES["stream_tile_m"])
+        elif cnt > 0:
+            t += -(-cnt // moe.GEMM_TILES["tiled_tile_m"])
+    return t * (n // moe.GEMM_TILES["col_tile"])
+
+
+def _ref_gemm(c):
+    idx = None if c["row_map"] is None else np.where(c["row_map"] >= 0, c["row_map"] // c["div"], 0)
+    ref, live = oracle.grouped_gemm(c["a"], c["a_sc"], c["fmt"], (c["w"], c["ws"]), c["counts"],
+                                    c["offsets"], idx)
+    return ref, live
+
+
+GEMM_SHAPES = [
+    # seed, E, N, K, counts, gather_k
+    (0, 4, 256, 256, [3, 0, 17, 100], 0),           # K/128 = 2: 4 row blocks per item
+    (1, 3, 384, 1024, [64, 65, 1], 0),              # K/128 = 8: 2 x 2 split
+    (2, 5, 512, 2048, [16, 0, 300, 7, 129], 0),     # K/128 = 16: 4-way K split
+    (3, 6, 256, 512, [9, 33, 0, 200, 2, 64], 8),    # gathered A rows (FC1 layout)
+    (4, 2, 1024, 7168, [5, 140], 8),
+]
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+@pytest.mark.parametrize("seed,e,n,k,counts,gk", GEMM_SHAPES)
+def test_gemm_exact_special_case_bitwise(fmt, seed, e, n, k, counts, gk):
+    """Codes in {0, +-0.5, +-1, +-2} and power-of-two scales: every partial sum
+    is exact in fp32, so the HIP result must equal the oracle bit for bit."""
+    say(f"gemm exact fmt={fmt} E={e} N={n} K={k} counts={counts} gather={gk}")
+    c = _gemm_case(seed, e, n, k, counts, True, fmt, gk)
+    got, tiles = _run_gemm(c)
+    ref, live = _ref_gemm(c)
+    total = int(c["offsets"][-1])
+    assert np.array_equal(got[:total][live], ref[live])
+    assert np.all(got[:total][~live] == POISON_BF16)
+    assert np.all(got[total:] == POISON_BF16)
+    assert tiles == _expected_tiles(c["counts"], n)
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "pow2", "ue8m0"])
+@pytest.mark.parametrize("seed,e,n,k,counts,gk", GEMM_SHAPES)
+def test_gemm_tolerance(fmt, seed, e, n, k, counts, gk):
+    say(f"gemm tol fmt={fmt} E={e} N={n} K={k} counts={counts} gather={gk}")
+    c = _gemm_case(seed + 100, e, n, k, counts, False, fmt, gk)
+    got, _ = _run_gemm(c)
+    ref, live = _ref_gemm(c)
+    total = int(c["offsets"][-1])
+    assert_bf16_close(got[:total][live], ref[live], "gemm")
+    assert np.all(got[:total][~live] == POISON_BF16)
+    assert np.all(got[total:] == POISON_BF16)
+
+
+def test_gemm_empty_experts_write_nothing():
+    c = _gemm_case(7, 3, 256, 256, [0, 0, 0], False, "fp32")
+    got, tiles = _run_gemm(c)
+    assert tiles == 0 and np.all(got == POISON_BF16)
+
+
+# ------------------------------------------------------------------ combine
+
+
+@pytest.mark.parametrize("t_cap,t_live,k,h,seed", [(8, 8, 2, 256, 0), (37, 30, 8, 4096, 1),
+                                                   (4, 4, 8, 7168, 2), (64, 0, 8, 128, 3)])
+def test_combine_tolerance(t_cap, t_live, k, h, seed):
+    say(f"combine t_cap={t_cap} t_live={t_live} K={k} H={h}")
+    g = np.random.default_rng(seed)
+    rows = 200
+    y = oracle.bf16_from_f64(g.standard_normal((rows, h)))
+    p2r = g.integers(-1, rows, t_cap * k).astype(np.int32)
+    w = g.uniform(0, 1, (t_cap, k)).astype(np.float32)
+    out = _full((t_cap, h), POISON_BF16, torch.int16)
+    moe.moe_topk_combine(up(y), up(p2r), up(w), t_live=_t_live(t_live), out=out)
+    torch.cuda.synchronize()
+    got = down(out)
+    ref = oracle.combine(y, p2r, w, t_live, h)
+    assert_bf16_close(got[:t_live], ref, "combine")
+    assert np.all(got[t_live:] == POISON_BF16)
+
+
+def test_combine_unit_weight_is_identity():
+    g = np.random.default_rng(5)
+    y = oracle.bf16_from_f64(g.standard_normal((50, 512)))
+    p2r = g.permutation(50)[:20].astype(np.int32)
+    out = moe.moe_topk_combine(up(y), up(p2r), up(np.ones((20, 1), np.float32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(down(out), y[p2r])
