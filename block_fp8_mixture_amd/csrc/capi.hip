@@ -37,9 +37,12 @@ size_t scale_bytes(int fmt) { return fmt == MOE_SCALE_UE8M0 ? 1 : 4; }
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Rows any routing of t_cap tokens can need: with n <= min(E, pairs) experts
+// in use, sum_e ceil(c_e / A) <= floor((pairs + n * (A - 1)) / A).
 int64_t min_row_cap64(int64_t t_cap, int64_t topk, int64_t num_experts, int64_t align_rows) {
   const int64_t pairs = t_cap * topk;
-  return pairs + (num_experts < pairs ? num_experts : pairs) * (align_rows - 1);
+  const int64_t used = num_experts < pairs ? num_experts : pairs;
+  return (pairs + used * (align_rows - 1)) / align_rows * align_rows;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

@@ -77,8 +77,9 @@ typedef enum {
 } moe_act;
 
 /* Smallest row capacity that holds any routing of t_cap tokens with top-k:
- * every pair plus (align_rows - 1) pad rows for each expert that can be in
- * use. Returns -1 if the arguments are invalid or the value overflows int32. */
+ * with P = t_cap * topk pairs and n = min(num_experts, P) experts in use,
+ * align_rows * floor((P + n * (align_rows - 1)) / align_rows). Returns -1 if
+ * the arguments are invalid or the value overflows int32. */
 int32_t moe_min_row_cap(int32_t t_cap, int32_t topk, int32_t num_experts, int32_t align_rows);
 
 /* Routing alignment (vLLM PR #59128, Purpose: a shared permutation helper

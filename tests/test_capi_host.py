@@ -1,0 +1,170 @@
+"""Host-only checks of the C ABI: the library loads without a GPU, exports
+every function include/moe_fp8.h declares, and rejects invalid requests with
+the documented status before touching the HIP runtime."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_fp8_mixture_amd as moe
+from block_fp8_mixture_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_fp8.h")
+OK, INVALID, UNSUPPORTED, CAPACITY = 0, 1, 2, 3
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for fn in ("moe_align", "moe_act_quant", "moe_grouped_gemm_fp8", "moe_silu_mul_quant",
+               "moe_topk_combine", "moe_forward"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_function(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_min_row_cap(lib):
+    assert moe.moe_min_row_cap(4096, 8, 32, 16) == 32768 + 32 * 15
+    assert moe.moe_min_row_cap(4, 8, 288, 16) == 32 + 32 * 15
+    assert moe.moe_min_row_cap(8, 2, 4, 16) == 64      # 16 pairs on 4 experts: at most 4 x 16 rows
+    assert moe.moe_min_row_cap(3, 1, 8, 4) == 12       # 3 pairs: at most 3 segments of 4
+    assert moe.moe_min_row_cap(0, 8, 4, 16) == 0
+    assert moe.moe_min_row_cap(5, 0, 4, 16) == -1
+    assert moe.moe_min_row_cap(1 << 30, 64, 4, 16) == -1
+
+
+def test_status_strings(lib):
+    assert moe.moe_status_string(0) == "ok"
+    assert moe.moe_status_string(3) == "capacity too small"
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+def test_align_validation(lib):
+    f = lib.moe_align
+    args = dict(ids=FAKE, t_cap=4, live=NULL, k=8, e=288, a=16, rc=512)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["ids"], a["t_cap"], a["live"], a["k"], a["e"], a["a"], a["rc"], FAKE, FAKE, FAKE,
+                 FAKE, NULL)
+    assert call(k=0) == INVALID
+    assert call(k=65) == INVALID
+    assert call(a=0) == INVALID
+    assert call(e=0) == INVALID
+    assert call(t_cap=-1) == INVALID
+    assert call(e=1025) == UNSUPPORTED
+    assert call(rc=511) == CAPACITY
+    assert call(ids=NULL) == INVALID
+    assert f(FAKE, 4, NULL, 8, 288, 16, 512, NULL, FAKE, FAKE, FAKE, NULL) == INVALID
+
+
+def test_act_quant_validation(lib):
+    f = lib.moe_act_quant
+    assert f(FAKE, 4, NULL, 100, 0, FAKE, FAKE, NULL) == INVALID    # hidden not a multiple of 128
+    assert f(FAKE, 4, NULL, 256, 3, FAKE, FAKE, NULL) == INVALID    # unknown format
+    assert f(NULL, 4, NULL, 256, 0, FAKE, FAKE, NULL) == INVALID
+    assert f(FAKE, 4, NULL, 256, 0, FAKE, NULL, NULL) == INVALID
+    assert f(NULL, 0, NULL, 256, 0, NULL, NULL, NULL) == OK         # nothing to do, nothing launched
+
+
+def test_gemm_validation(lib):
+    f = lib.moe_grouped_gemm_fp8
+
+    def call(n=256, k=256, fmt=0, div=1, e=4, rc=64, mr=0, a=FAKE, c=FAKE, w=FAKE):
+        return f(a, FAKE, fmt, 64, NULL, div, w, FAKE, FAKE, FAKE, e, rc, mr, n, k, c, NULL, NULL)
+    assert call(n=200) == INVALID
+    assert call(k=0) == INVALID
+    assert call(fmt=7) == INVALID
+    assert call(div=0) == INVALID
+    assert call(e=0) == INVALID
+    assert call(e=2000) == UNSUPPORTED
+    assert call(mr=-1) == INVALID
+    assert call(a=NULL) == INVALID
+    assert call(w=NULL) == INVALID
+    assert call(rc=0, a=NULL, c=NULL) == OK
+
+
+def test_silu_mul_quant_validation(lib):
+    f = lib.moe_silu_mul_quant
+
+    def call(inter=256, act=0, lim=7.0, fmt=0, rc=64, gu=FAKE):
+        return f(gu, inter, FAKE, FAKE, 4, rc, act, lim, fmt, FAKE, FAKE, NULL)
+    assert call(inter=100) == INVALID
+    assert call(act=3) == INVALID
+    assert call(act=1, lim=0.0) == INVALID
+    assert call(act=2, lim=-1.0) == INVALID
+    assert call(act=1, lim=float("nan")) == INVALID
+    assert call(fmt=5) == INVALID
+    assert call(gu=NULL) == INVALID
+    assert call(rc=0, gu=NULL) == OK
+
+
+def test_combine_validation(lib):
+    f = lib.moe_topk_combine
+    assert f(FAKE, 64, FAKE, FAKE, 4, NULL, 0, 256, FAKE, NULL) == INVALID
+    assert f(FAKE, 64, FAKE, FAKE, 4, NULL, 8, 200, FAKE, NULL) == INVALID
+    assert f(FAKE, 64, NULL, FAKE, 4, NULL, 8, 256, FAKE, NULL) == INVALID
+    assert f(NULL, 0, NULL, NULL, 0, NULL, 8, 256, NULL, NULL) == OK
+
+
+def _problem(**kw):
+    d = dict(num_experts=32, hidden=7168, inter=2048, topk=8, t_cap=4096, align_rows=16,
+             row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"))
+    d.update(kw)
+    return B._Problem(**d)
+
+
+def test_workspace_plan_layout(lib):
+    for fmt in (0, 2):
+        p = _problem(scale_fmt=fmt)
+        lay = B._Layout()
+        assert lib.moe_workspace_plan(ctypes.byref(p), ctypes.byref(lay)) == OK
+        R = lay.row_cap
+        assert R == 32768 + 32 * 15
+        sb = 1 if fmt == 2 else 4
+        spans = [("expert_counts", 32 * 4), ("expert_offsets", 33 * 4), ("row_to_pair", R * 4),
+                 ("pair_to_row", 4096 * 8 * 4), ("xq", 4096 * 7168), ("xs", 56 * 4096 * sb),
+                 ("c1", R * 4096 * 2), ("hq", R * 2048), ("hs", 16 * R * sb), ("y", R * 7168 * 2)]
+        end = 0
+        for name, size in spans:
+            start = getattr(lay, name)
+            assert start % 256 == 0 and start >= end, name
+            end = start + size
+        assert lay.total >= end
+        assert lib.moe_workspace_bytes(ctypes.byref(p)) == lay.total
+
+
+def test_forward_validation(lib):
+    lay = B._Layout()
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(hidden=100)), ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(row_cap=100)), ctypes.byref(lay)) == CAPACITY
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(act=1, clamp_limit=0.0)),
+                                  ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(num_experts=4096)),
+                                  ctypes.byref(lay)) == UNSUPPORTED
+    assert lib.moe_workspace_bytes(ctypes.byref(_problem(inter=0))) == 0
+    p = _problem()
+    t = B._Tensors(*([FAKE.value] * 9))
+    need = lib.moe_workspace_bytes(ctypes.byref(p))
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(t), FAKE, need - 1, NULL) == CAPACITY
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(t), NULL, need, NULL) == INVALID
+    t0 = B._Tensors(*([FAKE.value] * 8 + [None]))
+    assert lib.moe_forward(ctypes.byref(p), ctypes.byref(t0), FAKE, need, NULL) == INVALID
+    assert lib.moe_forward(ctypes.byref(_problem(t_cap=0)), ctypes.byref(t), FAKE, need, NULL) == OK
