@@ -1,0 +1,300 @@
+"""Benchmark of the block-scaled FP8 expert layer on one MI355X.
+
+Default workload: decode-sized layer, 288 experts, top-8, hidden 4096,
+intermediate 512, 4 tokens, fp32 activation scales, plain SwiGLU, the weights
+FP8 E4M3 with 128x128 fp32 block scales (TensorRT-LLM PR #21250,
+Performance). One step is one whole forward of the layer (align, act quant,
+FC1, SiLU*up+quant, FC2, top-k combine), replayed from a captured HIP graph
+with all inputs resident in HBM. Before every step the L2 and the 256 MB
+Infinity Cache are flushed by writing 1 GiB, so weights stream from HBM
+(the pages time with a cold L2, vLLM PR #59128, SM100 on B200).
+
+Printed: one JSON line. `value` is the median cold layer latency in
+microseconds (HIP events around each replay); `ms_per_step` is the wall
+clock of the bracketed timed loop divided by the steps (it includes the
+flush). `roofline` describes the dominant kernel (the FC1 weight-streaming
+GEMM), timed on its own with HIP events on the stream it runs on.
+`cpu_baseline` is the CPU oracle on the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
+PAGES_DECODE_T4_US = 64.7    # TensorRT-LLM PR #21250, Performance (H200, context only)
+FLUSH_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode",
+                    choices=["tiny", "decode", "padded", "full", "sweep"])
+    ap.add_argument("--tokens", type=int, default=None, help="live tokens (default per config)")
+    ap.add_argument("--fmt", default=None, help="activation scale format")
+    ap.add_argument("--act", default="swiglu")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    return ap.parse_args()
+
+
+DEFAULT_TOKENS = {"tiny": (8, 8), "decode": (4, 4), "padded": (512, 16), "full": (4096, 4096),
+                  "sweep": (4096, 4096)}
+
+
+def live_stats(ids, t_live, num_experts):
+    import numpy as np
+    flat = ids[:t_live].reshape(-1)
+    flat = flat[(flat >= 0) & (flat < num_experts)]
+    return len(np.unique(flat)), len(flat)
+
+
+def algorithmic(cfg, n_live_experts, pairs, t_live):
+    """Bytes the layer must move at least, and FLOPs on live rows only.
+
+    Per expert: FC1 codes 2I*H + fp32 block scales (2I/128)(H/128)*4, FC2
+    codes H*I + (H/128)(I/128)*4. Plus BF16 x in and BF16 out (2*T*H each).
+    FLOPs: FC1 2*P*2I*H + FC2 2*P*H*I = 6*P*H*I.
+    """
+    H, I = cfg.hidden, cfg.inter
+    per_expert = 2 * I * H + (2 * I // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4
+    bmin = n_live_experts * per_expert + 2 * t_live * H * 2
+    flops = 6 * pairs * H * I
+    return bmin, flops
+
+
+def fc1_bytes(cfg, n_live_experts, pairs):
+    """Algorithmic bytes of one FC1 launch: live experts' FC1 codes + scales,
+    the gathered A rows (codes + fp32 scales) and the BF16 output rows."""
+    H, I = cfg.hidden, cfg.inter
+    per_expert = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+    return n_live_experts * per_expert + pairs * (H + (H // 128) * 4) + pairs * 2 * I * 2
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", "gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_key):
+    """HBM traffic of the FC1 kernel from the committed rocprofv3 --pmc summary,
+    used only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "fc1_stream_gemm_decode_t4_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("gemm_source_sha256_16") != kernel_source_hash() or d.get("workload") != workload_key:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, ids, w, t_live, fmt, act, weights):
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    import oracle
+    (w1q, w1s), (w2q, w2s) = weights
+    runs = []
+    budget = 25.0
+    t_start = time.perf_counter()
+    while len(runs) < 3 and (time.perf_counter() - t_start) < budget:
+        t0 = time.perf_counter()
+        oracle.forward(x, ids, w, (w1q, w1s), (w2q, w2s), t_live, cfg.align_rows, fmt, act)
+        runs.append(time.perf_counter() - t0)
+    med = statistics.median(runs)
+    return {"value": med * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole layer, {t_live} tokens of the benchmarked workload, median of "
+                      f"{len(runs)} run(s) of oracle.forward (numpy fp64)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the expert layer here is "
+              f"a single-GPU kernel library", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_fp8_mixture_amd as moe
+    import synth
+
+    cfg = synth.get(args.config)
+    t_cap, t_live = DEFAULT_TOKENS[args.config]
+    if args.tokens is not None:
+        t_cap = t_live = args.tokens
+    fmt = args.fmt or cfg.scale_fmts[0]
+    act = args.act
+    lim = 7.0 if act != "swiglu" else float("inf")
+    dev = torch.device("cuda", 0)
+    E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    t0 = time.perf_counter()
+    x, ids, w = synth.make_workload(cfg, t_cap)
+    weights = synth.ExpertWeights(cfg).stacked(threads=16)
+    (w1q, w1s), (w2q, w2s) = weights
+    d_w = [up(a) for a in (w1q, w1s, w2q, w2s)]
+    dx, dids, dw = up(x), up(ids), up(w)
+    dlive = up(np.array([t_live], np.int32))
+    print(f"# inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, cfg.align_rows, 0, fmt, act, lim)
+    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=dev)
+    out = torch.zeros((t_cap, H), dtype=torch.int16, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def fwd():
+        moe.moe_forward(dx, dids, dw, *d_w, fmt, act, lim, cfg.align_rows, 0, t_live=dlive,
+                        out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        graph.replay()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        starts[i].record(stream)
+        graph.replay()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    lat_us = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))
+    med = statistics.median(lat_us)
+    p10 = lat_us[int(0.1 * (len(lat_us) - 1))]
+    p90 = lat_us[int(0.9 * (len(lat_us) - 1))]
+    print(f"# layer latency median {med:.2f} us (p10 {p10:.2f}, p90 {p90:.2f}) over "
+          f"{args.steps} steps", file=sys.stderr, flush=True)
+
+    # ---- dominant kernel alone: FC1 grouped GEMM on the forward's intermediates
+    n_live_e, pairs = live_stats(ids, t_live, E)
+    R = lay["row_cap"]
+
+    def ws_i32(name, n):
+        return ws[lay[name]:lay[name] + 4 * n].view(torch.int32)
+    counts, offsets = ws_i32("expert_counts", E), ws_i32("expert_offsets", E + 1)
+    r2p = ws_i32("row_to_pair", R)
+    xq = ws[lay["xq"]:lay["xq"] + t_cap * H].view(t_cap, H)
+    sb = 1 if fmt == "ue8m0" else 4
+    xs_raw = ws[lay["xs"]:lay["xs"] + (H // 128) * t_cap * sb]
+    xs = (xs_raw if fmt == "ue8m0" else xs_raw.view(torch.float32)).view(H // 128, t_cap)
+    c1 = torch.empty((R, 2 * I), dtype=torch.int16, device=dev)
+    k_us = []
+    for i in range(args.kernel_reps):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        moe.moe_grouped_gemm_fp8(xq, xs, fmt, d_w[0], d_w[1], counts, offsets, R, a_row_map=r2p,
+                                 a_row_div=K, max_rows_per_expert=min(pairs, R), out=c1)
+        b.record(stream)
+        k_us.append((a, b))
+    torch.cuda.synchronize()
+    k_us = [a.elapsed_time(b) * 1e3 for a, b in k_us]
+    k_avg = statistics.mean(k_us)
+    fc1_b = fc1_bytes(cfg, n_live_e, pairs)
+    fc1_flops = 2 * pairs * 2 * I * H
+    workload_key = f"{args.config}:T{t_live}:{fmt}"
+    traffic = load_traffic(workload_key)
+    tiled = pairs > 0 and pairs / max(n_live_e, 1) > moe.GEMM_TILES["stream_max_rows"]
+    if tiled:
+        roof = {"kernel": "gemm_tiled_kernel (FC1)", "bound": "mfma",
+                "achieved": round(fc1_flops / (k_avg * 1e-6) / 1e12, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fc1_flops / (k_avg * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"kernel": "gemm_stream_kernel (FC1)", "bound": "hbm",
+                "achieved": round(fc1_b / (k_avg * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(fc1_b / (k_avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel_avg_us": round(k_avg, 3),
+                 "algorithmic_bytes": fc1_b, "algorithmic_flops": fc1_flops})
+
+    # A plain 256 MiB device copy, so counter runs (FETCH_SIZE / WRITE_SIZE)
+    # can be scaled by what the counters read for a copy of known size.
+    cal_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    for _ in range(3):
+        cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    bmin, flops = algorithmic(cfg, n_live_e, pairs, t_live)
+    res = {
+        "metric": "MoE layer latency (us) + live-row TFLOP/s and HBM GB/s vs roofline",
+        "value": round(med, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": (round(med / PAGES_DECODE_T4_US, 4)
+                        if (args.config, t_live, fmt, act) == ("decode", 4, "fp32", "swiglu")
+                        else None),
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {E} experts, hidden {H}, intermediate {I}, top-{K}, "
+                        f"{t_live} live of {t_cap} tokens, {fmt} activation scales, {act}",
+            "experts": E, "hidden": H, "intermediate": I, "topk": K, "tokens": t_live,
+            "token_capacity": t_cap, "act_scale_fmt": fmt, "activation": act,
+            "cache": "warm" if args.no_flush else "flushed before every step",
+        },
+        "latency_us": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3)},
+        "live_experts": n_live_e,
+        "live_pairs": pairs,
+        "live_tflops": round(flops / (med * 1e-6) / 1e12, 4),
+        "hbm_gbs_min_bytes": round(bmin / (med * 1e-6) / 1e9, 1),
+        "frac_fp8_peak": round(flops / (med * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 5),
+        "frac_hbm_peak": round(bmin / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, ids, w, t_live, fmt, act, weights)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
