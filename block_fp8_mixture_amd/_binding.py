@@ -13,7 +13,7 @@ SCALE_FMTS = {"fp32": 0, "pow2": 1, "ue8m0": 2}
 ACTS = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_clamp_after_silu": 2}
 # Row-tile geometry of the grouped GEMM (mirrors the header's macros), used to
 # interpret the tiles_visited counter.
-GEMM_TILES = {"stream_tile_m": 16, "stream_max_rows": 64, "tiled_tile_m": 128, "col_tile": 128}
+GEMM_TILES = {"stream_tile_m": 16, "stream_max_rows": 64, "tiled_tile_m": 256, "col_tile": 128}
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "capacity too small",
            4: "HIP runtime error"}

@@ -33,6 +33,12 @@ bool act_ok(int a) {
   return a == MOE_ACT_SWIGLU || a == MOE_ACT_SWIGLU_CLAMP || a == MOE_ACT_SWIGLU_CLAMP_AFTER_SILU;
 }
 bool dim128(int32_t d) { return d > 0 && d % 128 == 0; }
+// Limits of the GEMM kernels: k <= 32768 (per-tile weight scale table in
+// LDS) and 32-bit byte offsets within one operand (a_rows * k and one
+// expert's n * k below 2^32).
+bool gemm_shape_ok(int64_t a_rows, int64_t n, int64_t k) {
+  return k <= 32768 && a_rows * k < (int64_t{1} << 32) && n * k < (int64_t{1} << 32);
+}
 size_t scale_bytes(int fmt) { return fmt == MOE_SCALE_UE8M0 ? 1 : 4; }
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -98,7 +104,8 @@ static moe_status gemm_checked(const moe::GemmArgs& g, void* stream) {
   if (!dim128(g.n) || !dim128(g.k) || !fmt_ok(g.fmt) || g.a_rows < 0 || g.a_row_div < 1 ||
       g.num_experts < 1 || g.row_cap < 0)
     return MOE_ERR_INVALID_ARG;
-  if (g.num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (g.num_experts > moe::kMaxExperts || !gemm_shape_ok(g.a_rows, g.n, g.k))
+    return MOE_ERR_UNSUPPORTED;
   if (!g.counts || !g.offsets || !g.w || !g.w_scales) return MOE_ERR_INVALID_ARG;
   if (g.row_cap > 0 && (!g.c || !g.a || !g.a_scales)) return MOE_ERR_INVALID_ARG;
   if (g.row_cap == 0) return MOE_OK;
@@ -177,6 +184,9 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   if (need > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   const int64_t rc = p->row_cap == 0 ? need : p->row_cap;
   if (rc < need) return MOE_ERR_CAPACITY;
+  if (!gemm_shape_ok(p->t_cap, 2 * static_cast<int64_t>(p->inter), p->hidden) ||
+      !gemm_shape_ok(rc, p->hidden, p->inter))
+    return MOE_ERR_UNSUPPORTED;
   const size_t E = p->num_experts, H = p->hidden, I = p->inter, T = p->t_cap;
   const size_t R = static_cast<size_t>(rc), P = T * p->topk, sb = scale_bytes(p->scale_fmt);
   size_t off = 0;

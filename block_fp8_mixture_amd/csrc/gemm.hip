@@ -8,28 +8,27 @@
 // grid covers only the expert blocks the batch can occupy; at decode sizes
 // most experts are empty and the GEMM must stream weights at bandwidth.
 //
-// Both kernels compute C^T tiles with v_mfma_f32_16x16x128_f8f6f4: the MFMA
-// "A" operand is 16 weight rows x 128 K, "B" is 16 token rows x 128 K, so one
-// MFMA covers exactly one 128-wide scale block. Its 16x16 fp32 result sits
-// with token = lane % 16 and weight row = 4 * (lane / 16) + v, which makes the
-// weight block scale uniform over the wave and the activation scale a single
-// value per lane: each K block costs one MFMA into a zeroed temporary and four
-// FMAs acc += temp * (sa * sw). Both operands carry 32 consecutive K bytes
-// per lane (lane / 16 selects which 32).
+// Both kernels compute C^T tiles (weights are the MFMA "A" operand, tokens
+// "B"), which makes the weight block scale uniform over a wave and the
+// activation scale a single value per lane.
 //
 // Work is found on the device: every workgroup compacts the experts it owns
 // (by row count) from expert_counts into LDS, then walks its share of the
 // resulting item list, so padded capacity and empty experts cost nothing.
 //
-//  * gemm_stream_kernel -- experts with 1..64 rows. An item is (expert, 16*WN
-//    weight rows); the 4 waves split the item as WN row blocks x KSPLIT K
-//    ranges. Weight fragments are loaded once into registers and reused for
-//    every 16-row token tile of the expert; K-split partial sums are added in
-//    a fixed order through LDS. This is the weight-streaming (HBM-bound) path.
-//  * gemm_tiled_kernel -- experts with more rows. 128 token x 128 weight
-//    tiles, K step 128, both operands staged through double-buffered LDS with
-//    an XOR swizzle of 16-byte chunks (conflict-free fragment reads); 2x2
-//    waves of 64x64.
+//  * gemm_stream_kernel -- experts with 1..64 rows, on
+//    v_mfma_f32_16x16x128_f8f6f4 (one MFMA = one 128-wide scale block; 16x16
+//    result with token = lane % 16, weight row = 4 * (lane / 16) + v). An item
+//    is (expert, 16*WN weight rows); the 4 waves split it as WN row blocks x
+//    KSPLIT K ranges and walk the expert's 16-row token tiles. Each K block
+//    is one MFMA into a zeroed temporary and four FMAs acc += t * (sa * sw);
+//    K-split partial sums are added in a fixed order through LDS. This is the
+//    weight-streaming (HBM-bound) path.
+//  * gemm_tiled_kernel -- experts with more rows: persistent, XCD-grouped
+//    256 x 256 tiles on v_mfma_f32_32x32x64_f8f6f4, operands staged through
+//    a 4-deep LDS ring of 64-byte K stages by direct-to-LDS loads, scales
+//    applied by rescaling the accumulator once per 128-wide block (details at
+//    the kernel).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -77,16 +76,16 @@ __device__ __forceinline__ int a_source_row(const GemmArgs& p, int r) {
 // Ordered compaction of the experts whose row count satisfies `want`, into
 // s_list[0..n). s_pref[i] gets the exclusive prefix sum of units(count) over
 // the listed experts and s_pref[n] the total. Returns n. All threads call it.
-template <typename Want, typename Units>
+template <int NT, typename Want, typename Units>
 __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int* s_list,
                                  int* s_pref, int* s_tmp) {
   const int num_experts = p.num_experts;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  constexpr int kW = kThreads / 64;
+  constexpr int kW = NT / 64;
   int run_n = 0, run_u = 0;
-  for (int base = 0; base < num_experts; base += kThreads) {
+  for (int base = 0; base < num_experts; base += NT) {
     const int e = base + tid;
     const int cnt = e < num_experts ? expert_rows(p, e) : 0;
     const bool flag = e < num_experts && want(cnt);
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs p) {
   __shared__ int s_tmp[2 * kThreads / 64];
   __shared__ v4f s_red[KSPLIT > 1 ? (KSPLIT - 1) * WN * 64 : 1];
 
-  const int n_list = build_expert_list(p, WantSmall(), NoUnits(), s_list, s_pref, s_tmp);
+  const int n_list = build_expert_list<kThreads>(p, WantSmall(), NoUnits(), s_list, s_pref, s_tmp);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -217,134 +216,313 @@ __global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs p) {
 
 // ---------------------------------------------------------------- tiled
 
-constexpr int BM = kTiledTileM;  // token rows per tile
-constexpr int BN = kColTile;     // weight rows per tile
-constexpr int BK = kGroup;
+constexpr int TM = kTiledTileM;   // token rows per tile (256)
+constexpr int TN = 256;           // weight rows per tile
+constexpr int SK = 64;            // K bytes per pipeline stage (half a scale block)
+constexpr int kTiledThreads = 512;
+constexpr int kStageA = TM * SK;              // token part of a stage (16 KB)
+constexpr int kStageBytes = (TM + TN) * SK;   // 32 KB
+constexpr int kGroupN = 8;                    // n-tiles per scheduling group
+constexpr int kMaxKBlocks = 256;              // K <= 32768 on this path
+// Scales below this are treated as this value inside the accumulator's
+// normalizer: a block whose scale is zero then adds 2^-64 times its raw dot
+// products (about 1e-20 of any real block's contribution) instead of making
+// the ratios overflow.
+constexpr float kScaleFloor = 5.42101086e-20f;  // 2^-64
 
-// Byte offset of 16-byte chunk c of tile row `row` in a [rows][128 B] LDS tile.
-__device__ __forceinline__ int swz(int row, int c) { return row * BK + ((c ^ (row & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Byte offset of 16-byte chunk c (0..3) of row `row` in a [rows][64 B] LDS
+// slab. gfx950's LDS has 64 four-byte banks, so rows r, r+4, r+8, r+12 start
+// on the same bank; XOR-ing the chunk with (row >> 2) & 3 gives the 16 lanes
+// one ds_read_b128 cycle serves (16 consecutive rows, same chunk) 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int c) { return row * SK + ((c ^ ((row >> 2) & 3)) << 4); }
 
 union Frag {
   uint4 u[2];
   v8i v;
 };
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_tiled_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][BN * BK];
-  __shared__ float s_sa[2][BM];
+// Workgroup barrier for the pipelined K loop. A fence (as in
+// __syncthreads()) would make the compiler wait for every vector-memory
+// operation in flight, including the direct-to-LDS loads of later stages, and
+// so collapse the pipeline. Instead the caller waits for exactly the data the
+// next stage needs (explicit vmcnt), this waits for the wave's own LDS
+// writes, and the "memory" clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Tile t of an expert with mt row tiles and nt column tiles, in the order
+// that keeps kGroupN column tiles x all row tiles of an expert together (so
+// the workgroups of one XCD share token and weight slabs in their L2).
+__device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, int* n) {
+  const int full = nt / kGroupN;
+  const int gsz = mt * kGroupN;
+  if (local < full * gsz) {
+    const int g = local / gsz, r = local % gsz;
+    *m = r / kGroupN;
+    *n = g * kGroupN + r % kGroupN;
+  } else {
+    const int r = local - full * gsz, gw = nt - full * kGroupN;
+    *m = r / gw;
+    *n = full * kGroupN + r % gw;
+  }
+}
+
+// Large-expert GEMM. A workgroup computes a 256 token x 256 weight tile with
+// 8 waves as 4 (tokens) x 2 (weights); wave (wm, wn) owns tokens
+// [64 wm, 64 wm + 64) x weights [128 wn, 128 wn + 128), as 2 x 4 tiles of
+// v_mfma_f32_32x32x64_f8f6f4 (weights are the MFMA "A" operand, tokens "B";
+// lane l holds token l % 32 and 16 weight rows, so the token scale is one
+// value per lane and the weight block scale one value per wave).
+//
+// K is walked in 64-byte stages: both operand slabs of a stage (256 x 64 B
+// each, 32 KB) are staged in LDS by direct-to-LDS loads through a ring of 4
+// stages issued 3 stages ahead; a 128-wide scale block is two stages.
+//
+// Scales: the accumulator is kept in units of the current block's scale
+// s = sa[token] * sw. At the first stage of each block it is multiplied by
+// s_prev / s (the token part comes precomputed from LDS, the weight part is
+// one value per wave), then the MFMAs add the block's raw FP8 dot products
+// into it; the epilogue multiplies by the last s. One VALU multiply per
+// element and block, no temporaries, no wait on an MFMA result. Power-of-two
+// ratios are exact.
+template <bool UE8M0>
+__global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
+  // Four stages and two token-scale buffers, all distinct objects, so the
+  // compiler can tell that a read never aliases a direct-to-LDS load in
+  // flight and does not wait for the prefetch.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_st3[kStageBytes];
+  __shared__ uint32_t s_sr0[TM];  // raw token scales of even / odd scale blocks
+  __shared__ uint32_t s_sr1[TM];  // (UE8M0 bytes arrive zero-extended)
+  __shared__ uint32_t s_srx[TM];  // sink of waves 4..7's copy of the scale loads
+  __shared__ __attribute__((aligned(16))) float s_rt[2][TM];  // token scale ratio of a block
+  __shared__ float s_sl[TM];                                  // token scale of the last block
+  __shared__ float s_ws[2][kMaxKBlocks];                      // weight block scales of the tile
   __shared__ int s_list[kMaxExperts];
   __shared__ int s_pref[kMaxExperts + 1];
-  __shared__ int s_tmp[2 * kThreads / 64];
+  __shared__ int s_tmp[2 * kTiledThreads / 64];
 
-  const int n_list = build_expert_list(p, WantLarge(), TiledUnits(), s_list, s_pref, s_tmp);
+  const int n_list = build_expert_list<kTiledThreads>(p, WantLarge(), TiledUnits(), s_list,
+                                                      s_pref, s_tmp);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1;   // token half of the tile
-  const int wn = wave >> 1;  // weight half of the tile
-  const int N = p.n, K = p.k, KB = K / BK;
-  const int n_tn = N / BN;
-  const int total = s_pref[n_list] * n_tn;
-  const int lrow = tid >> 3;  // load row within a 32-row slab
-  const int lc = tid & 7;     // load chunk (16 bytes) within the row
+  // Waves are spread over the 4 SIMDs round-robin; pairing (wm, wn) as
+  // below puts the two waves of a 64-token slice on different SIMDs, so a
+  // tail tile of up to 128 rows still keeps all four SIMDs busy.
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int N = p.n, K = p.k, KB = K / kGroup, NS = K / SK;
+  const int nt = (N + TN - 1) / TN;
+  const int total = s_pref[n_list] * nt;
+  const int G = gridDim.x;
+  // Persistent grid: consecutive tiles go to one XCD (workgroups are
+  // dispatched round-robin over the 8 XCDs).
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int tok = tid & (TM - 1);
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mt_all = tile / n_tn;
-    const int nt = tile % n_tn;
+  for (int tile = vid; tile < total; tile += G) {
+    const int tm_all = tile / nt;
     int lo = 0, hi = n_list - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= mt_all) lo = mid; else hi = mid - 1;
+      if (s_pref[mid] <= tm_all) lo = mid; else hi = mid - 1;
     }
     const int e = s_list[lo];
-    const int mt = mt_all - s_pref[lo];
-    const int cnt = expert_rows(p, e);
-    const int rows_here = min(BM, cnt - mt * BM);
-    const int row0 = p.offsets[e] + mt * BM;
-    const int n0 = nt * BN;
+    const int mt_e = s_pref[lo + 1] - s_pref[lo];
+    int mt, ntile;
+    tile_coords(tile - s_pref[lo] * nt, mt_e, nt, &mt, &ntile);
+    const int cnt = __builtin_amdgcn_readfirstlane(expert_rows(p, e));
+    const int rows_here = min(TM, cnt - mt * TM);
+    const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]) + mt * TM;
+    const int n0 = ntile * TN;
+    const bool wave_on = wm * 64 < rows_here && n0 + wn * 128 < N;
+    const uint8_t* wbase = p.w + static_cast<int64_t>(e) * N * K;
 
-    const uint8_t* asrc[4];
-    bool aval[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lrow + 32 * i;
-      const int ar = row < rows_here ? a_source_row(p, row0 + row) : -1;
-      aval[i] = ar >= 0;
-      asrc[i] = p.a + static_cast<int64_t>(aval[i] ? ar : 0) * K + lc * 16;
+    for (int i = tid; i < 2 * KB; i += kTiledThreads) {
+      const int blk = i / KB, kb = i % KB, nb = n0 / kGroup + blk;
+      s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
     }
-    const uint8_t* wsrc = p.w + (static_cast<int64_t>(e) * N + n0 + lrow) * K + lc * 16;
-    const int sa_row = tid < rows_here ? a_source_row(p, row0 + tid) : -1;
-    const float* wsp = p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + nt) * KB;
-
-    uint4 ra[4], rw[4];
-    float rs = 0.0f;
-    auto gload = [&](int kb) {
+    // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
+    // instructions of 16 rows each; lane l lands in slot l & 3 of row
+    // 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps there.
+    uint32_t aoff[2], woff[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = aval[i] ? *reinterpret_cast<const uint4*>(asrc[i] + kb * BK) : uint4{0, 0, 0, 0};
-        rw[i] = *reinterpret_cast<const uint4*>(wsrc + static_cast<int64_t>(32 * i) * K + kb * BK);
-      }
-      if (tid < BM)
-        rs = sa_row >= 0 ? load_scale(p.a_scales, p.fmt, static_cast<int64_t>(kb) * p.a_rows + sa_row) : 0.0f;
-    };
-    auto lstore = [&](int buf) {
+    for (int i = 0; i < 2; ++i) {
+      const int row = wave * 32 + 16 * i + (lane >> 2);
+      const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
+      const int ar = row < rows_here ? a_source_row(p, row0 + row) : -1;
+      aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
+      const int wr = n0 + row < N ? n0 + row : n0;
+      woff[i] = static_cast<uint32_t>(wr) * K + chunk;
+    }
+    const int sa_row = tok < rows_here ? a_source_row(p, row0 + tok) : -1;
+    const int my_src = sa_row < 0 ? 0 : sa_row;
+
+    auto issue = [&](int j, uint8_t* stage) {  // operand slabs of stage j
+      const int s = j < NS ? j : NS - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int off = swz(lrow + 32 * i, lc);
-        *reinterpret_cast<uint4*>(&s_a[buf][off]) = ra[i];
-        *reinterpret_cast<uint4*>(&s_w[buf][off]) = rw[i];
-      }
-      if (tid < BM) s_sa[buf][tid] = rs;
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(p.a + (aoff[i] + s * SK), (lds_void*)(stage + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+    };
+    // Token scales of block kb. Waves 0..3 load them into `buf`; waves
+    // 4..7 load the same values into a sink so that every wave has the same
+    // number of loads in flight and one vmcnt immediate fits all of them.
+    auto issue_s = [&](int kb, uint32_t* buf) {
+      uint32_t* dst = (wave < TM / 64 ? buf : s_srx) + (wave & 3) * 64;
+      const int64_t idx = static_cast<int64_t>(kb < KB ? kb : KB - 1) * p.a_rows + my_src;
+      if constexpr (UE8M0)
+        __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.a_scales) + idx, (lds_void*)dst, 1, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(static_cast<const uint32_t*>(p.a_scales) + idx, (lds_void*)dst, 4, 0, 0);
+    };
+    auto decode_sa = [&](uint32_t raw) -> float {
+      const float v = sa_row < 0 ? 1.0f : __uint_as_float(UE8M0 ? raw << 23 : raw);
+      return v > kScaleFloor ? v : kScaleFloor;
     };
 
-    v4f acc[4][4];
+    v16f acc[4][2];  // [weight tile][token tile]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    float tok_prev = 1.0f;  // this thread's token scale of the previous block
+    float sw_norm = 1.0f;   // weight part of the accumulator's normalizer
 
-    gload(0);
-    lstore(0);
+    // Prologue: stages 0..2 (and the token scales of blocks 0 and 1); each
+    // stage issues [A x2][W x2] then, when it starts a block, [S]. The order
+    // is pinned so the vmcnt waits can count.
+    __syncthreads();  // s_ws visible; the previous tile is done with every stage
+    issue(0, s_st0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_s(0, s_sr0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(1, s_st1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(2, s_st2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_s(1, s_sr1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): stage 0 and block 0's scales landed
+    if (tid < TM) {
+      tok_prev = decode_sa(s_sr0[tok]);
+      s_rt[0][(tok & 31) * 8 + (tok >> 5)] = 1.0f;
+      if (KB == 1) s_sl[(tok & 31) * 8 + (tok >> 5)] = tok_prev;
+    }
+
+    // Stage j. Entry: stage j is visible to all waves (barrier of stage j-1
+    // or the prologue's); stages j+1 and j+2 may be in flight. Each stage
+    // issues [A x2][W x2] for stage j+3, then [S] if stage j+3 starts a
+    // block. Stage j+1 (and, when it starts a block, its scales) has landed
+    // once only stage j+2's loads remain: 4 when j+1 starts a block, else 4
+    // plus the scales issued after stage j+2. If stage j+1 starts block kb,
+    // its token ratios are published; then the barrier, the loads, and the 8
+    // MFMAs of stage j.
+    auto stage = [&](int j, const uint8_t* cur, uint8_t* fill, const uint32_t* sr_next,
+                     float* rt_next, const float* rt_cur, uint32_t* sr_fill, bool next_starts,
+                     bool cur_starts, bool fill_starts) {
+      if (next_starts)
+        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+      if (next_starts) {
+        const int kb_next = (j + 1) >> 1;
+        const float t = decode_sa(sr_next[tok]);
+        const float r = tok_prev * __builtin_amdgcn_rcpf(t);
+        if (tid < TM && kb_next < KB) {
+          rt_next[(tok & 31) * 8 + (tok >> 5)] = r;
+          if (kb_next == KB - 1) s_sl[(tok & 31) * 8 + (tok >> 5)] = t;
+        }
+        tok_prev = t;
+      }
+      lds_barrier();
+      issue(j + 3, fill);
+      __builtin_amdgcn_sched_barrier(0);
+      if (fill_starts) issue_s((j + 3) >> 1, sr_fill);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!wave_on || j >= NS) return;
+      if (cur_starts) {
+        const int kb = j >> 1;
+        const float sw = fmaxf(s_ws[wn][kb], kScaleFloor);
+        const float q = sw_norm * __builtin_amdgcn_rcpf(sw);
+        sw_norm = sw;
+        const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
+        const float ratio0 = r2.x * q, ratio1 = r2.y * q;
+#pragma unroll
+        for (int wt = 0; wt < 4; ++wt) {
+          acc[wt][0] = acc[wt][0] * ratio0;
+          acc[wt][1] = acc[wt][1] * ratio1;
+        }
+      }
+      const uint8_t* sA = cur;
+      const uint8_t* sW = cur + kStageA;
+      const int c0 = 2 * (lane >> 5);
+      Frag af[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int r = wm * 64 + tt * 32 + (lane & 31);
+        af[tt].u[0] = *reinterpret_cast<const uint4*>(sA + swz(r, c0));
+        af[tt].u[1] = *reinterpret_cast<const uint4*>(sA + swz(r, c0 + 1));
+      }
+#pragma unroll
+      for (int wt = 0; wt < 4; ++wt) {
+        const int r = wn * 128 + wt * 32 + (lane & 31);
+        Frag wf;
+        wf.u[0] = *reinterpret_cast<const uint4*>(sW + swz(r, c0));
+        wf.u[1] = *reinterpret_cast<const uint4*>(sW + swz(r, c0 + 1));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf.v, af[tt].v, acc[wt][tt],
+                                                                         0, 0, 0, 0, 0, 0);
+      }
+    };
+
+    lds_barrier();
+    // Four stages per iteration (unconditional: past the end a stage only
+    // loads clamped, unused data and skips its compute, so every path issues
+    // the same vector-memory sequence). Stage j uses buffer j % 4; block
+    // kb's token scales use buffer kb % 2.
+    for (int j = 0; j < NS; j += 4) {
+      stage(j, s_st0, s_st3, s_sr0, s_rt[0], s_rt[0], s_sr1, false, true, false);
+      stage(j + 1, s_st1, s_st0, s_sr1, s_rt[1], s_rt[0], s_sr0, true, false, true);
+      stage(j + 2, s_st2, s_st1, s_sr1, s_rt[1], s_rt[1], s_sr0, false, true, false);
+      stage(j + 3, s_st3, s_st2, s_sr0, s_rt[0], s_rt[1], s_sr1, true, false, true);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // trailing loads of this tile done before any stage is reused
     __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-      const int cur = kb & 1;
-      if (kb + 1 < KB) gload(kb + 1);
-      const float sw = wsp[kb];
-      float sc[4];
-#pragma unroll
-      for (int ts = 0; ts < 4; ++ts) sc[ts] = s_sa[cur][wm * 64 + ts * 16 + (lane & 15)] * sw;
-      Frag wf[4], af[4];
-      const int c0 = 2 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rw_ = wn * 64 + i * 16 + (lane & 15);
-        wf[i].u[0] = *reinterpret_cast<const uint4*>(&s_w[cur][swz(rw_, c0)]);
-        wf[i].u[1] = *reinterpret_cast<const uint4*>(&s_w[cur][swz(rw_, c0 + 1)]);
-        const int ra_ = wm * 64 + i * 16 + (lane & 15);
-        af[i].u[0] = *reinterpret_cast<const uint4*>(&s_a[cur][swz(ra_, c0)]);
-        af[i].u[1] = *reinterpret_cast<const uint4*>(&s_a[cur][swz(ra_, c0 + 1)]);
-      }
-#pragma unroll
-      for (int ws = 0; ws < 4; ++ws)
-#pragma unroll
-        for (int ts = 0; ts < 4; ++ts)
-          acc[ws][ts] = fma4(mfma_fp8(wf[ws].v, af[ts].v), sc[ts], acc[ws][ts]);
-      if (kb + 1 < KB) lstore(cur ^ 1);
-      __syncthreads();
-    }
 
+    if (wave_on) {
+      const float f = sw_norm;
+      const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
+      const float fs[2] = {sl.x * f, sl.y * f};
 #pragma unroll
-    for (int ts = 0; ts < 4; ++ts) {
-      const int j = wm * 64 + ts * 16 + (lane & 15);
-      if (j < rows_here) {
-        uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * 64 + 4 * (lane >> 4);
+      for (int tt = 0; tt < 2; ++tt) {
+        const int j = wm * 64 + tt * 32 + (lane & 31);
+        if (j < rows_here) {
+          uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * 128 + 4 * (lane >> 5);
 #pragma unroll
-        for (int ws = 0; ws < 4; ++ws)
-          *reinterpret_cast<uint2*>(crow + ws * 16) = pack_bf16x4(acc[ws][ts]);
+          for (int wt = 0; wt < 4; ++wt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              v4f v = {acc[wt][tt][4 * g], acc[wt][tt][4 * g + 1], acc[wt][tt][4 * g + 2], acc[wt][tt][4 * g + 3]};
+              *reinterpret_cast<uint2*>(crow + wt * 32 + g * 8) = pack_bf16x4(v * fs[tt]);
+            }
+        }
       }
     }
-    if (tid == 0 && p.tiles_visited) atomicAdd(p.tiles_visited, 1);
+    if (tid == 0 && p.tiles_visited) atomicAdd(p.tiles_visited, min(TN, N - n0) / kColTile);
   }
 }
 
@@ -371,15 +549,18 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
   else err = launch_stream<4, 1>(g, live_bound, stream);
   if (err != hipSuccess) return err;
   if (g.max_rows_per_expert > kStreamMaxRows) {
-    // Row tiles of the large experts: at most ceil(rows / BM) + one partial
-    // tile per expert that can be large.
+    // Tiles of the large experts: at most ceil(rows / TM) + one partial row
+    // tile per expert that can be large, times the column tiles.
     const int64_t rows = g.row_cap;
-    const int64_t large_experts = rows / (kStreamMaxRows + 1) < live_bound ? rows / (kStreamMaxRows + 1) : live_bound;
-    const int64_t tiles = ((rows + BM - 1) / BM + large_experts) * (g.n / BN);
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
+    const int64_t large = rows / (kStreamMaxRows + 1) < live_bound ? rows / (kStreamMaxRows + 1) : live_bound;
+    const int64_t tiles = ((rows + TM - 1) / TM + large) * ((g.n + TN - 1) / TN);
+    const int64_t cap = device_cu_count();
     const int grid = static_cast<int>(tiles < cap ? tiles : cap);
     if (grid > 0) {
-      hipLaunchKernelGGL(gemm_tiled_kernel, dim3(grid), dim3(kThreads), 0, stream, g);
+      if (g.fmt == kUe8m0)
+        hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      else
+        hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3(grid), dim3(kTiledThreads), 0, stream, g);
       err = hipGetLastError();
     }
   }

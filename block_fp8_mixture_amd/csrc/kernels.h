@@ -9,7 +9,7 @@ namespace moe {
 constexpr int kMaxExperts = 1024;     // LDS tables in align and the GEMM schedulers
 constexpr int kStreamTileM = 16;      // row tile of the weight-streaming GEMM
 constexpr int kStreamMaxRows = 64;    // experts with at most this many rows stream
-constexpr int kTiledTileM = 128;      // row tile of the MFMA-tiled GEMM
+constexpr int kTiledTileM = 256;      // row tile of the MFMA-tiled GEMM
 constexpr int kColTile = 128;         // column tile (= weight block rows)
 
 hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,

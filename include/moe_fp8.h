@@ -147,7 +147,8 @@ moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live
  *   tiles_visited  device int32 or NULL; when given, the number of
  *               (row tile, column tile) pairs computed is ADDED to it
  * Errors: INVALID_ARG (n or k not positive multiples of 128, null pointers,
- * a_row_div < 1, unknown fmt). */
+ * a_row_div < 1, unknown fmt); UNSUPPORTED (num_experts above 1024, k above
+ * 32768, a_rows * k or n * k at or above 2^32). */
 moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
                                 int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
                                 const uint8_t* w, const float* w_scales,
@@ -163,7 +164,7 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
  * tiles are MOE_GEMM_COL_TILE wide in both. */
 #define MOE_GEMM_STREAM_TILE_M 16
 #define MOE_GEMM_STREAM_MAX_ROWS 64
-#define MOE_GEMM_TILED_TILE_M 128
+#define MOE_GEMM_TILED_TILE_M 256
 #define MOE_GEMM_COL_TILE 128
 
 /* Fused SiLU(gate) * up + 1x128 FP8 quantization of the FC2 input, over live
@@ -243,7 +244,9 @@ typedef struct {
   int32_t row_cap;       /* effective row capacity */
 } moe_workspace_layout;
 
-/* Fills `layout` for problem `p`. Errors: INVALID_ARG, CAPACITY. */
+/* Fills `layout` for problem `p`. Errors: INVALID_ARG, CAPACITY, UNSUPPORTED
+ * (num_experts above 1024, or a GEMM shape beyond moe_grouped_gemm_fp8's
+ * limits). */
 moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* layout);
 
 /* Bytes of workspace moe_forward needs for `p` (0 if `p` is invalid). */
