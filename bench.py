@@ -6,8 +6,10 @@ FP8 E4M3 with 128x128 fp32 block scales (TensorRT-LLM PR #21250,
 Performance). One step is one whole forward of the layer (align, act quant,
 FC1, SiLU*up+quant, FC2, top-k combine), replayed from a captured HIP graph
 with all inputs resident in HBM. Before every step the L2 and the 256 MB
-Infinity Cache are flushed by writing 1 GiB, so weights stream from HBM
-(the pages time with a cold L2, vLLM PR #59128, SM100 on B200).
+Infinity Cache are flushed by reading 1 GiB of unrelated data, so weights
+stream from HBM (the pages time with a cold L2, vLLM PR #59128, SM100 on
+B200). A read leaves the caches clean: flushing by writing would leave
+dirty lines whose write-back competes with the layer's own reads.
 
 Printed: one JSON line. `value` is the median cold layer latency in
 microseconds (HIP events around each replay); `ms_per_step` is the wall
@@ -164,7 +166,11 @@ def main():
     lay = moe.moe_workspace_plan(E, H, I, K, t_cap, cfg.align_rows, 0, fmt, act, lim)
     ws = torch.zeros(lay["total"], dtype=torch.uint8, device=dev)
     out = torch.zeros((t_cap, H), dtype=torch.int16, device=dev)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush_caches():
+        torch.sum(flush, dim=0, out=flush_sink)
 
     def fwd():
         moe.moe_forward(dx, dids, dw, *d_w, fmt, act, lim, cfg.align_rows, 0, t_live=dlive,
@@ -185,7 +191,7 @@ def main():
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         if not args.no_flush:
-            flush.fill_(float(i))
+            flush_caches()
         graph.replay()
     torch.cuda.synchronize()
 
@@ -195,7 +201,7 @@ def main():
     w0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
-            flush.fill_(float(i))
+            flush_caches()
         starts[i].record(stream)
         graph.replay()
         ends[i].record(stream)
@@ -224,7 +230,7 @@ def main():
     k_us = []
     for i in range(args.kernel_reps):
         if not args.no_flush:
-            flush.fill_(float(i))
+            flush_caches()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         moe.moe_grouped_gemm_fp8(xq, xs, fmt, d_w[0], d_w[1], counts, offsets, R, a_row_map=r2p,

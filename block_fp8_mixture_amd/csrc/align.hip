@@ -38,6 +38,9 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int E = num_experts;
+  // The first id this thread counts is loaded together with the live count
+  // (ids holds t_cap * topk entries, so the load is in bounds either way).
+  const int e_first = tid < static_cast<int64_t>(t_cap) * topk ? ids[tid] : -1;
   const int n_pairs = clamp_live(t_live_dev, t_cap) * topk;
   const int c0 = blockIdx.x * kChunk;
   if (blockIdx.x > 0 && c0 >= n_pairs) return;
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
 
   // Phase 1: per-expert counts of all live pairs and of pairs before the chunk.
   for (int p = tid; p < n_pairs; p += kThreads) {
-    const int e = ids[p];
+    const int e = p == tid ? e_first : ids[p];
     if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
       atomicAdd(&s_total[e], 1);
       if (p < c0) atomicAdd(&s_before[e], 1);

@@ -61,10 +61,12 @@ __device__ __forceinline__ uint2 pack_bf16x4(v4f v) {
 // Live rows of expert e, or 0 when its endpoints do not describe a segment
 // inside [0, row_cap): metadata that is not what moe_align produces can make
 // results meaningless but never makes a kernel touch memory out of bounds.
-__device__ __forceinline__ int expert_rows(const GemmArgs& p, int e) {
-  const int o0 = p.offsets[e], o1 = p.offsets[e + 1], c = p.counts[e];
-  if (o0 < 0 || o1 < o0 || o1 > p.row_cap || c <= 0) return 0;
+__device__ __forceinline__ int segment_rows(int o0, int o1, int c, int row_cap) {
+  if (o0 < 0 || o1 < o0 || o1 > row_cap || c <= 0) return 0;
   return c < o1 - o0 ? c : o1 - o0;
+}
+__device__ __forceinline__ int expert_rows(const GemmArgs& p, int e) {
+  return segment_rows(p.offsets[e], p.offsets[e + 1], p.counts[e], p.row_cap);
 }
 
 // A row feeding output row r, or -1 when the map points outside A.
@@ -75,19 +77,37 @@ __device__ __forceinline__ int a_source_row(const GemmArgs& p, int r) {
 
 // Ordered compaction of the experts whose row count satisfies `want`, into
 // s_list[0..n). s_pref[i] gets the exclusive prefix sum of units(count) over
-// the listed experts and s_pref[n] the total. Returns n. All threads call it.
+// the listed experts and s_pref[n] the total; when s_cnt / s_row0 are given
+// they get each listed expert's live rows and first row. Returns n. All
+// threads call it.
 template <int NT, typename Want, typename Units>
 __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int* s_list,
-                                 int* s_pref, int* s_tmp) {
+                                 int* s_pref, int* s_tmp, int* s_cnt = nullptr,
+                                 int* s_row0 = nullptr) {
   const int num_experts = p.num_experts;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   constexpr int kW = NT / 64;
+  constexpr int kC = (kMaxExperts + NT - 1) / NT;
+  // All metadata loads are issued before the first wait (unconditionally,
+  // at a clamped index, so no branch separates them).
+  int cnts[kC], row0s[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int e = c * NT + tid < num_experts ? c * NT + tid : num_experts - 1;
+    row0s[c] = p.offsets[e];
+    cnts[c] = p.offsets[e + 1];
+    cnts[c] = segment_rows(row0s[c], cnts[c], p.counts[e], p.row_cap);
+    if (c * NT + tid >= num_experts) cnts[c] = 0;
+  }
   int run_n = 0, run_u = 0;
-  for (int base = 0; base < num_experts; base += NT) {
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int base = c * NT;
+    if (base >= num_experts) break;
     const int e = base + tid;
-    const int cnt = e < num_experts ? expert_rows(p, e) : 0;
+    const int cnt = cnts[c];
     const bool flag = e < num_experts && want(cnt);
     const int u = flag ? units(cnt) : 0;
     const uint64_t mask = __ballot(flag);
@@ -111,6 +131,10 @@ __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int*
     if (flag) {
       s_list[bn + pos] = e;
       s_pref[bn + pos] = bu + incl - u;
+      if (s_cnt) {
+        s_cnt[bn + pos] = cnt;
+        s_row0[bn + pos] = row0s[c];
+      }
     }
     for (int w = 0; w < kW; ++w) {
       run_n += s_tmp[w];
@@ -138,80 +162,274 @@ struct TiledUnits {
 
 // ---------------------------------------------------------------- streaming
 
-template <int WN, int KSPLIT>
-__global__ __launch_bounds__(kThreads) void gemm_stream_kernel(GemmArgs p) {
-  static_assert(WN * KSPLIT == kThreads / 64, "4 waves per item");
-  constexpr int KCH = 8;                               // K blocks per register chunk
+struct TokenTiles {
+  __device__ int operator()(int c) const { return (c + kStreamTileM - 1) / kStreamTileM; }
+};
+
+// Task t of the ordered list of a kernel whose tasks are (expert, block of
+// weight rows, 16-row token tile): expert L.list[i], weight block rb, token
+// rows [16 mt, 16 mt + 16) of the expert's segment. Decoded from LDS only,
+// so finding a task never waits on global memory.
+struct StreamTask {
+  int e, rb, mt, cnt, row0;
+};
+
+struct StreamLists {
+  const int* list;
+  const int* pref;
+  const int* cnt;
+  const int* row0;
+  int n;
+};
+
+// t is uniform over the wave; readfirstlane tells the compiler so, which
+// keeps the task bookkeeping in scalar registers and branches.
+__device__ __forceinline__ StreamTask stream_task(const StreamLists& L, int n_rb, int t) {
+  const int key = t / n_rb;
+  int lo = 0, hi = L.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(L.pref[mid]) <= key) lo = mid; else hi = mid - 1;
+  }
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  StreamTask r;
+  r.e = __builtin_amdgcn_readfirstlane(L.list[lo]);
+  const int p0 = __builtin_amdgcn_readfirstlane(L.pref[lo]);
+  const int n_mt = __builtin_amdgcn_readfirstlane(L.pref[lo + 1]) - p0;
+  const int local = t - p0 * n_rb;
+  r.rb = local / n_mt;
+  r.mt = local % n_mt;
+  r.cnt = __builtin_amdgcn_readfirstlane(L.cnt[lo]);
+  r.row0 = __builtin_amdgcn_readfirstlane(L.row0[lo]);
+  return r;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const int const_int;
+
+// Load through the scalar data cache (a uniform address). Scalar loads are
+// counted by lgkmcnt, apart from the vector-memory queue, so waiting for one
+// never waits for the direct-to-LDS loads in flight.
+__device__ __forceinline__ int scalar_load(const int* q) { return *(const const_int*)(q); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 layout: vmcnt bits [3:0] and [15:14], expcnt and
+// lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// The LDS reads of one streaming stage: weight and token fragments (two
+// 16-byte halves each, 1 KB apart) and the two scales. Written as assembly
+// with its own lgkmcnt wait, so the compiler neither sees LDS reads that
+// might alias the direct-to-LDS loads in flight into other stages (it would
+// make them wait for every vector-memory operation) nor can use a result
+// early. Outputs are early-clobber: none may share a register with an
+// address that a later read of the block still needs.
+__device__ __forceinline__ void read_stage(uint32_t w0_addr, uint32_t w1_addr, uint32_t a0_addr,
+                                           uint32_t a1_addr, uint32_t sa_addr, uint32_t sw_addr,
+                                           uint4& w0, uint4& w1, uint4& a0, uint4& a1,
+                                           uint32_t& sa, uint32_t& sw) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b32 %4, %10\n\t"
+      "ds_read_b32 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w0), "=&v"(w1), "=&v"(a0), "=&v"(a1), "=&v"(sa), "=&v"(sw)
+      : "v"(w0_addr), "v"(w1_addr), "v"(a0_addr), "v"(a1_addr), "v"(sa_addr), "v"(sw_addr));
+}
+
+// Byte offset of 16-byte chunk c of row `row` in a slab of 128-byte rows.
+// Rows are written whole (8 lanes x 16 bytes each); chunk c of a row sits in
+// slot c ^ ((row >> 1) & 7), which gives the 16 lanes one ds_read_b128 cycle
+// serves (16 consecutive rows, the same chunk) distinct bank groups on the
+// 64 four-byte banks of gfx950's LDS.
+__device__ __forceinline__ uint32_t swz128(int row, int c) {
+  return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+}
+
+constexpr int kSD = 5;                           // stages in a workgroup's ring
+constexpr int kSGroupsPerCu = 2;                 // streaming workgroups per CU
+constexpr int kSRows = 64;                       // weight rows per task
+constexpr int kSW = kSRows * kGroup;             // weight slab of a stage (8 KB)
+constexpr int kSA = kStreamTileM * kGroup;       // token slab of a stage (2 KB)
+constexpr int kSStage = kSW + kSA + 256 + 256;   // + token scales + weight scale
+
+// Decode-sized experts (1..64 rows): weight streaming, bound by HBM.
+//
+// A task is (expert, 64 weight rows, one 16-row token tile) over the full K;
+// the four waves own 16 weight rows each. Tasks are ordered expert-major,
+// then weight block, then token tile, and consecutive tasks go to
+// workgroups on the same XCD, so the token tiles of one weight block (at
+// most 4) share its reads in L2. The K blocks of a workgroup's tasks form one
+// stream of stages (one 128-wide K block each: 64 weight rows, the 16 token
+// rows, their scales and the weight block scale), staged through a ring of
+// kSD LDS buffers by direct-to-LDS loads issued kSD - 1 stages ahead, so the
+// loads stay in flight across task boundaries. Each load moves whole
+// 128-byte lines (8 rows x 128 bytes): the number of lines a CU can have in
+// flight, not bytes, is what bounds its share of HBM bandwidth. Every wave
+// issues exactly three loads per stage (two for its weight rows, one for a
+// token half, the token scales or the weight scale), so one vmcnt immediate
+// fits all waves.
+//
+// Per K block: one v_mfma_f32_16x16x128_f8f6f4 into a zeroed temporary
+// (result: token = lane % 16, weight row = 4 * (lane / 16) + v), then
+// acc += t * (sa * sw) with four FMAs. Lanes whose token is past the expert's
+// rows load stand-in data from valid addresses and are never stored.
+template <bool UE8M0>
+__global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSD * kSStage];
   __shared__ int s_list[kMaxExperts];
   __shared__ int s_pref[kMaxExperts + 1];
   __shared__ int s_tmp[2 * kThreads / 64];
-  __shared__ v4f s_red[KSPLIT > 1 ? (KSPLIT - 1) * WN * 64 : 1];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_row0[kMaxExperts];
 
-  const int n_list = build_expert_list<kThreads>(p, WantSmall(), NoUnits(), s_list, s_pref, s_tmp);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wn = wave % WN;
-  const int ks = wave / WN;
-  constexpr int NB = 16 * WN;
+  const int n_list = build_expert_list<kThreads>(p, WantSmall(), TokenTiles(), s_list, s_pref,
+                                                 s_tmp, s_cnt, s_row0);
+  const StreamLists L{s_list, s_pref, s_cnt, s_row0, __builtin_amdgcn_readfirstlane(n_list)};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.n, K = p.k, KB = K / kGroup;
-  const int n_blocks = N / NB;
-  const int total = n_list * n_blocks;
-  const int kb0 = ks * KB / KSPLIT;
-  const int kb1 = (ks + 1) * KB / KSPLIT;
+  const int n_rb = N / kSRows;
+  const int n_tasks = __builtin_amdgcn_readfirstlane(s_pref[L.n]) * n_rb;
+  const int G = gridDim.x;
+  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  if (vid >= n_tasks) return;  // uniform over the workgroup; no barrier has been passed yet
+  const int total = ((n_tasks - vid + G - 1) / G) * KB;  // stages this workgroup streams
+  const int tok = lane & 15;
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int e = s_list[item / n_blocks];
-    const int nb = item % n_blocks;
-    const int cnt = expert_rows(p, e);
-    const int row0 = p.offsets[e];
-    const int n_mt = (cnt + kStreamTileM - 1) / kStreamTileM;
-    const int n0 = nb * NB + wn * 16;
-    const uint8_t* wp = p.w + (static_cast<int64_t>(e) * N + n0 + (lane & 15)) * K + (lane >> 4) * 32;
-    const float* wsp = p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + n0 / kGroup) * KB;
-
-    // One token tile at a time (decode experts have one); a second tile of
-    // the same expert re-reads this wave's weight slice, which is in L2.
-    for (int mt = 0; mt < n_mt; ++mt) {
-      const int j = mt * kStreamTileM + (lane & 15);
-      const int src = j < cnt ? a_source_row(p, row0 + j) : -1;
-      const bool rv = src >= 0;
-      const int arow = rv ? src : 0;
-      const uint8_t* ap = p.a + static_cast<int64_t>(arow) * K + (lane >> 4) * 32;
-      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int kc = kb0; kc < kb1; kc += KCH) {
-        v8i wf[KCH], af[KCH];
-        float sa[KCH];
-#pragma unroll
-        for (int q = 0; q < KCH; ++q) {
-          if (kc + q < kb1) {
-            wf[q] = *reinterpret_cast<const v8i*>(wp + static_cast<int64_t>(kc + q) * kGroup);
-            if (rv) {
-              af[q] = *reinterpret_cast<const v8i*>(ap + (kc + q) * kGroup);
-              sa[q] = load_scale(p.a_scales, p.fmt, static_cast<int64_t>(kc + q) * p.a_rows + arow);
-            } else {
-              af[q] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-              sa[q] = 0.0f;
-            }
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < KCH; ++q)
-          if (kc + q < kb1) acc = fma4(mfma_fp8(wf[q], af[q]), sa[q] * wsp[kc + q], acc);
-      }
-      if constexpr (KSPLIT > 1) {
-        if (ks > 0) s_red[((ks - 1) * WN + wn) * 64 + lane] = acc;
-        __syncthreads();
-        if (ks == 0)
-          for (int s = 1; s < KSPLIT; ++s) acc = acc + s_red[((s - 1) * WN + wn) * 64 + lane];
-        __syncthreads();
-      }
-      if (ks == 0 && j < cnt)
-        *reinterpret_cast<uint2*>(p.c + static_cast<int64_t>(row0 + j) * N + n0 + 4 * (lane >> 4)) =
-            pack_bf16x4(acc);
+  // ---- issue side: per-lane sources of the current task's loads
+  int i_task = vid, i_kb = 0;
+  const uint8_t* i_w = nullptr;   // this lane's weight bytes, first 8-row group
+  const uint8_t* i_w1 = nullptr;  // and second 8-row group
+  const uint8_t* i_x = nullptr;   // third load: token row slot, token scale or weight scale
+  int64_t i_xstep = 0;            // bytes between the third load's K blocks
+  // Loads move whole 128-byte lines: lane l of a load covers row 8 i + l / 8
+  // of its 8-row group and 16-byte chunk (l % 8) ^ sw(row), which lands in
+  // LDS slot l % 8 of that row (see swz128).
+  const int grow = lane >> 3;
+  auto start_task = [&](int t) {
+    const StreamTask k = stream_task(L, n_rb, t);
+    const int wrow = wave * 16 + grow;  // this lane's row in the wave's first 8-row group
+    const uint8_t* wrow_p = p.w + (static_cast<int64_t>(k.e) * N + k.rb * kSRows + wrow) * K;
+    i_w = wrow_p + (((lane & 7) ^ ((wrow >> 1) & 7)) << 4);
+    i_w1 = wrow_p + 8 * static_cast<int64_t>(K) + (((lane & 7) ^ (((wrow + 8) >> 1) & 7)) << 4);
+    const float* wsp = p.w_scales + (static_cast<int64_t>(k.e) * (N / kGroup) + (k.rb * kSRows) / kGroup) * KB;
+    if (wave == 3) {
+      i_x = reinterpret_cast<const uint8_t*>(wsp);
+      i_xstep = 4;
+      return;
     }
-    if (tid == 0 && p.tiles_visited && (nb * NB) % kColTile == 0) atomicAdd(p.tiles_visited, n_mt);
+    // Source row of this lane's token: token 8 * wave + l / 8 for the token
+    // slab (waves 0, 1), token l % 16 for the token scales (wave 2).
+    // Row-map entries come via the scalar cache, each index kept inside the
+    // expert's segment.
+    const int my_tok = wave < 2 ? wave * 8 + grow : tok;
+    const int first = k.mt * kStreamTileM;
+    const int last = k.row0 + k.cnt - 1;
+    int ar = k.row0 + first + my_tok;
+    if (p.a_row_map) {
+      int m = 0;
+#pragma unroll
+      for (int i = 0; i < kStreamTileM; ++i) {
+        const int r = k.row0 + first + i < last ? k.row0 + first + i : last;
+        const int v = scalar_load(p.a_row_map + r);
+        m = my_tok == i ? v : m;
+      }
+      ar = m / p.a_row_div;
+    }
+    const bool valid = first + my_tok < k.cnt && static_cast<unsigned>(ar) < static_cast<unsigned>(p.a_rows);
+    if (wave < 2) {
+      const int chunk = ((lane & 7) ^ ((my_tok >> 1) & 7)) << 4;
+      i_x = valid ? p.a + static_cast<int64_t>(ar) * K + chunk : i_w;  // stand-in: this lane's weight bytes
+      i_xstep = kGroup;
+    } else if (valid) {
+      i_x = static_cast<const uint8_t*>(p.a_scales) + static_cast<int64_t>(ar) * (UE8M0 ? 1 : 4);
+      i_xstep = static_cast<int64_t>(p.a_rows) * (UE8M0 ? 1 : 4);
+    } else {
+      i_x = reinterpret_cast<const uint8_t*>(wsp);  // stand-in: any valid address, one per K block
+      i_xstep = 4;
+    }
+  };
+  auto issue = [&](uint8_t* st) {
+    __builtin_amdgcn_global_load_lds(i_w + i_kb * kGroup, (lds_void*)(st + wave * 2048), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(st + wave * 2048 + 1024), 16, 0, 0);
+    const uint8_t* x = i_x + i_kb * i_xstep;
+    if (wave < 2)
+      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + wave * 1024), 16, 0, 0);
+    else if (wave == 2 && UE8M0)
+      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + kSA), 1, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + kSA + (wave - 2) * 256), 4, 0, 0);
+    if (++i_kb == KB) {
+      i_kb = 0;
+      i_task += G;
+      if (i_task < n_tasks) start_task(i_task);
+    }
+  };
+
+  // ---- compute side
+  int c_task = vid, c_kb = 0;
+  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const uint8_t* st) {
+    union {
+      uint4 u[2];
+      v8i v;
+    } wf, af;
+    uint32_t sraw, swraw;
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st));
+    const int c0 = 2 * (lane >> 4);  // fragment chunks c0, c0 + 1 of row tok
+    read_stage(base + wave * 2048 + swz128(tok, c0), base + wave * 2048 + swz128(tok, c0 + 1),
+               base + kSW + swz128(tok, c0), base + kSW + swz128(tok, c0 + 1),
+               base + kSW + kSA + tok * 4, base + kSW + kSA + 256, wf.u[0], wf.u[1], af.u[0],
+               af.u[1], sraw, swraw);
+    const float sa = UE8M0 ? __uint_as_float(sraw << 23) : __uint_as_float(sraw);
+    const float sw = __uint_as_float(swraw);
+    if (c_kb == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
+    if (++c_kb == KB) {
+      const StreamTask k = stream_task(L, n_rb, c_task);
+      const int j = k.mt * kStreamTileM + tok;
+      if (j < k.cnt)
+        *reinterpret_cast<uint2*>(p.c + static_cast<int64_t>(k.row0 + j) * N + k.rb * kSRows + wave * 16 + 4 * (lane >> 4)) =
+            pack_bf16x4(acc);
+      if (threadIdx.x == 0 && p.tiles_visited && (k.rb * kSRows) % kColTile == 0) atomicAdd(p.tiles_visited, 1);
+      c_kb = 0;
+      c_task += G;
+    }
+  };
+
+  start_task(i_task);
+  for (int d = 0; d < kSD - 1; ++d)
+    if (d < total) issue(s_ring + d * kSStage);
+  // Stage s: wait for this wave's loads of stage s (three per stage; in the
+  // steady state stages s+1 .. s+kSD-2 are still in flight, near the end
+  // fewer, and then everything is waited for), barrier so every wave's part
+  // is visible and stage s-1 is free, issue stage s+kSD-1 into it, compute s.
+  int slot = 0;  // s % kSD
+  for (int s = 0; s < total; ++s) {
+    if (s + kSD - 2 < total)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (kSD - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    const int prev = slot == 0 ? kSD - 1 : slot - 1;
+    if (s + kSD - 1 < total) issue(s_ring + prev * kSStage);
+    compute(s_ring + slot * kSStage);
+    slot = slot == kSD - 1 ? 0 : slot + 1;
   }
+}
+
+hipError_t launch_stream(const GemmArgs& g, hipStream_t stream) {
+  const int grid = device_cu_count() * kSGroupsPerCu;
+  if (g.fmt == kUe8m0)
+    hipLaunchKernelGGL(gemm_stream_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL(gemm_stream_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- tiled
@@ -230,7 +448,6 @@ constexpr int kMaxKBlocks = 256;              // K <= 32768 on this path
 // the ratios overflow.
 constexpr float kScaleFloor = 5.42101086e-20f;  // 2^-64
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Byte offset of 16-byte chunk c (0..3) of row `row` in a [rows][64 B] LDS
@@ -526,27 +743,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   }
 }
 
-template <int WN, int KSPLIT>
-hipError_t launch_stream(const GemmArgs& g, int live_bound, hipStream_t stream) {
-  const int n_blocks = g.n / (16 * WN);
-  const int64_t items = static_cast<int64_t>(live_bound) * n_blocks;
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
-  const int grid = static_cast<int>(items < cap ? items : cap);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_stream_kernel<WN, KSPLIT>), dim3(grid), dim3(kThreads), 0, stream, g);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
   const int live_bound = g.max_live_experts < g.num_experts ? g.max_live_experts : g.num_experts;
   if (live_bound <= 0) return hipSuccess;
-  const int kb = g.k / kGroup;
-  hipError_t err;
-  if (kb >= 16) err = launch_stream<1, 4>(g, live_bound, stream);
-  else if (kb >= 8) err = launch_stream<2, 2>(g, live_bound, stream);
-  else err = launch_stream<4, 1>(g, live_bound, stream);
+  hipError_t err = launch_stream(g, stream);
   if (err != hipSuccess) return err;
   if (g.max_rows_per_expert > kStreamMaxRows) {
     // Tiles of the large experts: at most ceil(rows / TM) + one partial row

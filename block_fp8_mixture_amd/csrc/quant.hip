@@ -58,14 +58,17 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int t_cap, const int32_t* __restrict__ t_live_dev,
     int hidden, uint8_t* __restrict__ xq, void* __restrict__ xs) {
   const int groups = hidden / kGroup;
-  const int n_live = clamp_live(t_live_dev, t_cap);
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
   const int l16 = threadIdx.x & 15;
-  if (gid >= static_cast<int64_t>(n_live) * groups) return;  // whole 16-lane groups exit
+  if (gid >= static_cast<int64_t>(t_cap) * groups) return;  // whole 16-lane groups exit
   const int t = static_cast<int>(gid / groups);
   const int g = static_cast<int>(gid % groups);
   const int64_t base = static_cast<int64_t>(t) * hidden + g * kGroup + l16 * 8;
-  const Vals8 v = unpack_bf16x8(*reinterpret_cast<const uint4*>(x + base));
+  // The row is inside x whether or not the token is live, so its load is
+  // issued together with the live-count load instead of after it.
+  const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
+  if (t >= clamp_live(t_live_dev, t_cap)) return;
+  const Vals8 v = unpack_bf16x8(raw);
   float s;
   const uint2 codes = quantize8<FMT>(v, &s);
   *reinterpret_cast<uint2*>(xq + base) = codes;
@@ -93,31 +96,57 @@ __device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
   return static_cast<float>(s * u);
 }
 
+// Blocks walk the (row, group) space with a grid stride. The expert
+// endpoints are staged in LDS once per block, so finding the expert of a row
+// (to skip padding) is a search in LDS, not a chain of dependent global
+// loads.
 template <int FMT, int ACT>
 __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gate_up, int inter, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int num_experts, int row_cap, float clamp_limit,
     uint8_t* __restrict__ hq, void* __restrict__ hs) {
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_cnt[kMaxExperts];
   const int groups = inter / kGroup;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
   const int l16 = threadIdx.x & 15;
-  const int total_rows = min(offsets[num_experts], row_cap);
-  if (gid >= static_cast<int64_t>(total_rows) * groups) return;
-  const int r = static_cast<int>(gid / groups);
-  const int g = static_cast<int>(gid % groups);
-  const int e = expert_of_row(offsets, num_experts, r);
-  if (r < offsets[e] || r - offsets[e] >= counts[e]) return;  // pad row: untouched
-  const int64_t src = static_cast<int64_t>(r) * (2 * inter) + g * kGroup + l16 * 8;
-  const Vals8 gv = unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_up + src));
-  const Vals8 uv = unpack_bf16x8(*reinterpret_cast<const uint4*>(gate_up + src + inter));
+  const int64_t n_groups = static_cast<int64_t>(row_cap) * groups;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kGroupsPerBlock;
+  int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
+  // First item's rows are loaded before the endpoints arrive (any row below
+  // row_cap is inside gate_up).
+  uint4 graw = {0, 0, 0, 0}, uraw = {0, 0, 0, 0};
+  if (gid < n_groups) {
+    const int64_t src = (gid / groups) * (2 * inter) + (gid % groups) * kGroup + l16 * 8;
+    graw = *reinterpret_cast<const uint4*>(gate_up + src);
+    uraw = *reinterpret_cast<const uint4*>(gate_up + src + inter);
+  }
+  for (int e = threadIdx.x; e <= num_experts; e += kThreads) {
+    s_off[e] = offsets[e];
+    if (e < num_experts) s_cnt[e] = counts[e];
+  }
+  __syncthreads();
+  const int total_rows = min(s_off[num_experts], row_cap);
   const double lim = clamp_limit;
-  Vals8 y;
+  for (bool first = true; gid < static_cast<int64_t>(total_rows) * groups; gid += stride, first = false) {
+    const int r = static_cast<int>(gid / groups);
+    const int g = static_cast<int>(gid % groups);
+    const int e = expert_of_row(s_off, num_experts, r);
+    if (r < s_off[e] || r - s_off[e] >= s_cnt[e]) continue;  // pad row: untouched
+    const int64_t src = static_cast<int64_t>(r) * (2 * inter) + g * kGroup + l16 * 8;
+    if (!first) {
+      graw = *reinterpret_cast<const uint4*>(gate_up + src);
+      uraw = *reinterpret_cast<const uint4*>(gate_up + src + inter);
+    }
+    const Vals8 gv = unpack_bf16x8(graw);
+    const Vals8 uv = unpack_bf16x8(uraw);
+    Vals8 y;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y.v[i] = swiglu<ACT>(gv.v[i], uv.v[i], lim);
-  float s;
-  const uint2 codes = quantize8<FMT>(y, &s);
-  *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + l16 * 8) = codes;
-  if (l16 == 0) store_scale(hs, FMT, static_cast<int64_t>(g) * row_cap + r, s);
+    for (int i = 0; i < 8; ++i) y.v[i] = swiglu<ACT>(gv.v[i], uv.v[i], lim);
+    float s;
+    const uint2 codes = quantize8<FMT>(y, &s);
+    *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + l16 * 8) = codes;
+    if (l16 == 0) store_scale(hs, FMT, static_cast<int64_t>(g) * row_cap + r, s);
+  }
 }
 
 template <int FMT>
@@ -136,7 +165,9 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
                       uint8_t* hq, void* hs, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
-  const int blocks = static_cast<int>((groups + kGroupsPerBlock - 1) / kGroupsPerBlock);
+  const int64_t need = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  const int blocks = static_cast<int>(need < cap ? need : cap);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((silu_mul_quant_kernel<FMT, ACT>), dim3(blocks), dim3(kThreads), 0, stream,
                      gate_up, inter, counts, offsets, num_experts, row_cap, clamp_limit, hq, hs);
