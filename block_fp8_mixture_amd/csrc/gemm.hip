@@ -69,9 +69,11 @@ __device__ __forceinline__ int expert_rows(const GemmArgs& p, int e) {
   return segment_rows(p.offsets[e], p.offsets[e + 1], p.counts[e], p.row_cap);
 }
 
-// A row feeding output row r, or -1 when the map points outside A.
+// A row feeding output row r, or -1 when the map points outside A. GATHER
+// is whether a row map is given (the kernels are specialised on it).
+template <bool GATHER>
 __device__ __forceinline__ int a_source_row(const GemmArgs& p, int r) {
-  const int ar = p.a_row_map ? p.a_row_map[r] / p.a_row_div : r;
+  const int ar = GATHER ? p.a_row_map[r] / p.a_row_div : r;
   return static_cast<unsigned>(ar) < static_cast<unsigned>(p.a_rows) ? ar : -1;
 }
 
@@ -277,7 +279,7 @@ constexpr int kSStage = kSW + kSA + 256 + 256;   // + token scales + weight scal
 // (result: token = lane % 16, weight row = 4 * (lane / 16) + v), then
 // acc += t * (sa * sw) with four FMAs. Lanes whose token is past the expert's
 // rows load stand-in data from valid addresses and are never stored.
-template <bool UE8M0>
+template <bool UE8M0, bool GATHER>
 __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSD * kSStage];
   __shared__ int s_list[kMaxExperts];
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
     const int first = k.mt * kStreamTileM;
     const int last = k.row0 + k.cnt - 1;
     int ar = k.row0 + first + my_tok;
-    if (p.a_row_map) {
+    if constexpr (GATHER) {
       int m = 0;
 #pragma unroll
       for (int i = 0; i < kStreamTileM; ++i) {
@@ -425,10 +427,11 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
 
 hipError_t launch_stream(const GemmArgs& g, hipStream_t stream) {
   const int grid = device_cu_count() * kSGroupsPerCu;
-  if (g.fmt == kUe8m0)
-    hipLaunchKernelGGL(gemm_stream_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(gemm_stream_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, g);
+  const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
+  if (u && m) hipLaunchKernelGGL((gemm_stream_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else if (u) hipLaunchKernelGGL((gemm_stream_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else if (m) hipLaunchKernelGGL((gemm_stream_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_stream_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -509,7 +512,7 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // into it; the epilogue multiplies by the last s. One VALU multiply per
 // element and block, no temporaries, no wait on an MFMA result. Power-of-two
 // ratios are exact.
-template <bool UE8M0>
+template <bool UE8M0, bool GATHER>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
   // Four stages and two token-scale buffers, all distinct objects, so the
   // compiler can tell that a read never aliases a direct-to-LDS load in
@@ -577,12 +580,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 32 + 16 * i + (lane >> 2);
       const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
-      const int ar = row < rows_here ? a_source_row(p, row0 + row) : -1;
+      const int ar = row < rows_here ? a_source_row<GATHER>(p, row0 + row) : -1;
       aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
       const int wr = n0 + row < N ? n0 + row : n0;
       woff[i] = static_cast<uint32_t>(wr) * K + chunk;
     }
-    const int sa_row = tok < rows_here ? a_source_row(p, row0 + tok) : -1;
+    const int sa_row = tok < rows_here ? a_source_row<GATHER>(p, row0 + tok) : -1;
     const int my_src = sa_row < 0 ? 0 : sa_row;
 
     auto issue = [&](int j, uint8_t* stage) {  // operand slabs of stage j
@@ -759,10 +762,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
     const int64_t cap = device_cu_count();
     const int grid = static_cast<int>(tiles < cap ? tiles : cap);
     if (grid > 0) {
-      if (g.fmt == kUe8m0)
-        hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3(grid), dim3(kTiledThreads), 0, stream, g);
-      else
-        hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
+      if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      else hipLaunchKernelGGL((gemm_tiled_kernel<false, false>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
       err = hipGetLastError();
     }
   }
