@@ -12,8 +12,12 @@ B200). A read leaves the caches clean: flushing by writing would leave
 dirty lines whose write-back competes with the layer's own reads.
 
 Printed: one JSON line. `value` is the median cold layer latency in
-microseconds (HIP events around each replay); `ms_per_step` is the wall
-clock of the bracketed timed loop divided by the steps (it includes the
+microseconds as the kernel span of one replay on the GPU timeline: two
+one-thread device-clock marks captured at both ends of the graph (the pages
+time the span of the layer's kernels, vLLM PR #59128, SM100 on B200). HIP
+events around each replay, which add the host-side graph launch latency,
+are reported beside it (`latency_us.events_median`). `ms_per_step` is the
+wall clock of the bracketed timed loop divided by the steps (it includes the
 flush). `roofline` describes the dominant kernel (the FC1 weight-streaming
 GEMM), timed on its own with HIP events on the stream it runs on.
 `cpu_baseline` is the CPU oracle on the same workload.
@@ -242,9 +246,27 @@ def main():
             fwd()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    # Device-clock marks at both ends of the graph: each replay's kernel span
+    # (first kernel start to last kernel end, plus the two one-thread marks)
+    # on the GPU timeline, as a kernel trace measures it.
+    import ctypes
+    bl = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
+    bl.moe_bench_mark.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    bl.moe_bench_clock_hz.restype = ctypes.c_int64
+    mark_cap = 2 * (args.steps + args.warmup + 8)
+    mark_slots = torch.zeros(mark_cap, dtype=torch.int64, device=dev)
+    mark_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def mark():
+        if bl.moe_bench_mark(mark_slots.data_ptr(), mark_ctr.data_ptr(), mark_cap,
+                             torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("device-clock mark launch failed")
+
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
+        mark()
         fwd()
+        mark()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -256,6 +278,7 @@ def main():
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mark_ctr.zero_()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for i in range(args.steps):
@@ -266,12 +289,18 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    lat_us = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))
+    ev_us = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))
+    ev_med = statistics.median(ev_us)
+    hz = bl.moe_bench_clock_hz()
+    marks = mark_slots[:2 * args.steps].cpu().numpy().reshape(-1, 2)
+    if hz <= 0 or int(mark_ctr.item()) != 2 * args.steps or (marks[:, 1] <= marks[:, 0]).any():
+        raise RuntimeError("device-clock marks incomplete")
+    lat_us = sorted(((marks[:, 1] - marks[:, 0]) * 1e6 / hz).tolist())
     med = statistics.median(lat_us)
     p10 = lat_us[int(0.1 * (len(lat_us) - 1))]
     p90 = lat_us[int(0.9 * (len(lat_us) - 1))]
-    print(f"# layer latency median {med:.2f} us (p10 {p10:.2f}, p90 {p90:.2f}) over "
-          f"{args.steps} steps", file=sys.stderr, flush=True)
+    print(f"# layer kernel span median {med:.2f} us (p10 {p10:.2f}, p90 {p90:.2f}); events around "
+          f"the replay {ev_med:.2f} us; over {args.steps} steps", file=sys.stderr, flush=True)
 
     # ---- dominant kernel alone: FC1 grouped GEMM on the forward's intermediates
     n_live_e, pairs = live_stats(ids, t_live, E)
@@ -360,7 +389,8 @@ def main():
             "token_capacity": t_cap, "act_scale_fmt": fmt, "activation": act,
             "cache": "warm" if args.no_flush else "flushed before every step",
         },
-        "latency_us": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3)},
+        "latency_us": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3),
+                       "events_median": round(ev_med, 3)},
         "live_experts": n_live_e,
         "live_pairs": pairs,
         "live_tflops": round(flops / (med * 1e-6) / 1e12, 4),

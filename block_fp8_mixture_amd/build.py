@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["align.hip", "quant.hip", "gemm.hip", "combine.hip", "capi.hip"]
+# Benchmark-only device-clock marks, a library of their own.
+BENCH_SOURCES = ["bench_clock.hip"]
+BENCH_LIB = os.path.join(HERE, "libmoebench.so")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -45,14 +48,16 @@ def build(verbose=False):
         out = _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, out
 
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(min(len(SOURCES) + len(BENCH_SOURCES), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
     for obj, out in results:
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *[o for o, _ in results]])
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, objs in ((LIB, results[:n]), (BENCH_LIB, results[n:])):
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *[o for o, _ in objs]])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -14,6 +14,7 @@
 // are ordered by an exclusive sum over per-wave counts.
 #include "device_common.h"
 #include "kernels.h"
+#include "quant_device.h"
 
 namespace moe {
 namespace {
@@ -22,8 +23,9 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 4096;
 
-__global__ __launch_bounds__(kThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
+// The work of align block `block` (all kThreads threads of a block call it).
+__device__ __forceinline__ void align_block(
+    int block, const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
     int32_t* __restrict__ pair_to_row) {
@@ -42,8 +44,8 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   // (ids holds t_cap * topk entries, so the load is in bounds either way).
   const int e_first = tid < static_cast<int64_t>(t_cap) * topk ? ids[tid] : -1;
   const int n_pairs = clamp_live(t_live_dev, t_cap) * topk;
-  const int c0 = blockIdx.x * kChunk;
-  if (blockIdx.x > 0 && c0 >= n_pairs) return;
+  const int c0 = block * kChunk;
+  if (block > 0 && c0 >= n_pairs) return;
 
   for (int e = tid; e < E; e += kThreads) {
     s_total[e] = 0;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     __syncthreads();
   }
 
-  if (blockIdx.x == 0) {
+  if (block == 0) {
     for (int e = tid; e < E; e += kThreads) {
       counts[e] = s_total[e];
       offsets[e] = s_off[e];
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   for (int base = c0; base < c1; base += kThreads) {
     const int p = base + tid;
     const bool in_range = p < c1;
-    const int e = in_range ? ids[p] : -1;
+    const int e = in_range ? (p == tid ? e_first : ids[p]) : -1;
     const bool ok = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
     const uint64_t below = (uint64_t(1) << lane) - 1;
     int rank = 0;
@@ -127,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
       pair_to_row[p] = -1;
     }
     __syncthreads();
+    if (base + kThreads >= c1) break;  // last round: the running counts are not needed again
     for (int x = tid; x < E; x += kThreads) {
       int s = 0;
       for (int w = 0; w < kWaves; ++w) {
@@ -139,16 +142,73 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
   }
 }
 
+__global__ __launch_bounds__(kThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
+    int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
+    int32_t* __restrict__ pair_to_row) {
+  align_block(blockIdx.x, ids, t_cap, t_live_dev, topk, num_experts, align_rows, counts, offsets,
+              row_to_pair, pair_to_row);
+}
+
+// Routing alignment and the activation quantization in one launch, for the
+// whole-layer entry point: the two do not depend on each other, so running
+// them as one grid removes a launch and overlaps their memory latencies.
+// Blocks [0, n_align) align; the rest quantize kThreads / 16 groups each.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void prep_kernel(
+    const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
+    int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
+    int32_t* __restrict__ pair_to_row, int n_align, const uint16_t* __restrict__ x, int hidden,
+    uint8_t* __restrict__ xq, void* __restrict__ xs) {
+  if (static_cast<int>(blockIdx.x) < n_align) {
+    align_block(blockIdx.x, ids, t_cap, t_live_dev, topk, num_experts, align_rows, counts,
+                offsets, row_to_pair, pair_to_row);
+    return;
+  }
+  const int64_t gid = static_cast<int64_t>(blockIdx.x - n_align) * (kThreads / 16) + (threadIdx.x >> 4);
+  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15);
+}
+
+int align_blocks(int t_cap, int topk) {
+  const int64_t pairs = static_cast<int64_t>(t_cap) * topk;
+  return static_cast<int>(pairs > 0 ? (pairs + kChunk - 1) / kChunk : 1);
+}
+
 }  // namespace
 
 hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                         int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                         int32_t* row_to_pair, int32_t* pair_to_row, hipStream_t stream) {
-  const int64_t pairs = static_cast<int64_t>(t_cap) * topk;
-  const int blocks = static_cast<int>(pairs > 0 ? (pairs + kChunk - 1) / kChunk : 1);
+  const int blocks = align_blocks(t_cap, topk);
   hipLaunchKernelGGL(align_kernel, dim3(blocks), dim3(kThreads), 0, stream, ids, t_cap,
                      t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
                      pair_to_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
+                       int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
+                       int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
+                       int fmt, uint8_t* xq, void* xs, hipStream_t stream) {
+  const int n_align = align_blocks(t_cap, topk);
+  const int64_t groups = static_cast<int64_t>(t_cap) * (hidden / kGroup);
+  const int64_t n_quant = (groups + kThreads / 16 - 1) / (kThreads / 16);
+  if (n_align + n_quant > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(n_align + n_quant));
+  if (fmt == kFp32)
+    hipLaunchKernelGGL(prep_kernel<kFp32>, grid, dim3(kThreads), 0, stream, ids, t_cap, t_live_dev,
+                       topk, num_experts, align_rows, counts, offsets, row_to_pair, pair_to_row,
+                       n_align, x, hidden, xq, xs);
+  else if (fmt == kFp32Pow2)
+    hipLaunchKernelGGL(prep_kernel<kFp32Pow2>, grid, dim3(kThreads), 0, stream, ids, t_cap,
+                       t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
+                       pair_to_row, n_align, x, hidden, xq, xs);
+  else
+    hipLaunchKernelGGL(prep_kernel<kUe8m0>, grid, dim3(kThreads), 0, stream, ids, t_cap,
+                       t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
+                       pair_to_row, n_align, x, hidden, xq, xs);
   return hipGetLastError();
 }
 

@@ -243,10 +243,10 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   const int64_t pairs64 = static_cast<int64_t>(p->t_cap) * p->topk;
   const int pairs = static_cast<int>(pairs64);
 
-  hipError_t e = moe::launch_align(t->topk_ids, p->t_cap, t->t_live_dev, p->topk,
-                                   p->num_experts, p->align_rows, counts, offsets, r2p, p2r, s);
-  if (e == hipSuccess)
-    e = moe::launch_act_quant(t->x, p->t_cap, t->t_live_dev, p->hidden, p->scale_fmt, xq, xs, s);
+  // Alignment and activation quantization share one launch (independent work).
+  hipError_t e = moe::launch_prep(t->topk_ids, p->t_cap, t->t_live_dev, p->topk, p->num_experts,
+                                  p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden,
+                                  p->scale_fmt, xq, xs, s);
 
   moe::GemmArgs g;
   g.fmt = p->scale_fmt;

@@ -16,6 +16,12 @@ hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev
                         int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                         int32_t* row_to_pair, int32_t* pair_to_row, hipStream_t stream);
 
+// moe_align and moe_act_quant of one layer in a single launch.
+hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
+                       int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
+                       int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
+                       int fmt, uint8_t* xq, void* xs, hipStream_t stream);
+
 hipError_t launch_act_quant(const uint16_t* x, int t_cap, const int32_t* t_live_dev, int hidden,
                             int fmt, uint8_t* xq, void* xs, hipStream_t stream);
 

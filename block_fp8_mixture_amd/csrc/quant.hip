@@ -5,12 +5,13 @@
 // codes = E4M3(x / scale); power-of-two scales round up (vLLM PR #59128,
 // Purpose: plain and power-of-two-rounded fp32 scales, packed UE8M0).
 //
-// Layout: 16 lanes own one 128-element group, 8 consecutive elements each
-// (one 16-byte BF16 load), so a 256-thread block quantizes 16 groups; the
-// group amax is a 4-step xor-shuffle reduction inside the 16 lanes. Codes
-// leave as one 8-byte store per lane, the scale from the group's first lane.
+// Activations: 16 lanes own one 128-element group, 8 consecutive elements
+// each (one 16-byte BF16 load); the group amax is a 4-step xor-shuffle
+// reduction inside the 16 lanes. SiLU * up: one wave per group, 2 elements
+// per lane. The scale leaves from the group's first lane.
 #include "device_common.h"
 #include "kernels.h"
+#include "quant_device.h"
 
 namespace moe {
 namespace {
@@ -18,61 +19,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGroupsPerBlock = kThreads / 16;
 
-struct Vals8 {
-  float v[8];
-};
-
-__device__ __forceinline__ Vals8 unpack_bf16x8(uint4 raw) {
-  Vals8 r;
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    r.v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
-  return r;
-}
-
-// Quantizes the 8 values this lane holds against the group's scale; returns
-// the 8 codes packed little-endian and writes the stored scale when asked.
-template <int FMT>
-__device__ __forceinline__ uint2 quantize8(const Vals8& x, float* scale_out) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
-  amax = group_max<16>(amax);
-  const float s = group_scale(amax, FMT);
-  const float inv = FMT == kFp32 ? 0.0f : 1.0f / s;  // exact for powers of two
-  float q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = scale_div(x.v[i], s, inv, FMT);
-  uint2 out;
-  out.x = cvt_pk_e4m3(q[0], q[1]) | (cvt_pk_e4m3(q[2], q[3]) << 16);
-  out.y = cvt_pk_e4m3(q[4], q[5]) | (cvt_pk_e4m3(q[6], q[7]) << 16);
-  *scale_out = s;
-  return out;
-}
-
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int t_cap, const int32_t* __restrict__ t_live_dev,
     int hidden, uint8_t* __restrict__ xq, void* __restrict__ xs) {
-  const int groups = hidden / kGroup;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
-  const int l16 = threadIdx.x & 15;
-  if (gid >= static_cast<int64_t>(t_cap) * groups) return;  // whole 16-lane groups exit
-  const int t = static_cast<int>(gid / groups);
-  const int g = static_cast<int>(gid % groups);
-  const int64_t base = static_cast<int64_t>(t) * hidden + g * kGroup + l16 * 8;
-  // The row is inside x whether or not the token is live, so its load is
-  // issued together with the live-count load instead of after it.
-  const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
-  if (t >= clamp_live(t_live_dev, t_cap)) return;
-  const Vals8 v = unpack_bf16x8(raw);
-  float s;
-  const uint2 codes = quantize8<FMT>(v, &s);
-  *reinterpret_cast<uint2*>(xq + base) = codes;
-  if (l16 == 0) store_scale(xs, FMT, static_cast<int64_t>(g) * t_cap + t, s);
+  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15);
 }
 
 enum Act : int { kSwiglu = 0, kSwigluClamp = 1, kSwigluClampAfterSilu = 2 };
@@ -96,10 +48,12 @@ __device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
   return static_cast<float>(s * u);
 }
 
-// Blocks walk the (row, group) space with a grid stride. The expert
-// endpoints are staged in LDS once per block, so finding the expert of a row
-// (to skip padding) is a search in LDS, not a chain of dependent global
-// loads.
+// One wave per 128-column group (2 elements per lane): at decode sizes only a
+// few dozen groups are live, so spreading each over a whole wave keeps the
+// serial fp64 SiLU work per lane short. Waves walk the (row, group) space with
+// a grid stride. The expert endpoints are staged in LDS once per block, so
+// finding the expert of a row (to skip padding) is a search in LDS, not a
+// chain of dependent global loads.
 template <int FMT, int ACT>
 __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gate_up, int inter, const int32_t* __restrict__ counts,
@@ -107,18 +61,19 @@ __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     uint8_t* __restrict__ hq, void* __restrict__ hs) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cnt[kMaxExperts];
+  constexpr int kWavesPerBlock = kThreads / 64;
   const int groups = inter / kGroup;
-  const int l16 = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63;
   const int64_t n_groups = static_cast<int64_t>(row_cap) * groups;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kGroupsPerBlock;
-  int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
-  // First item's rows are loaded before the endpoints arrive (any row below
-  // row_cap is inside gate_up).
-  uint4 graw = {0, 0, 0, 0}, uraw = {0, 0, 0, 0};
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+  int64_t gid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  // The first group's inputs are loaded before the endpoints arrive (any row
+  // below row_cap is inside gate_up).
+  uint32_t graw = 0, uraw = 0;
   if (gid < n_groups) {
-    const int64_t src = (gid / groups) * (2 * inter) + (gid % groups) * kGroup + l16 * 8;
-    graw = *reinterpret_cast<const uint4*>(gate_up + src);
-    uraw = *reinterpret_cast<const uint4*>(gate_up + src + inter);
+    const int64_t src = (gid / groups) * (2 * inter) + (gid % groups) * kGroup + lane * 2;
+    graw = *reinterpret_cast<const uint32_t*>(gate_up + src);
+    uraw = *reinterpret_cast<const uint32_t*>(gate_up + src + inter);
   }
   for (int e = threadIdx.x; e <= num_experts; e += kThreads) {
     s_off[e] = offsets[e];
@@ -132,20 +87,20 @@ __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     const int g = static_cast<int>(gid % groups);
     const int e = expert_of_row(s_off, num_experts, r);
     if (r < s_off[e] || r - s_off[e] >= s_cnt[e]) continue;  // pad row: untouched
-    const int64_t src = static_cast<int64_t>(r) * (2 * inter) + g * kGroup + l16 * 8;
+    const int64_t src = static_cast<int64_t>(r) * (2 * inter) + g * kGroup + lane * 2;
     if (!first) {
-      graw = *reinterpret_cast<const uint4*>(gate_up + src);
-      uraw = *reinterpret_cast<const uint4*>(gate_up + src + inter);
+      graw = *reinterpret_cast<const uint32_t*>(gate_up + src);
+      uraw = *reinterpret_cast<const uint32_t*>(gate_up + src + inter);
     }
-    const Vals8 gv = unpack_bf16x8(graw);
-    const Vals8 uv = unpack_bf16x8(uraw);
-    Vals8 y;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y.v[i] = swiglu<ACT>(gv.v[i], uv.v[i], lim);
-    float s;
-    const uint2 codes = quantize8<FMT>(y, &s);
-    *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + l16 * 8) = codes;
-    if (l16 == 0) store_scale(hs, FMT, static_cast<int64_t>(g) * row_cap + r, s);
+    const float y0 = swiglu<ACT>(bf16_to_f32(graw & 0xFFFFu), bf16_to_f32(uraw & 0xFFFFu), lim);
+    const float y1 = swiglu<ACT>(bf16_to_f32(graw >> 16), bf16_to_f32(uraw >> 16), lim);
+    const float amax = group_max<64>(fmaxf(fabsf(y0), fabsf(y1)));
+    const float sc = group_scale(amax, FMT);
+    const float inv = FMT == kFp32 ? 0.0f : 1.0f / sc;  // exact for powers of two
+    const uint32_t codes = cvt_pk_e4m3(scale_div(y0, sc, inv, FMT), scale_div(y1, sc, inv, FMT));
+    *reinterpret_cast<uint16_t*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + lane * 2) =
+        static_cast<uint16_t>(codes);
+    if (lane == 0) store_scale(hs, FMT, static_cast<int64_t>(g) * row_cap + r, sc);
   }
 }
 
@@ -165,7 +120,7 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
                       uint8_t* hq, void* hs, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
-  const int64_t need = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const int64_t need = (groups + kThreads / 64 - 1) / (kThreads / 64);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
   const int blocks = static_cast<int>(need < cap ? need : cap);
   if (blocks == 0) return hipSuccess;

@@ -1,0 +1,73 @@
+// Device helpers of the 1x128 FP8 quantization, shared by the activation
+// quantization kernel and the fused routing + quantization kernel.
+//
+// Rule (vLLM PR #65794, Details): scale = max(amax / 448, 1 / (448 * 512)),
+// codes = E4M3(x / scale); power-of-two scales round up. 16 lanes own one
+// 128-element group, 8 consecutive elements each (one 16-byte BF16 load);
+// the group amax is a 4-step xor-shuffle reduction inside the 16 lanes.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+struct Vals8 {
+  float v[8];
+};
+
+__device__ __forceinline__ Vals8 unpack_bf16x8(uint4 raw) {
+  Vals8 r;
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    r.v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  return r;
+}
+
+// Quantizes the 8 values this lane holds against the group's scale; returns
+// the 8 codes packed little-endian and writes the stored scale when asked.
+template <int FMT>
+__device__ __forceinline__ uint2 quantize8(const Vals8& x, float* scale_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
+  amax = group_max<16>(amax);
+  const float s = group_scale(amax, FMT);
+  const float inv = FMT == kFp32 ? 0.0f : 1.0f / s;  // exact for powers of two
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = scale_div(x.v[i], s, inv, FMT);
+  uint2 out;
+  out.x = cvt_pk_e4m3(q[0], q[1]) | (cvt_pk_e4m3(q[2], q[3]) << 16);
+  out.y = cvt_pk_e4m3(q[4], q[5]) | (cvt_pk_e4m3(q[6], q[7]) << 16);
+  *scale_out = s;
+  return out;
+}
+
+// Quantizes group gid (token gid / (hidden / 128), group gid % (hidden / 128))
+// of x with the 16 lanes l16 = 0..15 that call it. Groups past t_cap exit;
+// groups of tokens past the live count are not written.
+template <int FMT>
+__device__ __forceinline__ void act_quant_group(const uint16_t* __restrict__ x, int t_cap,
+                                                const int32_t* __restrict__ t_live_dev, int hidden,
+                                                uint8_t* __restrict__ xq, void* __restrict__ xs,
+                                                int64_t gid, int l16) {
+  const int groups = hidden / kGroup;
+  if (gid >= static_cast<int64_t>(t_cap) * groups) return;  // whole 16-lane groups exit
+  const int t = static_cast<int>(gid / groups);
+  const int g = static_cast<int>(gid % groups);
+  const int64_t base = static_cast<int64_t>(t) * hidden + g * kGroup + l16 * 8;
+  // The row is inside x whether or not the token is live, so its load is
+  // issued together with the live-count load instead of after it.
+  const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
+  if (t >= clamp_live(t_live_dev, t_cap)) return;
+  const Vals8 v = unpack_bf16x8(raw);
+  float s;
+  const uint2 codes = quantize8<FMT>(v, &s);
+  *reinterpret_cast<uint2*>(xq + base) = codes;
+  if (l16 == 0) store_scale(xs, FMT, static_cast<int64_t>(g) * t_cap + t, s);
+}
+
+}  // namespace moe
