@@ -29,6 +29,8 @@
 //    a 4-deep LDS ring of 64-byte K stages by direct-to-LDS loads, scales
 //    applied by rescaling the accumulator once per 128-wide block (details at
 //    the kernel).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -80,8 +82,9 @@ __device__ __forceinline__ int a_source_row(const GemmArgs& p, int r) {
 // Ordered compaction of the experts whose row count satisfies `want`, into
 // s_list[0..n). s_pref[i] gets the exclusive prefix sum of units(count) over
 // the listed experts and s_pref[n] the total; when s_cnt / s_row0 are given
-// they get each listed expert's live rows and first row. Returns n. All
-// threads call it.
+// they get each listed expert's live rows and first row (s_cnt == s_list
+// packs the expert id into bits 0..15 and the rows above them, for counts
+// below 2^15). Returns n. All threads call it.
 template <int NT, typename Want, typename Units>
 __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int* s_list,
                                  int* s_pref, int* s_tmp, int* s_cnt = nullptr,
@@ -131,9 +134,12 @@ __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int*
       bu += s_tmp[kW + w];
     }
     if (flag) {
-      s_list[bn + pos] = e;
+      if (s_cnt != s_list) s_list[bn + pos] = e;
       s_pref[bn + pos] = bu + incl - u;
-      if (s_cnt) {
+      if (s_cnt == s_list) {  // packed: expert id in bits 0..15, count above
+        s_list[bn + pos] = e | (cnt << 16);
+        s_row0[bn + pos] = row0s[c];
+      } else if (s_cnt) {
         s_cnt[bn + pos] = cnt;
         s_row0[bn + pos] = row0s[c];
       }
@@ -177,9 +183,8 @@ struct StreamTask {
 };
 
 struct StreamLists {
-  const int* list;
+  const int* list;  // expert id | live rows << 16
   const int* pref;
-  const int* cnt;
   const int* row0;
   int n;
 };
@@ -195,13 +200,14 @@ __device__ __forceinline__ StreamTask stream_task(const StreamLists& L, int n_rb
   }
   lo = __builtin_amdgcn_readfirstlane(lo);
   StreamTask r;
-  r.e = __builtin_amdgcn_readfirstlane(L.list[lo]);
+  const int packed = __builtin_amdgcn_readfirstlane(L.list[lo]);
+  r.e = packed & 0xFFFF;
+  r.cnt = packed >> 16;
   const int p0 = __builtin_amdgcn_readfirstlane(L.pref[lo]);
   const int n_mt = __builtin_amdgcn_readfirstlane(L.pref[lo + 1]) - p0;
   const int local = t - p0 * n_rb;
   r.rb = local / n_mt;
   r.mt = local % n_mt;
-  r.cnt = __builtin_amdgcn_readfirstlane(L.cnt[lo]);
   r.row0 = __builtin_amdgcn_readfirstlane(L.row0[lo]);
   return r;
 }
@@ -251,29 +257,78 @@ __device__ __forceinline__ uint32_t swz128(int row, int c) {
   return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
 }
 
-constexpr int kSD = 5;                           // stages in a workgroup's ring
-constexpr int kSGroupsPerCu = 2;                 // streaming workgroups per CU
-constexpr int kSRows = 64;                       // weight rows per task
-constexpr int kSW = kSRows * kGroup;             // weight slab of a stage (8 KB)
-constexpr int kSA = kStreamTileM * kGroup;       // token slab of a stage (2 KB)
-constexpr int kSStage = kSW + kSA + 256 + 256;   // + token scales + weight scale
+// Workgroup barrier for the pipelined K loop. A fence (as in
+// __syncthreads()) would make the compiler wait for every vector-memory
+// operation in flight, including the direct-to-LDS loads of later stages, and
+// so collapse the pipeline. Instead the caller waits for exactly the data the
+// next stage needs (explicit vmcnt), this waits for the wave's own LDS
+// writes, and the "memory" clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Two ways to cut the work into tasks, chosen per launch on the device:
+//  A: (expert, 64 weight rows, 16-token tile); the 4 waves own 16 weight rows
+//     each; a stage is one 128-wide K block (64 rows x 128 B of weights).
+//  B, when there are fewer A tasks than about 3/4 of the workgroups (few live
+//     experts): (expert, 16 weight rows, 16-token tile); a stage is 4
+//     consecutive K blocks, one per wave, and the waves' partial sums are
+//     added in LDS in wave order at the end of the task. Four times as many
+//     tasks, so few live experts still keep every CU streaming.
+constexpr int kSRowsA = 64;  // weight rows of an A task
+constexpr int kSRowsB = 16;  // weight rows of a B task
+// A stage: [W: wave w's rows 16w..16w+15, 128 B each, swz128] 8 KB,
+//          [tokens: 16 rows x 128 B, swz128] 2 KB,
+//          [token scales: 64 x 4 B, lane l -> token l % 16] [weight scale].
+// B stage: [W of K block w: 16 rows x 128 B, swz128] 4 x 2 KB,
+//          [tokens of K block w: 16 rows x 128 B, swz128] 4 x 2 KB,
+//          [token scales: lane l -> K block l / 16, token l % 16]
+//          [weight scales: lane l -> K block l % 4].
+constexpr int kOffTokA = kSRowsA * kGroup;
+constexpr int kOffSclA = kOffTokA + kStreamTileM * kGroup;
+constexpr int kSStageA = kOffSclA + 512;  // 10752
+constexpr int kOffTokB = 4 * 2048;
+constexpr int kOffSclB = 8 * 2048;
+constexpr int kSStageB = kOffSclB + 512;  // 16896
+constexpr int kSDA = 6;                   // stages in an A ring
+constexpr int kSDB = 4;                   // stages in a B ring
+constexpr int kSLoadsA = 3;               // loads per wave and stage
+constexpr int kSLoadsB = 5;
+constexpr int kSRing = kSDA * kSStageA > kSDB * kSStageB ? kSDA * kSStageA : kSDB * kSStageB;
+constexpr int kSGroupsPerCu = 2;          // streaming workgroups per CU
+
+// One wave's fp32 partial (16 B per lane) to LDS, and the in-order sum of the
+// 4 waves' partials (1 KB apart), as assembly for the same reason as
+// read_stage.
+__device__ __forceinline__ void lds_store_v4f(uint32_t addr, v4f v) {
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ v4f lds_sum4_v4f(uint32_t addr) {
+  v4f a, b, c, d;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(addr));
+  return ((a + b) + c) + d;
+}
 
 // Decode-sized experts (1..64 rows): weight streaming, bound by HBM.
 //
-// A task is (expert, 64 weight rows, one 16-row token tile) over the full K;
-// the four waves own 16 weight rows each. Tasks are ordered expert-major,
-// then weight block, then token tile, and consecutive tasks go to
-// workgroups on the same XCD, so the token tiles of one weight block (at
-// most 4) share its reads in L2. The K blocks of a workgroup's tasks form one
-// stream of stages (one 128-wide K block each: 64 weight rows, the 16 token
-// rows, their scales and the weight block scale), staged through a ring of
-// kSD LDS buffers by direct-to-LDS loads issued kSD - 1 stages ahead, so the
-// loads stay in flight across task boundaries. Each load moves whole
-// 128-byte lines (8 rows x 128 bytes): the number of lines a CU can have in
-// flight, not bytes, is what bounds its share of HBM bandwidth. Every wave
-// issues exactly three loads per stage (two for its weight rows, one for a
-// token half, the token scales or the weight scale), so one vmcnt immediate
-// fits all waves.
+// Tasks are ordered expert-major, then weight block, then token tile, and
+// consecutive tasks go to workgroups on the same XCD, so the token tiles of
+// one weight block (at most 4) share its reads in L2. The stages of a
+// workgroup's tasks form one stream, staged through a ring of LDS buffers by
+// direct-to-LDS loads issued (ring - 1) stages ahead, so loads stay in
+// flight across task boundaries. Each load moves whole 128-byte lines (8 rows
+// x 128 bytes): the number of lines a CU can have in flight, not bytes, is
+// what bounds its share of HBM bandwidth. Every wave issues the same number
+// of loads per stage, so one vmcnt immediate fits all waves.
 //
 // Per K block: one v_mfma_f32_16x16x128_f8f6f4 into a zeroed temporary
 // (result: token = lane % 16, weight row = 4 * (lane / 16) + v), then
@@ -281,148 +336,199 @@ constexpr int kSStage = kSW + kSA + 256 + 256;   // + token scales + weight scal
 // rows load stand-in data from valid addresses and are never stored.
 template <bool UE8M0, bool GATHER>
 __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSD * kSStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSRing];
   __shared__ int s_list[kMaxExperts];
   __shared__ int s_pref[kMaxExperts + 1];
   __shared__ int s_tmp[2 * kThreads / 64];
-  __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_row0[kMaxExperts];
 
   const int n_list = build_expert_list<kThreads>(p, WantSmall(), TokenTiles(), s_list, s_pref,
-                                                 s_tmp, s_cnt, s_row0);
-  const StreamLists L{s_list, s_pref, s_cnt, s_row0, __builtin_amdgcn_readfirstlane(n_list)};
+                                                 s_tmp, s_list, s_row0);
+  const StreamLists L{s_list, s_pref, s_row0, __builtin_amdgcn_readfirstlane(n_list)};
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.n, K = p.k, KB = K / kGroup;
-  const int n_rb = N / kSRows;
-  const int n_tasks = __builtin_amdgcn_readfirstlane(s_pref[L.n]) * n_rb;
+  const int tiles = __builtin_amdgcn_readfirstlane(s_pref[L.n]);
   const int G = gridDim.x;
-  const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
-  if (vid >= n_tasks) return;  // uniform over the workgroup; no barrier has been passed yet
-  const int total = ((n_tasks - vid + G - 1) / G) * KB;  // stages this workgroup streams
-  const int tok = lane & 15;
+  // The stage loop is compiled once per task shape (mode), so neither
+  // carries the other's instructions.
+  auto run = [&](auto mode_tag) {
+    constexpr bool modeB = decltype(mode_tag)::value;
+    constexpr int rows_t = modeB ? kSRowsB : kSRowsA;  // weight rows per task
+    const int n_rb = N / rows_t;
+    const int n_tasks = tiles * n_rb;
+    const int per_task = modeB ? (KB + 3) / 4 : KB;  // stages per task
+    constexpr int SS = modeB ? kSStageB : kSStageA;
+    constexpr int D = modeB ? kSDB : kSDA;
+    const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+    if (vid >= n_tasks) return;  // uniform over the workgroup; no barrier has been passed yet
+    const int total = ((n_tasks - vid + G - 1) / G) * per_task;  // stages this workgroup streams
+    const int tok = lane & 15;
+    const int grow = lane >> 3;
 
-  // ---- issue side: per-lane sources of the current task's loads
-  int i_task = vid, i_kb = 0;
-  const uint8_t* i_w = nullptr;   // this lane's weight bytes, first 8-row group
-  const uint8_t* i_w1 = nullptr;  // and second 8-row group
-  const uint8_t* i_x = nullptr;   // third load: token row slot, token scale or weight scale
-  int64_t i_xstep = 0;            // bytes between the third load's K blocks
-  // Loads move whole 128-byte lines: lane l of a load covers row 8 i + l / 8
-  // of its 8-row group and 16-byte chunk (l % 8) ^ sw(row), which lands in
-  // LDS slot l % 8 of that row (see swz128).
-  const int grow = lane >> 3;
-  auto start_task = [&](int t) {
-    const StreamTask k = stream_task(L, n_rb, t);
-    const int wrow = wave * 16 + grow;  // this lane's row in the wave's first 8-row group
-    const uint8_t* wrow_p = p.w + (static_cast<int64_t>(k.e) * N + k.rb * kSRows + wrow) * K;
-    i_w = wrow_p + (((lane & 7) ^ ((wrow >> 1) & 7)) << 4);
-    i_w1 = wrow_p + 8 * static_cast<int64_t>(K) + (((lane & 7) ^ (((wrow + 8) >> 1) & 7)) << 4);
-    const float* wsp = p.w_scales + (static_cast<int64_t>(k.e) * (N / kGroup) + (k.rb * kSRows) / kGroup) * KB;
-    if (wave == 3) {
-      i_x = reinterpret_cast<const uint8_t*>(wsp);
-      i_xstep = 4;
-      return;
-    }
-    // Source row of this lane's token: token 8 * wave + l / 8 for the token
-    // slab (waves 0, 1), token l % 16 for the token scales (wave 2).
-    // Row-map entries come via the scalar cache, each index kept inside the
-    // expert's segment.
-    const int my_tok = wave < 2 ? wave * 8 + grow : tok;
-    const int first = k.mt * kStreamTileM;
-    const int last = k.row0 + k.cnt - 1;
-    int ar = k.row0 + first + my_tok;
-    if constexpr (GATHER) {
-      int m = 0;
-#pragma unroll
-      for (int i = 0; i < kStreamTileM; ++i) {
-        const int r = k.row0 + first + i < last ? k.row0 + first + i : last;
-        const int v = scalar_load(p.a_row_map + r);
-        m = my_tok == i ? v : m;
+    // ---- issue side. Loads move whole 128-byte lines: lane l covers row
+    // 8 h + l / 8 of a 16-row slab (h = 0, 1) and 16-byte chunk
+    // (l % 8) ^ ((row >> 1) & 7), which lands in LDS slot l % 8 (swz128).
+    int i_task = vid, i_st = 0;
+    const uint8_t* i_w0 = nullptr;  // this lane's weight bytes at K block 0, slab rows 0..7
+    const uint8_t* i_w1 = nullptr;  //   slab rows 8..15
+    const uint8_t* i_t0 = nullptr;  // token bytes: A, the wave's token half; B, tokens 0..7
+    const uint8_t* i_t1 = nullptr;  // B: tokens 8..15
+    const uint8_t* i_s = nullptr;   // scale loads (A: waves 2, 3; B: all waves, fifth load)
+    int64_t i_sstep = 0;            // their bytes per K block
+    auto chunk_of = [&](int row) { return ((lane & 7) ^ ((row >> 1) & 7)) << 4; };
+    auto start_task = [&](int t) {
+      const StreamTask k = stream_task(L, n_rb, t);
+      // A: the wave's 16 of the task's 64 rows. B: the task's 16 rows.
+      const int r0 = k.rb * rows_t + (modeB ? 0 : wave * 16);
+      const uint8_t* wb = p.w + (static_cast<int64_t>(k.e) * N + r0) * K;
+      i_w0 = wb + grow * static_cast<int64_t>(K) + chunk_of(grow);
+      i_w1 = wb + (grow + 8) * static_cast<int64_t>(K) + chunk_of(grow + 8);
+      const uint8_t* wsp = reinterpret_cast<const uint8_t*>(
+          p.w_scales + (static_cast<int64_t>(k.e) * (N / kGroup) + r0 / kGroup) * KB);
+      // Tokens whose rows this lane loads (ta, tb) and whose scale it loads
+      // (tok). Row-map entries come via the scalar cache, each index kept
+      // inside the expert's segment.
+      const int first = k.mt * kStreamTileM;
+      const int last = k.row0 + k.cnt - 1;
+      const int ta = modeB ? grow : wave * 8 + grow;
+      const int tb = grow + 8;
+      int ra = k.row0 + first + ta, rb = k.row0 + first + tb, rs = k.row0 + first + tok;
+      if constexpr (GATHER) {
+        int ma = 0, mb = 0, ms = 0;
+  #pragma unroll
+        for (int i = 0; i < kStreamTileM; ++i) {
+          const int r = k.row0 + first + i < last ? k.row0 + first + i : last;
+          const int v = scalar_load(p.a_row_map + r);
+          ma = ta == i ? v : ma;
+          mb = tb == i ? v : mb;
+          ms = tok == i ? v : ms;
+        }
+        ra = ma / p.a_row_div;
+        rb = mb / p.a_row_div;
+        rs = ms / p.a_row_div;
       }
-      ar = m / p.a_row_div;
-    }
-    const bool valid = first + my_tok < k.cnt && static_cast<unsigned>(ar) < static_cast<unsigned>(p.a_rows);
-    if (wave < 2) {
-      const int chunk = ((lane & 7) ^ ((my_tok >> 1) & 7)) << 4;
-      i_x = valid ? p.a + static_cast<int64_t>(ar) * K + chunk : i_w;  // stand-in: this lane's weight bytes
-      i_xstep = kGroup;
-    } else if (valid) {
-      i_x = static_cast<const uint8_t*>(p.a_scales) + static_cast<int64_t>(ar) * (UE8M0 ? 1 : 4);
-      i_xstep = static_cast<int64_t>(p.a_rows) * (UE8M0 ? 1 : 4);
-    } else {
-      i_x = reinterpret_cast<const uint8_t*>(wsp);  // stand-in: any valid address, one per K block
-      i_xstep = 4;
-    }
-  };
-  auto issue = [&](uint8_t* st) {
-    __builtin_amdgcn_global_load_lds(i_w + i_kb * kGroup, (lds_void*)(st + wave * 2048), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(st + wave * 2048 + 1024), 16, 0, 0);
-    const uint8_t* x = i_x + i_kb * i_xstep;
-    if (wave < 2)
-      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + wave * 1024), 16, 0, 0);
-    else if (wave == 2 && UE8M0)
-      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + kSA), 1, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(x, (lds_void*)(st + kSW + kSA + (wave - 2) * 256), 4, 0, 0);
-    if (++i_kb == KB) {
-      i_kb = 0;
-      i_task += G;
-      if (i_task < n_tasks) start_task(i_task);
-    }
-  };
+      auto valid = [&](int tk, int ar) {
+        return first + tk < k.cnt && static_cast<unsigned>(ar) < static_cast<unsigned>(p.a_rows);
+      };
+      // Stand-ins for idle lanes: the lane's own weight bytes, or the weight
+      // scales (valid addresses for every K block).
+      i_t0 = valid(ta, ra) ? p.a + static_cast<int64_t>(ra) * K + chunk_of(ta) : i_w0;
+      i_t1 = valid(tb, rb) ? p.a + static_cast<int64_t>(rb) * K + chunk_of(tb) : i_w1;
+      const bool loads_sa = modeB ? wave == 0 : wave == 2;
+      if (loads_sa && valid(tok, rs)) {
+        i_s = static_cast<const uint8_t*>(p.a_scales) + static_cast<int64_t>(rs) * (UE8M0 ? 1 : 4);
+        i_sstep = static_cast<int64_t>(p.a_rows) * (UE8M0 ? 1 : 4);
+      } else {
+        i_s = wsp;
+        i_sstep = 4;
+      }
+    };
+    auto issue = [&](uint8_t* st) {
+      if constexpr (!modeB) {
+        const int kb = i_st;
+        __builtin_amdgcn_global_load_lds(i_w0 + kb * kGroup, (lds_void*)(st + wave * 2048), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(i_w1 + kb * kGroup, (lds_void*)(st + wave * 2048 + 1024), 16, 0, 0);
+        if (wave < 2)
+          __builtin_amdgcn_global_load_lds(i_t0 + kb * kGroup, (lds_void*)(st + kOffTokA + wave * 1024), 16, 0, 0);
+        else if (wave == 2 && UE8M0)
+          __builtin_amdgcn_global_load_lds(i_s + kb * i_sstep, (lds_void*)(st + kOffSclA), 1, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(i_s + kb * i_sstep, (lds_void*)(st + kOffSclA + (wave - 2) * 256), 4, 0, 0);
+      } else {
+        const int kb = min(4 * i_st + wave, KB - 1);  // past the end: clamped, never used
+        __builtin_amdgcn_global_load_lds(i_w0 + kb * kGroup, (lds_void*)(st + wave * 2048), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(i_w1 + kb * kGroup, (lds_void*)(st + wave * 2048 + 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(i_t0 + kb * kGroup, (lds_void*)(st + kOffTokB + wave * 2048), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(i_t1 + kb * kGroup, (lds_void*)(st + kOffTokB + wave * 2048 + 1024), 16, 0, 0);
+        // Wave 0: token scales of the stage's 4 K blocks (lane l, block l / 16).
+        // Waves 1..3: the weight scales (lane l, block l % 4; waves 2 and 3
+        // store the same values as wave 1).
+        const int kbs = min(4 * i_st + (wave == 0 ? lane >> 4 : lane & 3), KB - 1);
+        if (wave == 0 && UE8M0)
+          __builtin_amdgcn_global_load_lds(i_s + kbs * i_sstep, (lds_void*)(st + kOffSclB), 1, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(i_s + kbs * i_sstep, (lds_void*)(st + kOffSclB + (wave == 0 ? 0 : 256)), 4, 0, 0);
+      }
+      if (++i_st == per_task) {
+        i_st = 0;
+        i_task += G;
+        if (i_task < n_tasks) start_task(i_task);
+      }
+    };
 
-  // ---- compute side
-  int c_task = vid, c_kb = 0;
-  v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](const uint8_t* st) {
-    union {
-      uint4 u[2];
-      v8i v;
-    } wf, af;
-    uint32_t sraw, swraw;
-    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st));
-    const int c0 = 2 * (lane >> 4);  // fragment chunks c0, c0 + 1 of row tok
-    read_stage(base + wave * 2048 + swz128(tok, c0), base + wave * 2048 + swz128(tok, c0 + 1),
-               base + kSW + swz128(tok, c0), base + kSW + swz128(tok, c0 + 1),
-               base + kSW + kSA + tok * 4, base + kSW + kSA + 256, wf.u[0], wf.u[1], af.u[0],
-               af.u[1], sraw, swraw);
-    const float sa = UE8M0 ? __uint_as_float(sraw << 23) : __uint_as_float(sraw);
-    const float sw = __uint_as_float(swraw);
-    if (c_kb == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
-    if (++c_kb == KB) {
+    // ---- compute side
+    int c_task = vid, c_st = 0;
+    v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const uint8_t* st) {
+      const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(st));
+      const int c0 = 2 * (lane >> 4);  // fragment chunks c0, c0 + 1 of row tok
+      if (c_st == 0) acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      const bool active = !modeB || 4 * c_st + wave < KB;  // B: this wave's K block exists
+      if (active) {
+        union {
+          uint4 u[2];
+          v8i v;
+        } wf, af;
+        uint32_t sraw, swraw;
+        const uint32_t wr = base + wave * 2048;
+        const uint32_t tr = modeB ? base + kOffTokB + wave * 2048 : base + kOffTokA;
+        const uint32_t sa = modeB ? base + kOffSclB + (wave * 16 + tok) * 4 : base + kOffSclA + tok * 4;
+        const uint32_t sw = modeB ? base + kOffSclB + 256 + wave * 4 : base + kOffSclA + 256;
+        read_stage(wr + swz128(tok, c0), wr + swz128(tok, c0 + 1), tr + swz128(tok, c0),
+                   tr + swz128(tok, c0 + 1), sa, sw, wf.u[0], wf.u[1], af.u[0], af.u[1], sraw, swraw);
+        const float fa = UE8M0 ? __uint_as_float(sraw << 23) : __uint_as_float(sraw);
+        acc = fma4(mfma_fp8(wf.v, af.v), fa * __uint_as_float(swraw), acc);
+      }
+      if (++c_st < per_task) return;
       const StreamTask k = stream_task(L, n_rb, c_task);
       const int j = k.mt * kStreamTileM + tok;
-      if (j < k.cnt)
-        *reinterpret_cast<uint2*>(p.c + static_cast<int64_t>(k.row0 + j) * N + k.rb * kSRows + wave * 16 + 4 * (lane >> 4)) =
-            pack_bf16x4(acc);
-      if (threadIdx.x == 0 && p.tiles_visited && (k.rb * kSRows) % kColTile == 0) atomicAdd(p.tiles_visited, 1);
-      c_kb = 0;
+      uint16_t* crow = p.c + static_cast<int64_t>(k.row0 + j) * N + k.rb * rows_t + 4 * (lane >> 4);
+      const bool count_tile = threadIdx.x == 0 && p.tiles_visited && (k.rb * rows_t) % kColTile == 0;
+      if constexpr (!modeB) {
+        if (j < k.cnt) *reinterpret_cast<uint2*>(crow + wave * 16) = pack_bf16x4(acc);
+      } else {
+        // Every wave is done reading this stage once all pass the barrier; its
+        // first 4 KB then hold the 4 partials, summed by wave 0 in wave order.
+        // (The buffer is refilled only after the next stage's barrier.)
+        lds_barrier();
+        lds_store_v4f(base + wave * 1024 + lane * 16, acc);
+        lds_barrier();
+        if (wave == 0) {
+          const v4f sum = lds_sum4_v4f(base + lane * 16);
+          if (j < k.cnt) *reinterpret_cast<uint2*>(crow) = pack_bf16x4(sum);
+        }
+      }
+      if (count_tile) atomicAdd(p.tiles_visited, 1);
+      c_st = 0;
       c_task += G;
+    };
+
+    start_task(i_task);
+    for (int d = 0; d < D - 1; ++d)
+      if (d < total) issue(s_ring + d * SS);
+    // Stage s: wait for this wave's loads of stage s (in the steady state
+    // stages s+1 .. s+D-2 are still in flight, near the end fewer, and then
+    // everything is waited for), barrier so every wave's part is visible and
+    // stage s-1 is free, issue stage s+D-1 into it, compute s.
+    int slot = 0;  // s % D
+    for (int s = 0; s < total; ++s) {
+      if (s + D - 2 >= total)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((modeB ? kSLoadsB : kSLoadsA) * (D - 2)));
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      const int prev = slot == 0 ? D - 1 : slot - 1;
+      if (s + D - 1 < total) issue(s_ring + prev * SS);
+      compute(s_ring + slot * SS);
+      slot = slot == D - 1 ? 0 : slot + 1;
     }
   };
-
-  start_task(i_task);
-  for (int d = 0; d < kSD - 1; ++d)
-    if (d < total) issue(s_ring + d * kSStage);
-  // Stage s: wait for this wave's loads of stage s (three per stage; in the
-  // steady state stages s+1 .. s+kSD-2 are still in flight, near the end
-  // fewer, and then everything is waited for), barrier so every wave's part
-  // is visible and stage s-1 is free, issue stage s+kSD-1 into it, compute s.
-  int slot = 0;  // s % kSD
-  for (int s = 0; s < total; ++s) {
-    if (s + kSD - 2 < total)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (kSD - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-    const int prev = slot == 0 ? kSD - 1 : slot - 1;
-    if (s + kSD - 1 < total) issue(s_ring + prev * kSStage);
-    compute(s_ring + slot * kSStage);
-    slot = slot == kSD - 1 ? 0 : slot + 1;
-  }
+  if (4 * tiles * (N / kSRowsA) < 3 * G)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 hipError_t launch_stream(const GemmArgs& g, hipStream_t stream) {
@@ -465,17 +571,6 @@ union Frag {
   v8i v;
 };
 
-// Workgroup barrier for the pipelined K loop. A fence (as in
-// __syncthreads()) would make the compiler wait for every vector-memory
-// operation in flight, including the direct-to-LDS loads of later stages, and
-// so collapse the pipeline. Instead the caller waits for exactly the data the
-// next stage needs (explicit vmcnt), this waits for the wave's own LDS
-// writes, and the "memory" clobber keeps the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
 
 // Tile t of an expert with mt row tiles and nt column tiles, in the order
 // that keeps kGroupN column tiles x all row tiles of an expert together (so
