@@ -251,13 +251,22 @@ def _ref_gemm(c):
     return ref, live
 
 
+# Counts of 32 streaming-sized experts (1..41 rows): enough (expert, 64-row)
+# tasks that the streaming kernel takes its 64-row task shape; the smaller
+# cases take the 16-row shape with K blocks split over the waves.
+_MANY = [(i * 7) % 41 + 1 for i in range(32)]
+
 GEMM_SHAPES = [
     # seed, E, N, K, counts, gather_k
-    (0, 4, 256, 256, [3, 0, 17, 100], 0),           # K/128 = 2: 4 row blocks per item
-    (1, 3, 384, 1024, [64, 65, 1], 0),              # K/128 = 8: 2 x 2 split
-    (2, 5, 512, 2048, [16, 0, 300, 7, 129], 0),     # K/128 = 16: 4-way K split
+    (0, 4, 256, 256, [3, 0, 17, 100], 0),           # streaming and tiled experts
+    (1, 3, 384, 1024, [64, 65, 1], 0),              # either side of the 64-row limit
+    (2, 5, 512, 2048, [16, 0, 300, 7, 129], 0),
     (3, 6, 256, 512, [9, 33, 0, 200, 2, 64], 8),    # gathered A rows (FC1 layout)
     (4, 2, 1024, 7168, [5, 140], 8),
+    (5, 3, 256, 640, [5, 20, 1], 0),                # K/128 = 5: waves idle in the last stage
+    (6, 3, 256, 384, [40, 3, 16], 8),               # K/128 = 3, gathered
+    (7, 32, 1024, 256, _MANY, 0),                   # 64-row streaming tasks
+    (8, 32, 1024, 384, _MANY, 8),                   # the same, gathered, K/128 = 3
 ]
 
 
