@@ -81,8 +81,10 @@ __device__ __forceinline__ void align_block(
     }
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
+    // Earlier waves' totals: independent LDS reads (no dependent chain).
     int run = incl - local;
-    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) run += w < wave ? s_wsum[w] : 0;
     for (int e = b; e < b + per && e < E; ++e) {
       s_off[e] = run;
       run += (s_total[e] + align_rows - 1) / align_rows * align_rows;
@@ -111,8 +113,10 @@ __device__ __forceinline__ void align_block(
     int rank = 0;
     uint64_t active = __ballot(ok);
     while (active) {
+      // The leader is uniform, so its expert is read with v_readlane (a
+      // scalar move), not a cross-lane LDS permute.
       const int leader = __ffsll(static_cast<unsigned long long>(active)) - 1;
-      const int le = __shfl(e, leader, 64);
+      const int le = __builtin_amdgcn_readlane(e, leader);
       const uint64_t same = __ballot(ok && e == le);
       if (ok && e == le) rank = __popcll(same & below);
       if (lane == leader) s_wave[wave][le] = static_cast<uint16_t>(__popcll(same));
@@ -121,7 +125,8 @@ __device__ __forceinline__ void align_block(
     __syncthreads();
     if (ok) {
       int prior = 0;
-      for (int w = 0; w < wave; ++w) prior += s_wave[w][e];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) prior += w < wave ? s_wave[w][e] : 0;
       const int row = s_off[e] + s_before[e] + s_run[e] + prior + rank;
       row_to_pair[row] = p;
       pair_to_row[p] = row;
