@@ -49,7 +49,7 @@ class _Layout(ctypes.Structure):
                 ("row_to_pair", ctypes.c_size_t), ("pair_to_row", ctypes.c_size_t),
                 ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t), ("c1", ctypes.c_size_t),
                 ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t), ("y", ctypes.c_size_t),
-                ("total", ctypes.c_size_t), ("row_cap", _i32)]
+                ("act", ctypes.c_size_t), ("total", ctypes.c_size_t), ("row_cap", _i32)]
 
 
 _SIGNATURES = {

@@ -205,7 +205,10 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   L->hq = take(R * I);
   L->hs = take((I / 128) * R * sb);
   L->y = take(R * H * 2);
+  const bool decode = moe::down_combine_fits(p->t_cap, p->topk, p->inter);
+  L->act = decode ? take(R * I * 4) : 0;
   L->total = off;
+  if (!decode) L->act = off;
   L->row_cap = static_cast<int32_t>(rc);
   return MOE_OK;
 }
@@ -238,6 +241,8 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   auto* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
   void* hs = ws + L.hs;
   auto* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  const bool decode = L.act < L.total;  // fused decode path (the plan lays out act)
+  auto* act = reinterpret_cast<float*>(ws + L.act);
   const hipStream_t s = as_stream(stream);
   const int R = L.row_cap;
   const int64_t pairs64 = static_cast<int64_t>(p->t_cap) * p->topk;
@@ -268,7 +273,40 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
     g.n = 2 * p->inter;
     g.k = p->hidden;
     g.c = c1;
+    if (decode) {  // SiLU(gate) * up in FC1's epilogue
+      g.act_out = act;
+      g.act = p->act;
+      g.act_limit = p->clamp_limit;
+    }
     e = moe::launch_grouped_gemm(g, s);
+    g.act_out = nullptr;
+  }
+  if (decode) {  // FC2 and the top-k combine in one launch
+    if (e == hipSuccess) {
+      moe::DownCombineArgs d;
+      d.act = act;
+      d.fmt = p->scale_fmt;
+      d.w = t->w2;
+      d.w_scales = t->w2_scales;
+      d.counts = counts;
+      d.offsets = offsets;
+      d.row_to_pair = r2p;
+      d.pair_to_row = p2r;
+      d.topk_w = t->topk_w;
+      d.t_live_dev = t->t_live_dev;
+      d.num_experts = p->num_experts;
+      d.row_cap = R;
+      d.t_cap = p->t_cap;
+      d.topk = p->topk;
+      d.hidden = p->hidden;
+      d.inter = p->inter;
+      d.hq = hq;
+      d.hs = hs;
+      d.y = y;
+      d.out = t->out;
+      e = moe::launch_down_combine(d, s);
+    }
+    return from_hip(e);
   }
   if (e == hipSuccess)
     e = moe::launch_silu_mul_quant(c1, p->inter, counts, offsets, p->num_experts, R, p->act,

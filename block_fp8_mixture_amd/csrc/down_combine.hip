@@ -1,0 +1,542 @@
+// FC2 and the top-k combine of a decode-sized layer in one launch.
+//
+// TensorRT-LLM PR #21250 (description; rounding-fix commit): at decode sizes
+// the FC2 GEMM streams the weights of the few live experts, and the top-k sum
+// scales the BF16 expert outputs by the routing weights in fp32. vLLM PR
+// #65794 (Details): the FC2 input is SiLU(gate) * up quantized per 1x128
+// group with the activation rule.
+//
+// A workgroup (8 waves, one per CU) owns 16 output columns -- 16 weight rows
+// of every live expert -- so the whole top-k sum of those columns is formed in
+// its LDS, with no further launch and no synchronisation between workgroups.
+//  1. Prologue: the live experts are compacted from the endpoints, and the
+//     FC2 input rows of all live pairs (fp32, written by the gated FC1) are
+//     quantized into LDS with the 1x128 rule. Workgroup 0 also stores codes
+//     and scales to the workspace, bit-identical to moe_silu_mul_quant.
+//  2. Each wave streams the 16 x I weight slab of every 8th listed expert
+//     through a private ring of 2 KB stages (16 rows x one 128-wide K block)
+//     by direct-to-LDS loads of whole 128-byte lines. A wave only waits for
+//     its own loads, so the loop has no workgroup barrier. Per stage and
+//     16-token tile: one v_mfma_f32_16x16x128_f8f6f4 (token = lane % 16,
+//     weight row = 4 * (lane / 16) + v) and acc += t * (sa * sw). After the
+//     last K block each live row's BF16-rounded result goes to the LDS slot
+//     of its (token, k) pair.
+//  3. Epilogue: out[t, cols] = BF16(sum over ascending k of w[t, k] * slot)
+//     with fp32 FMAs -- the arithmetic and order of moe_topk_combine -- and
+//     the rows to the workspace's FC2 output.
+#include "device_common.h"
+#include "gemm_device.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kDcThreads = 512;
+constexpr int kDcWaves = kDcThreads / 64;
+constexpr int kDcDepth = 7;             // stages in a wave's ring
+constexpr int kDcStage = 16 * kGroup;   // 16 weight rows x 128 bytes
+constexpr int kDcTiles = kDcMaxPairs / kStreamTileM;  // token tiles of one expert, at most
+
+// Two 16-byte LDS reads with their own wait, as assembly: the compiler then
+// neither sees reads that might alias the direct-to-LDS loads in flight
+// (which would make it wait for all of them) nor uses a result early.
+__device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& r0, uint4& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1));
+}
+
+// A stage's reads for the first token tile: weight and token fragments and
+// the two scales, all in flight together under one wait.
+__device__ __forceinline__ void lds_read_stage(uint32_t w0, uint32_t w1, uint32_t t0, uint32_t t1,
+                                               uint32_t sa, uint32_t sw, uint4& rw0, uint4& rw1,
+                                               uint4& rt0, uint4& rt1, float& fsa, float& fsw) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b32 %4, %10\n\t"
+      "ds_read_b32 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(rw0), "=&v"(rw1), "=&v"(rt0), "=&v"(rt1), "=&v"(fsa), "=&v"(fsw)
+      : "v"(w0), "v"(w1), "v"(t0), "v"(t1), "v"(sa), "v"(sw));
+}
+
+// Token fragments and scale of a further token tile.
+__device__ __forceinline__ void lds_read_tile(uint32_t t0, uint32_t t1, uint32_t sa, uint4& rt0,
+                                              uint4& rt1, float& fsa) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(rt0), "=&v"(rt1), "=&v"(fsa)
+      : "v"(t0), "v"(t1), "v"(sa));
+}
+
+// Global loads the compiler does not track. Its wait insertion does not
+// count direct-to-LDS loads as later vector-memory operations, so a register
+// load issued before them would be waited for with vmcnt(0), draining the
+// weight stream; these are waited for explicitly (prefetch_wait) instead.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 gload_b128(const void* a) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(a));
+  return r;
+}
+__device__ __forceinline__ uint32_t gload_b32(const void* a) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(a));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombineArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kDcWaves * kDcDepth * kDcStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tok[kDcTokBytes];  // codes, row stride I + 16
+  __shared__ float s_sa[kDcMaxScales];   // token scale of (compact row, K block)
+  __shared__ float s_sw[kDcMaxScales];   // weight scale of (list entry, K block), this column block
+  __shared__ __attribute__((aligned(16))) float s_slot[kDcMaxPairs * 16];  // pair q's 16 columns
+  __shared__ int s_e[kDcMaxPairs];       // list entry -> expert
+  __shared__ int s_cnt[kDcMaxPairs];     //   its live rows
+  __shared__ int s_c0[kDcMaxPairs];      //   its first compact row
+  __shared__ int s_r0[kDcMaxPairs];      //   its first source row
+  __shared__ int s_row[kDcMaxPairs];     // compact row -> source row
+  __shared__ int s_pair[kDcMaxPairs];    //   its pair
+  __shared__ int s_p2r[kDcMaxPairs];     // pair -> row
+  __shared__ float s_tw[kDcMaxPairs];    // pair -> routing weight
+  __shared__ int s_wn[kDcWaves], s_wr[kDcWaves];
+  __shared__ int s_nlist, s_nrows;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = p.num_experts, N = p.hidden, I = p.inter, KB = I / kGroup, TK = p.topk;
+  const int TS = I + 16;              // token row stride in LDS (odd multiple of 16 bytes)
+  const int PQ = p.t_cap * TK;        // pairs of capacity (<= kDcMaxPairs)
+  const int n_cb = N / 16;
+  const int G = gridDim.x;
+  // Table limits (all met by consistent metadata of a problem the host admitted).
+  const int list_cap = min(kDcMaxPairs, kDcMaxScales / KB);
+  const int row_cap_lds = min(list_cap, kDcTokBytes / TS);
+
+  // ---- 1. live experts, in expert order (two 512-expert chunks)
+  int cnt_c[2] = {0, 0}, row0_c[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c == 1 && E <= kDcThreads) break;  // uniform
+    const int e = tid + c * kDcThreads;
+    const int ec = e < E ? e : E - 1;
+    row0_c[c] = p.offsets[ec];
+    cnt_c[c] = e < E ? segment_rows(row0_c[c], p.offsets[ec + 1], p.counts[ec], p.row_cap) : 0;
+  }
+  if (tid < PQ) {
+    s_p2r[tid] = p.pair_to_row[tid];
+    s_tw[tid] = p.topk_w[tid];
+  }
+  // Through the scalar cache: a vector load still in flight here would be
+  // waited for (vmcnt) in the middle of the prologue's prefetch.
+  const int t_live = p.t_live_dev ? min(max(scalar_load(p.t_live_dev), 0), p.t_cap) : p.t_cap;
+  if (tid == 0) {
+    s_nlist = 0;
+    s_nrows = 0;
+  }
+  int run_n = 0, run_r = 0;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c == 1 && E <= kDcThreads) break;  // uniform
+    const int cnt = cnt_c[c];
+    const bool flag = cnt > 0;
+    const uint64_t mask = __ballot(flag);
+    const int pos = __popcll(mask & ((uint64_t(1) << lane) - 1));
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) {
+      s_wn[wave] = __popcll(mask);
+      s_wr[wave] = incl;
+    }
+    __syncthreads();
+    int bn = run_n, br = run_r;
+#pragma unroll
+    for (int w = 0; w < kDcWaves; ++w) {
+      bn += w < wave ? s_wn[w] : 0;
+      br += w < wave ? s_wr[w] : 0;
+    }
+    const int i = bn + pos, c0 = br + incl - cnt;
+    if (flag && i < list_cap && c0 + cnt <= row_cap_lds) {  // the valid entries form a prefix
+      s_e[i] = tid + c * kDcThreads;
+      s_cnt[i] = cnt;
+      s_c0[i] = c0;
+      s_r0[i] = row0_c[c];
+      atomicMax(&s_nlist, i + 1);
+      atomicMax(&s_nrows, c0 + cnt);
+    }
+#pragma unroll
+    for (int w = 0; w < kDcWaves; ++w) {
+      run_n += s_wn[w];
+      run_r += s_wr[w];
+    }
+    __syncthreads();
+  }
+  // Nothing is in flight yet; an explicit wait here also tells the compiler
+  // that the endpoint loads are done on every path, so it does not wait for
+  // them (and with them for the prefetch below) when it reuses their registers.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  const int n_list = __builtin_amdgcn_readfirstlane(s_nlist);
+  const int n_rows = __builtin_amdgcn_readfirstlane(s_nrows);
+
+  // Compact row c of list entry `ent`: a search over the entries' first rows.
+  auto entry_of = [&](int c) {
+    int lo = 0, hi = n_list - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_c0[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  // ---- per-wave weight stream of column block n0
+  const int my_n = wave < n_list ? (n_list - 1 - wave) / kDcWaves + 1 : 0;
+  const int total = my_n * KB;  // stages of this wave
+  uint8_t* ring = s_ring + wave * (kDcDepth * kDcStage);
+  const int grow = lane >> 3;
+  const int chunk_lo = ((lane & 7) ^ ((grow >> 1) & 7)) << 4;        // slab row grow
+  const int chunk_hi = ((lane & 7) ^ (((grow + 8) >> 1) & 7)) << 4;  // slab row grow + 8
+  int i_ent = wave, i_kb = 0;
+  // Stand-ins (valid addresses) for the stages past a wave's last one that
+  // the stream start issues so that it always issues the same number.
+  const uint8_t* i_w0 = p.w + lane * 16;
+  const uint8_t* i_w1 = p.w + lane * 16;
+  auto i_set = [&](int n0) {
+    const int e = __builtin_amdgcn_readfirstlane(s_e[i_ent]);
+    const uint8_t* wb = p.w + (static_cast<int64_t>(e) * N + n0) * I;
+    i_w0 = wb + static_cast<int64_t>(grow) * I + chunk_lo;
+    i_w1 = wb + static_cast<int64_t>(grow + 8) * I + chunk_hi;
+  };
+  auto issue = [&](uint8_t* st, int n0) {
+    __builtin_amdgcn_global_load_lds(i_w0 + i_kb * kGroup, (lds_void*)(st), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
+    if (++i_kb == KB) {
+      i_kb = 0;
+      i_ent += kDcWaves;
+      if (i_ent < n_list) i_set(n0);
+    }
+  };
+  // Always kDcDepth - 1 stages (2 loads each), so the compiler knows how
+  // many loads follow anything issued before, and a wave with fewer stages
+  // fills the rest of its ring with stand-in loads that are never read.
+  auto start_stream = [&](int n0) {
+    i_ent = wave;
+    i_kb = 0;
+    if (total > 0) i_set(n0);
+#pragma unroll
+    for (int d = 0; d < kDcDepth - 1; ++d) {
+      __builtin_amdgcn_global_load_lds(i_w0 + i_kb * kGroup, (lds_void*)(ring + d * kDcStage), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(ring + d * kDcStage + 1024), 16, 0, 0);
+      // Advance to stage d + 1 if it exists: the loop's issues then
+      // continue from stage kDcDepth - 1, and past the last stage the
+      // stand-ins repeat it.
+      if (d + 1 < total && ++i_kb == KB) {
+        i_kb = 0;
+        i_ent += kDcWaves;
+        i_set(n0);
+      }
+    }
+  };
+  // Weight scales of the listed experts' rows n0..n0+15 (one 128-row block):
+  // one per thread (n_list * KB <= kDcMaxScales <= kDcThreads).
+  // An untracked load issued by every thread (a valid stand-in address when
+  // it has no entry), so it is in flight together with the stream start.
+  auto fetch_sw_first = [&](int n0) {
+    const int x = n_list > 0 ? min(tid, n_list * KB - 1) : 0;
+    const int e = n_list > 0 ? s_e[x / KB] : 0;
+    return gload_b32(p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + n0 / kGroup) * KB + x % KB);
+  };
+
+  // ---- 1b. FC2 input: 16 lanes per compact row, 8 float4 per lane per
+  // 512-column chunk; lanes l16 and chunks u cover columns 4 * (16 u + l16),
+  // so a 128-column group is u = 2g, 2g + 1 over the 16 lanes. The loads of
+  // a wave's first rows and chunk (all of them at decode sizes), its row-map
+  // entries and the weight scales go out before the first weight stages.
+  const int l16 = lane & 15;
+  const bool writer = blockIdx.x == 0;
+  auto src_row = [&](int c) {
+    const int cc = c < n_rows ? c : n_rows - 1;
+    const int ent = entry_of(cc);
+    return s_r0[ent] + cc - s_c0[ent];
+  };
+  auto load_chunk = [&](float4* v, int r, int col0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // columns past I (unused) load a valid stand-in
+      const int col = min(col0 + 4 * (16 * u + l16), I - 4);
+      v[u] = *reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(r) * I + col);
+    }
+  };
+  // Prefetch, in this order: 8 row chunks and the row-map entry (waves that
+  // own rows), the weight scale (every thread), then the 2 * (kDcDepth - 1)
+  // loads of the stream start. Waiting until only the last 2 * kDcDepth - 1
+  // (resp. 2 * kDcDepth - 2) remain waits for the rows (resp. the scale)
+  // and nothing of the stream.
+  float4 v[8];
+  u32x4 vr[8];
+  uint32_t pair_first = 0;
+  int r_first = 0;
+  const bool has_rows = wave * 4 < n_rows;  // uniform
+  if (has_rows) {
+    r_first = src_row(wave * 4 + (lane >> 4));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      vr[u] = gload_b128(p.act + static_cast<int64_t>(r_first) * I + min(4 * (16 * u + l16), I - 4));
+    pair_first = gload_b32(p.row_to_pair + r_first);
+  }
+  int cb = blockIdx.x;  // < n_cb: the grid has at most n_cb workgroups
+  uint32_t sw_first = fetch_sw_first(cb * 16);
+  start_stream(cb * 16);
+  if (has_rows) {
+    static_assert(2 * kDcDepth - 1 == 13, "wait immediate below");
+    asm volatile("s_waitcnt vmcnt(13)"
+                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
+                   "+v"(vr[6]), "+v"(vr[7]), "+v"(pair_first));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u].x = __uint_as_float(vr[u][0]);
+      v[u].y = __uint_as_float(vr[u][1]);
+      v[u].z = __uint_as_float(vr[u][2]);
+      v[u].w = __uint_as_float(vr[u][3]);
+    }
+  }
+
+  // Quantizes chunk col0 of compact row c (source row r) into LDS, and for
+  // workgroup 0 into the workspace.
+  auto quant_chunk = [&](const float4* v, int c, int r, int col0) {
+    const bool row_ok = c < n_rows;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int colg = col0 + g * kGroup;
+      if (colg >= I) break;  // uniform
+      const float4 a = v[2 * g], b = v[2 * g + 1];
+      float amax = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+      amax = group_max<16>(amax);
+      const float sc = group_scale(amax, FMT);
+      const float inv = FMT == kFp32 ? 0.0f : 1.0f / sc;  // exact for powers of two
+      const uint32_t qa = cvt_pk_e4m3(scale_div(a.x, sc, inv, FMT), scale_div(a.y, sc, inv, FMT)) |
+                          (cvt_pk_e4m3(scale_div(a.z, sc, inv, FMT), scale_div(a.w, sc, inv, FMT)) << 16);
+      const uint32_t qb = cvt_pk_e4m3(scale_div(b.x, sc, inv, FMT), scale_div(b.y, sc, inv, FMT)) |
+                          (cvt_pk_e4m3(scale_div(b.z, sc, inv, FMT), scale_div(b.w, sc, inv, FMT)) << 16);
+      const int ca = col0 + 4 * (32 * g + l16), cbb = ca + 64;
+      if (row_ok) {
+        *reinterpret_cast<uint32_t*>(s_tok + c * TS + ca) = qa;
+        *reinterpret_cast<uint32_t*>(s_tok + c * TS + cbb) = qb;
+        if (l16 == 0) s_sa[c * KB + colg / kGroup] = sc;
+        if (writer) {
+          *reinterpret_cast<uint32_t*>(p.hq + static_cast<int64_t>(r) * I + ca) = qa;
+          *reinterpret_cast<uint32_t*>(p.hq + static_cast<int64_t>(r) * I + cbb) = qb;
+          if (l16 == 0) store_scale(p.hs, FMT, static_cast<int64_t>(colg / kGroup) * p.row_cap + r, sc);
+        }
+      }
+    }
+  };
+  // The first rows and chunk, from the loads issued above (straight-line
+  // code, so the waits for them let the weight stages stay in flight) ...
+  if (wave * 4 < n_rows) {
+    const int c = wave * 4 + (lane >> 4);
+    if (c < n_rows && l16 == 0) {
+      s_row[c] = r_first;
+      s_pair[c] = static_cast<int>(pair_first);
+    }
+    quant_chunk(v, c, r_first, 0);
+  }
+  // ... then any further chunks and rows (beyond the decode sizes).
+  for (int rb = wave * 4; rb < n_rows; rb += kDcWaves * 4) {
+    const int c = rb + (lane >> 4);
+    const int r = src_row(c);
+    if (rb != wave * 4 && c < n_rows && l16 == 0) {
+      s_row[c] = r;
+      s_pair[c] = p.row_to_pair[r];
+    }
+    for (int col0 = rb == wave * 4 ? 512 : 0; col0 < I; col0 += 512) {
+      load_chunk(v, r, col0);
+      quant_chunk(v, c, r, col0);
+    }
+    // Tells the compiler these loads are done on every path out of the loop
+    // (they are: their values were used), so code after it does not wait.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  const int tok = lane & 15;
+  const int c0 = 2 * (lane >> 4);  // fragment chunks c0, c0 + 1 of a 128-byte K block
+  const uint32_t tok_base = lds_addr(s_tok) + c0 * 16;
+  const uint32_t sa_base = lds_addr(s_sa), sw_base = lds_addr(s_sw);
+
+  for (; cb < n_cb; cb += G) {
+    const int n0 = cb * 16;
+    if (cb != static_cast<int>(blockIdx.x)) {
+      sw_first = fetch_sw_first(n0);
+      start_stream(n0);
+    }
+    // The scale load is older than the stream start's loads (later
+    // operations only make this wait longer).
+    static_assert(2 * kDcDepth - 2 == 12, "wait immediate below");
+    asm volatile("s_waitcnt vmcnt(12)" : "+v"(sw_first));
+    if (tid < n_list * KB) s_sw[tid] = __uint_as_float(sw_first);
+    for (int x = tid; x < PQ * 16; x += kDcThreads) s_slot[x] = 0.0f;
+    lds_barrier();  // tokens, scales and zeroed slots visible
+
+    // ---- 2. stream: wait for stage s, refill the slot of stage s - 1, compute s.
+    int c_ent = wave, c_kb = 0, slot = 0;
+    int e_cnt = 0, e_c0 = 0;
+    if (c_ent < n_list) {
+      e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[c_ent]);
+      e_c0 = __builtin_amdgcn_readfirstlane(s_c0[c_ent]);
+    }
+    v4f acc[kDcTiles];
+#pragma unroll
+    for (int m = 0; m < kDcTiles; ++m) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < total; ++s) {
+      if (s + kDcDepth - 2 >= total)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kDcDepth - 2)));
+      const int prev = slot == 0 ? kDcDepth - 1 : slot - 1;
+      if (s + kDcDepth - 1 < total) issue(ring + prev * kDcStage, n0);
+      const uint32_t st = lds_addr(ring + slot * kDcStage);
+      union {
+        uint4 u[2];
+        v8i v;
+      } wf, af;
+      const int n_mt = (e_cnt + kStreamTileM - 1) / kStreamTileM;
+      float sa, sw;
+      {
+        const int row = min(e_c0 + tok, n_rows - 1);
+        const uint32_t ta = tok_base + row * TS + c_kb * kGroup;
+        lds_read_stage(st + swz128(tok, c0), st + swz128(tok, c0 + 1), ta, ta + 16,
+                       sa_base + (row * KB + c_kb) * 4, sw_base + (c_ent * KB + c_kb) * 4, wf.u[0],
+                       wf.u[1], af.u[0], af.u[1], sa, sw);
+        acc[0] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc[0]);
+      }
+#pragma unroll
+      for (int m = 1; m < kDcTiles; ++m) {
+        if (m < n_mt) {
+          const int row = min(e_c0 + m * kStreamTileM + tok, n_rows - 1);
+          const uint32_t ta = tok_base + row * TS + c_kb * kGroup;
+          lds_read_tile(ta, ta + 16, sa_base + (row * KB + c_kb) * 4, af.u[0], af.u[1], sa);
+          acc[m] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc[m]);
+        }
+      }
+      if (++c_kb == KB) {  // expert done: BF16-rounded rows to their pairs' slots
+#pragma unroll
+        for (int m = 0; m < kDcTiles; ++m) {
+          const int j = m * kStreamTileM + tok;
+          if (m < n_mt && j < e_cnt) {
+            const int q = s_pair[e_c0 + j];
+            if (static_cast<unsigned>(q) < static_cast<unsigned>(PQ)) {
+              float4 o;
+              o.x = bf16_to_f32(f32_to_bf16(acc[m][0]));
+              o.y = bf16_to_f32(f32_to_bf16(acc[m][1]));
+              o.z = bf16_to_f32(f32_to_bf16(acc[m][2]));
+              o.w = bf16_to_f32(f32_to_bf16(acc[m][3]));
+              *reinterpret_cast<float4*>(s_slot + q * 16 + 4 * (lane >> 4)) = o;
+            }
+          }
+          acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        c_kb = 0;
+        c_ent += kDcWaves;
+        if (c_ent < n_list) {
+          e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[c_ent]);
+          e_c0 = __builtin_amdgcn_readfirstlane(s_c0[c_ent]);
+        }
+      }
+      slot = slot == kDcDepth - 1 ? 0 : slot + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
+    lds_barrier();  // every slot of this column block written
+
+    // ---- 3. top-k sum of the 16 columns (two threads per token), then the
+    // FC2 output rows (two threads per compact row).
+    for (int x = tid; x < t_live * 2; x += kDcThreads) {
+      const int t = x >> 1, h = x & 1;
+      float a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = 0.0f;
+      for (int k0 = 0; k0 < TK; k0 += 8) {
+        bool ok[8];
+        float w[8];
+        float4 lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int q = t * TK + min(k0 + j, TK - 1);
+          ok[j] = k0 + j < TK && static_cast<unsigned>(s_p2r[q]) < static_cast<unsigned>(p.row_cap);
+          w[j] = s_tw[q];
+          lo[j] = *reinterpret_cast<const float4*>(s_slot + q * 16 + 8 * h);
+          hi[j] = *reinterpret_cast<const float4*>(s_slot + q * 16 + 8 * h + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (!ok[j]) continue;
+          a[0] = fmaf(w[j], lo[j].x, a[0]);
+          a[1] = fmaf(w[j], lo[j].y, a[1]);
+          a[2] = fmaf(w[j], lo[j].z, a[2]);
+          a[3] = fmaf(w[j], lo[j].w, a[3]);
+          a[4] = fmaf(w[j], hi[j].x, a[4]);
+          a[5] = fmaf(w[j], hi[j].y, a[5]);
+          a[6] = fmaf(w[j], hi[j].z, a[6]);
+          a[7] = fmaf(w[j], hi[j].w, a[7]);
+        }
+      }
+      uint4 o;
+      o.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+      o.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+      o.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
+      o.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
+      *reinterpret_cast<uint4*>(p.out + static_cast<int64_t>(t) * N + n0 + 8 * h) = o;
+    }
+    for (int x = tid; x < n_rows * 2; x += kDcThreads) {
+      const int c = x >> 1, h = x & 1;
+      const int q = s_pair[c];
+      if (static_cast<unsigned>(q) >= static_cast<unsigned>(PQ)) continue;
+      const float* v = s_slot + q * 16 + 8 * h;
+      uint4 o;
+      o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+      o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+      *reinterpret_cast<uint4*>(p.y + static_cast<int64_t>(s_row[c]) * N + n0 + 8 * h) = o;
+    }
+    lds_barrier();  // slots and weight scales free for the next column block
+  }
+}
+
+}  // namespace
+
+hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t stream) {
+  if (a.t_cap == 0) return hipSuccess;
+  if (!down_combine_fits(a.t_cap, a.topk, a.inter) || a.hidden % 16 != 0 ||
+      a.num_experts > kMaxExperts || a.num_experts < 1)
+    return hipErrorInvalidValue;
+  const int n_cb = a.hidden / 16;
+  const int cus = device_cu_count();
+  const int grid = n_cb < cus ? n_cb : cus;
+  if (a.fmt == kFp32)
+    hipLaunchKernelGGL(down_combine_kernel<kFp32>, dim3(grid), dim3(kDcThreads), 0, stream, a);
+  else if (a.fmt == kFp32Pow2)
+    hipLaunchKernelGGL(down_combine_kernel<kFp32Pow2>, dim3(grid), dim3(kDcThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(down_combine_kernel<kUe8m0>, dim3(grid), dim3(kDcThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -32,41 +32,16 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "gemm_device.h"
 #include "kernels.h"
+#include "quant_device.h"
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ v4f fma4(v4f t, float s, v4f acc) {
-  v4f r;
-  r[0] = __builtin_fmaf(t[0], s, acc[0]);
-  r[1] = __builtin_fmaf(t[1], s, acc[1]);
-  r[2] = __builtin_fmaf(t[2], s, acc[2]);
-  r[3] = __builtin_fmaf(t[3], s, acc[3]);
-  return r;
-}
 
-__device__ __forceinline__ v4f mfma_fp8(v8i w, v8i x) {
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, zero, 0, 0, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint2 pack_bf16x4(v4f v) {
-  uint2 o;
-  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-  return o;
-}
-
-// Live rows of expert e, or 0 when its endpoints do not describe a segment
-// inside [0, row_cap): metadata that is not what moe_align produces can make
-// results meaningless but never makes a kernel touch memory out of bounds.
-__device__ __forceinline__ int segment_rows(int o0, int o1, int c, int row_cap) {
-  if (o0 < 0 || o1 < o0 || o1 > row_cap || c <= 0) return 0;
-  return c < o1 - o0 ? c : o1 - o0;
-}
 __device__ __forceinline__ int expert_rows(const GemmArgs& p, int e) {
   return segment_rows(p.offsets[e], p.offsets[e + 1], p.counts[e], p.row_cap);
 }
@@ -212,18 +187,6 @@ __device__ __forceinline__ StreamTask stream_task(const StreamLists& L, int n_rb
   return r;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(4))) const int const_int;
-
-// Load through the scalar data cache (a uniform address). Scalar loads are
-// counted by lgkmcnt, apart from the vector-memory queue, so waiting for one
-// never waits for the direct-to-LDS loads in flight.
-__device__ __forceinline__ int scalar_load(const int* q) { return *(const const_int*)(q); }
-
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding (gfx9 layout: vmcnt bits [3:0] and [15:14], expcnt and
-// lgkmcnt left at their maxima).
-constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // The LDS reads of one streaming stage: weight and token fragments (two
 // 16-byte halves each, 1 KB apart) and the two scales. Written as assembly
@@ -248,26 +211,6 @@ __device__ __forceinline__ void read_stage(uint32_t w0_addr, uint32_t w1_addr, u
       : "v"(w0_addr), "v"(w1_addr), "v"(a0_addr), "v"(a1_addr), "v"(sa_addr), "v"(sw_addr));
 }
 
-// Byte offset of 16-byte chunk c of row `row` in a slab of 128-byte rows.
-// Rows are written whole (8 lanes x 16 bytes each); chunk c of a row sits in
-// slot c ^ ((row >> 1) & 7), which gives the 16 lanes one ds_read_b128 cycle
-// serves (16 consecutive rows, the same chunk) distinct bank groups on the
-// 64 four-byte banks of gfx950's LDS.
-__device__ __forceinline__ uint32_t swz128(int row, int c) {
-  return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-}
-
-// Workgroup barrier for the pipelined K loop. A fence (as in
-// __syncthreads()) would make the compiler wait for every vector-memory
-// operation in flight, including the direct-to-LDS loads of later stages, and
-// so collapse the pipeline. Instead the caller waits for exactly the data the
-// next stage needs (explicit vmcnt), this waits for the wave's own LDS
-// writes, and the "memory" clobber keeps the compiler from moving memory
-// accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
 
 // Two ways to cut the work into tasks, chosen per launch on the device:
 //  A: (expert, 64 weight rows, 16-token tile); the 4 waves own 16 weight rows
@@ -334,7 +277,14 @@ __device__ __forceinline__ v4f lds_sum4_v4f(uint32_t addr) {
 // (result: token = lane % 16, weight row = 4 * (lane / 16) + v), then
 // acc += t * (sa * sw) with four FMAs. Lanes whose token is past the expert's
 // rows load stand-in data from valid addresses and are never stored.
-template <bool UE8M0, bool GATHER>
+//
+// GATED (FC1 of a decode layer, weight rows = [gate; up]): each 16-row block
+// holds gate columns j..j+7 in its rows 0..7 and the up columns j..j+7 in
+// rows 8..15, so after the last K block a lane of the lower half holds
+// gate values whose up partners sit 32 lanes higher; one cross-lane swap
+// brings them together and the activation is applied to the BF16-rounded
+// pair (the values C holds), written in fp32 for the FC2 prologue.
+template <bool UE8M0, bool GATHER, bool GATED>
 __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSRing];
   __shared__ int s_list[kMaxExperts];
@@ -348,6 +298,7 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.n, K = p.k, KB = K / kGroup;
+  const int I = N / 2;  // GATED: gate rows [0, I), up rows [I, N)
   const int tiles = __builtin_amdgcn_readfirstlane(s_pref[L.n]);
   const int G = gridDim.x;
   // The stage loop is compiled once per task shape (mode), so neither
@@ -380,12 +331,17 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
     auto start_task = [&](int t) {
       const StreamTask k = stream_task(L, n_rb, t);
       // A: the wave's 16 of the task's 64 rows. B: the task's 16 rows.
+      // GATED: 8 gate rows from jg and the 8 up rows of the same columns.
       const int r0 = k.rb * rows_t + (modeB ? 0 : wave * 16);
-      const uint8_t* wb = p.w + (static_cast<int64_t>(k.e) * N + r0) * K;
-      i_w0 = wb + grow * static_cast<int64_t>(K) + chunk_of(grow);
-      i_w1 = wb + (grow + 8) * static_cast<int64_t>(K) + chunk_of(grow + 8);
-      const uint8_t* wsp = reinterpret_cast<const uint8_t*>(
-          p.w_scales + (static_cast<int64_t>(k.e) * (N / kGroup) + r0 / kGroup) * KB);
+      const int jg = k.rb * (rows_t / 2) + (modeB ? 0 : wave * 8);
+      const int rlo = GATED ? jg : r0, rhi = GATED ? I + jg : r0 + 8;
+      const uint8_t* we = p.w + static_cast<int64_t>(k.e) * N * K;
+      i_w0 = we + (rlo + grow) * static_cast<int64_t>(K) + chunk_of(grow);
+      i_w1 = we + (rhi + grow) * static_cast<int64_t>(K) + chunk_of(grow + 8);
+      const float* ws_e = p.w_scales + static_cast<int64_t>(k.e) * (N / kGroup) * KB;
+      // Weight scale rows of the lower and upper 8 rows (one block unless GATED).
+      const uint8_t* wsp = reinterpret_cast<const uint8_t*>(ws_e + (rlo / kGroup) * KB);
+      const uint8_t* wsp_hi = reinterpret_cast<const uint8_t*>(ws_e + (rhi / kGroup) * KB);
       // Tokens whose rows this lane loads (ta, tb) and whose scale it loads
       // (tok). Row-map entries come via the scalar cache, each index kept
       // inside the expert's segment.
@@ -420,7 +376,10 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
         i_s = static_cast<const uint8_t*>(p.a_scales) + static_cast<int64_t>(rs) * (UE8M0 ? 1 : 4);
         i_sstep = static_cast<int64_t>(p.a_rows) * (UE8M0 ? 1 : 4);
       } else {
-        i_s = wsp;
+        // Weight scales. GATED: lanes whose copy serves the upper 8 rows (A:
+        // lanes 32..63; B: lanes with bit 2 set) load the up rows' scale.
+        const bool hi = GATED && (modeB ? ((lane >> 2) & 1) != 0 : lane >= 32);
+        i_s = hi ? wsp_hi : wsp;
         i_sstep = 4;
       }
     };
@@ -474,7 +433,10 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
         const uint32_t wr = base + wave * 2048;
         const uint32_t tr = modeB ? base + kOffTokB + wave * 2048 : base + kOffTokA;
         const uint32_t sa = modeB ? base + kOffSclB + (wave * 16 + tok) * 4 : base + kOffSclA + tok * 4;
-        const uint32_t sw = modeB ? base + kOffSclB + 256 + wave * 4 : base + kOffSclA + 256;
+        // Result rows 8..15 (lanes 32..63) take the upper rows' weight scale.
+        const int hi = GATED ? lane >> 5 : 0;
+        const uint32_t sw = modeB ? base + kOffSclB + 256 + (wave + 4 * hi) * 4
+                                  : base + kOffSclA + 256 + hi * 128;
         read_stage(wr + swz128(tok, c0), wr + swz128(tok, c0 + 1), tr + swz128(tok, c0),
                    tr + swz128(tok, c0 + 1), sa, sw, wf.u[0], wf.u[1], af.u[0], af.u[1], sraw, swraw);
         const float fa = UE8M0 ? __uint_as_float(sraw << 23) : __uint_as_float(sraw);
@@ -485,8 +447,30 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
       const int j = k.mt * kStreamTileM + tok;
       uint16_t* crow = p.c + static_cast<int64_t>(k.row0 + j) * N + k.rb * rows_t + 4 * (lane >> 4);
       const bool count_tile = threadIdx.x == 0 && p.tiles_visited && (k.rb * rows_t) % kColTile == 0;
+      // GATED epilogue of one 16-row block with first gate column jg.
+      auto gated_store = [&](v4f v, int jg) {
+        const uint2 packed = pack_bf16x4(v);
+        const int col = (lane < 32 ? jg : I + jg) + 4 * ((lane >> 4) & 1);
+        const int64_t row = k.row0 + j;
+        uint2 other;
+        other.x = __shfl_xor(packed.x, 32, 64);
+        other.y = __shfl_xor(packed.y, 32, 64);
+        if (j >= k.cnt) return;
+        *reinterpret_cast<uint2*>(p.c + row * N + col) = packed;
+        if (lane >= 32) return;
+        const double lim = p.act_limit;
+        float4 a;
+        a.x = swiglu_any(p.act, bf16_to_f32(packed.x & 0xFFFFu), bf16_to_f32(other.x & 0xFFFFu), lim);
+        a.y = swiglu_any(p.act, bf16_to_f32(packed.x >> 16), bf16_to_f32(other.x >> 16), lim);
+        a.z = swiglu_any(p.act, bf16_to_f32(packed.y & 0xFFFFu), bf16_to_f32(other.y & 0xFFFFu), lim);
+        a.w = swiglu_any(p.act, bf16_to_f32(packed.y >> 16), bf16_to_f32(other.y >> 16), lim);
+        *reinterpret_cast<float4*>(p.act_out + row * I + col) = a;
+      };
       if constexpr (!modeB) {
-        if (j < k.cnt) *reinterpret_cast<uint2*>(crow + wave * 16) = pack_bf16x4(acc);
+        if constexpr (GATED)
+          gated_store(acc, k.rb * (kSRowsA / 2) + wave * 8);
+        else if (j < k.cnt)
+          *reinterpret_cast<uint2*>(crow + wave * 16) = pack_bf16x4(acc);
       } else {
         // Every wave is done reading this stage once all pass the barrier; its
         // first 4 KB then hold the 4 partials, summed by wave 0 in wave order.
@@ -496,7 +480,10 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
         lds_barrier();
         if (wave == 0) {
           const v4f sum = lds_sum4_v4f(base + lane * 16);
-          if (j < k.cnt) *reinterpret_cast<uint2*>(crow) = pack_bf16x4(sum);
+          if constexpr (GATED)
+            gated_store(sum, k.rb * (kSRowsB / 2));
+          else if (j < k.cnt)
+            *reinterpret_cast<uint2*>(crow) = pack_bf16x4(sum);
         }
       }
       if (count_tile) atomicAdd(p.tiles_visited, 1);
@@ -534,10 +521,15 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
 hipError_t launch_stream(const GemmArgs& g, hipStream_t stream) {
   const int grid = device_cu_count() * kSGroupsPerCu;
   const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
-  if (u && m) hipLaunchKernelGGL((gemm_stream_kernel<true, true>), dim3(grid), dim3(kThreads), 0, stream, g);
-  else if (u) hipLaunchKernelGGL((gemm_stream_kernel<true, false>), dim3(grid), dim3(kThreads), 0, stream, g);
-  else if (m) hipLaunchKernelGGL((gemm_stream_kernel<false, true>), dim3(grid), dim3(kThreads), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_stream_kernel<false, false>), dim3(grid), dim3(kThreads), 0, stream, g);
+  if (g.act_out) {
+    if (!m) return hipErrorInvalidValue;
+    if (u) hipLaunchKernelGGL((gemm_stream_kernel<true, true, true>), dim3(grid), dim3(kThreads), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_stream_kernel<false, true, true>), dim3(grid), dim3(kThreads), 0, stream, g);
+  }
+  else if (u && m) hipLaunchKernelGGL((gemm_stream_kernel<true, true, false>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else if (u) hipLaunchKernelGGL((gemm_stream_kernel<true, false, false>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else if (m) hipLaunchKernelGGL((gemm_stream_kernel<false, true, false>), dim3(grid), dim3(kThreads), 0, stream, g);
+  else hipLaunchKernelGGL((gemm_stream_kernel<false, false, false>), dim3(grid), dim3(kThreads), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -846,6 +838,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
   const int live_bound = g.max_live_experts < g.num_experts ? g.max_live_experts : g.num_experts;
   if (live_bound <= 0) return hipSuccess;
+  if (g.act_out && (g.max_rows_per_expert > kStreamMaxRows || g.n % 64 != 0)) return hipErrorInvalidValue;
   hipError_t err = launch_stream(g, stream);
   if (err != hipSuccess) return err;
   if (g.max_rows_per_expert > kStreamMaxRows) {

@@ -1,0 +1,73 @@
+// Device helpers shared by the FP8 GEMM kernels: MFMA and scale steps,
+// direct-to-LDS bookkeeping (wait immediates, barrier without a fence,
+// swizzled 128-byte rows) and segment checks of the expert endpoints.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ v4f fma4(v4f t, float s, v4f acc) {
+  v4f r;
+  r[0] = __builtin_fmaf(t[0], s, acc[0]);
+  r[1] = __builtin_fmaf(t[1], s, acc[1]);
+  r[2] = __builtin_fmaf(t[2], s, acc[2]);
+  r[3] = __builtin_fmaf(t[3], s, acc[3]);
+  return r;
+}
+
+__device__ __forceinline__ v4f mfma_fp8(v8i w, v8i x) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, zero, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(v4f v) {
+  uint2 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  return o;
+}
+
+// Live rows of expert e, or 0 when its endpoints do not describe a segment
+// inside [0, row_cap): metadata that is not what moe_align produces can make
+// results meaningless but never makes a kernel touch memory out of bounds.
+__device__ __forceinline__ int segment_rows(int o0, int o1, int c, int row_cap) {
+  if (o0 < 0 || o1 < o0 || o1 > row_cap || c <= 0) return 0;
+  return c < o1 - o0 ? c : o1 - o0;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) const int const_int;
+
+// Load through the scalar data cache (a uniform address). Scalar loads are
+// counted by lgkmcnt, apart from the vector-memory queue, so waiting for one
+// never waits for the direct-to-LDS loads in flight.
+__device__ __forceinline__ int scalar_load(const int* q) { return *(const const_int*)(q); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding (gfx9 layout: vmcnt bits [3:0] and [15:14], expcnt and
+// lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Byte offset of 16-byte chunk c of row `row` in a slab of 128-byte rows.
+// Rows are written whole (8 lanes x 16 bytes each); chunk c of a row sits in
+// slot c ^ ((row >> 1) & 7), which gives the 16 lanes one ds_read_b128 cycle
+// serves (16 consecutive rows, the same chunk) distinct bank groups on the
+// 64 four-byte banks of gfx950's LDS.
+__device__ __forceinline__ uint32_t swz128(int row, int c) {
+  return static_cast<uint32_t>(row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+}
+
+// Workgroup barrier for the pipelined K loop. A fence (as in
+// __syncthreads()) would make the compiler wait for every vector-memory
+// operation in flight, including the direct-to-LDS loads of later stages, and
+// so collapse the pipeline. Instead the caller waits for exactly the data the
+// next stage needs (explicit vmcnt), this waits for the wave's own LDS
+// writes, and the "memory" clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+}  // namespace moe

@@ -53,9 +53,58 @@ struct GemmArgs {
   int k;
   uint16_t* c;
   int32_t* tiles_visited;
+  // Gated FC1 (decode layers): when act_out is set, the weight rows are
+  // gate rows [0, n/2) and up rows [n/2, n); every 16-row block the kernel
+  // visits pairs 8 gate rows with the 8 up rows of the same columns, and
+  // besides C it writes act_out[row, j] = act(gate, up) in fp32 ([row_cap,
+  // n/2]) from the BF16-rounded C values. Needs a row map and experts of at
+  // most kStreamMaxRows rows.
+  float* act_out = nullptr;
+  int act = 0;
+  float act_limit = 0.0f;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
+
+// FC2 and the top-k combine of a decode-sized layer in one launch: a
+// workgroup owns 16 output columns of every live expert. Limits of its LDS
+// tables: at most kDcMaxPairs routed pairs of capacity, their quantized
+// rows (I + 16 bytes each) within kDcTokBytes, and pairs x I/128 within
+// kDcMaxScales.
+constexpr int kDcMaxPairs = 64;
+constexpr int kDcTokBytes = 24576;
+constexpr int kDcMaxScales = 256;
+
+inline bool down_combine_fits(int64_t t_cap, int64_t topk, int64_t inter) {
+  const int64_t pairs = t_cap * topk;
+  return pairs >= 1 && pairs <= kDcMaxPairs && pairs * (inter + 16) <= kDcTokBytes &&
+         pairs * (inter / 128) <= kDcMaxScales;
+}
+
+struct DownCombineArgs {
+  const float* act;           // [row_cap, I] fp32 FC2 input before quantization
+  int fmt;
+  const uint8_t* w;           // [E, H, I] E4M3
+  const float* w_scales;      // [E, H/128, I/128]
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* row_to_pair;
+  const int32_t* pair_to_row;
+  const float* topk_w;        // [t_cap, topk]
+  const int32_t* t_live_dev;  // nullable: t_cap
+  int num_experts;
+  int row_cap;
+  int t_cap;
+  int topk;
+  int hidden;
+  int inter;
+  uint8_t* hq;                // [row_cap, I] quantized FC2 input (workspace copy)
+  void* hs;                   // [I/128][row_cap] its scales
+  uint16_t* y;                // [row_cap, H] FC2 output rows (workspace copy)
+  uint16_t* out;              // [t_cap, H]
+};
+
+hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t stream);
 
 int device_cu_count();
 

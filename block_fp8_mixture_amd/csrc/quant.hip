@@ -27,26 +27,6 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
   act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15);
 }
 
-enum Act : int { kSwiglu = 0, kSwigluClamp = 1, kSwigluClampAfterSilu = 2 };
-
-// SiLU(g) * u in double, rounded once to float (vLLM PR #65794, Details: no
-// intermediate BF16 rounding). Clamp variants as TensorRT-LLM PR #21250's
-// test coverage names them, with limit L: clamp gate above and up to [-L, L]
-// before SiLU, or clamp SiLU's output above and up to [-L, L].
-template <int ACT>
-__device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
-  double g = gf, u = uf;
-  if (ACT == kSwigluClamp) {
-    g = fmin(g, lim);
-    u = fmin(fmax(u, -lim), lim);
-  }
-  double s = g / (1.0 + exp(-g));
-  if (ACT == kSwigluClampAfterSilu) {
-    s = fmin(s, lim);
-    u = fmin(fmax(u, -lim), lim);
-  }
-  return static_cast<float>(s * u);
-}
 
 // One wave per 128-column group (2 elements per lane): at decode sizes only a
 // few dozen groups are live, so spreading each over a whole wave keeps the

@@ -1,5 +1,5 @@
-// Device helpers of the 1x128 FP8 quantization, shared by the activation
-// quantization kernel and the fused routing + quantization kernel.
+// Device helpers of the 1x128 FP8 quantization and of the gated activation,
+// shared by the quantization kernels and the fused kernels of the layer.
 //
 // Rule (vLLM PR #65794, Details): scale = max(amax / 448, 1 / (448 * 512)),
 // codes = E4M3(x / scale); power-of-two scales round up. 16 lanes own one
@@ -68,6 +68,34 @@ __device__ __forceinline__ void act_quant_group(const uint16_t* __restrict__ x, 
   const uint2 codes = quantize8<FMT>(v, &s);
   *reinterpret_cast<uint2*>(xq + base) = codes;
   if (l16 == 0) store_scale(xs, FMT, static_cast<int64_t>(g) * t_cap + t, s);
+}
+
+enum Act : int { kSwiglu = 0, kSwigluClamp = 1, kSwigluClampAfterSilu = 2 };
+
+// SiLU(g) * u in double, rounded once to float (vLLM PR #65794, Details: no
+// intermediate BF16 rounding). Clamp variants as TensorRT-LLM PR #21250's
+// test coverage names them, with limit L: clamp gate above and up to [-L, L]
+// before SiLU, or clamp SiLU's output above and up to [-L, L].
+template <int ACT>
+__device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
+  double g = gf, u = uf;
+  if (ACT == kSwigluClamp) {
+    g = fmin(g, lim);
+    u = fmin(fmax(u, -lim), lim);
+  }
+  double s = g / (1.0 + exp(-g));
+  if (ACT == kSwigluClampAfterSilu) {
+    s = fmin(s, lim);
+    u = fmin(fmax(u, -lim), lim);
+  }
+  return static_cast<float>(s * u);
+}
+
+// The activation chosen at run time (a uniform branch).
+__device__ __forceinline__ float swiglu_any(int act, float g, float u, double lim) {
+  if (act == kSwigluClamp) return swiglu<kSwigluClamp>(g, u, lim);
+  if (act == kSwigluClampAfterSilu) return swiglu<kSwigluClampAfterSilu>(g, u, lim);
+  return swiglu<kSwiglu>(g, u, lim);
 }
 
 }  // namespace moe

@@ -240,6 +240,9 @@ typedef struct {
   size_t hq;             /* uint8 [row_cap, I] */
   size_t hs;             /* scales [I/128][row_cap] */
   size_t y;              /* BF16 [row_cap, H] */
+  size_t act;            /* fp32 [row_cap, I] SiLU(gate)*up before quantization; laid out
+                            only on the decode path (t_cap*topk <= 64 and the quantized
+                            FC2 input rows fit 24 KiB of LDS), else equal to total */
   size_t total;          /* bytes required */
   int32_t row_cap;       /* effective row capacity */
 } moe_workspace_layout;
@@ -256,6 +259,11 @@ size_t moe_workspace_bytes(const moe_problem* p);
  * -> topk_combine, enqueued on one stream with no host synchronization
  * (vLLM PR #59128, SM100 on B200: the full-expert benchmark scope; the layer
  * replays inside a captured graph with the token count on the device).
+ * On the decode path (see moe_workspace_layout.act) the layer takes three
+ * launches: align + act_quant, FC1 with SiLU(gate)*up in its epilogue, and
+ * FC2 with the top-k combine (TensorRT-LLM PR #21250, description: fewer
+ * launches at decode sizes). The workspace then holds the same alignment,
+ * codes and scales, bit for bit, and FC1/FC2 rows within the GEMM tolerance.
  * `workspace` is device memory of at least moe_workspace_bytes(p) bytes, laid
  * out as moe_workspace_plan describes; its prior contents do not matter.
  * Errors: INVALID_ARG, CAPACITY (workspace or row_cap too small), HIP. */
