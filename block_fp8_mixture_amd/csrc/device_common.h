@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -57,11 +59,20 @@ __device__ __forceinline__ void store_scale(void* base, int fmt, int64_t idx, fl
     static_cast<float*>(base)[idx] = s;
 }
 
-// x / s for one element, as the rule states it. For power-of-two scales the
-// reciprocal is exact, so multiplying by it gives the same correctly rounded
-// quotient with one instruction.
-__device__ __forceinline__ float scale_div(float x, float s, float inv_pow2, int fmt) {
-  return fmt == kFp32 ? x / s : x * inv_pow2;
+// x / s for one element, correctly rounded as the rule states it, given
+// inv = 1 / s (an IEEE division, once per group). For power-of-two scales inv
+// is exact and so is x * inv. Otherwise Markstein's correction: with
+// q0 = RN(x * inv) and the exact remainder r = x - q0 * s (one FMA), RN(q0 +
+// r * inv) is the correctly rounded quotient when inv is the correctly rounded
+// reciprocal and nothing underflows (P. Markstein, IBM J. Res. Dev. 34(1),
+// 1990). Here |x / s| <= 448 and s >= 1/229376, and a remainder can only
+// underflow for |x / s| far below half the smallest E4M3 subnormal, whose
+// code is zero either way. The sign is copied back so that -0 stays -0.
+__device__ __forceinline__ float scale_div(float x, float s, float inv, int fmt) {
+  const float q0 = x * inv;
+  if (fmt != kFp32) return q0;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
 }
 
 // Two float32 values -> two E4M3 codes (low 16 bits: a in byte 0, b in byte 1).
@@ -77,11 +88,32 @@ __device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b) {
 
 // ---- wave helpers ------------------------------------------------------------
 
-// Max over aligned groups of `width` lanes (width a power of two <= 64).
+// Max over aligned groups of `width` lanes (16, 32 or 64). Inside a 16-lane
+// row with DPP moves (no LDS round trip): swap neighbours, swap pairs, mirror
+// each half row, mirror the row; then across rows through lane reads.
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = width / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  static_assert(width == 16 || width == 32 || width == 64, "group width");
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      0xF, 0xF, false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+  if constexpr (width > 16) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    if constexpr (width == 32) {
+      const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      v = lane < 32 ? fmaxf(r0, r1) : fmaxf(r2, r3);
+    } else {
+      v = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    }
+  }
   return v;
 }
 

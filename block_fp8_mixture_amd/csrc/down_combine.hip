@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
       amax = group_max<16>(amax);
       const float sc = group_scale(amax, FMT);
-      const float inv = FMT == kFp32 ? 0.0f : 1.0f / sc;  // exact for powers of two
+      const float inv = 1.0f / sc;  // IEEE division, once per group
       const uint32_t qa = cvt_pk_e4m3(scale_div(a.x, sc, inv, FMT), scale_div(a.y, sc, inv, FMT)) |
                           (cvt_pk_e4m3(scale_div(a.z, sc, inv, FMT), scale_div(a.w, sc, inv, FMT)) << 16);
       const uint32_t qb = cvt_pk_e4m3(scale_div(b.x, sc, inv, FMT), scale_div(b.y, sc, inv, FMT)) |

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     const float y1 = swiglu<ACT>(bf16_to_f32(graw >> 16), bf16_to_f32(uraw >> 16), lim);
     const float amax = group_max<64>(fmaxf(fabsf(y0), fabsf(y1)));
     const float sc = group_scale(amax, FMT);
-    const float inv = FMT == kFp32 ? 0.0f : 1.0f / sc;  // exact for powers of two
+    const float inv = 1.0f / sc;  // IEEE division, once per group
     const uint32_t codes = cvt_pk_e4m3(scale_div(y0, sc, inv, FMT), scale_div(y1, sc, inv, FMT));
     *reinterpret_cast<uint16_t*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + lane * 2) =
         static_cast<uint16_t>(codes);

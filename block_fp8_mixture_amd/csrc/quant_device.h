@@ -35,7 +35,7 @@ __device__ __forceinline__ uint2 quantize8(const Vals8& x, float* scale_out) {
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
   amax = group_max<16>(amax);
   const float s = group_scale(amax, FMT);
-  const float inv = FMT == kFp32 ? 0.0f : 1.0f / s;  // exact for powers of two
+  const float inv = 1.0f / s;  // IEEE division, once per group
   float q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = scale_div(x.v[i], s, inv, FMT);
