@@ -40,7 +40,12 @@ PAGES_DECODE_T4_US = 64.7    # TensorRT-LLM PR #21250, Performance (H200, contex
 FLUSH_BYTES = 1 << 30
 MALL_BYTES = 256 << 20       # MI355X Infinity Cache
 CAL_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
-TRAFFIC_FILE = "fc1_gemm_decode_t4_fp32_traffic.json"
+
+
+def traffic_file(workload_key):
+    """profiles/ file of the FC1 traffic summary of a workload, e.g.
+    fc1_gemm_decode_t4_fp32_traffic.json for decode:T4:fp32."""
+    return "fc1_gemm_" + workload_key.replace(":", "_").lower() + "_traffic.json"
 
 
 def parse():
@@ -105,7 +110,7 @@ def kernel_source_hash():
 def load_traffic(workload_key):
     """HBM traffic of the FC1 kernel from the committed rocprofv3 --pmc summary,
     used only if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
+    path = os.path.join(ROOT, "profiles", traffic_file(workload_key))
     try:
         with open(path) as f:
             d = json.load(f)
@@ -159,7 +164,7 @@ def traffic_from(args, fetch_dir, write_dir):
     res = {"workload": f"{args.config}:T{t_live}:{fmt}", "gemm_source_sha256_16": kernel_source_hash(),
            "bytes_per_launch": out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"],
            "counters": out}
-    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE)
+    path = os.path.join(ROOT, "profiles", traffic_file(res["workload"]))
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
