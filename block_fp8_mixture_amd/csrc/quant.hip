@@ -5,10 +5,10 @@
 // codes = E4M3(x / scale); power-of-two scales round up (vLLM PR #59128,
 // Purpose: plain and power-of-two-rounded fp32 scales, packed UE8M0).
 //
-// Activations: 16 lanes own one 128-element group, 8 consecutive elements
-// each (one 16-byte BF16 load); the group amax is a 4-step xor-shuffle
-// reduction inside the 16 lanes. SiLU * up: one wave per group, 2 elements
-// per lane. The scale leaves from the group's first lane.
+// 16 lanes own one 128-element group, 8 consecutive elements each (one
+// 16-byte BF16 load per operand); the group amax is a DPP reduction inside
+// the 16 lanes, and the scale leaves from the group's first lane. The same
+// layout serves the activations (per token) and SiLU * up (per live row).
 #include "device_common.h"
 #include "kernels.h"
 #include "quant_device.h"
@@ -28,12 +28,13 @@ __global__ __launch_bounds__(kThreads) void act_quant_kernel(
 }
 
 
-// One wave per 128-column group (2 elements per lane): at decode sizes only a
-// few dozen groups are live, so spreading each over a whole wave keeps the
-// serial fp64 SiLU work per lane short. Waves walk the (row, group) space with
-// a grid stride. The expert endpoints are staged in LDS once per block, so
-// finding the expert of a row (to skip padding) is a search in LDS, not a
-// chain of dependent global loads.
+// 16 lanes per 128-column group, 8 consecutive columns each: one 16-byte
+// load of gate and one of up per lane, 8 independent fp64 SiLU evaluations,
+// and the group amax by DPP moves inside the 16 lanes. Threads walk the (row,
+// group) space with a grid stride, two groups per step whose four loads are
+// issued before either is used; the expert of a row (to skip padding) is
+// found by a search over endpoints staged in LDS once per block, while the
+// loads are in flight.
 template <int FMT, int ACT>
 __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gate_up, int inter, const int32_t* __restrict__ counts,
@@ -41,46 +42,46 @@ __global__ __launch_bounds__(kThreads) void silu_mul_quant_kernel(
     uint8_t* __restrict__ hq, void* __restrict__ hs) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cnt[kMaxExperts];
-  constexpr int kWavesPerBlock = kThreads / 64;
   const int groups = inter / kGroup;
-  const int lane = threadIdx.x & 63;
-  const int64_t n_groups = static_cast<int64_t>(row_cap) * groups;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-  int64_t gid = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  // The first group's inputs are loaded before the endpoints arrive (any row
-  // below row_cap is inside gate_up).
-  uint32_t graw = 0, uraw = 0;
-  if (gid < n_groups) {
-    const int64_t src = (gid / groups) * (2 * inter) + (gid % groups) * kGroup + lane * 2;
-    graw = *reinterpret_cast<const uint32_t*>(gate_up + src);
-    uraw = *reinterpret_cast<const uint32_t*>(gate_up + src + inter);
-  }
+  const int l16 = threadIdx.x & 15;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kGroupsPerBlock;
   for (int e = threadIdx.x; e <= num_experts; e += kThreads) {
     s_off[e] = offsets[e];
     if (e < num_experts) s_cnt[e] = counts[e];
   }
   __syncthreads();
-  const int total_rows = min(s_off[num_experts], row_cap);
+  const int64_t n = static_cast<int64_t>(min(s_off[num_experts], row_cap)) * groups;
   const double lim = clamp_limit;
-  for (bool first = true; gid < static_cast<int64_t>(total_rows) * groups; gid += stride, first = false) {
-    const int r = static_cast<int>(gid / groups);
-    const int g = static_cast<int>(gid % groups);
-    const int e = expert_of_row(s_off, num_experts, r);
-    if (r < s_off[e] || r - s_off[e] >= s_cnt[e]) continue;  // pad row: untouched
-    const int64_t src = static_cast<int64_t>(r) * (2 * inter) + g * kGroup + lane * 2;
-    if (!first) {
-      graw = *reinterpret_cast<const uint32_t*>(gate_up + src);
-      uraw = *reinterpret_cast<const uint32_t*>(gate_up + src + inter);
+  for (int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4); gid < n;
+       gid += 2 * stride) {
+    int64_t rows[2];
+    int gs[2];
+    uint4 gr[2], ur[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t q = gid + k * stride < n ? gid + k * stride : gid;  // in-range stand-in
+      rows[k] = q / groups;
+      gs[k] = static_cast<int>(q % groups);
+      const int64_t src = rows[k] * (2 * inter) + gs[k] * kGroup + l16 * 8;
+      gr[k] = *reinterpret_cast<const uint4*>(gate_up + src);
+      ur[k] = *reinterpret_cast<const uint4*>(gate_up + src + inter);
     }
-    const float y0 = swiglu<ACT>(bf16_to_f32(graw & 0xFFFFu), bf16_to_f32(uraw & 0xFFFFu), lim);
-    const float y1 = swiglu<ACT>(bf16_to_f32(graw >> 16), bf16_to_f32(uraw >> 16), lim);
-    const float amax = group_max<64>(fmaxf(fabsf(y0), fabsf(y1)));
-    const float sc = group_scale(amax, FMT);
-    const float inv = 1.0f / sc;  // IEEE division, once per group
-    const uint32_t codes = cvt_pk_e4m3(scale_div(y0, sc, inv, FMT), scale_div(y1, sc, inv, FMT));
-    *reinterpret_cast<uint16_t*>(hq + static_cast<int64_t>(r) * inter + g * kGroup + lane * 2) =
-        static_cast<uint16_t>(codes);
-    if (lane == 0) store_scale(hs, FMT, static_cast<int64_t>(g) * row_cap + r, sc);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int r = static_cast<int>(rows[k]);
+      const int e = expert_of_row(s_off, num_experts, r);
+      // Whole 16-lane groups agree on this test, so the DPP moves below
+      // always see a fully active row of lanes.
+      if (gid + k * stride >= n || r < s_off[e] || r - s_off[e] >= s_cnt[e]) continue;  // pad row
+      const Vals8 g8 = unpack_bf16x8(gr[k]), u8 = unpack_bf16x8(ur[k]);
+      Vals8 y;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y.v[i] = swiglu<ACT>(g8.v[i], u8.v[i], lim);
+      float sc;
+      const uint2 codes = quantize8<FMT>(y, &sc);
+      *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * inter + gs[k] * kGroup + l16 * 8) = codes;
+      if (l16 == 0) store_scale(hs, FMT, static_cast<int64_t>(gs[k]) * row_cap + r, sc);
+    }
   }
 }
 
@@ -100,7 +101,7 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
                       uint8_t* hq, void* hs, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
-  const int64_t need = (groups + kThreads / 64 - 1) / (kThreads / 64);
+  const int64_t need = (groups + 2 * kGroupsPerBlock - 1) / (2 * kGroupsPerBlock);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
   const int blocks = static_cast<int>(need < cap ? need : cap);
   if (blocks == 0) return hipSuccess;
