@@ -218,6 +218,37 @@ size_t moe_workspace_bytes(const moe_problem* p) {
   return moe_workspace_plan(p, &L) == MOE_OK ? L.total : 0;
 }
 
+namespace {
+
+// FC2 and the top-k combine of the decode path, reading the workspace.
+hipError_t launch_down_combine_step(const moe_problem* p, const moe_tensors* t,
+                                    const moe_workspace_layout& L, char* ws, hipStream_t s) {
+  moe::DownCombineArgs d;
+  d.act = reinterpret_cast<const float*>(ws + L.act);
+  d.fmt = p->scale_fmt;
+  d.w = t->w2;
+  d.w_scales = t->w2_scales;
+  d.counts = reinterpret_cast<const int32_t*>(ws + L.expert_counts);
+  d.offsets = reinterpret_cast<const int32_t*>(ws + L.expert_offsets);
+  d.row_to_pair = reinterpret_cast<const int32_t*>(ws + L.row_to_pair);
+  d.pair_to_row = reinterpret_cast<const int32_t*>(ws + L.pair_to_row);
+  d.topk_w = t->topk_w;
+  d.t_live_dev = t->t_live_dev;
+  d.num_experts = p->num_experts;
+  d.row_cap = L.row_cap;
+  d.t_cap = p->t_cap;
+  d.topk = p->topk;
+  d.hidden = p->hidden;
+  d.inter = p->inter;
+  d.hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+  d.hs = ws + L.hs;
+  d.y = reinterpret_cast<uint16_t*>(ws + L.y);
+  d.out = t->out;
+  return moe::launch_down_combine(d, s);
+}
+
+}  // namespace
+
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
                        size_t workspace_bytes, void* stream) {
   moe_workspace_layout L;
@@ -248,10 +279,41 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   const int64_t pairs64 = static_cast<int64_t>(p->t_cap) * p->topk;
   const int pairs = static_cast<int>(pairs64);
 
+  hipError_t e = hipSuccess;
+  if (decode && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {
+    // Routing, activation quantization and FC1 with SiLU(gate) * up in one launch.
+    moe::DecodeFc1Args f;
+    f.ids = t->topk_ids;
+    f.t_live_dev = t->t_live_dev;
+    f.t_cap = p->t_cap;
+    f.topk = p->topk;
+    f.num_experts = p->num_experts;
+    f.align_rows = p->align_rows;
+    f.row_cap = R;
+    f.x = t->x;
+    f.hidden = p->hidden;
+    f.inter = p->inter;
+    f.fmt = p->scale_fmt;
+    f.w = t->w1;
+    f.w_scales = t->w1_scales;
+    f.act = p->act;
+    f.act_limit = p->clamp_limit;
+    f.counts = counts;
+    f.offsets = offsets;
+    f.row_to_pair = r2p;
+    f.pair_to_row = p2r;
+    f.xq = xq;
+    f.xs = xs;
+    f.c1 = c1;
+    f.act_out = act;
+    e = moe::launch_fc1_decode(f, s);
+    if (e == hipSuccess) e = launch_down_combine_step(p, t, L, ws, s);
+    return from_hip(e);
+  }
   // Alignment and activation quantization share one launch (independent work).
-  hipError_t e = moe::launch_prep(t->topk_ids, p->t_cap, t->t_live_dev, p->topk, p->num_experts,
-                                  p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden,
-                                  p->scale_fmt, xq, xs, s);
+  e = moe::launch_prep(t->topk_ids, p->t_cap, t->t_live_dev, p->topk, p->num_experts,
+                       p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden, p->scale_fmt, xq,
+                       xs, s);
 
   moe::GemmArgs g;
   g.fmt = p->scale_fmt;
@@ -282,30 +344,7 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
     g.act_out = nullptr;
   }
   if (decode) {  // FC2 and the top-k combine in one launch
-    if (e == hipSuccess) {
-      moe::DownCombineArgs d;
-      d.act = act;
-      d.fmt = p->scale_fmt;
-      d.w = t->w2;
-      d.w_scales = t->w2_scales;
-      d.counts = counts;
-      d.offsets = offsets;
-      d.row_to_pair = r2p;
-      d.pair_to_row = p2r;
-      d.topk_w = t->topk_w;
-      d.t_live_dev = t->t_live_dev;
-      d.num_experts = p->num_experts;
-      d.row_cap = R;
-      d.t_cap = p->t_cap;
-      d.topk = p->topk;
-      d.hidden = p->hidden;
-      d.inter = p->inter;
-      d.hq = hq;
-      d.hs = hs;
-      d.y = y;
-      d.out = t->out;
-      e = moe::launch_down_combine(d, s);
-    }
+    if (e == hipSuccess) e = launch_down_combine_step(p, t, L, ws, s);
     return from_hip(e);
   }
   if (e == hipSuccess)

@@ -106,6 +106,46 @@ struct DownCombineArgs {
 
 hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t stream);
 
+// FC1 of a decode-sized layer with the routing alignment and the activation
+// quantization in its prologue (one launch instead of two). Needs the
+// decode-path limits above plus all t_cap tokens' codes within kF1TokBytes
+// of LDS (row stride H + 16) and t_cap x H/128 scales within kF1MaxScales.
+constexpr int kF1TokBytes = 24576;
+constexpr int kF1MaxScales = 256;
+
+inline bool fc1_decode_fits(int64_t t_cap, int64_t topk, int64_t hidden, int64_t inter) {
+  return down_combine_fits(t_cap, topk, inter) && t_cap * (hidden + 16) <= kF1TokBytes &&
+         t_cap * (hidden / 128) <= kF1MaxScales;
+}
+
+struct DecodeFc1Args {
+  const int32_t* ids;         // [t_cap, topk]
+  const int32_t* t_live_dev;  // nullable: t_cap
+  int t_cap;
+  int topk;
+  int num_experts;
+  int align_rows;
+  int row_cap;
+  const uint16_t* x;          // [t_cap, H] BF16
+  int hidden;
+  int inter;
+  int fmt;
+  const uint8_t* w;           // [E, 2I, H] E4M3: gate rows [0, I), up rows [I, 2I)
+  const float* w_scales;      // [E, 2I/128, H/128]
+  int act;
+  float act_limit;
+  int32_t* counts;            // workspace copies, as moe_align writes them
+  int32_t* offsets;
+  int32_t* row_to_pair;
+  int32_t* pair_to_row;
+  uint8_t* xq;                // workspace copies, as moe_act_quant writes them
+  void* xs;
+  uint16_t* c1;               // [row_cap, 2I] BF16
+  float* act_out;             // [row_cap, I] fp32 SiLU(gate) * up
+};
+
+hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream);
+
 int device_cu_count();
 
 }  // namespace moe
