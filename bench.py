@@ -100,10 +100,23 @@ def fc1_bytes(cfg, n_live_experts, pairs):
     return n_live_experts * per_expert + pairs * (H + (H // 128) * 4) + pairs * 2 * I * 2
 
 
+def fc1_decode_bytes(cfg, n_live_experts, pairs, t_live):
+    """Algorithmic bytes of one decode-path FC1 launch (routing, activation
+    quantization, FC1 and SiLU): live experts' FC1 codes + scales, the BF16
+    token rows read, the codes + fp32 scales written, the BF16 C1 rows and the
+    fp32 SiLU(gate)*up rows."""
+    H, I = cfg.hidden, cfg.inter
+    per_expert = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+    return (n_live_experts * per_expert + t_live * H * 2 + t_live * (H + (H // 128) * 4)
+            + pairs * 2 * I * 2 + pairs * I * 4)
+
+
 def kernel_source_hash():
+    """Hash of the FC1 kernels' sources (the traffic summaries are keyed by it)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", "gemm.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("gemm.hip", "fc1_decode.hip"):
+        with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -145,12 +158,15 @@ def traffic_from(args, fetch_dir, write_dir):
     t_cap, t_live = DEFAULT_TOKENS[args.config]
     if args.tokens is not None:
         t_cap = t_live = args.tokens
-    want = f"<{'true' if fmt == 'ue8m0' else 'false'}, true>"
+    want = f"<{'true' if fmt == 'ue8m0' else 'false'}, true"
+    want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }>"
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _counter_rows(d, counter)
-        fc1 = [v for n, v in per.values() if ("gemm_stream_kernel" in n or "gemm_tiled_kernel" in n)
-               and want in n]
+        fc1 = [v for n, v in per.values() if want_dec in n]
+        if not fc1:
+            fc1 = [v for n, v in per.values()
+                   if ("gemm_stream_kernel" in n or "gemm_tiled_kernel" in n) and want in n]
         # the calibration copies are the run's last three copy dispatches
         copies = [per[k][1] for k in sorted(per) if "copyBuffer" in per[k][0]][-3:]
         if not fc1 or not copies:
@@ -329,10 +345,25 @@ def main():
     w1_copies = [(d_w[0], d_w[1])] + [(d_w[0].clone(), d_w[1].clone()) for _ in range(n_copies - 1)]
     max_rows = min(pairs, R)
 
+    # On the decode path the layer's FC1 is the fused kernel (routing, activation
+    # quantization, FC1, SiLU); it is timed through its own entry point on a
+    # workspace of its own. Elsewhere FC1 is the grouped GEMM.
+    ws_f = torch.empty_like(ws)
+    try:
+        moe.moe_fc1_decode(dx, dids, d_w[0], d_w[1], I, fmt, act, lim, cfg.align_rows, 0,
+                           t_live=dlive, workspace=ws_f)
+        fused = True
+    except moe.MoeError:
+        fused = False
+
     def fc1(i):
         wq, ws_ = w1_copies[i % n_copies]
-        moe.moe_grouped_gemm_fp8(xq, xs, fmt, wq, ws_, counts, offsets, R, a_row_map=r2p,
-                                 a_row_div=K, max_rows_per_expert=max_rows, out=c1)
+        if fused:
+            moe.moe_fc1_decode(dx, dids, wq, ws_, I, fmt, act, lim, cfg.align_rows, 0,
+                               t_live=dlive, workspace=ws_f)
+        else:
+            moe.moe_grouped_gemm_fp8(xq, xs, fmt, wq, ws_, counts, offsets, R, a_row_map=r2p,
+                                     a_row_div=K, max_rows_per_expert=max_rows, out=c1)
     for i in range(n_copies):
         fc1(i)
     torch.cuda.synchronize()
@@ -344,13 +375,16 @@ def main():
     torch.cuda.synchronize()
     k_avg = a.elapsed_time(b) * 1e3 / args.kernel_reps
     del w1_copies
-    fc1_b = fc1_bytes(cfg, n_live_e, pairs)
+    fc1_b = fc1_decode_bytes(cfg, n_live_e, pairs, t_live) if fused else fc1_bytes(cfg, n_live_e, pairs)
     fc1_flops = 2 * pairs * 2 * I * H
     workload_key = f"{args.config}:T{t_live}:{fmt}"
     traffic = load_traffic(workload_key)
     tiled = pairs > 0 and pairs / max(n_live_e, 1) > moe.GEMM_TILES["stream_max_rows"]
     kname = ("gemm_tiled_kernel" if tiled else "gemm_stream_kernel") + \
         f"<{'true' if fmt == 'ue8m0' else 'false'}, true> (FC1)"
+    if fused:
+        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }> "
+                 "(routing, activation quantization, FC1, SiLU)")
     if tiled:
         roof = {"kernel": kname, "bound": "mfma",
                 "achieved": round(fc1_flops / (k_avg * 1e-6) / 1e12, 2), "peak": FP8_PEAK_TFLOPS,

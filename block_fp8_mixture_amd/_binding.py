@@ -67,6 +67,8 @@ _SIGNATURES = {
     "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Problem)]),
     "moe_forward": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
                                    ctypes.c_size_t, _vp]),
+    "moe_fc1_decode": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
+                                      ctypes.c_size_t, _vp]),
 }
 
 
@@ -322,3 +324,31 @@ def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", a
                          workspace.numel(), _stream())
     _check("moe_forward", st)
     return out, workspace
+
+
+def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
+                   clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None,
+                   workspace=None):
+    """The decode path's first launch alone (routing, activation quantization and
+    FC1 with SiLU(gate)*up), writing moe_forward's workspace. Returns the workspace."""
+    lib = load_library()
+    xb = _bf16_view(x, "x")
+    t_cap, hidden = xb.shape
+    _need(topk_ids, "topk_ids", torch.int32, ndim=2)
+    _need(w1, "w1", torch.uint8, ndim=3)
+    _need(w1_scales, "w1_scales", torch.float32, ndim=3)
+    num_experts, two_i, h1 = w1.shape
+    if h1 != hidden or two_i != 2 * inter:
+        raise ValueError("w1 shape disagrees with x / inter")
+    prob = _problem(num_experts, hidden, inter, topk_ids.shape[1], t_cap, align_rows, row_cap,
+                    fmt, act, clamp_limit)
+    need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xb.device)
+    _need(workspace, "workspace", torch.uint8)
+    tens = _Tensors(_ptr(xb), _ptr(topk_ids), None, _live(t_live), _ptr(w1), _ptr(w1_scales),
+                    None, None, None)
+    st = lib.moe_fc1_decode(ctypes.byref(prob), ctypes.byref(tens), _ptr(workspace),
+                            workspace.numel(), _stream())
+    _check("moe_fc1_decode", st)
+    return workspace

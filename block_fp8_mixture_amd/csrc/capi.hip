@@ -247,7 +247,50 @@ hipError_t launch_down_combine_step(const moe_problem* p, const moe_tensors* t,
   return moe::launch_down_combine(d, s);
 }
 
+// Routing, activation quantization and FC1 of the decode path, writing the workspace.
+hipError_t launch_fc1_decode_step(const moe_problem* p, const moe_tensors* t,
+                                  const moe_workspace_layout& L, char* ws, hipStream_t s) {
+  moe::DecodeFc1Args f;
+  f.ids = t->topk_ids;
+  f.t_live_dev = t->t_live_dev;
+  f.t_cap = p->t_cap;
+  f.topk = p->topk;
+  f.num_experts = p->num_experts;
+  f.align_rows = p->align_rows;
+  f.row_cap = L.row_cap;
+  f.x = t->x;
+  f.hidden = p->hidden;
+  f.inter = p->inter;
+  f.fmt = p->scale_fmt;
+  f.w = t->w1;
+  f.w_scales = t->w1_scales;
+  f.act = p->act;
+  f.act_limit = p->clamp_limit;
+  f.counts = reinterpret_cast<int32_t*>(ws + L.expert_counts);
+  f.offsets = reinterpret_cast<int32_t*>(ws + L.expert_offsets);
+  f.row_to_pair = reinterpret_cast<int32_t*>(ws + L.row_to_pair);
+  f.pair_to_row = reinterpret_cast<int32_t*>(ws + L.pair_to_row);
+  f.xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  f.xs = ws + L.xs;
+  f.c1 = reinterpret_cast<uint16_t*>(ws + L.c1);
+  f.act_out = reinterpret_cast<float*>(ws + L.act);
+  return moe::launch_fc1_decode(f, s);
+}
+
 }  // namespace
+
+moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  moe_workspace_layout L;
+  const moe_status st = moe_workspace_plan(p, &L);
+  if (st != MOE_OK) return st;
+  if (!(L.act < L.total) || !moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter))
+    return MOE_ERR_UNSUPPORTED;
+  if (!t || !workspace) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
+  if (!t->x || !t->topk_ids || !t->w1 || !t->w1_scales) return MOE_ERR_INVALID_ARG;
+  return from_hip(launch_fc1_decode_step(p, t, L, static_cast<char*>(workspace), as_stream(stream)));
+}
 
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
                        size_t workspace_bytes, void* stream) {
@@ -282,31 +325,7 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   hipError_t e = hipSuccess;
   if (decode && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {
     // Routing, activation quantization and FC1 with SiLU(gate) * up in one launch.
-    moe::DecodeFc1Args f;
-    f.ids = t->topk_ids;
-    f.t_live_dev = t->t_live_dev;
-    f.t_cap = p->t_cap;
-    f.topk = p->topk;
-    f.num_experts = p->num_experts;
-    f.align_rows = p->align_rows;
-    f.row_cap = R;
-    f.x = t->x;
-    f.hidden = p->hidden;
-    f.inter = p->inter;
-    f.fmt = p->scale_fmt;
-    f.w = t->w1;
-    f.w_scales = t->w1_scales;
-    f.act = p->act;
-    f.act_limit = p->clamp_limit;
-    f.counts = counts;
-    f.offsets = offsets;
-    f.row_to_pair = r2p;
-    f.pair_to_row = p2r;
-    f.xq = xq;
-    f.xs = xs;
-    f.c1 = c1;
-    f.act_out = act;
-    e = moe::launch_fc1_decode(f, s);
+    e = launch_fc1_decode_step(p, t, L, ws, s);
     if (e == hipSuccess) e = launch_down_combine_step(p, t, L, ws, s);
     return from_hip(e);
   }

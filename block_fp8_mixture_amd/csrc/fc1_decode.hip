@@ -100,63 +100,73 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // ---- routing (wave 0; lane = pair)
+  // ---- routing (wave 0; lane = pair). Expert ids are compared bit by bit,
+  // most significant first, with one ballot per bit: every lane learns the
+  // valid lanes with the same expert (eq) and with a smaller one (lt), so
+  // ranks in pair order, counts, the entry index in expert order and the
+  // compact offset are popcounts; the aligned-row and tile prefixes over the
+  // entries are one wave scan.
   if (wave == 0) {
     const int n_pairs = t_live * TK;
     const bool live = lane < n_pairs && lane < PQ;
     const bool ok = live && static_cast<unsigned>(my_id) < static_cast<unsigned>(E);
     const uint64_t below = (uint64_t(1) << lane) - 1;
-    uint64_t active = __ballot(ok), leaders = 0;
-    int rank = 0, cnt = 0;
-    while (active) {  // one round per distinct expert; ranks in pair order
-      const int ld = __ffsll(static_cast<unsigned long long>(active)) - 1;
-      const int le = __builtin_amdgcn_readlane(my_id, ld);
-      const uint64_t same = __ballot(ok && my_id == le);
-      if (ok && my_id == le) {
-        rank = __popcll(same & below);
-        cnt = __popcll(same);
+    const uint64_t valid = __ballot(ok);
+    const int nb = 32 - __builtin_clz(static_cast<unsigned>(max(E - 1, 1)));  // bits of an expert id
+    uint64_t eq = valid, lt = 0;
+    for (int b = nb - 1; b >= 0; --b) {
+      const bool bit = (my_id >> b) & 1;
+      const uint64_t m = __ballot(ok && bit);
+      if (bit) {
+        lt |= eq & ~m;
+        eq &= m;
+      } else {
+        eq &= ~m;
       }
-      leaders |= uint64_t(1) << ld;
-      active &= ~same;
     }
-    // Per lane: the experts below its own, their rows, aligned rows and tiles.
-    int pos = 0, c0 = 0, row0 = 0, tp = 0, total = 0, tiles_all = 0;
-    for (uint64_t m = leaders; m; m &= m - 1) {
-      const int ld = __ffsll(static_cast<unsigned long long>(m)) - 1;
-      const int le = __builtin_amdgcn_readlane(my_id, ld);
-      const int lc = __builtin_amdgcn_readlane(cnt, ld);
-      const int lr = (lc + A - 1) / A * A;
-      const int lt = (lc + kStreamTileM - 1) / kStreamTileM;
-      if (le < my_id) {
-        ++pos;
-        c0 += lc;
-        row0 += lr;
-        tp += lt;
-      }
-      total += lr;
-      tiles_all += lt;
-    }
-    if (ok && ((leaders >> lane) & 1)) {
+    const int rank = __popcll(eq & below), cnt = __popcll(eq);
+    const uint64_t leaders = __ballot(ok && rank == 0);
+    const int n_live = __popcll(leaders);
+    const int pos = __popcll(lt & leaders);  // entry of this lane's expert
+    const int c0 = __popcll(lt);             // live pairs of smaller experts
+    if (ok && rank == 0) {
       s_e[pos] = my_id;
       s_cnt[pos] = cnt;
       s_c0[pos] = c0;
-      s_row0[pos] = row0;
-      s_tp[pos] = tp;
+      s_row0[pos] = (cnt + A - 1) / A * A;                          // prefixed below
+      s_tp[pos] = (cnt + kStreamTileM - 1) / kStreamTileM;          // prefixed below
+    }
+    // Exclusive prefixes over the entries (lane = entry; one wave, so its LDS
+    // accesses are ordered).
+    const int vr = lane < n_live ? s_row0[lane] : 0;
+    const int vt = lane < n_live ? s_tp[lane] : 0;
+    int ir = vr, it = vt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int ur = __shfl_up(ir, d, 64), ut = __shfl_up(it, d, 64);
+      if (lane >= d) {
+        ir += ur;
+        it += ut;
+      }
+    }
+    if (lane < n_live) {
+      s_row0[lane] = ir - vr;
+      s_tp[lane] = it - vt;
+    }
+    if (lane == 63) {
+      s_nlive = n_live;
+      s_total = ir;
+      s_tp[n_live] = it;
     }
     if (ok) {
+      const int row = s_row0[pos] + rank;
       const int c = c0 + rank;
       s_ctok[c] = lane / TK;
-      s_crow[c] = row0 + rank;
+      s_crow[c] = row;
       s_cpair[c] = lane;
-      s_prow[lane] = row0 + rank;
+      s_prow[lane] = row;
     } else if (live) {
       s_prow[lane] = -1;
-    }
-    if (lane == 0) {
-      const int n_live = __popcll(leaders);
-      s_nlive = n_live;
-      s_total = total;
-      s_tp[n_live] = tiles_all;
     }
   }
   __syncthreads();

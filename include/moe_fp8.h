@@ -270,6 +270,22 @@ size_t moe_workspace_bytes(const moe_problem* p);
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The first launch of moe_forward's decode path, on its own: routing
+ * alignment, activation quantization and FC1 with SiLU(gate)*up in one
+ * kernel (vLLM PR #59128, Purpose; vLLM PR #65794, Details; TensorRT-LLM
+ * PR #21250, For MoE owners). It exists so that the kernel can be timed and
+ * tested alone. It applies when the problem takes the decode path
+ * (moe_workspace_layout.act laid out) and all t_cap tokens' codes fit 24 KiB
+ * of LDS at a row stride of H+16 bytes, with t_cap*H/128 <= 256.
+ * It writes, bit for bit as moe_align and moe_act_quant would:
+ * expert_counts, expert_offsets, row_to_pair, pair_to_row, xq and xs. It
+ * also writes c1 for the live rows and act (fp32 SiLU(gate)*up). The arguments
+ * are those of moe_forward: t->w2, t->w2_scales, t->topk_w and t->out are
+ * not read.
+ * Errors: UNSUPPORTED (not such a problem), INVALID_ARG, CAPACITY, HIP. */
+moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -168,3 +168,29 @@ def test_forward_validation(lib):
     t0 = B._Tensors(*([FAKE.value] * 8 + [None]))
     assert lib.moe_forward(ctypes.byref(p), ctypes.byref(t0), FAKE, need, NULL) == INVALID
     assert lib.moe_forward(ctypes.byref(_problem(t_cap=0)), ctypes.byref(t), FAKE, need, NULL) == OK
+
+
+def test_decode_plan_lays_out_act_and_fc1_decode_validates(lib):
+    # decode-sized problem: the plan lays out act [R, I] fp32 at the end
+    p = _problem(num_experts=288, hidden=4096, inter=512, topk=8, t_cap=4)
+    lay = B._Layout()
+    assert lib.moe_workspace_plan(ctypes.byref(p), ctypes.byref(lay)) == OK
+    assert lay.act % 256 == 0 and lay.act >= lay.y + lay.row_cap * 4096 * 2
+    assert lay.total >= lay.act + lay.row_cap * 512 * 4
+    # 4096 tokens: no act buffer (act == total)
+    big = B._Layout()
+    assert lib.moe_workspace_plan(ctypes.byref(_problem()), ctypes.byref(big)) == OK
+    assert big.act == big.total
+    need = lib.moe_workspace_bytes(ctypes.byref(p))
+    t = B._Tensors(*([FAKE.value] * 9))
+    f = lib.moe_fc1_decode
+    assert f(ctypes.byref(_problem()), ctypes.byref(t), FAKE, big.total, NULL) == UNSUPPORTED
+    assert f(ctypes.byref(p), ctypes.byref(t), FAKE, need - 1, NULL) == CAPACITY
+    assert f(ctypes.byref(p), ctypes.byref(t), NULL, need, NULL) == INVALID
+    tx = B._Tensors(None, *([FAKE.value] * 8))
+    assert f(ctypes.byref(p), ctypes.byref(tx), FAKE, need, NULL) == INVALID
+    # 8 tokens at H = 6144 fit the decode path but not FC1's resident activations
+    p8 = _problem(num_experts=256, hidden=6144, inter=256, topk=8, t_cap=8)
+    l8 = B._Layout()
+    assert lib.moe_workspace_plan(ctypes.byref(p8), ctypes.byref(l8)) == OK and l8.act < l8.total
+    assert f(ctypes.byref(p8), ctypes.byref(t), FAKE, l8.total, NULL) == UNSUPPORTED

@@ -287,3 +287,66 @@ def test_padded_tiles_are_skipped():
     capacity_tiles = -(-R // 16) * (2 * I // 128)
     assert int(tiles.item()) == live_tiles
     assert live_tiles * 4 < capacity_tiles
+
+
+FC1_DECODE_RUNS = [
+    ("decode", 4, 4, "fp32", "swiglu", INF),
+    ("decode", 4, 3, "ue8m0", "swiglu_clamp", 7.0),
+    ("decode", 1, 1, "pow2", "swiglu_clamp_after_silu", 7.0),
+    ("tiny", 8, 5, "fp32", "swiglu", INF),
+    ("sweep", 1, 1, "fp32", "swiglu", INF),
+]
+
+
+@pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim", FC1_DECODE_RUNS)
+def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
+    """The decode path's first launch on its own: alignment and activation codes
+    bit-exact, C1 rows within the GEMM tolerance, act = SiLU(gate)*up of the GPU's
+    own C1 rows bit for bit, and nothing written outside the live rows."""
+    cfg = synth.get(name)
+    say(f"fc1_decode {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act}")
+    E, H, I, K, A = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, cfg.align_rows
+    x, ids, w = synth.make_workload(cfg, t_cap)
+    (w1q, w1s), _ = host_weights(name)
+    d_w1q, d_w1s, _, _ = device_weights(name)
+    lim32 = float(np.float32(lim))
+    row_cap = cfg.row_cap or 0
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32)
+    assert lay["act"] < lay["total"]
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    moe.moe_fc1_decode(up(x), up(ids), d_w1q, d_w1s, I, fmt, act, lim32, A, row_cap,
+                       t_live=up(np.array([t_live], np.int32)), workspace=ws)
+    torch.cuda.synchronize()
+    R = lay["row_cap"]
+    sdt = np.uint8 if fmt == "ue8m0" else np.float32
+    al = oracle.align(ids, t_live, E, A)
+    assert np.array_equal(_ws_view(ws, lay, "expert_counts", np.int32, (E,)), al["counts"])
+    assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, (E + 1,)), al["offsets"])
+    total = int(al["offsets"][-1])
+    r2p = _ws_view(ws, lay, "row_to_pair", np.int32, (R,))
+    assert np.array_equal(r2p[:total], al["row_to_pair"])
+    assert np.all(r2p[total:].view(np.uint32) == np.uint32(POISON_U8 * 0x01010101))
+    p2r = _ws_view(ws, lay, "pair_to_row", np.int32, (t_cap * K,))
+    assert np.array_equal(p2r[:t_live * K], al["pair_to_row"])
+    xq = _ws_view(ws, lay, "xq", np.uint8, (t_cap, H))
+    xs = _ws_view(ws, lay, "xs", sdt, (H // 128, t_cap))
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    assert np.array_equal(xq[:t_live], rq)
+    assert np.all(xq[t_live:] == POISON_U8)
+    assert np.array_equal(np.ascontiguousarray(xs[:, :t_live]).view(np.uint8),
+                          np.ascontiguousarray(rs).view(np.uint8))
+    c1 = _ws_view(ws, lay, "c1", np.uint16, (R, 2 * I))
+    act_rows = _ws_view(ws, lay, "act", np.float32, (R, I))
+    sa_x = oracle.scales_to_f64(xs, fmt)
+    live_rows = np.flatnonzero(np.isin(np.arange(R), al["pair_to_row"][al["pair_to_row"] >= 0]))
+    for e in np.flatnonzero(al["counts"] > 0):
+        seg = np.arange(al["offsets"][e], al["offsets"][e] + al["counts"][e])
+        tok = al["row_to_pair"][seg] // K
+        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e])
+        assert_bf16_close(c1[seg], ref_c1, f"FC1 expert {e}")
+        g = oracle.bf16_bits_to_f64(c1[seg][:, :I])
+        u = oracle.bf16_bits_to_f64(c1[seg][:, I:])
+        ref_act = oracle.moe.swiglu(g, u, act, lim32)
+        assert np.array_equal(act_rows[seg].view(np.uint32), ref_act.view(np.uint32)), e
+    dead = np.setdiff1d(np.arange(R), live_rows)
+    assert np.all(c1[dead] == (POISON_U8 << 8 | POISON_U8))
