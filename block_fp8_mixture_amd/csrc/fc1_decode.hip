@@ -79,6 +79,10 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   __shared__ int s_cpair[kDcMaxPairs];    //   its pair
   __shared__ int s_prow[kDcMaxPairs];     // pair -> aligned row, or -1
   __shared__ int s_nlive, s_total;
+  // K-split partial sums: [task parity][wave][lane] x 16 bytes, and per group
+  // of waves the number of shares that have arrived (counts up for good).
+  __shared__ __attribute__((aligned(16))) uint8_t s_part[2 * kF1Waves * 64 * 16];
+  __shared__ int s_arrive[kF1Waves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   // ranks in pair order, counts, the entry index in expert order and the
   // compact offset are popcounts; the aligned-row and tile prefixes over the
   // entries are one wave scan.
+  if (tid < kF1Waves) s_arrive[tid] = 0;
   if (wave == 0) {
     const int n_pairs = t_live * TK;
     const bool live = lane < n_pairs && lane < PQ;
@@ -201,13 +206,22 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
     if (tid < min(t_live * TK, PQ)) p.pair_to_row[tid] = s_prow[tid];
   }
 
-  // ---- per-wave task stream
+  // ---- per-wave task stream. With few tasks (1 token: one per 16 weight
+  // rows of each live expert) S waves of a workgroup share each task, each
+  // over its own 1/S of K; S is the largest power of two up to 8 that still
+  // leaves at most one task per group of S waves and divides the K blocks.
   const int n_rb = I / 8;  // 16-row blocks (8 gate + 8 up rows)
   const int n_tasks = s_tp[n_live] * n_rb;
   const int NW = gridDim.x * kF1Waves;
-  const int gw = blockIdx.x * kF1Waves + wave;
-  const int my_tasks = gw < n_tasks ? (n_tasks - 1 - gw) / NW + 1 : 0;
-  const int total = my_tasks * KB;  // stages of this wave
+  int S = 1;
+  while (S < kF1Waves && n_tasks * (2 * S) <= NW && KB % (2 * S) == 0) S *= 2;
+  S = __builtin_amdgcn_readfirstlane(S);
+  const int NG = NW / S;                                   // groups of S waves
+  const int gidx = blockIdx.x * (kF1Waves / S) + wave / S;  // this wave's group
+  const int kbs = KB / S;                                  // K blocks of a share
+  const int kb_lo = (wave % S) * kbs, kb_hi = kb_lo + kbs;
+  const int my_tasks = gidx < n_tasks ? (n_tasks - 1 - gidx) / NG + 1 : 0;
+  const int total = my_tasks * kbs;  // stages of this wave
   uint8_t* ring = s_ring + wave * (kF1Depth * kF1Stage);
   const int grow = lane >> 3;
   const int chunk_lo = ((lane & 7) ^ ((grow >> 1) & 7)) << 4;        // slab row grow
@@ -233,7 +247,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   // Issue side: stage pointers of the current task. Stand-ins (valid
   // addresses) serve the stages past a wave's last one that the stream start
   // issues so that it always issues the same number of loads.
-  int i_task = gw, i_kb = 0;
+  int i_task = gidx, i_kb = kb_lo;
   const uint8_t* i_w0 = p.w + lane * 16;
   const uint8_t* i_w1 = p.w + lane * 16;
   const uint8_t* i_s = reinterpret_cast<const uint8_t*>(p.w_scales);
@@ -254,9 +268,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
     __builtin_amdgcn_global_load_lds(i_s + i_kb * 4, (lds_void*)(st + kF1StageW), 4, 0, 0);
   };
   auto advance = [&]() {
-    if (++i_kb == KB) {
-      i_kb = 0;
-      i_task += NW;
+    if (++i_kb == kb_hi) {
+      i_kb = kb_lo;
+      i_task += NG;
       if (i_task < n_tasks) i_set();
     }
   };
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   const int c0f = 2 * (lane >> 4);  // fragment chunks c0f, c0f + 1 of a 128-byte K block
   const uint32_t x_base = lds_addr(s_x) + c0f * 16;
   const uint32_t xs_base = lds_addr(s_xs);
-  int c_task = gw, c_kb = 0, slot = 0;
+  int c_task = gidx, c_kb = kb_lo, slot = 0, c_iter = 0;
   Task ck{0, 0, 0};
   int c_rows = 0, c_crow0 = 0, c_t = 0;  // task's live rows in the tile, compact row base, lane's token
   auto c_set = [&]() {
@@ -329,14 +343,36 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
                   xs_base + (c_t * KB + c_kb) * 4, st + kF1StageW + ((lane >> 5) << 2), wf.u[0],
                   wf.u[1], af.u[0], af.u[1], sa, sw);
     acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
-    if (++c_kb == KB) {
+    if (++c_kb == kb_hi) {
+      // This wave's share of the task is done. With S > 1 the partial goes to
+      // LDS and the last share of the group to arrive adds the S partials in
+      // wave order (a fixed order, whoever arrives last) and stores.
+      bool store = true;
+      if (S > 1) {
+        const uint32_t part = lds_addr(s_part) + (((c_iter & 1) * kF1Waves) * 64 + lane) * 16;
+        const uint32_t mine = part + wave * 1024;
+        asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(mine), "v"(acc) : "memory");
+        int old = 0;
+        if (lane == 0) old = atomicAdd(&s_arrive[wave / S], 1);
+        old = __builtin_amdgcn_readfirstlane(old);
+        store = (old + 1) % S == 0;
+        if (store) {
+          const uint32_t first = part + (wave / S) * S * 1024;
+          acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int w = 0; w < S; ++w) {
+            v4f v;
+            asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(first + w * 1024) : "memory");
+            acc += v;
+          }
+        }
+      }
       // Task done. Lanes 0..31 hold gate columns jg + 4 (lane / 16) + v of
       // token tok, lanes 32..63 the up values of the same columns.
       const uint2 packed = pack_bf16x4(acc);
       uint2 other;
       other.x = __shfl_xor(packed.x, 32, 64);
       other.y = __shfl_xor(packed.y, 32, 64);
-      if (tok < c_rows) {
+      if (store && tok < c_rows) {
         const int jg = ck.rb * 8;
         const int col = (lane < 32 ? jg : I + jg) + 4 * ((lane >> 4) & 1);
         const int64_t row = s_crow[c_crow0 + tok];
@@ -351,8 +387,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
         }
       }
       acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      c_kb = 0;
-      c_task += NW;
+      c_kb = kb_lo;
+      c_task += NG;
+      ++c_iter;
       if (c_task < n_tasks) c_set();
     }
     slot = slot == kF1Depth - 1 ? 0 : slot + 1;
