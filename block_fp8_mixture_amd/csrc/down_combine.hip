@@ -33,8 +33,10 @@ namespace {
 
 constexpr int kDcThreads = 512;
 constexpr int kDcWaves = kDcThreads / 64;
-constexpr int kDcDepth = 7;             // stages in a wave's ring
-constexpr int kDcStage = 16 * kGroup;   // 16 weight rows x 128 bytes
+constexpr int kDcDepth = 6;               // stages in a wave's ring
+constexpr int kDcStageW = 16 * kGroup;    // 16 weight rows x 128 bytes
+constexpr int kDcStage = kDcStageW + 256; // + the stage's weight block scale (64 x 4-byte slots)
+constexpr int kDcLoads = 3;               // loads per wave and stage
 constexpr int kDcTiles = kDcMaxPairs / kStreamTileM;  // token tiles of one expert, at most
 
 // Two 16-byte LDS reads with their own wait, as assembly: the compiler then
@@ -103,7 +105,6 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kDcWaves * kDcDepth * kDcStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_tok[kDcTokBytes];  // codes, row stride I + 16
   __shared__ float s_sa[kDcMaxScales];   // token scale of (compact row, K block)
-  __shared__ float s_sw[kDcMaxScales];   // weight scale of (list entry, K block), this column block
   __shared__ __attribute__((aligned(16))) float s_slot[kDcMaxPairs * 16];  // pair q's 16 columns
   __shared__ int s_e[kDcMaxPairs];       // list entry -> expert
   __shared__ int s_cnt[kDcMaxPairs];     //   its live rows
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
     s_nlist = 0;
     s_nrows = 0;
   }
+  for (int x = tid; x < PQ * 16; x += kDcThreads) s_slot[x] = 0.0f;  // ordered by the barriers below
   int run_n = 0, run_r = 0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -219,22 +221,25 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
   // the stream start issues so that it always issues the same number.
   const uint8_t* i_w0 = p.w + lane * 16;
   const uint8_t* i_w1 = p.w + lane * 16;
+  const uint8_t* i_s = reinterpret_cast<const uint8_t*>(p.w_scales);
   auto i_set = [&](int n0) {
     const int e = __builtin_amdgcn_readfirstlane(s_e[i_ent]);
     const uint8_t* wb = p.w + (static_cast<int64_t>(e) * N + n0) * I;
     i_w0 = wb + static_cast<int64_t>(grow) * I + chunk_lo;
     i_w1 = wb + static_cast<int64_t>(grow + 8) * I + chunk_hi;
+    i_s = reinterpret_cast<const uint8_t*>(p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + n0 / kGroup) * KB);
   };
   auto issue = [&](uint8_t* st, int n0) {
     __builtin_amdgcn_global_load_lds(i_w0 + i_kb * kGroup, (lds_void*)(st), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(i_s + i_kb * 4, (lds_void*)(st + kDcStageW), 4, 0, 0);
     if (++i_kb == KB) {
       i_kb = 0;
       i_ent += kDcWaves;
       if (i_ent < n_list) i_set(n0);
     }
   };
-  // Always kDcDepth - 1 stages (2 loads each), so the compiler knows how
+  // Always kDcDepth - 1 stages (kDcLoads loads each), so the compiler knows how
   // many loads follow anything issued before, and a wave with fewer stages
   // fills the rest of its ring with stand-in loads that are never read.
   auto start_stream = [&](int n0) {
@@ -245,6 +250,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
     for (int d = 0; d < kDcDepth - 1; ++d) {
       __builtin_amdgcn_global_load_lds(i_w0 + i_kb * kGroup, (lds_void*)(ring + d * kDcStage), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(ring + d * kDcStage + 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(i_s + i_kb * 4, (lds_void*)(ring + d * kDcStage + kDcStageW), 4, 0, 0);
       // Advance to stage d + 1 if it exists: the loop's issues then
       // continue from stage kDcDepth - 1, and past the last stage the
       // stand-ins repeat it.
@@ -255,27 +261,29 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       }
     }
   };
-  // Weight scales of the listed experts' rows n0..n0+15 (one 128-row block):
-  // one per thread (n_list * KB <= kDcMaxScales <= kDcThreads).
-  // An untracked load issued by every thread (a valid stand-in address when
-  // it has no entry), so it is in flight together with the stream start.
-  auto fetch_sw_first = [&](int n0) {
-    const int x = n_list > 0 ? min(tid, n_list * KB - 1) : 0;
-    const int e = n_list > 0 ? s_e[x / KB] : 0;
-    return gload_b32(p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + n0 / kGroup) * KB + x % KB);
-  };
-
-  // ---- 1b. FC2 input: 16 lanes per compact row, 8 float4 per lane per
-  // 512-column chunk; lanes l16 and chunks u cover columns 4 * (16 u + l16),
-  // so a 128-column group is u = 2g, 2g + 1 over the 16 lanes. The loads of
-  // a wave's first rows and chunk (all of them at decode sizes), its row-map
-  // entries and the weight scales go out before the first weight stages.
-  const int l16 = lane & 15;
+  // ---- 1b. FC2 input rows of this wave's experts (every 8th listed one).
+  // 16 lanes per row, 4 rows per pass; lanes l16 and chunks u cover columns
+  // 4 * (16 u + l16) of a 512-column chunk, so a 128-column group is u = 2g,
+  // 2g + 1 over the 16 lanes. A wave's MFMAs read only the rows it quantizes
+  // itself, so no workgroup barrier separates this from its weight stream.
+  const int l16 = lane & 15, lg = lane >> 4;
   const bool writer = blockIdx.x == 0;
-  auto src_row = [&](int c) {
-    const int cc = c < n_rows ? c : n_rows - 1;
-    const int ent = entry_of(cc);
-    return s_r0[ent] + cc - s_c0[ent];
+  int my_rows = 0;
+  for (int i = wave; i < n_list; i += kDcWaves) my_rows += s_cnt[i];
+  my_rows = __builtin_amdgcn_readfirstlane(my_rows);
+  // Compact and source row of this wave's k-th row (k < my_rows).
+  auto wave_row = [&](int k, int* c, int* r) {
+    for (int i = wave; i < n_list; i += kDcWaves) {
+      const int cnt = s_cnt[i];
+      if (k < cnt) {
+        *c = s_c0[i] + k;
+        *r = s_r0[i] + k;
+        return;
+      }
+      k -= cnt;
+    }
+    *c = 0;
+    *r = 0;
   };
   auto load_chunk = [&](float4* v, int r, int col0) {
 #pragma unroll
@@ -284,44 +292,9 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       v[u] = *reinterpret_cast<const float4*>(p.act + static_cast<int64_t>(r) * I + col);
     }
   };
-  // Prefetch, in this order: 8 row chunks and the row-map entry (waves that
-  // own rows), the weight scale (every thread), then the 2 * (kDcDepth - 1)
-  // loads of the stream start. Waiting until only the last 2 * kDcDepth - 1
-  // (resp. 2 * kDcDepth - 2) remain waits for the rows (resp. the scale)
-  // and nothing of the stream.
-  float4 v[8];
-  u32x4 vr[8];
-  uint32_t pair_first = 0;
-  int r_first = 0;
-  const bool has_rows = wave * 4 < n_rows;  // uniform
-  if (has_rows) {
-    r_first = src_row(wave * 4 + (lane >> 4));
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      vr[u] = gload_b128(p.act + static_cast<int64_t>(r_first) * I + min(4 * (16 * u + l16), I - 4));
-    pair_first = gload_b32(p.row_to_pair + r_first);
-  }
-  int cb = blockIdx.x;  // < n_cb: the grid has at most n_cb workgroups
-  uint32_t sw_first = fetch_sw_first(cb * 16);
-  start_stream(cb * 16);
-  if (has_rows) {
-    static_assert(2 * kDcDepth - 1 == 13, "wait immediate below");
-    asm volatile("s_waitcnt vmcnt(13)"
-                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
-                   "+v"(vr[6]), "+v"(vr[7]), "+v"(pair_first));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      v[u].x = __uint_as_float(vr[u][0]);
-      v[u].y = __uint_as_float(vr[u][1]);
-      v[u].z = __uint_as_float(vr[u][2]);
-      v[u].w = __uint_as_float(vr[u][3]);
-    }
-  }
-
   // Quantizes chunk col0 of compact row c (source row r) into LDS, and for
   // workgroup 0 into the workspace.
-  auto quant_chunk = [&](const float4* v, int c, int r, int col0) {
-    const bool row_ok = c < n_rows;
+  auto quant_chunk = [&](const float4* v, bool row_ok, int c, int r, int col0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int colg = col0 + g * kGroup;
@@ -349,51 +322,75 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       }
     }
   };
-  // The first rows and chunk, from the loads issued above (straight-line
-  // code, so the waits for them let the weight stages stay in flight) ...
-  if (wave * 4 < n_rows) {
-    const int c = wave * 4 + (lane >> 4);
-    if (c < n_rows && l16 == 0) {
-      s_row[c] = r_first;
-      s_pair[c] = static_cast<int>(pair_first);
-    }
-    quant_chunk(v, c, r_first, 0);
+  // Prefetch of the first pass (4 rows, first 512 columns) and its row-map
+  // entries as untracked loads, then the stream start's kDcLoads * (kDcDepth
+  // - 1) loads; waiting until only those remain waits for the prefetch and
+  // nothing of the stream.
+  float4 v[8];
+  u32x4 vr[8];
+  uint32_t pair_first = 0;
+  int c_first = 0, r_first = 0;
+  const bool row_first = lg < my_rows;
+  if (my_rows > 0) {  // uniform
+    wave_row(lg, &c_first, &r_first);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      vr[u] = gload_b128(p.act + static_cast<int64_t>(r_first) * I + min(4 * (16 * u + l16), I - 4));
+    pair_first = gload_b32(p.row_to_pair + r_first);
   }
-  // ... then any further chunks and rows (beyond the decode sizes).
-  for (int rb = wave * 4; rb < n_rows; rb += kDcWaves * 4) {
-    const int c = rb + (lane >> 4);
-    const int r = src_row(c);
-    if (rb != wave * 4 && c < n_rows && l16 == 0) {
+  int cb = blockIdx.x;  // < n_cb: the grid has at most n_cb workgroups
+  start_stream(cb * 16);
+  if (my_rows > 0) {
+    static_assert(kDcLoads * (kDcDepth - 1) == 15, "wait immediate below");
+    asm volatile("s_waitcnt vmcnt(15)"
+                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
+                   "+v"(vr[6]), "+v"(vr[7]), "+v"(pair_first));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v[u].x = __uint_as_float(vr[u][0]);
+      v[u].y = __uint_as_float(vr[u][1]);
+      v[u].z = __uint_as_float(vr[u][2]);
+      v[u].w = __uint_as_float(vr[u][3]);
+    }
+    if (row_first && l16 == 0) {
+      s_row[c_first] = r_first;
+      s_pair[c_first] = static_cast<int>(pair_first);
+    }
+    quant_chunk(v, row_first, c_first, r_first, 0);
+  }
+  // Further chunks and rows (beyond the decode sizes).
+  for (int k0 = 0; k0 < my_rows; k0 += 4) {
+    const bool row_ok = k0 + lg < my_rows;
+    int c = 0, r = 0;
+    wave_row(row_ok ? k0 + lg : 0, &c, &r);
+    if (k0 > 0 && row_ok && l16 == 0) {
       s_row[c] = r;
       s_pair[c] = p.row_to_pair[r];
     }
-    for (int col0 = rb == wave * 4 ? 512 : 0; col0 < I; col0 += 512) {
+    for (int col0 = k0 == 0 ? 512 : 0; col0 < I; col0 += 512) {
       load_chunk(v, r, col0);
-      quant_chunk(v, c, r, col0);
+      quant_chunk(v, row_ok, c, r, col0);
     }
     // Tells the compiler these loads are done on every path out of the loop
     // (they are: their values were used), so code after it does not wait.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
+  // The loop below reads these rows through assembly the compiler does not
+  // see; keep the stores above it.
+  asm volatile("" ::: "memory");
 
   const int tok = lane & 15;
   const int c0 = 2 * (lane >> 4);  // fragment chunks c0, c0 + 1 of a 128-byte K block
   const uint32_t tok_base = lds_addr(s_tok) + c0 * 16;
-  const uint32_t sa_base = lds_addr(s_sa), sw_base = lds_addr(s_sw);
+  const uint32_t sa_base = lds_addr(s_sa);
 
   for (; cb < n_cb; cb += G) {
     const int n0 = cb * 16;
     if (cb != static_cast<int>(blockIdx.x)) {
-      sw_first = fetch_sw_first(n0);
+      for (int x = tid; x < PQ * 16; x += kDcThreads) s_slot[x] = 0.0f;
+      lds_barrier();  // zeroed slots visible
       start_stream(n0);
     }
-    // The scale load is older than the stream start's loads (later
-    // operations only make this wait longer).
-    static_assert(2 * kDcDepth - 2 == 12, "wait immediate below");
-    asm volatile("s_waitcnt vmcnt(12)" : "+v"(sw_first));
-    if (tid < n_list * KB) s_sw[tid] = __uint_as_float(sw_first);
-    for (int x = tid; x < PQ * 16; x += kDcThreads) s_slot[x] = 0.0f;
-    lds_barrier();  // tokens, scales and zeroed slots visible
 
     // ---- 2. stream: wait for stage s, refill the slot of stage s - 1, compute s.
     int c_ent = wave, c_kb = 0, slot = 0;
@@ -409,7 +406,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       if (s + kDcDepth - 2 >= total)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (kDcDepth - 2)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDcLoads * (kDcDepth - 2)));
       const int prev = slot == 0 ? kDcDepth - 1 : slot - 1;
       if (s + kDcDepth - 1 < total) issue(ring + prev * kDcStage, n0);
       const uint32_t st = lds_addr(ring + slot * kDcStage);
@@ -423,8 +420,8 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
         const int row = min(e_c0 + tok, n_rows - 1);
         const uint32_t ta = tok_base + row * TS + c_kb * kGroup;
         lds_read_stage(st + swz128(tok, c0), st + swz128(tok, c0 + 1), ta, ta + 16,
-                       sa_base + (row * KB + c_kb) * 4, sw_base + (c_ent * KB + c_kb) * 4, wf.u[0],
-                       wf.u[1], af.u[0], af.u[1], sa, sw);
+                       sa_base + (row * KB + c_kb) * 4, st + kDcStageW, wf.u[0], wf.u[1], af.u[0],
+                       af.u[1], sa, sw);
         acc[0] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc[0]);
       }
 #pragma unroll
@@ -516,7 +513,7 @@ __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombine
       o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
       *reinterpret_cast<uint4*>(p.y + static_cast<int64_t>(s_row[c]) * N + n0 + 8 * h) = o;
     }
-    lds_barrier();  // slots and weight scales free for the next column block
+    lds_barrier();  // slots free for the next column block
   }
 }
 
