@@ -18,8 +18,10 @@ time the span of the layer's kernels, vLLM PR #59128, SM100 on B200). HIP
 events around each replay, which add the host-side graph launch latency,
 are reported beside it (`latency_us.events_median`). `ms_per_step` is the
 wall clock of the bracketed timed loop divided by the steps (it includes the
-flush). `roofline` describes the dominant kernel (the FC1 weight-streaming
-GEMM), timed on its own with HIP events on the stream it runs on.
+flush). `roofline` describes the dominant kernel, timed on its own with HIP
+events on the stream it runs on: on the decode path the layer is one kernel
+(routing, quantization, FC1, SiLU, a grid barrier, FC2 and the combine), so
+it is that kernel; elsewhere it is the FC1 grouped GEMM.
 `cpu_baseline` is the CPU oracle on the same workload.
 """
 
@@ -43,9 +45,9 @@ CAL_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
 
 
 def traffic_file(workload_key):
-    """profiles/ file of the FC1 traffic summary of a workload, e.g.
-    fc1_gemm_decode_t4_fp32_traffic.json for decode:T4:fp32."""
-    return "fc1_gemm_" + workload_key.replace(":", "_").lower() + "_traffic.json"
+    """profiles/ file of the dominant kernel's traffic summary of a workload,
+    e.g. roofline_kernel_decode_t4_fp32_traffic.json for decode:T4:fp32."""
+    return "roofline_kernel_" + workload_key.replace(":", "_").lower() + "_traffic.json"
 
 
 def parse():
@@ -111,10 +113,23 @@ def fc1_decode_bytes(cfg, n_live_experts, pairs, t_live):
             + pairs * 2 * I * 2 + pairs * I * 4)
 
 
+def decode_layer_bytes(cfg, n_live_experts, pairs, t_live):
+    """Algorithmic bytes of the one-launch decode layer: the FC1 launch's
+    bytes (fc1_decode_bytes), the live experts' FC2 codes + scales, the fp32
+    SiLU(gate)*up rows read back, the FC2 input codes + fp32 scales and the
+    BF16 FC2 rows written to the workspace, the routing weights read and the
+    BF16 output rows written."""
+    H, I = cfg.hidden, cfg.inter
+    per_expert = H * I + (H // 128) * (I // 128) * 4
+    return (fc1_decode_bytes(cfg, n_live_experts, pairs, t_live) + n_live_experts * per_expert
+            + pairs * I * 4 + pairs * (I + (I // 128) * 4) + pairs * H * 2 + pairs * 4
+            + t_live * H * 2)
+
+
 def kernel_source_hash():
-    """Hash of the FC1 kernels' sources (the traffic summaries are keyed by it)."""
+    """Hash of the dominant kernels' sources (the traffic summaries are keyed by it)."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "fc1_decode.hip"):
+    for name in ("gemm.hip", "fc1_decode.hip", "gemm_device.h"):
         with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -159,14 +174,18 @@ def traffic_from(args, fetch_dir, write_dir):
     if args.tokens is not None:
         t_cap = t_live = args.tokens
     want = f"<{'true' if fmt == 'ue8m0' else 'false'}, true"
-    want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }>"
+    want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true>"
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _counter_rows(d, counter)
         fc1 = [v for n, v in per.values() if want_dec in n]
-        if not fc1:
-            fc1 = [v for n, v in per.values()
-                   if ("gemm_stream_kernel" in n or "gemm_tiled_kernel" in n) and want in n]
+        if not fc1:  # the FC1 GEMM: of its kernels, the one that moves the most bytes
+            groups = {}
+            for n, v in per.values():
+                if ("gemm_stream_kernel" in n or "gemm_tiled_kernel" in n) and want in n:
+                    groups.setdefault(n, []).append(v)
+            if groups:
+                fc1 = max(groups.values(), key=sum)
         # the calibration copies are the run's last three copy dispatches
         copies = [per[k][1] for k in sorted(per) if "copyBuffer" in per[k][0]][-3:]
         if not fc1 or not copies:
@@ -336,18 +355,10 @@ def main():
     xs_raw = ws[lay["xs"]:lay["xs"] + (H // 128) * t_cap * sb]
     xs = (xs_raw if fmt == "ue8m0" else xs_raw.view(torch.float32)).view(H // 128, t_cap)
     c1 = torch.empty((R, 2 * I), dtype=torch.int16, device=dev)
-    # FC1 alone, back to back over rotating copies of W1: the copies' live
-    # experts together exceed L2 + the 256 MB Infinity Cache, so every launch
-    # streams its weights from HBM, while back-to-back launches keep the
-    # dispatch overhead out of the average (as a kernel trace measures it).
-    live_w1 = max(n_live_e, 1) * (2 * I * H + (2 * I // 128) * (H // 128) * 4)
-    n_copies = int(min(8, max(2, -(-3 * MALL_BYTES // live_w1) + 1)))
-    w1_copies = [(d_w[0], d_w[1])] + [(d_w[0].clone(), d_w[1].clone()) for _ in range(n_copies - 1)]
-    max_rows = min(pairs, R)
-
-    # On the decode path the layer's FC1 is the fused kernel (routing, activation
-    # quantization, FC1, SiLU); it is timed through its own entry point on a
-    # workspace of its own. Elsewhere FC1 is the grouped GEMM.
+    # On the decode path the whole layer is one kernel (the decode FC1's
+    # limits hold, so moe_forward launches the one-launch layer); it is timed
+    # through moe_forward on a workspace of its own. Elsewhere the dominant
+    # kernel is the FC1 grouped GEMM.
     ws_f = torch.empty_like(ws)
     try:
         moe.moe_fc1_decode(dx, dids, d_w[0], d_w[1], I, fmt, act, lim, cfg.align_rows, 0,
@@ -355,14 +366,30 @@ def main():
         fused = True
     except moe.MoeError:
         fused = False
+    out_f = torch.empty_like(out)
+
+    # The kernel alone, back to back over rotating copies of its weights: the
+    # copies' live experts together exceed L2 + the 256 MB Infinity Cache, so
+    # every launch streams its weights from HBM, while back-to-back launches
+    # keep the dispatch overhead out of the average (as a kernel trace
+    # measures it).
+    per_e = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+    if fused:
+        per_e += H * I + (H // 128) * (I // 128) * 4
+    live_w = max(n_live_e, 1) * per_e
+    n_copies = int(min(8, max(2, -(-3 * MALL_BYTES // live_w) + 1)))
+    idx = (0, 1, 2, 3) if fused else (0, 1)
+    w_copies = [tuple(d_w[j] for j in idx)] + \
+        [tuple(d_w[j].clone() for j in idx) for _ in range(n_copies - 1)]
+    max_rows = min(pairs, R)
 
     def fc1(i):
-        wq, ws_ = w1_copies[i % n_copies]
+        wc = w_copies[i % n_copies]
         if fused:
-            moe.moe_fc1_decode(dx, dids, wq, ws_, I, fmt, act, lim, cfg.align_rows, 0,
-                               t_live=dlive, workspace=ws_f)
+            moe.moe_forward(dx, dids, dw, *wc, fmt, act, lim, cfg.align_rows, 0, t_live=dlive,
+                            out=out_f, workspace=ws_f)
         else:
-            moe.moe_grouped_gemm_fp8(xq, xs, fmt, wq, ws_, counts, offsets, R, a_row_map=r2p,
+            moe.moe_grouped_gemm_fp8(xq, xs, fmt, wc[0], wc[1], counts, offsets, R, a_row_map=r2p,
                                      a_row_div=K, max_rows_per_expert=max_rows, out=c1)
     for i in range(n_copies):
         fc1(i)
@@ -374,17 +401,18 @@ def main():
     b.record(stream)
     torch.cuda.synchronize()
     k_avg = a.elapsed_time(b) * 1e3 / args.kernel_reps
-    del w1_copies
-    fc1_b = fc1_decode_bytes(cfg, n_live_e, pairs, t_live) if fused else fc1_bytes(cfg, n_live_e, pairs)
-    fc1_flops = 2 * pairs * 2 * I * H
+    del w_copies
+    fc1_b = decode_layer_bytes(cfg, n_live_e, pairs, t_live) if fused else fc1_bytes(cfg, n_live_e, pairs)
+    fc1_flops = 6 * pairs * H * I if fused else 2 * pairs * 2 * I * H
     workload_key = f"{args.config}:T{t_live}:{fmt}"
     traffic = load_traffic(workload_key)
     tiled = pairs > 0 and pairs / max(n_live_e, 1) > moe.GEMM_TILES["stream_max_rows"]
     kname = ("gemm_tiled_kernel" if tiled else "gemm_stream_kernel") + \
         f"<{'true' if fmt == 'ue8m0' else 'false'}, true> (FC1)"
     if fused:
-        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }> "
-                 "(routing, activation quantization, FC1, SiLU)")
+        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true> "
+                 "(the whole decode layer: routing, activation quantization, FC1, SiLU, "
+                 "grid barrier, FC2, top-k combine)")
     if tiled:
         roof = {"kernel": kname, "bound": "mfma",
                 "achieved": round(fc1_flops / (k_avg * 1e-6) / 1e12, 2), "peak": FP8_PEAK_TFLOPS,

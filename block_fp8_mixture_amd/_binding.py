@@ -69,6 +69,7 @@ _SIGNATURES = {
                                    ctypes.c_size_t, _vp]),
     "moe_fc1_decode": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
                                       ctypes.c_size_t, _vp]),
+    "moe_barrier_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
 }
 
 
@@ -352,3 +353,12 @@ def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
                             workspace.numel(), _stream())
     _check("moe_fc1_decode", st)
     return workspace
+
+
+def moe_barrier_timeouts():
+    """Waits at the one-launch decode layer's grid barrier that gave up on the
+    current device (sticky count; nonzero means some launch's outputs are unreliable)."""
+    lib = load_library()
+    n = ctypes.c_uint32(0)
+    _check("moe_barrier_timeouts", lib.moe_barrier_timeouts(ctypes.byref(n)))
+    return int(n.value)

@@ -221,8 +221,8 @@ size_t moe_workspace_bytes(const moe_problem* p) {
 namespace {
 
 // FC2 and the top-k combine of the decode path, reading the workspace.
-hipError_t launch_down_combine_step(const moe_problem* p, const moe_tensors* t,
-                                    const moe_workspace_layout& L, char* ws, hipStream_t s) {
+moe::DownCombineArgs down_combine_args(const moe_problem* p, const moe_tensors* t,
+                                      const moe_workspace_layout& L, char* ws) {
   moe::DownCombineArgs d;
   d.act = reinterpret_cast<const float*>(ws + L.act);
   d.fmt = p->scale_fmt;
@@ -244,12 +244,12 @@ hipError_t launch_down_combine_step(const moe_problem* p, const moe_tensors* t,
   d.hs = ws + L.hs;
   d.y = reinterpret_cast<uint16_t*>(ws + L.y);
   d.out = t->out;
-  return moe::launch_down_combine(d, s);
+  return d;
 }
 
 // Routing, activation quantization and FC1 of the decode path, writing the workspace.
-hipError_t launch_fc1_decode_step(const moe_problem* p, const moe_tensors* t,
-                                  const moe_workspace_layout& L, char* ws, hipStream_t s) {
+moe::DecodeFc1Args fc1_decode_args(const moe_problem* p, const moe_tensors* t,
+                                   const moe_workspace_layout& L, char* ws) {
   moe::DecodeFc1Args f;
   f.ids = t->topk_ids;
   f.t_live_dev = t->t_live_dev;
@@ -274,7 +274,7 @@ hipError_t launch_fc1_decode_step(const moe_problem* p, const moe_tensors* t,
   f.xs = ws + L.xs;
   f.c1 = reinterpret_cast<uint16_t*>(ws + L.c1);
   f.act_out = reinterpret_cast<float*>(ws + L.act);
-  return moe::launch_fc1_decode(f, s);
+  return f;
 }
 
 }  // namespace
@@ -289,7 +289,13 @@ moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* work
   if (!t || !workspace) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
   if (!t->x || !t->topk_ids || !t->w1 || !t->w1_scales) return MOE_ERR_INVALID_ARG;
-  return from_hip(launch_fc1_decode_step(p, t, L, static_cast<char*>(workspace), as_stream(stream)));
+  return from_hip(moe::launch_fc1_decode(fc1_decode_args(p, t, L, static_cast<char*>(workspace)),
+                                         as_stream(stream)));
+}
+
+moe_status moe_barrier_timeouts(uint32_t* count) {
+  if (!count) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::decode_layer_timeouts(count));
 }
 
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
@@ -323,10 +329,19 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   const int pairs = static_cast<int>(pairs64);
 
   hipError_t e = hipSuccess;
+  if (decode && moe::decode_layer_fits(p->t_cap, p->topk, p->hidden, p->inter) &&
+      moe::decode_layer_grid() > 0) {
+    // The whole layer in one launch.
+    moe::DecodeLayerArgs a;
+    a.f1 = fc1_decode_args(p, t, L, ws);
+    a.f2 = down_combine_args(p, t, L, ws);
+    return from_hip(moe::launch_decode_layer(a, s));
+  }
   if (decode && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {
-    // Routing, activation quantization and FC1 with SiLU(gate) * up in one launch.
-    e = launch_fc1_decode_step(p, t, L, ws, s);
-    if (e == hipSuccess) e = launch_down_combine_step(p, t, L, ws, s);
+    // Routing, activation quantization and FC1 with SiLU(gate) * up in one
+    // launch, then FC2 with the combine.
+    e = moe::launch_fc1_decode(fc1_decode_args(p, t, L, ws), s);
+    if (e == hipSuccess) e = moe::launch_down_combine(down_combine_args(p, t, L, ws), s);
     return from_hip(e);
   }
   // Alignment and activation quantization share one launch (independent work).
@@ -363,7 +378,7 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
     g.act_out = nullptr;
   }
   if (decode) {  // FC2 and the top-k combine in one launch
-    if (e == hipSuccess) e = launch_down_combine_step(p, t, L, ws, s);
+    if (e == hipSuccess) e = moe::launch_down_combine(down_combine_args(p, t, L, ws), s);
     return from_hip(e);
   }
   if (e == hipSuccess)

@@ -39,67 +39,6 @@ constexpr int kDcStage = kDcStageW + 256; // + the stage's weight block scale (6
 constexpr int kDcLoads = 3;               // loads per wave and stage
 constexpr int kDcTiles = kDcMaxPairs / kStreamTileM;  // token tiles of one expert, at most
 
-// Two 16-byte LDS reads with their own wait, as assembly: the compiler then
-// neither sees reads that might alias the direct-to-LDS loads in flight
-// (which would make it wait for all of them) nor uses a result early.
-__device__ __forceinline__ void lds_read2(uint32_t a0, uint32_t a1, uint4& r0, uint4& r1) {
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1)
-      : "v"(a0), "v"(a1));
-}
-
-// A stage's reads for the first token tile: weight and token fragments and
-// the two scales, all in flight together under one wait.
-__device__ __forceinline__ void lds_read_stage(uint32_t w0, uint32_t w1, uint32_t t0, uint32_t t1,
-                                               uint32_t sa, uint32_t sw, uint4& rw0, uint4& rw1,
-                                               uint4& rt0, uint4& rt1, float& fsa, float& fsw) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %7\n\t"
-      "ds_read_b128 %2, %8\n\t"
-      "ds_read_b128 %3, %9\n\t"
-      "ds_read_b32 %4, %10\n\t"
-      "ds_read_b32 %5, %11\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(rw0), "=&v"(rw1), "=&v"(rt0), "=&v"(rt1), "=&v"(fsa), "=&v"(fsw)
-      : "v"(w0), "v"(w1), "v"(t0), "v"(t1), "v"(sa), "v"(sw));
-}
-
-// Token fragments and scale of a further token tile.
-__device__ __forceinline__ void lds_read_tile(uint32_t t0, uint32_t t1, uint32_t sa, uint4& rt0,
-                                              uint4& rt1, float& fsa) {
-  asm volatile(
-      "ds_read_b128 %0, %3\n\t"
-      "ds_read_b128 %1, %4\n\t"
-      "ds_read_b32 %2, %5\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(rt0), "=&v"(rt1), "=&v"(fsa)
-      : "v"(t0), "v"(t1), "v"(sa));
-}
-
-// Global loads the compiler does not track. Its wait insertion does not
-// count direct-to-LDS loads as later vector-memory operations, so a register
-// load issued before them would be waited for with vmcnt(0), draining the
-// weight stream; these are waited for explicitly (prefetch_wait) instead.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4 gload_b128(const void* a) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(a));
-  return r;
-}
-__device__ __forceinline__ uint32_t gload_b32(const void* a) {
-  uint32_t r;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(a));
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
 template <int FMT>
 __global__ __launch_bounds__(kDcThreads, 1) void down_combine_kernel(DownCombineArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kDcWaves * kDcDepth * kDcStage];

@@ -31,6 +31,8 @@
 #include "kernels.h"
 #include "quant_device.h"
 
+#include <atomic>
+
 namespace moe {
 namespace {
 
@@ -41,31 +43,37 @@ constexpr int kF1StageW = 16 * kGroup;       // 8 gate + 8 up rows x 128 bytes
 constexpr int kF1Stage = kF1StageW + 256;    // + the two weight scales (64 x 4-byte slots)
 constexpr int kF1Loads = 3;                  // loads per wave and stage
 constexpr int kF1XLoads = kF1TokBytes / 8 / kF1Threads;  // 16-byte (8-value) activation loads per thread
+constexpr int kF1Tiles2 = kDcMaxPairs / kStreamTileM;    // FC2 token tiles of one expert, at most
 
-__device__ __forceinline__ uint32_t lds_addr(const void* q) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(q));
+// Grid barrier of the one-launch layer: per workgroup the epoch (launch
+// count) it has reached, the epoch workgroup 0 has released, and a sticky
+// count of waits that gave up (a workgroup that was not resident).
+__device__ unsigned g_dl_flag[kDlMaxGrid];
+__device__ unsigned g_dl_release;
+__device__ unsigned g_dl_timeouts;
+constexpr int kDlSpinLimit = 1 << 21;  // polls (about a microsecond each) before a wait gives up
+constexpr int kDlPreStages = 2;        // FC2 stages a wave issues before the grid barrier
+
+__device__ __forceinline__ unsigned flag_load(const unsigned* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(unsigned* a, unsigned v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void flag_wait(const unsigned* a, unsigned v) {
+  for (int it = 0; flag_load(a) != v; ++it) {
+    if (it == kDlSpinLimit) {
+      atomicAdd(&g_dl_timeouts, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
 }
 
-// A stage's reads: weight fragments, token fragments and both scales, in
-// flight together under one wait (assembly: the compiler neither sees reads
-// that might alias the direct-to-LDS loads in flight nor uses a result early).
-__device__ __forceinline__ void f1_read_stage(uint32_t w0, uint32_t w1, uint32_t t0, uint32_t t1,
-                                              uint32_t sa, uint32_t sw, uint4& rw0, uint4& rw1,
-                                              uint4& rt0, uint4& rt1, float& fsa, float& fsw) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %7\n\t"
-      "ds_read_b128 %2, %8\n\t"
-      "ds_read_b128 %3, %9\n\t"
-      "ds_read_b32 %4, %10\n\t"
-      "ds_read_b32 %5, %11\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(rw0), "=&v"(rw1), "=&v"(rt0), "=&v"(rt1), "=&v"(fsa), "=&v"(fsw)
-      : "v"(w0), "v"(w1), "v"(t0), "v"(t1), "v"(sa), "v"(sw));
-}
-
-template <int FMT>
-__global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args p) {
+template <int FMT, bool FUSED>
+__global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerArgs a) {
+  const DecodeFc1Args& p = a.f1;
+  const DownCombineArgs& q = a.f2;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kF1Waves * kF1Depth * kF1Stage];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kF1TokBytes];  // codes, row stride H + 16
   __shared__ float s_xs[kF1MaxScales];    // token scale of (token, K block) at t * KB + kb
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   // of waves the number of shares that have arrived (counts up for good).
   __shared__ __attribute__((aligned(16))) uint8_t s_part[2 * kF1Waves * 64 * 16];
   __shared__ int s_arrive[kF1Waves];
+  __shared__ float s_tw[kDcMaxPairs];     // pair -> routing weight (one-launch layer)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,6 +103,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
 
   // ---- 1. everything the prologue reads, issued together
   const int my_id = tid < PQ ? p.ids[tid] : -1;
+  const float my_tw = FUSED && tid < PQ ? q.topk_w[tid] : 0.0f;
+  // This launch's epoch at the grid barrier.
+  const unsigned epoch = FUSED ? flag_load(&g_dl_flag[blockIdx.x]) + 1u : 0u;
   const int t_live = p.t_live_dev ? min(max(scalar_load(p.t_live_dev), 0), p.t_cap) : p.t_cap;
   const int n_chunks = p.t_cap * H / 8;  // 16-byte chunks of x
   uint4 xr[kF1XLoads];
@@ -111,6 +123,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   // compact offset are popcounts; the aligned-row and tile prefixes over the
   // entries are one wave scan.
   if (tid < kF1Waves) s_arrive[tid] = 0;
+  if (FUSED && tid < PQ) s_tw[tid] = my_tw;
   if (wave == 0) {
     const int n_pairs = t_live * TK;
     const bool live = lane < n_pairs && lane < PQ;
@@ -206,21 +219,27 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
     if (tid < min(t_live * TK, PQ)) p.pair_to_row[tid] = s_prow[tid];
   }
 
-  // ---- per-wave task stream. With few tasks (1 token: one per 16 weight
-  // rows of each live expert) S waves of a workgroup share each task, each
-  // over its own 1/S of K; S is the largest power of two up to 8 that still
-  // leaves at most one task per group of S waves and divides the K blocks.
+  // ---- per-wave task stream. A workgroup takes a contiguous block of the
+  // tasks (neighbouring row blocks of an expert stay on one CU, which streams
+  // faster than spreading them), the blocks split as evenly as the grid
+  // allows. With few tasks (1 token: one per 16 weight rows of each live
+  // expert) S waves of a workgroup share each task, each over its own 1/S of
+  // K; S is the largest power of two up to 8 that still leaves at most one
+  // task per group of S waves and divides the K blocks.
   const int n_rb = I / 8;  // 16-row blocks (8 gate + 8 up rows)
   const int n_tasks = s_tp[n_live] * n_rb;
-  const int NW = gridDim.x * kF1Waves;
+  const int G1 = gridDim.x;
+  const int t_lo = static_cast<int>(static_cast<int64_t>(blockIdx.x) * n_tasks / G1);
+  const int t_hi = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * n_tasks / G1);
+  const int wg_max = (n_tasks + G1 - 1) / G1;  // tasks of the fullest workgroup
   int S = 1;
-  while (S < kF1Waves && n_tasks * (2 * S) <= NW && KB % (2 * S) == 0) S *= 2;
+  while (S < kF1Waves && wg_max * (2 * S) <= kF1Waves && KB % (2 * S) == 0) S *= 2;
   S = __builtin_amdgcn_readfirstlane(S);
-  const int NG = NW / S;                                   // groups of S waves
-  const int gidx = blockIdx.x * (kF1Waves / S) + wave / S;  // this wave's group
-  const int kbs = KB / S;                                  // K blocks of a share
+  const int NG = kF1Waves / S;  // groups of S waves in a workgroup
+  const int gl = wave / S;      // this wave's group
+  const int kbs = KB / S;       // K blocks of a share
   const int kb_lo = (wave % S) * kbs, kb_hi = kb_lo + kbs;
-  const int my_tasks = gidx < n_tasks ? (n_tasks - 1 - gidx) / NG + 1 : 0;
+  const int my_tasks = gl < t_hi - t_lo ? (t_hi - t_lo - 1 - gl) / NG + 1 : 0;
   const int total = my_tasks * kbs;  // stages of this wave
   uint8_t* ring = s_ring + wave * (kF1Depth * kF1Stage);
   const int grow = lane >> 3;
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   // Issue side: stage pointers of the current task. Stand-ins (valid
   // addresses) serve the stages past a wave's last one that the stream start
   // issues so that it always issues the same number of loads.
-  int i_task = gidx, i_kb = kb_lo;
+  int i_task = t_lo + gl, i_kb = kb_lo;
   const uint8_t* i_w0 = p.w + lane * 16;
   const uint8_t* i_w1 = p.w + lane * 16;
   const uint8_t* i_s = reinterpret_cast<const uint8_t*>(p.w_scales);
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
     if (++i_kb == kb_hi) {
       i_kb = kb_lo;
       i_task += NG;
-      if (i_task < n_tasks) i_set();
+      if (i_task < t_hi) i_set();
     }
   };
   if (total > 0) i_set();
@@ -309,7 +328,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
   const int c0f = 2 * (lane >> 4);  // fragment chunks c0f, c0f + 1 of a 128-byte K block
   const uint32_t x_base = lds_addr(s_x) + c0f * 16;
   const uint32_t xs_base = lds_addr(s_xs);
-  int c_task = gidx, c_kb = kb_lo, slot = 0, c_iter = 0;
+  int c_task = t_lo + gl, c_kb = kb_lo, slot = 0, c_iter = 0;
   Task ck{0, 0, 0};
   int c_rows = 0, c_crow0 = 0, c_t = 0;  // task's live rows in the tile, compact row base, lane's token
   auto c_set = [&]() {
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
     } wf, af;
     float sa, sw;
     const uint32_t ta = x_base + c_t * XS + c_kb * kGroup;
-    f1_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
+    lds_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
                   xs_base + (c_t * KB + c_kb) * 4, st + kF1StageW + ((lane >> 5) << 2), wf.u[0],
                   wf.u[1], af.u[0], af.u[1], sa, sw);
     acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
@@ -378,23 +397,298 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeFc1Args
         const int64_t row = s_crow[c_crow0 + tok];
         *reinterpret_cast<uint2*>(p.c1 + row * N + col) = packed;
         if (lane < 32) {
-          float4 a;
-          a.x = swiglu_any(p.act, bf16_to_f32(packed.x & 0xFFFFu), bf16_to_f32(other.x & 0xFFFFu), lim);
-          a.y = swiglu_any(p.act, bf16_to_f32(packed.x >> 16), bf16_to_f32(other.x >> 16), lim);
-          a.z = swiglu_any(p.act, bf16_to_f32(packed.y & 0xFFFFu), bf16_to_f32(other.y & 0xFFFFu), lim);
-          a.w = swiglu_any(p.act, bf16_to_f32(packed.y >> 16), bf16_to_f32(other.y >> 16), lim);
-          *reinterpret_cast<float4*>(p.act_out + row * I + col) = a;
+          float4 av;
+          av.x = swiglu_any(p.act, bf16_to_f32(packed.x & 0xFFFFu), bf16_to_f32(other.x & 0xFFFFu), lim);
+          av.y = swiglu_any(p.act, bf16_to_f32(packed.x >> 16), bf16_to_f32(other.x >> 16), lim);
+          av.z = swiglu_any(p.act, bf16_to_f32(packed.y & 0xFFFFu), bf16_to_f32(other.y & 0xFFFFu), lim);
+          av.w = swiglu_any(p.act, bf16_to_f32(packed.y >> 16), bf16_to_f32(other.y >> 16), lim);
+          if constexpr (FUSED)  // read by other workgroups after the grid barrier
+            gstore_b128_wt(p.act_out + row * I + col, u32x4{__float_as_uint(av.x), __float_as_uint(av.y),
+                                                            __float_as_uint(av.z), __float_as_uint(av.w)});
+          else
+            *reinterpret_cast<float4*>(p.act_out + row * I + col) = av;
         }
       }
       acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       c_kb = kb_lo;
       c_task += NG;
       ++c_iter;
-      if (c_task < n_tasks) c_set();
+      if (c_task < t_hi) c_set();
     }
     slot = slot == kF1Depth - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
+  if constexpr (FUSED) {
+    // ---- 4. FC2 and the top-k combine in the same launch. A workgroup owns
+    // 16 output columns of every live expert (column blocks blockIdx.x + G j),
+    // as launch_down_combine; the list of live experts is the routing above.
+    const int G = gridDim.x;
+    const int KB2 = I / kGroup, TS = I + 16;
+    const int n_cb = H / 16;
+    const int n_rows = n_live > 0 ? __builtin_amdgcn_readfirstlane(s_c0[n_live - 1] + s_cnt[n_live - 1]) : 0;
+    uint8_t* const s_tok = s_x;                             // FC2 input codes, row stride I + 16
+    float* const s_sa = s_xs;                               // their scales at c * KB2 + kb
+    float* const s_slot = reinterpret_cast<float*>(s_part);  // pair q's 16 columns
+    const int my_n = wave < n_live ? (n_live - 1 - wave) / kF1Waves + 1 : 0;
+    const int total2 = my_n * KB2;  // FC2 stages of this wave per column block
+    int j_ent = wave, j_kb = 0;
+    const uint8_t* j_w0 = q.w + lane * 16;
+    const uint8_t* j_w1 = q.w + lane * 16;
+    const uint8_t* j_s = reinterpret_cast<const uint8_t*>(q.w_scales);
+    auto j_set = [&](int n0) {
+      const int e = __builtin_amdgcn_readfirstlane(s_e[j_ent]);
+      const uint8_t* wb = q.w + (static_cast<int64_t>(e) * H + n0) * I;
+      j_w0 = wb + static_cast<int64_t>(grow) * I + chunk_lo;
+      j_w1 = wb + static_cast<int64_t>(grow + 8) * I + chunk_hi;
+      j_s = reinterpret_cast<const uint8_t*>(q.w_scales + (static_cast<int64_t>(e) * (H / kGroup) + n0 / kGroup) * KB2);
+    };
+    auto j_issue = [&](uint8_t* st) {
+      __builtin_amdgcn_global_load_lds(j_w0 + j_kb * kGroup, (lds_void*)(st), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(j_w1 + j_kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(j_s + j_kb * 4, (lds_void*)(st + kF1StageW), 4, 0, 0);
+    };
+    auto j_advance = [&](int n0) {
+      if (++j_kb == KB2) {
+        j_kb = 0;
+        j_ent += kF1Waves;
+        if (j_ent < n_live) j_set(n0);
+      }
+    };
+    // Stages d0..d1-1 of the stream start, which always issues kF1Depth - 1
+    // stages (past the wave's last one, stand-ins).
+    auto j_start = [&](int n0, int d0, int d1) {
+      if (d0 == 0) {
+        j_ent = wave;
+        j_kb = 0;
+        if (total2 > 0) j_set(n0);
+      }
+      for (int d = d0; d < d1; ++d) {
+        j_issue(ring + d * kF1Stage);
+        if (d + 1 < total2) j_advance(n0);
+      }
+    };
+    int cb = blockIdx.x;
+    const bool has_cb = cb < n_cb;  // uniform
+    // The first FC2 stages go out before the barrier: the ring of a wave is
+    // free once its FC1 stream is done, and the weights do not depend on FC1.
+    // Only a few: the act rows loaded after the barrier complete behind them.
+    if (has_cb) j_start(cb * 16, 0, kDlPreStages);
+
+    // ---- grid barrier. Every wave has waited for its act stores (write-
+    // through) above; after the workgroup barrier workgroup 0's thread 0 (for
+    // the others, their thread 0) publishes the epoch, workgroup 0 waits for
+    // every workgroup's epoch and releases it. Waits are bounded: one that
+    // gives up is counted and the launch goes on.
+    lds_barrier();
+    if (tid == 0) flag_store(&g_dl_flag[blockIdx.x], epoch);
+    if (blockIdx.x == 0) {
+      for (int j = tid; j < G; j += kF1Threads) flag_wait(&g_dl_flag[j], epoch);
+      lds_barrier();
+      if (tid == 0) flag_store(&g_dl_release, epoch);
+    } else if (tid == 0) {
+      flag_wait(&g_dl_release, epoch);
+    }
+    for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;  // the K-split partials are done
+    lds_barrier();
+
+    // ---- 5. FC2 input rows of this wave's experts (every kF1Waves-th live
+    // entry), read at device scope: 16 lanes per row, 4 rows per pass; lanes
+    // l16 and chunks u cover columns 4 (16 u + l16) of a 512-column chunk.
+    const int l16 = lane & 15, lg = lane >> 4;
+    const bool writer = blockIdx.x == 0;
+    int my_rows = 0;
+    for (int i = wave; i < n_live; i += kF1Waves) my_rows += s_cnt[i];
+    my_rows = __builtin_amdgcn_readfirstlane(my_rows);
+    auto wave_row = [&](int k) {  // compact row of this wave's k-th row
+      for (int i = wave; i < n_live; i += kF1Waves) {
+        const int cnt = s_cnt[i];
+        if (k < cnt) return s_c0[i] + k;
+        k -= cnt;
+      }
+      return 0;
+    };
+    if (has_cb) {
+      for (int k0 = 0; k0 < my_rows; k0 += 4) {
+        const bool row_ok = k0 + lg < my_rows;
+        const int c = wave_row(row_ok ? k0 + lg : 0);
+        const int r = s_crow[c];
+        for (int col0 = 0; col0 < I; col0 += 512) {
+          u32x4 vr[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)  // columns past I (unused) load a valid stand-in
+            vr[u] = gload_b128_dev(p.act_out + static_cast<int64_t>(r) * I + min(col0 + 4 * (16 * u + l16), I - 4));
+          asm volatile("s_waitcnt vmcnt(0)"
+                       : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
+                         "+v"(vr[6]), "+v"(vr[7]));
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int colg = col0 + g * kGroup;
+            if (colg >= I) break;  // uniform
+            const u32x4 ra = vr[2 * g], rb = vr[2 * g + 1];
+            const float a0 = __uint_as_float(ra[0]), a1 = __uint_as_float(ra[1]), a2 = __uint_as_float(ra[2]),
+                        a3 = __uint_as_float(ra[3]), b0 = __uint_as_float(rb[0]), b1 = __uint_as_float(rb[1]),
+                        b2 = __uint_as_float(rb[2]), b3 = __uint_as_float(rb[3]);
+            float amax = fmaxf(fmaxf(fabsf(a0), fabsf(a1)), fmaxf(fabsf(a2), fabsf(a3)));
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b0), fabsf(b1)), fmaxf(fabsf(b2), fabsf(b3))));
+            amax = group_max<16>(amax);
+            const float sc = group_scale(amax, FMT);
+            const float inv = 1.0f / sc;  // IEEE division, once per group
+            const uint32_t qa = cvt_pk_e4m3(scale_div(a0, sc, inv, FMT), scale_div(a1, sc, inv, FMT)) |
+                                (cvt_pk_e4m3(scale_div(a2, sc, inv, FMT), scale_div(a3, sc, inv, FMT)) << 16);
+            const uint32_t qb = cvt_pk_e4m3(scale_div(b0, sc, inv, FMT), scale_div(b1, sc, inv, FMT)) |
+                                (cvt_pk_e4m3(scale_div(b2, sc, inv, FMT), scale_div(b3, sc, inv, FMT)) << 16);
+            const int ca = col0 + 4 * (32 * g + l16), cbb = ca + 64;
+            if (row_ok) {
+              *reinterpret_cast<uint32_t*>(s_tok + c * TS + ca) = qa;
+              *reinterpret_cast<uint32_t*>(s_tok + c * TS + cbb) = qb;
+              if (l16 == 0) s_sa[c * KB2 + colg / kGroup] = sc;
+              if (writer) {
+                *reinterpret_cast<uint32_t*>(q.hq + static_cast<int64_t>(r) * I + ca) = qa;
+                *reinterpret_cast<uint32_t*>(q.hq + static_cast<int64_t>(r) * I + cbb) = qb;
+                if (l16 == 0) store_scale(q.hs, FMT, static_cast<int64_t>(colg / kGroup) * q.row_cap + r, sc);
+              }
+            }
+          }
+        }
+      }
+    }
+    // The loop below reads these rows through assembly the compiler does not
+    // see; keep the stores above it.
+    asm volatile("" ::: "memory");
+    if (has_cb) j_start(cb * 16, kDlPreStages, kF1Depth - 1);
+
+    const uint32_t tok_base = lds_addr(s_tok) + c0f * 16;
+    const uint32_t sa_base = lds_addr(s_sa);
+    for (; cb < n_cb; cb += G) {
+      const int n0 = cb * 16;
+      if (cb != static_cast<int>(blockIdx.x)) {
+        for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;
+        lds_barrier();  // zeroed slots visible
+        j_start(n0, 0, kF1Depth - 1);
+      }
+      // ---- 6. stream: wait for stage s, refill the slot of stage s - 1, compute s.
+      int e_ent = wave, e_kb = 0, slot2 = 0;
+      int e_cnt = 0, e_c0 = 0;
+      if (e_ent < n_live) {
+        e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e_ent]);
+        e_c0 = __builtin_amdgcn_readfirstlane(s_c0[e_ent]);
+      }
+      v4f acc2[kF1Tiles2];
+#pragma unroll
+      for (int m = 0; m < kF1Tiles2; ++m) acc2[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int s = 0; s < total2; ++s) {
+        if (s + kF1Depth - 2 >= total2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kF1Loads * (kF1Depth - 2)));
+        const int prev = slot2 == 0 ? kF1Depth - 1 : slot2 - 1;
+        if (s + kF1Depth - 1 < total2) {
+          j_issue(ring + prev * kF1Stage);
+          j_advance(n0);
+        }
+        const uint32_t st = lds_addr(ring + slot2 * kF1Stage);
+        union {
+          uint4 u[2];
+          v8i v;
+        } wf, af;
+        const int n_mt = (e_cnt + kStreamTileM - 1) / kStreamTileM;
+        float sa, sw;
+        {
+          const int row = min(e_c0 + tok, n_rows - 1);
+          const uint32_t ta = tok_base + row * TS + e_kb * kGroup;
+          lds_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
+                         sa_base + (row * KB2 + e_kb) * 4, st + kF1StageW, wf.u[0], wf.u[1], af.u[0],
+                         af.u[1], sa, sw);
+          acc2[0] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc2[0]);
+        }
+#pragma unroll
+        for (int m = 1; m < kF1Tiles2; ++m) {
+          if (m < n_mt) {
+            const int row = min(e_c0 + m * kStreamTileM + tok, n_rows - 1);
+            const uint32_t ta = tok_base + row * TS + e_kb * kGroup;
+            lds_read_tile(ta, ta + 16, sa_base + (row * KB2 + e_kb) * 4, af.u[0], af.u[1], sa);
+            acc2[m] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc2[m]);
+          }
+        }
+        if (++e_kb == KB2) {  // expert done: BF16-rounded rows to their pairs' slots
+#pragma unroll
+          for (int m = 0; m < kF1Tiles2; ++m) {
+            const int j = m * kStreamTileM + tok;
+            if (m < n_mt && j < e_cnt) {
+              const int qp = s_cpair[e_c0 + j];
+              float4 o;
+              o.x = bf16_to_f32(f32_to_bf16(acc2[m][0]));
+              o.y = bf16_to_f32(f32_to_bf16(acc2[m][1]));
+              o.z = bf16_to_f32(f32_to_bf16(acc2[m][2]));
+              o.w = bf16_to_f32(f32_to_bf16(acc2[m][3]));
+              *reinterpret_cast<float4*>(s_slot + qp * 16 + 4 * (lane >> 4)) = o;
+            }
+            acc2[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+          e_kb = 0;
+          e_ent += kF1Waves;
+          if (e_ent < n_live) {
+            e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e_ent]);
+            e_c0 = __builtin_amdgcn_readfirstlane(s_c0[e_ent]);
+          }
+        }
+        slot2 = slot2 == kF1Depth - 1 ? 0 : slot2 + 1;
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
+      lds_barrier();  // every slot of this column block written
+
+      // ---- 7. top-k sum of the 16 columns (two threads per token) in the
+      // arithmetic and order of moe_topk_combine, then the FC2 output rows.
+      for (int x = tid; x < t_live * 2; x += kF1Threads) {
+        const int t = x >> 1, h = x & 1;
+        float o8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o8[i] = 0.0f;
+        for (int k0 = 0; k0 < TK; k0 += 8) {
+          bool ok[8];
+          float w[8];
+          float4 lo[8], hi[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int qp = t * TK + min(k0 + j, TK - 1);
+            ok[j] = k0 + j < TK && static_cast<unsigned>(s_prow[qp]) < static_cast<unsigned>(p.row_cap);
+            w[j] = s_tw[qp];
+            lo[j] = *reinterpret_cast<const float4*>(s_slot + qp * 16 + 8 * h);
+            hi[j] = *reinterpret_cast<const float4*>(s_slot + qp * 16 + 8 * h + 4);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (!ok[j]) continue;
+            o8[0] = fmaf(w[j], lo[j].x, o8[0]);
+            o8[1] = fmaf(w[j], lo[j].y, o8[1]);
+            o8[2] = fmaf(w[j], lo[j].z, o8[2]);
+            o8[3] = fmaf(w[j], lo[j].w, o8[3]);
+            o8[4] = fmaf(w[j], hi[j].x, o8[4]);
+            o8[5] = fmaf(w[j], hi[j].y, o8[5]);
+            o8[6] = fmaf(w[j], hi[j].z, o8[6]);
+            o8[7] = fmaf(w[j], hi[j].w, o8[7]);
+          }
+        }
+        uint4 o;
+        o.x = f32_to_bf16(o8[0]) | (f32_to_bf16(o8[1]) << 16);
+        o.y = f32_to_bf16(o8[2]) | (f32_to_bf16(o8[3]) << 16);
+        o.z = f32_to_bf16(o8[4]) | (f32_to_bf16(o8[5]) << 16);
+        o.w = f32_to_bf16(o8[6]) | (f32_to_bf16(o8[7]) << 16);
+        *reinterpret_cast<uint4*>(q.out + static_cast<int64_t>(t) * H + n0 + 8 * h) = o;
+      }
+      for (int x = tid; x < n_rows * 2; x += kF1Threads) {
+        const int c = x >> 1, h = x & 1;
+        const float* v = s_slot + s_cpair[c] * 16 + 8 * h;
+        uint4 o;
+        o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+        o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+        o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+        o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+        *reinterpret_cast<uint4*>(q.y + static_cast<int64_t>(s_crow[c]) * H + n0 + 8 * h) = o;
+      }
+      lds_barrier();  // slots free for the next column block
+    }
+  }
 }
 
 }  // namespace
@@ -404,14 +698,56 @@ hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream) {
   if (!fc1_decode_fits(a.t_cap, a.topk, a.hidden, a.inter) || a.num_experts > kMaxExperts ||
       a.num_experts < 1 || a.align_rows < 1)
     return hipErrorInvalidValue;
+  DecodeLayerArgs l{};
+  l.f1 = a;
   const dim3 grid(static_cast<unsigned>(device_cu_count()));
   if (a.fmt == kFp32)
-    hipLaunchKernelGGL(fc1_decode_kernel<kFp32>, grid, dim3(kF1Threads), 0, stream, a);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, false>), grid, dim3(kF1Threads), 0, stream, l);
   else if (a.fmt == kFp32Pow2)
-    hipLaunchKernelGGL(fc1_decode_kernel<kFp32Pow2>, grid, dim3(kF1Threads), 0, stream, a);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, false>), grid, dim3(kF1Threads), 0, stream, l);
   else
-    hipLaunchKernelGGL(fc1_decode_kernel<kUe8m0>, grid, dim3(kF1Threads), 0, stream, a);
+    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, false>), grid, dim3(kF1Threads), 0, stream, l);
   return hipGetLastError();
+}
+
+// The grid barrier needs every workgroup resident at once: one per CU, at
+// most kDlMaxGrid, and the same grid on every launch on a device (the
+// epochs count launches per workgroup).
+int decode_layer_grid() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v != 0) return v > 0 ? v : 0;
+  int cus = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true>, kF1Threads, 0) !=
+          hipSuccess ||
+      cus < 1 || cus > kDlMaxGrid || occ < 1)
+    v = -1;
+  else
+    v = cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v > 0 ? v : 0;
+}
+
+hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream) {
+  if (a.f1.t_cap == 0) return hipSuccess;
+  const int grid = decode_layer_grid();
+  if (!decode_layer_fits(a.f1.t_cap, a.f1.topk, a.f1.hidden, a.f1.inter) || grid < 1 ||
+      a.f1.num_experts > kMaxExperts || a.f1.num_experts < 1 || a.f1.align_rows < 1)
+    return hipErrorInvalidValue;
+  if (a.f1.fmt == kFp32)
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+  else if (a.f1.fmt == kFp32Pow2)
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t decode_layer_timeouts(uint32_t* out) {
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(g_dl_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
 }
 
 }  // namespace moe

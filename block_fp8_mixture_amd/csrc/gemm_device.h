@@ -70,4 +70,72 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// LDS byte address of a __shared__ object (for assembly operands).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// A stage's reads for the first token tile: weight and token fragments and
+// the two scales, all in flight together under one wait. Assembly: the
+// compiler then neither sees reads that might alias the direct-to-LDS loads
+// in flight (which would make it wait for all of them) nor uses a result
+// early.
+__device__ __forceinline__ void lds_read_stage(uint32_t w0, uint32_t w1, uint32_t t0, uint32_t t1,
+                                               uint32_t sa, uint32_t sw, uint4& rw0, uint4& rw1,
+                                               uint4& rt0, uint4& rt1, float& fsa, float& fsw) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b32 %4, %10\n\t"
+      "ds_read_b32 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(rw0), "=&v"(rw1), "=&v"(rt0), "=&v"(rt1), "=&v"(fsa), "=&v"(fsw)
+      : "v"(w0), "v"(w1), "v"(t0), "v"(t1), "v"(sa), "v"(sw));
+}
+
+// Token fragments and scale of a further token tile.
+__device__ __forceinline__ void lds_read_tile(uint32_t t0, uint32_t t1, uint32_t sa, uint4& rt0,
+                                              uint4& rt1, float& fsa) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(rt0), "=&v"(rt1), "=&v"(fsa)
+      : "v"(t0), "v"(t1), "v"(sa));
+}
+
+// Global loads the compiler does not track. Its wait insertion does not
+// count direct-to-LDS loads as later vector-memory operations, so a register
+// load issued before them would be waited for with vmcnt(0), draining the
+// weight stream; these are waited for by an explicit s_waitcnt in assembly
+// that names their registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 gload_b128(const void* a) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(a));
+  return r;
+}
+__device__ __forceinline__ uint32_t gload_b32(const void* a) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(a));
+  return r;
+}
+
+// Data handed from one workgroup to another inside a launch, across XCDs
+// whose L2 caches are not coherent with each other: the store writes
+// through to memory (system scope), the load reads at device scope (the
+// cache bits of relaxed atomics of those scopes). Untracked, like the loads
+// above.
+__device__ __forceinline__ void gstore_b128_wt(void* a, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x4 gload_b128_dev(const void* a) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(a));
+  return r;
+}
+
 }  // namespace moe

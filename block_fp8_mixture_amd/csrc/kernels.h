@@ -146,6 +146,30 @@ struct DecodeFc1Args {
 
 hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream);
 
+// The whole decode layer in one launch: the FC1 kernel above, a barrier
+// across the grid (one workgroup per CU, all resident), then FC2 and the
+// top-k combine as launch_down_combine computes them. f2's act is f1's
+// act_out; its counts, offsets and row maps are not read (the routing is
+// the launch's own). Launches on one device must not overlap in time: the
+// barrier's epochs live in device globals.
+constexpr int kDlMaxGrid = 1024;
+
+inline bool decode_layer_fits(int64_t t_cap, int64_t topk, int64_t hidden, int64_t inter) {
+  return fc1_decode_fits(t_cap, topk, hidden, inter) && hidden % 16 == 0;
+}
+
+struct DecodeLayerArgs {
+  DecodeFc1Args f1;
+  DownCombineArgs f2;
+};
+
+hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream);
+// Grid of launch_decode_layer on the current device (one workgroup per CU),
+// or 0 where its workgroups cannot all be resident.
+int decode_layer_grid();
+// Waits at the grid barrier that gave up (sticky, per device).
+hipError_t decode_layer_timeouts(uint32_t* out);
+
 int device_cu_count();
 
 }  // namespace moe

@@ -259,11 +259,20 @@ size_t moe_workspace_bytes(const moe_problem* p);
  * -> topk_combine, enqueued on one stream with no host synchronization
  * (vLLM PR #59128, SM100 on B200: the full-expert benchmark scope; the layer
  * replays inside a captured graph with the token count on the device).
- * On the decode path (see moe_workspace_layout.act) the layer takes three
- * launches: align + act_quant, FC1 with SiLU(gate)*up in its epilogue, and
- * FC2 with the top-k combine (TensorRT-LLM PR #21250, description: fewer
- * launches at decode sizes). The workspace then holds the same alignment,
- * codes and scales, bit for bit, and FC1/FC2 rows within the GEMM tolerance.
+ * On the decode path (see moe_workspace_layout.act) the launches are fewer
+ * (TensorRT-LLM PR #21250, description: at decode sizes each launch's fixed
+ * cost counts). When moe_fc1_decode's limits hold and H is a multiple of 16,
+ * the layer is ONE launch: one workgroup per CU runs routing, activation
+ * quantization and FC1 with SiLU(gate)*up, meets the others at a barrier
+ * across the grid, then runs FC2 with the top-k combine for its output
+ * columns. That launch needs all its workgroups resident at once, so calls
+ * on one device must not overlap in time (one stream, or ordered streams),
+ * and the GPU should not be shared with work that holds CUs for long (see
+ * moe_barrier_timeouts). Otherwise the decode path takes two or three
+ * launches: [align + act_quant, then FC1 with SiLU(gate)*up] or the fused
+ * FC1 of moe_fc1_decode, then FC2 with the top-k combine. The workspace then
+ * holds the same alignment, codes and scales, bit for bit, and FC1/FC2 rows
+ * within the GEMM tolerance.
  * `workspace` is device memory of at least moe_workspace_bytes(p) bytes, laid
  * out as moe_workspace_plan describes; its prior contents do not matter.
  * Errors: INVALID_ARG, CAPACITY (workspace or row_cap too small), HIP. */
@@ -285,6 +294,15 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
  * Errors: UNSUPPORTED (not such a problem), INVALID_ARG, CAPACITY, HIP. */
 moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Number of waits at the grid barrier of moe_forward's one-launch decode
+ * path that gave up on the current device since the library was loaded
+ * (sticky). A wait gives up after about two seconds without the other
+ * workgroups, which only happens when some of them could not become resident
+ * (CUs held by other work); that launch's outputs are then unreliable. Reads
+ * device memory synchronously.
+ * Errors: INVALID_ARG (count NULL), HIP. */
+moe_status moe_barrier_timeouts(uint32_t* count);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

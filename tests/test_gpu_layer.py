@@ -56,6 +56,7 @@ def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_
     moe.moe_forward(up(x), up(ids), up(w), d_w1q, d_w1s, d_w2q, d_w2s, fmt, act, lim32, A,
                     row_cap, t_live=up(np.array([t_live], np.int32)), out=out, workspace=ws)
     torch.cuda.synchronize()
+    assert moe.moe_barrier_timeouts() == 0, "a wait at the decode layer's grid barrier gave up"
     R = lay["row_cap"]
     sdt = np.uint8 if fmt == "ue8m0" else np.float32
 
@@ -212,14 +213,20 @@ def test_dropped_ids_and_empty_routing():
     assert np.all(down(out) == POISON_BF16)
 
 
-def test_graph_replay_with_changing_routing_and_live_count():
+REPLAYS = {
+    32: [(11, 32), (12, 7), (13, 1), (14, 0), (15, 20)],  # the general schedule
+    4: [(11, 4), (12, 3), (13, 1), (14, 0), (15, 2), (16, 4)],  # the one-launch decode layer
+}
+
+
+@pytest.mark.parametrize("t_cap", sorted(REPLAYS))
+def test_graph_replay_with_changing_routing_and_live_count(t_cap):
     """Capture the layer once; replay it with new routing, tokens and live
     counts written into the captured buffers (vLLM PR #59128, SM100 on B200:
     graph replay with changing routing, one live row, empty routing and a
     device token count)."""
     name = "decode"
     cfg = synth.get(name)
-    t_cap = 32
     (w1q, w1s), (w2q, w2s) = host_weights(name)
     d = device_weights(name)
     x0, ids0, w0 = synth.make_workload(cfg, t_cap, 10)
@@ -238,7 +245,7 @@ def test_graph_replay_with_changing_routing_and_live_count():
     with torch.cuda.graph(graph):
         moe.moe_forward(sx, sids, sw, *d, t_live=st, out=out, workspace=ws)
     torch.cuda.synchronize()
-    for variant, t_live in [(11, 32), (12, 7), (13, 1), (14, 0), (15, 20)]:
+    for variant, t_live in REPLAYS[t_cap]:
         say(f"  replay variant={variant} t_live={t_live}")
         x, ids, w = synth.make_workload(cfg, t_cap, variant)
         sx.copy_(up(x))
@@ -257,6 +264,7 @@ def test_graph_replay_with_changing_routing_and_live_count():
             assert_bf16_close(got[:t_live], ref, f"replay {variant}")
             eager = _forward(x, ids, w, name, t_live=t_live)
             assert np.array_equal(eager[:t_live], got[:t_live])
+    assert moe.moe_barrier_timeouts() == 0
 
 
 def test_padded_tiles_are_skipped():
