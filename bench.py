@@ -129,7 +129,7 @@ def decode_layer_bytes(cfg, n_live_experts, pairs, t_live):
 def kernel_source_hash():
     """Hash of the dominant kernels' sources (the traffic summaries are keyed by it)."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "fc1_decode.hip", "gemm_device.h"):
+    for name in ("gemm.hip", "fc1_decode.hip", "gemm_device.h", "fc2_decode.h"):
         with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -27,6 +27,7 @@
 //     gets both BF16 halves, and act the fp32 SiLU(gate) * up of the
 //     BF16-rounded pair (fp64 inside, rounded once).
 #include "device_common.h"
+#include "fc2_decode.h"
 #include "gemm_device.h"
 #include "kernels.h"
 #include "quant_device.h"
@@ -36,14 +37,15 @@
 namespace moe {
 namespace {
 
-constexpr int kF1Threads = 512;
-constexpr int kF1Waves = kF1Threads / 64;
-constexpr int kF1Depth = 6;                  // stages in a wave's ring
-constexpr int kF1StageW = 16 * kGroup;       // 8 gate + 8 up rows x 128 bytes
-constexpr int kF1Stage = kF1StageW + 256;    // + the two weight scales (64 x 4-byte slots)
-constexpr int kF1Loads = 3;                  // loads per wave and stage
+// The one-launch layer reuses each wave's ring for FC2, so both streams
+// share the ring geometry of fc2_decode.h.
+constexpr int kF1Threads = kDecThreads;
+constexpr int kF1Waves = kDecWaves;
+constexpr int kF1Depth = kDecDepth;          // stages in a wave's ring
+constexpr int kF1StageW = kDecStageW;        // 8 gate + 8 up rows x 128 bytes
+constexpr int kF1Stage = kDecStage;          // + the two weight scales (64 x 4-byte slots)
+constexpr int kF1Loads = kDecLoads;          // loads per wave and stage
 constexpr int kF1XLoads = kF1TokBytes / 8 / kF1Threads;  // 16-byte (8-value) activation loads per thread
-constexpr int kF1Tiles2 = kDcMaxPairs / kStreamTileM;    // FC2 token tiles of one expert, at most
 
 // Grid barrier of the one-launch layer: per workgroup the epoch (launch
 // count) it has reached, the epoch workgroup 0 has released, and a sticky
@@ -52,7 +54,6 @@ __device__ unsigned g_dl_flag[kDlMaxGrid];
 __device__ unsigned g_dl_release;
 __device__ unsigned g_dl_timeouts;
 constexpr int kDlSpinLimit = 1 << 21;  // polls (about a microsecond each) before a wait gives up
-constexpr int kDlPreStages = 2;        // FC2 stages a wave issues before the grid barrier
 
 __device__ __forceinline__ unsigned flag_load(const unsigned* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -419,66 +420,40 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
   if constexpr (FUSED) {
-    // ---- 4. FC2 and the top-k combine in the same launch. A workgroup owns
-    // 16 output columns of every live expert (column blocks blockIdx.x + G j),
-    // as launch_down_combine; the list of live experts is the routing above.
+    // ---- 4. FC2 and the top-k combine in the same launch (fc2_decode.h). A
+    // workgroup owns 16 output columns of every live expert (column blocks
+    // blockIdx.x + G j), as launch_down_combine; the list of live experts and
+    // their rows is the routing above.
     const int G = gridDim.x;
-    const int KB2 = I / kGroup, TS = I + 16;
     const int n_cb = H / 16;
-    const int n_rows = n_live > 0 ? __builtin_amdgcn_readfirstlane(s_c0[n_live - 1] + s_cnt[n_live - 1]) : 0;
+    DecodeTables t;
+    t.e = s_e;
+    t.cnt = s_cnt;
+    t.c0 = s_c0;
+    t.r0 = s_row0;
+    t.row = s_crow;
+    t.pair = s_cpair;
+    t.p2r = s_prow;
+    t.tw = s_tw;
+    t.n_list = n_live;
+    t.n_rows = n_live > 0 ? __builtin_amdgcn_readfirstlane(s_c0[n_live - 1] + s_cnt[n_live - 1]) : 0;
+    t.n_pairs = PQ;
     uint8_t* const s_tok = s_x;                             // FC2 input codes, row stride I + 16
-    float* const s_sa = s_xs;                               // their scales at c * KB2 + kb
+    float* const s_sa = s_xs;                               // their scales
     float* const s_slot = reinterpret_cast<float*>(s_part);  // pair q's 16 columns
-    const int my_n = wave < n_live ? (n_live - 1 - wave) / kF1Waves + 1 : 0;
-    const int total2 = my_n * KB2;  // FC2 stages of this wave per column block
-    int j_ent = wave, j_kb = 0;
-    const uint8_t* j_w0 = q.w + lane * 16;
-    const uint8_t* j_w1 = q.w + lane * 16;
-    const uint8_t* j_s = reinterpret_cast<const uint8_t*>(q.w_scales);
-    auto j_set = [&](int n0) {
-      const int e = __builtin_amdgcn_readfirstlane(s_e[j_ent]);
-      const uint8_t* wb = q.w + (static_cast<int64_t>(e) * H + n0) * I;
-      j_w0 = wb + static_cast<int64_t>(grow) * I + chunk_lo;
-      j_w1 = wb + static_cast<int64_t>(grow + 8) * I + chunk_hi;
-      j_s = reinterpret_cast<const uint8_t*>(q.w_scales + (static_cast<int64_t>(e) * (H / kGroup) + n0 / kGroup) * KB2);
-    };
-    auto j_issue = [&](uint8_t* st) {
-      __builtin_amdgcn_global_load_lds(j_w0 + j_kb * kGroup, (lds_void*)(st), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(j_w1 + j_kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(j_s + j_kb * 4, (lds_void*)(st + kF1StageW), 4, 0, 0);
-    };
-    auto j_advance = [&](int n0) {
-      if (++j_kb == KB2) {
-        j_kb = 0;
-        j_ent += kF1Waves;
-        if (j_ent < n_live) j_set(n0);
-      }
-    };
-    // Stages d0..d1-1 of the stream start, which always issues kF1Depth - 1
-    // stages (past the wave's last one, stand-ins).
-    auto j_start = [&](int n0, int d0, int d1) {
-      if (d0 == 0) {
-        j_ent = wave;
-        j_kb = 0;
-        if (total2 > 0) j_set(n0);
-      }
-      for (int d = d0; d < d1; ++d) {
-        j_issue(ring + d * kF1Stage);
-        if (d + 1 < total2) j_advance(n0);
-      }
-    };
+    Fc2Stream st;
+    st.init(q.w, q.w_scales, t, ring, H, I, wave, lane);
     int cb = blockIdx.x;
     const bool has_cb = cb < n_cb;  // uniform
     // The first FC2 stages go out before the barrier: the ring of a wave is
     // free once its FC1 stream is done, and the weights do not depend on FC1.
-    // Only a few: the act rows loaded after the barrier complete behind them.
-    if (has_cb) j_start(cb * 16, 0, kDlPreStages);
+    if (has_cb) st.start(cb * 16, 0, kDecPreStages);
 
     // ---- grid barrier. Every wave has waited for its act stores (write-
-    // through) above; after the workgroup barrier workgroup 0's thread 0 (for
-    // the others, their thread 0) publishes the epoch, workgroup 0 waits for
-    // every workgroup's epoch and releases it. Waits are bounded: one that
-    // gives up is counted and the launch goes on.
+    // through) above; after the workgroup barrier thread 0 publishes the
+    // workgroup's epoch, workgroup 0 waits for every workgroup's epoch and
+    // releases the epoch. Waits are bounded: one that gives up is counted and
+    // the launch goes on.
     lds_barrier();
     if (tid == 0) flag_store(&g_dl_flag[blockIdx.x], epoch);
     if (blockIdx.x == 0) {
@@ -491,201 +466,24 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;  // the K-split partials are done
     lds_barrier();
 
-    // ---- 5. FC2 input rows of this wave's experts (every kF1Waves-th live
-    // entry), read at device scope: 16 lanes per row, 4 rows per pass; lanes
-    // l16 and chunks u cover columns 4 (16 u + l16) of a 512-column chunk.
-    const int l16 = lane & 15, lg = lane >> 4;
-    const bool writer = blockIdx.x == 0;
-    int my_rows = 0;
-    for (int i = wave; i < n_live; i += kF1Waves) my_rows += s_cnt[i];
-    my_rows = __builtin_amdgcn_readfirstlane(my_rows);
-    auto wave_row = [&](int k) {  // compact row of this wave's k-th row
-      for (int i = wave; i < n_live; i += kF1Waves) {
-        const int cnt = s_cnt[i];
-        if (k < cnt) return s_c0[i] + k;
-        k -= cnt;
-      }
-      return 0;
-    };
+    // ---- 5. this wave's FC2 input rows, read at device scope (other
+    // workgroups wrote them), then the rest of the stream start
     if (has_cb) {
-      for (int k0 = 0; k0 < my_rows; k0 += 4) {
-        const bool row_ok = k0 + lg < my_rows;
-        const int c = wave_row(row_ok ? k0 + lg : 0);
-        const int r = s_crow[c];
-        for (int col0 = 0; col0 < I; col0 += 512) {
-          u32x4 vr[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)  // columns past I (unused) load a valid stand-in
-            vr[u] = gload_b128_dev(p.act_out + static_cast<int64_t>(r) * I + min(col0 + 4 * (16 * u + l16), I - 4));
-          asm volatile("s_waitcnt vmcnt(0)"
-                       : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
-                         "+v"(vr[6]), "+v"(vr[7]));
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int colg = col0 + g * kGroup;
-            if (colg >= I) break;  // uniform
-            const u32x4 ra = vr[2 * g], rb = vr[2 * g + 1];
-            const float a0 = __uint_as_float(ra[0]), a1 = __uint_as_float(ra[1]), a2 = __uint_as_float(ra[2]),
-                        a3 = __uint_as_float(ra[3]), b0 = __uint_as_float(rb[0]), b1 = __uint_as_float(rb[1]),
-                        b2 = __uint_as_float(rb[2]), b3 = __uint_as_float(rb[3]);
-            float amax = fmaxf(fmaxf(fabsf(a0), fabsf(a1)), fmaxf(fabsf(a2), fabsf(a3)));
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(b0), fabsf(b1)), fmaxf(fabsf(b2), fabsf(b3))));
-            amax = group_max<16>(amax);
-            const float sc = group_scale(amax, FMT);
-            const float inv = 1.0f / sc;  // IEEE division, once per group
-            const uint32_t qa = cvt_pk_e4m3(scale_div(a0, sc, inv, FMT), scale_div(a1, sc, inv, FMT)) |
-                                (cvt_pk_e4m3(scale_div(a2, sc, inv, FMT), scale_div(a3, sc, inv, FMT)) << 16);
-            const uint32_t qb = cvt_pk_e4m3(scale_div(b0, sc, inv, FMT), scale_div(b1, sc, inv, FMT)) |
-                                (cvt_pk_e4m3(scale_div(b2, sc, inv, FMT), scale_div(b3, sc, inv, FMT)) << 16);
-            const int ca = col0 + 4 * (32 * g + l16), cbb = ca + 64;
-            if (row_ok) {
-              *reinterpret_cast<uint32_t*>(s_tok + c * TS + ca) = qa;
-              *reinterpret_cast<uint32_t*>(s_tok + c * TS + cbb) = qb;
-              if (l16 == 0) s_sa[c * KB2 + colg / kGroup] = sc;
-              if (writer) {
-                *reinterpret_cast<uint32_t*>(q.hq + static_cast<int64_t>(r) * I + ca) = qa;
-                *reinterpret_cast<uint32_t*>(q.hq + static_cast<int64_t>(r) * I + cbb) = qb;
-                if (l16 == 0) store_scale(q.hs, FMT, static_cast<int64_t>(colg / kGroup) * q.row_cap + r, sc);
-              }
-            }
-          }
-        }
-      }
+      fc2_quant_rows<FMT, true>(t, wave, lane, p.act_out, I, s_tok, s_sa, blockIdx.x == 0, q.hq, q.hs,
+                                q.row_cap, nullptr, nullptr, nullptr);
+      st.start(cb * 16, kDecPreStages, kDecDepth - 1);
     }
-    // The loop below reads these rows through assembly the compiler does not
-    // see; keep the stores above it.
-    asm volatile("" ::: "memory");
-    if (has_cb) j_start(cb * 16, kDlPreStages, kF1Depth - 1);
-
-    const uint32_t tok_base = lds_addr(s_tok) + c0f * 16;
-    const uint32_t sa_base = lds_addr(s_sa);
+    // ---- 6. stream and combine per column block
     for (; cb < n_cb; cb += G) {
       const int n0 = cb * 16;
       if (cb != static_cast<int>(blockIdx.x)) {
         for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;
         lds_barrier();  // zeroed slots visible
-        j_start(n0, 0, kF1Depth - 1);
+        st.start(n0, 0, kDecDepth - 1);
       }
-      // ---- 6. stream: wait for stage s, refill the slot of stage s - 1, compute s.
-      int e_ent = wave, e_kb = 0, slot2 = 0;
-      int e_cnt = 0, e_c0 = 0;
-      if (e_ent < n_live) {
-        e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e_ent]);
-        e_c0 = __builtin_amdgcn_readfirstlane(s_c0[e_ent]);
-      }
-      v4f acc2[kF1Tiles2];
-#pragma unroll
-      for (int m = 0; m < kF1Tiles2; ++m) acc2[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int s = 0; s < total2; ++s) {
-        if (s + kF1Depth - 2 >= total2)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kF1Loads * (kF1Depth - 2)));
-        const int prev = slot2 == 0 ? kF1Depth - 1 : slot2 - 1;
-        if (s + kF1Depth - 1 < total2) {
-          j_issue(ring + prev * kF1Stage);
-          j_advance(n0);
-        }
-        const uint32_t st = lds_addr(ring + slot2 * kF1Stage);
-        union {
-          uint4 u[2];
-          v8i v;
-        } wf, af;
-        const int n_mt = (e_cnt + kStreamTileM - 1) / kStreamTileM;
-        float sa, sw;
-        {
-          const int row = min(e_c0 + tok, n_rows - 1);
-          const uint32_t ta = tok_base + row * TS + e_kb * kGroup;
-          lds_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
-                         sa_base + (row * KB2 + e_kb) * 4, st + kF1StageW, wf.u[0], wf.u[1], af.u[0],
-                         af.u[1], sa, sw);
-          acc2[0] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc2[0]);
-        }
-#pragma unroll
-        for (int m = 1; m < kF1Tiles2; ++m) {
-          if (m < n_mt) {
-            const int row = min(e_c0 + m * kStreamTileM + tok, n_rows - 1);
-            const uint32_t ta = tok_base + row * TS + e_kb * kGroup;
-            lds_read_tile(ta, ta + 16, sa_base + (row * KB2 + e_kb) * 4, af.u[0], af.u[1], sa);
-            acc2[m] = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc2[m]);
-          }
-        }
-        if (++e_kb == KB2) {  // expert done: BF16-rounded rows to their pairs' slots
-#pragma unroll
-          for (int m = 0; m < kF1Tiles2; ++m) {
-            const int j = m * kStreamTileM + tok;
-            if (m < n_mt && j < e_cnt) {
-              const int qp = s_cpair[e_c0 + j];
-              float4 o;
-              o.x = bf16_to_f32(f32_to_bf16(acc2[m][0]));
-              o.y = bf16_to_f32(f32_to_bf16(acc2[m][1]));
-              o.z = bf16_to_f32(f32_to_bf16(acc2[m][2]));
-              o.w = bf16_to_f32(f32_to_bf16(acc2[m][3]));
-              *reinterpret_cast<float4*>(s_slot + qp * 16 + 4 * (lane >> 4)) = o;
-            }
-            acc2[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-          e_kb = 0;
-          e_ent += kF1Waves;
-          if (e_ent < n_live) {
-            e_cnt = __builtin_amdgcn_readfirstlane(s_cnt[e_ent]);
-            e_c0 = __builtin_amdgcn_readfirstlane(s_c0[e_ent]);
-          }
-        }
-        slot2 = slot2 == kF1Depth - 1 ? 0 : slot2 + 1;
-      }
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
+      fc2_stream_block(st, n0, t, s_tok, s_sa, s_slot, lane);
       lds_barrier();  // every slot of this column block written
-
-      // ---- 7. top-k sum of the 16 columns (two threads per token) in the
-      // arithmetic and order of moe_topk_combine, then the FC2 output rows.
-      for (int x = tid; x < t_live * 2; x += kF1Threads) {
-        const int t = x >> 1, h = x & 1;
-        float o8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o8[i] = 0.0f;
-        for (int k0 = 0; k0 < TK; k0 += 8) {
-          bool ok[8];
-          float w[8];
-          float4 lo[8], hi[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int qp = t * TK + min(k0 + j, TK - 1);
-            ok[j] = k0 + j < TK && static_cast<unsigned>(s_prow[qp]) < static_cast<unsigned>(p.row_cap);
-            w[j] = s_tw[qp];
-            lo[j] = *reinterpret_cast<const float4*>(s_slot + qp * 16 + 8 * h);
-            hi[j] = *reinterpret_cast<const float4*>(s_slot + qp * 16 + 8 * h + 4);
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (!ok[j]) continue;
-            o8[0] = fmaf(w[j], lo[j].x, o8[0]);
-            o8[1] = fmaf(w[j], lo[j].y, o8[1]);
-            o8[2] = fmaf(w[j], lo[j].z, o8[2]);
-            o8[3] = fmaf(w[j], lo[j].w, o8[3]);
-            o8[4] = fmaf(w[j], hi[j].x, o8[4]);
-            o8[5] = fmaf(w[j], hi[j].y, o8[5]);
-            o8[6] = fmaf(w[j], hi[j].z, o8[6]);
-            o8[7] = fmaf(w[j], hi[j].w, o8[7]);
-          }
-        }
-        uint4 o;
-        o.x = f32_to_bf16(o8[0]) | (f32_to_bf16(o8[1]) << 16);
-        o.y = f32_to_bf16(o8[2]) | (f32_to_bf16(o8[3]) << 16);
-        o.z = f32_to_bf16(o8[4]) | (f32_to_bf16(o8[5]) << 16);
-        o.w = f32_to_bf16(o8[6]) | (f32_to_bf16(o8[7]) << 16);
-        *reinterpret_cast<uint4*>(q.out + static_cast<int64_t>(t) * H + n0 + 8 * h) = o;
-      }
-      for (int x = tid; x < n_rows * 2; x += kF1Threads) {
-        const int c = x >> 1, h = x & 1;
-        const float* v = s_slot + s_cpair[c] * 16 + 8 * h;
-        uint4 o;
-        o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-        o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-        o.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
-        o.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
-        *reinterpret_cast<uint4*>(q.y + static_cast<int64_t>(s_crow[c]) * H + n0 + 8 * h) = o;
-      }
+      fc2_combine(t, s_slot, t_live, TK, p.row_cap, H, n0, q.out, q.y, tid);
       lds_barrier();  // slots free for the next column block
     }
   }
