@@ -291,22 +291,23 @@ def main():
     # on the GPU timeline, as a kernel trace measures it.
     import ctypes
     bl = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
-    bl.moe_bench_mark.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    bl.moe_bench_mark.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
+                                  ctypes.c_void_p]
     bl.moe_bench_clock_hz.restype = ctypes.c_int64
     mark_cap = 2 * (args.steps + args.warmup + 8)
     mark_slots = torch.zeros(mark_cap, dtype=torch.int64, device=dev)
     mark_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def mark():
-        if bl.moe_bench_mark(mark_slots.data_ptr(), mark_ctr.data_ptr(), mark_cap,
+    def mark(closing):
+        if bl.moe_bench_mark(mark_slots.data_ptr(), mark_ctr.data_ptr(), mark_cap, int(closing),
                              torch.cuda.current_stream().cuda_stream) != 0:
             raise RuntimeError("device-clock mark launch failed")
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        mark()
+        mark(False)
         fwd()
-        mark()
+        mark(True)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
