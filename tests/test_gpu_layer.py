@@ -267,6 +267,45 @@ def test_graph_replay_with_changing_routing_and_live_count(t_cap):
     assert moe.moe_barrier_timeouts() == 0
 
 
+# A shape outside the five workloads, for the one-launch decode layer's
+# limits: ids of 10 bits (1000 experts) and top-16, so all 64 pair slots of
+# the layer's LDS tables are live at 4 tokens.
+WIDE = synth.Workload(name="wide", index=9, num_experts=1000, hidden=512, inter=256, topk=16,
+                      tokens=(4,), t_cap=4, align_rows=16, row_cap=0, scale_fmts=("fp32",))
+
+
+@pytest.mark.parametrize("t_live,fmt", [(4, "fp32"), (3, "ue8m0")])
+def test_one_launch_layer_wide_routing(t_live, fmt):
+    cfg = WIDE
+    E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk
+    say(f"wide routing E={E} top-{K} t_live={t_live} fmt={fmt}")
+    x, ids, w = synth.make_workload(cfg, 4)
+    ew = synth.ExpertWeights(cfg)
+    w1q = np.zeros((E, 2 * I, H), np.uint8)
+    w1s = np.zeros((E, 2 * I // 128, H // 128), np.float32)
+    w2q = np.zeros((E, H, I), np.uint8)
+    w2s = np.zeros((E, H // 128, I // 128), np.float32)
+    for e in np.unique(ids):  # only routed experts are ever read
+        (w1q[e], w1s[e]), (w2q[e], w2s[e]) = ew.fc1(e), ew.fc2(e)
+    lay = moe.moe_workspace_plan(E, H, I, K, 4, cfg.align_rows, 0, fmt)
+    assert lay["act"] < lay["total"]  # the decode path
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    out = torch.full((4, H), POISON_BF16, dtype=torch.int16, device=dev())
+    moe.moe_forward(up(x), up(ids), up(w), up(w1q), up(w1s), up(w2q), up(w2s), fmt,
+                    align_rows=cfg.align_rows, t_live=up(np.array([t_live], np.int32)), out=out,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert moe.moe_barrier_timeouts() == 0
+    al = oracle.align(ids, t_live, E, cfg.align_rows)
+    assert np.array_equal(_ws_view(ws, lay, "expert_counts", np.int32, (E,)), al["counts"])
+    assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, (E + 1,)), al["offsets"])
+    got = down(out)
+    assert np.all(got[t_live:] == POISON_BF16)
+    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, t_live, fmt)
+    err = assert_bf16_close(got[:t_live], ref, "wide layer")
+    say(f"  layer max err / max|ref| = {err:.3e}")
+
+
 def test_padded_tiles_are_skipped():
     """On the 512-capacity / 16-live workload the FC1 GEMM visits exactly the
     tiles that hold live rows, far fewer than the capacity holds."""
