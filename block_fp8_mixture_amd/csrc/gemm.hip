@@ -536,7 +536,7 @@ hipError_t launch_stream(const GemmArgs& g, hipStream_t stream) {
 // ---------------------------------------------------------------- tiled
 
 constexpr int TM = kTiledTileM;   // token rows per tile (256)
-constexpr int TN = 256;           // weight rows per tile
+constexpr int TN = 256;           // weight rows per tile (the narrow variant: 64)
 constexpr int SK = 64;            // K bytes per pipeline stage (half a scale block)
 constexpr int kTiledThreads = 512;
 constexpr int kStageA = TM * SK;              // token part of a stage (16 KB)
@@ -581,12 +581,15 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
   }
 }
 
-// Large-expert GEMM. A workgroup computes a 256 token x 256 weight tile with
-// 8 waves as 4 (tokens) x 2 (weights); wave (wm, wn) owns tokens
-// [64 wm, 64 wm + 64) x weights [128 wn, 128 wn + 128), as 2 x 4 tiles of
-// v_mfma_f32_32x32x64_f8f6f4 (weights are the MFMA "A" operand, tokens "B";
-// lane l holds token l % 32 and 16 weight rows, so the token scale is one
-// value per lane and the weight block scale one value per wave).
+// Large-expert GEMM. A workgroup computes a 256 token x TNT weight tile
+// (TNT = 256, or 64 when the launch has too few 256-wide tiles to fill the
+// CUs) with 8 waves as 4 (tokens) x 2 (weights); wave (wm, wn) owns tokens
+// [64 wm, 64 wm + 64) x weights [TNT/2 wn, TNT/2 (wn + 1)), as 2 x TNT/64
+// tiles of v_mfma_f32_32x32x64_f8f6f4 (weights are the MFMA "A" operand,
+// tokens "B"; lane l holds token l % 32 and 16 weight rows, so the token
+// scale is one value per lane and the weight block scale one value per
+// wave). The narrow variant keeps the stage layout: its W slab rows past 64
+// hold copies of the first 64 and are never read.
 //
 // K is walked in 64-byte stages: both operand slabs of a stage (256 x 64 B
 // each, 32 KB) are staged in LDS by direct-to-LDS loads through a ring of 4
@@ -599,8 +602,12 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // into it; the epilogue multiplies by the last s. One VALU multiply per
 // element and block, no temporaries, no wait on an MFMA result. Power-of-two
 // ratios are exact.
-template <bool UE8M0, bool GATHER>
+template <bool UE8M0, bool GATHER, int TNT>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
+  static_assert(TNT == 256 || TNT == 64, "tile widths");
+  constexpr int WN = TNT / 2;   // weight rows of a wave
+  constexpr int WT = WN / 32;   // its 32-row MFMA tiles
+  constexpr int LPS = TNT == 256 ? 4 : 3;  // direct-to-LDS loads per wave and stage
   // Four stages and two token-scale buffers, all distinct objects, so the
   // compiler can tell that a read never aliases a direct-to-LDS load in
   // flight and does not wait for the prefetch.
@@ -629,7 +636,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   const int wm = wave >> 1;
   const int wn = wave & 1;
   const int N = p.n, K = p.k, KB = K / kGroup, NS = K / SK;
-  const int nt = (N + TN - 1) / TN;
+  const int nt = (N + TNT - 1) / TNT;
   const int total = s_pref[n_list] * nt;
   const int G = gridDim.x;
   // Persistent grid: consecutive tiles go to one XCD (workgroups are
@@ -651,8 +658,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     const int cnt = __builtin_amdgcn_readfirstlane(expert_rows(p, e));
     const int rows_here = min(TM, cnt - mt * TM);
     const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]) + mt * TM;
-    const int n0 = ntile * TN;
-    const bool wave_on = wm * 64 < rows_here && n0 + wn * 128 < N;
+    const int n0 = ntile * TNT;
+    const bool wave_on = wm * 64 < rows_here && n0 + wn * WN < N;
     const uint8_t* wbase = p.w + static_cast<int64_t>(e) * N * K;
 
     for (int i = tid; i < 2 * KB; i += kTiledThreads) {
@@ -660,8 +667,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
     }
     // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
-    // instructions of 16 rows each; lane l lands in slot l & 3 of row
-    // 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps there.
+    // instructions of 16 rows each (the narrow tile's 64 weight rows: rows
+    // [8 w, 8 w + 8) as one instruction of 32 lanes); lane l lands in slot
+    // l & 3 of row 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps
+    // there.
     uint32_t aoff[2], woff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -669,8 +678,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
       const int ar = row < rows_here ? a_source_row<GATHER>(p, row0 + row) : -1;
       aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
-      const int wr = n0 + row < N ? n0 + row : n0;
-      woff[i] = static_cast<uint32_t>(wr) * K + chunk;
+      const int wrow = TNT == 256 ? row : wave * 8 + (lane >> 2) % 8;
+      const int wchunk = TNT == 256 ? chunk : ((lane & 3) ^ ((wrow >> 2) & 3)) << 4;
+      const int wr = n0 + wrow < N ? n0 + wrow : n0;
+      woff[i] = static_cast<uint32_t>(wr) * K + wchunk;
     }
     const int sa_row = tok < rows_here ? a_source_row<GATHER>(p, row0 + tok) : -1;
     const int my_src = sa_row < 0 ? 0 : sa_row;
@@ -680,9 +691,13 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(p.a + (aoff[i] + s * SK), (lds_void*)(stage + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+      if constexpr (TNT == 256) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+      } else if (lane < 32) {
+        __builtin_amdgcn_global_load_lds(wbase + (woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 8 * SK), 16, 0, 0);
+      }
     };
     // Token scales of block kb. Waves 0..3 load them into `buf`; waves
     // 4..7 load the same values into a sink so that every wave has the same
@@ -700,9 +715,9 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       return v > kScaleFloor ? v : kScaleFloor;
     };
 
-    v16f acc[4][2];  // [weight tile][token tile]
+    v16f acc[WT][2];  // [weight tile][token tile]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
     float tok_prev = 1.0f;  // this thread's token scale of the previous block
@@ -722,7 +737,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     __builtin_amdgcn_sched_barrier(0);
     issue_s(1, s_sr1);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9): stage 0 and block 0's scales landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS + 1));  // stage 0 and block 0's scales landed
     if (tid < TM) {
       tok_prev = decode_sa(s_sr0[tok]);
       s_rt[0][(tok & 31) * 8 + (tok >> 5)] = 1.0f;
@@ -731,19 +746,20 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 
     // Stage j. Entry: stage j is visible to all waves (barrier of stage j-1
     // or the prologue's); stages j+1 and j+2 may be in flight. Each stage
-    // issues [A x2][W x2] for stage j+3, then [S] if stage j+3 starts a
-    // block. Stage j+1 (and, when it starts a block, its scales) has landed
-    // once only stage j+2's loads remain: 4 when j+1 starts a block, else 4
-    // plus the scales issued after stage j+2. If stage j+1 starts block kb,
+    // issues [A x2][W x2, or x1 for the narrow tile] (LPS loads) for stage
+    // j+3, then [S] if stage j+3 starts a block. Stage j+1 (and, when it
+    // starts a block, its scales) has landed once only stage j+2's loads
+    // remain: LPS when j+1 starts a block, else LPS plus the scales issued
+    // after stage j+2. If stage j+1 starts block kb,
     // its token ratios are published; then the barrier, the loads, and the 8
     // MFMAs of stage j.
     auto stage = [&](int j, const uint8_t* cur, uint8_t* fill, const uint32_t* sr_next,
                      float* rt_next, const float* rt_cur, uint32_t* sr_fill, bool next_starts,
                      bool cur_starts, bool fill_starts) {
       if (next_starts)
-        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
       else
-        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS + 1));
       if (next_starts) {
         const int kb_next = (j + 1) >> 1;
         const float t = decode_sa(sr_next[tok]);
@@ -762,13 +778,13 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       if (!wave_on || j >= NS) return;
       if (cur_starts) {
         const int kb = j >> 1;
-        const float sw = fmaxf(s_ws[wn][kb], kScaleFloor);
+        const float sw = fmaxf(s_ws[(wn * WN) / kGroup][kb], kScaleFloor);
         const float q = sw_norm * __builtin_amdgcn_rcpf(sw);
         sw_norm = sw;
         const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
         const float ratio0 = r2.x * q, ratio1 = r2.y * q;
 #pragma unroll
-        for (int wt = 0; wt < 4; ++wt) {
+        for (int wt = 0; wt < WT; ++wt) {
           acc[wt][0] = acc[wt][0] * ratio0;
           acc[wt][1] = acc[wt][1] * ratio1;
         }
@@ -784,8 +800,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         af[tt].u[1] = *reinterpret_cast<const uint4*>(sA + swz(r, c0 + 1));
       }
 #pragma unroll
-      for (int wt = 0; wt < 4; ++wt) {
-        const int r = wn * 128 + wt * 32 + (lane & 31);
+      for (int wt = 0; wt < WT; ++wt) {
+        const int r = wn * WN + wt * 32 + (lane & 31);
         Frag wf;
         wf.u[0] = *reinterpret_cast<const uint4*>(sW + swz(r, c0));
         wf.u[1] = *reinterpret_cast<const uint4*>(sW + swz(r, c0 + 1));
@@ -818,9 +834,9 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       for (int tt = 0; tt < 2; ++tt) {
         const int j = wm * 64 + tt * 32 + (lane & 31);
         if (j < rows_here) {
-          uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * 128 + 4 * (lane >> 5);
+          uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * WN + 4 * (lane >> 5);
 #pragma unroll
-          for (int wt = 0; wt < 4; ++wt)
+          for (int wt = 0; wt < WT; ++wt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               v4f v = {acc[wt][tt][4 * g], acc[wt][tt][4 * g + 1], acc[wt][tt][4 * g + 2], acc[wt][tt][4 * g + 3]};
@@ -829,7 +845,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         }
       }
     }
-    if (tid == 0 && p.tiles_visited) atomicAdd(p.tiles_visited, min(TN, N - n0) / kColTile);
+    if (tid == 0 && p.tiles_visited)  // (row tile, 128-column tile) pairs, each counted once
+      atomicAdd(p.tiles_visited, TNT >= kColTile ? min(TNT, N - n0) / kColTile : (n0 % kColTile == 0 ? 1 : 0));
   }
 }
 
@@ -846,15 +863,27 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
     // tile per expert that can be large, times the column tiles.
     const int64_t rows = g.row_cap;
     const int64_t large = rows / (kStreamMaxRows + 1) < live_bound ? rows / (kStreamMaxRows + 1) : live_bound;
-    const int64_t tiles = ((rows + TM - 1) / TM + large) * ((g.n + TN - 1) / TN);
+    const int64_t row_tiles = (rows + TM - 1) / TM + large;
     const int64_t cap = device_cu_count();
+    // 64-wide tiles when 256-wide ones would leave CUs idle (few large
+    // experts on a narrow N, e.g. FC1 of a 256-intermediate layer).
+    const bool narrow = row_tiles * ((g.n + TN - 1) / TN) < 2 * cap && g.n % 64 == 0;
+    const int64_t tiles = row_tiles * (narrow ? g.n / 64 : (g.n + TN - 1) / TN);
     const int grid = static_cast<int>(tiles < cap ? tiles : cap);
     if (grid > 0) {
       const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
-      if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
-      else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
-      else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
-      else hipLaunchKernelGGL((gemm_tiled_kernel<false, false>), dim3(grid), dim3(kTiledThreads), 0, stream, g);
+      const dim3 gr(grid), bl(kTiledThreads);
+      if (narrow) {
+        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, 64>), gr, bl, 0, stream, g);
+        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, 64>), gr, bl, 0, stream, g);
+        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, 64>), gr, bl, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, 64>), gr, bl, 0, stream, g);
+      } else {
+        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, TN>), gr, bl, 0, stream, g);
+        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, TN>), gr, bl, 0, stream, g);
+        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, TN>), gr, bl, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, TN>), gr, bl, 0, stream, g);
+      }
       err = hipGetLastError();
     }
   }

@@ -267,6 +267,7 @@ GEMM_SHAPES = [
     (6, 3, 256, 384, [40, 3, 16], 8),               # K/128 = 3, gathered
     (7, 32, 1024, 256, _MANY, 0),                   # 64-row streaming tasks
     (8, 32, 1024, 384, _MANY, 8),                   # the same, gathered, K/128 = 3
+    (9, 8, 8192, 256, [300] * 8, 0),                # enough tiles for 256-wide weight tiles
 ]
 
 
