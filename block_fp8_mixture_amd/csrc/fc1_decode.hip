@@ -1,5 +1,4 @@
-// FC1 of a decode-sized layer, with the routing alignment and the activation
-// quantization in its prologue: one launch instead of two.
+// The decode-sized layer in one launch, and its FC1 half on its own.
 //
 // vLLM PR #59128 (Purpose) and TensorRT-LLM PR #21250 (sequence diagram):
 // alignment yields per-expert contiguous rows and prefix-sum endpoints, and
@@ -26,6 +25,13 @@
 //  3. Epilogue of a task. One cross-lane swap pairs gate and up values; C1
 //     gets both BF16 halves, and act the fp32 SiLU(gate) * up of the
 //     BF16-rounded pair (fp64 inside, rounded once).
+// The one-launch layer (FUSED) goes on:
+//  4. A barrier across the grid (every workgroup resident, one per CU): the
+//     act rows, written through to memory, are complete once it opens.
+//  5. FC2 and the top-k combine for the workgroup's 16 output columns, as
+//     fc2_decode.h describes, in the same LDS (token codes -> FC2 input
+//     codes, K-split partials -> pair slots, each wave's ring -> its FC2
+//     stream). The first FC2 stages go out before the barrier.
 #include "device_common.h"
 #include "fc2_decode.h"
 #include "gemm_device.h"
