@@ -76,6 +76,8 @@ enum Act : int { kSwiglu = 0, kSwigluClamp = 1, kSwigluClampAfterSilu = 2 };
 // intermediate BF16 rounding). Clamp variants as TensorRT-LLM PR #21250's
 // test coverage names them, with limit L: clamp gate above and up to [-L, L]
 // before SiLU, or clamp SiLU's output above and up to [-L, L].
+__device__ __forceinline__ double silu_f64(double g) { return g / (1.0 + exp(-g)); }
+
 template <int ACT>
 __device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
   double g = gf, u = uf;
@@ -83,7 +85,60 @@ __device__ __forceinline__ float swiglu(float gf, float uf, double lim) {
     g = fmin(g, lim);
     u = fmin(fmax(u, -lim), lim);
   }
-  double s = g / (1.0 + exp(-g));
+  double s = silu_f64(g);
+  if (ACT == kSwigluClampAfterSilu) {
+    s = fmin(s, lim);
+    u = fmin(fmax(u, -lim), lim);
+  }
+  return static_cast<float>(s * u);
+}
+
+// SiLU of BF16 gates by table. A gate is a BF16 value, so silu_f64 of every
+// gate with |g| in [2^-12, 2^4) -- where nearly all of them fall -- fits in a
+// 32 KB table that a workgroup fills once in LDS with silu_f64 itself; a gate
+// outside that range (zero, tiny, huge, not finite, or a clamp limit that is
+// not a BF16 value) takes silu_f64 directly. Either way the double is the one
+// swiglu() computes, so the results are bit-identical to it; the table only
+// replaces an fp64 exp and division per element by an LDS read.
+constexpr int kSiluLutLo = 127 - 12;              // biased exponent of 2^-12
+constexpr int kSiluLutExps = 16;                  // 2^-12 <= |g| < 2^4
+constexpr int kSiluLutSize = kSiluLutExps * 256;  // 128 mantissas x 2 signs per exponent
+
+// Entry i holds the BF16 value with magnitude bits (i >> 1) + (kSiluLutLo << 7)
+// and sign i & 1.
+__device__ __forceinline__ void fill_silu_lut(double* lut, int tid, int nthreads) {
+  for (int i = tid; i < kSiluLutSize; i += nthreads) {
+    const uint32_t bits = ((static_cast<uint32_t>(i) & 1u) << 15) |
+                          ((static_cast<uint32_t>(i) >> 1) + (kSiluLutLo << 7));
+    lut[i] = silu_f64(static_cast<double>(bf16_to_f32(bits)));
+  }
+}
+
+// Table entry of gate g, or -1 when g is not a tabulated BF16 value.
+__device__ __forceinline__ int silu_lut_index(float g) {
+  const uint32_t b = __float_as_uint(g);
+  const uint32_t mag = ((b >> 16) & 0x7FFFu) - static_cast<uint32_t>(kSiluLutLo << 7);
+  return ((b & 0xFFFFu) == 0 && mag < static_cast<uint32_t>(kSiluLutExps * 128))
+             ? static_cast<int>(mag * 2 + (b >> 31))
+             : -1;
+}
+
+// swiglu<ACT> with the SiLU from `lut` (filled by fill_silu_lut) where it
+// has the gate.
+template <int ACT>
+__device__ __forceinline__ float swiglu_lut(float gf, float uf, double lim, const double* lut) {
+  float g = gf;
+  double u = uf;
+  if (ACT == kSwigluClamp) {
+    g = static_cast<float>(fmin(static_cast<double>(gf), lim));  // gf or the limit, both floats
+    u = fmin(fmax(u, -lim), lim);
+  }
+  const int i = silu_lut_index(g);
+  double s;
+  if (i >= 0)
+    s = lut[i];
+  else
+    s = silu_f64(g);
   if (ACT == kSwigluClampAfterSilu) {
     s = fmin(s, lim);
     u = fmin(fmax(u, -lim), lim);

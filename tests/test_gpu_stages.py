@@ -183,6 +183,64 @@ def test_silu_mul_quant_bit_exact(fmt, act, lim, amp, inter, e, seed):
         assert np.all(np.isnan(gs[:, ~live]))
 
 
+def _gate_specials(g, shape):
+    """BF16 gate bits around and outside the SiLU table's range [2^-12, 2^4):
+    zeros of both signs, tiny and huge magnitudes, the range's end points and
+    their BF16 neighbours."""
+    edges = np.array([2.0 ** -12, 2.0 ** 4], np.float32).view(np.uint32) >> 16
+    pool = np.concatenate([edges - 1, edges, edges + 1, [0, 1, 0x7F, 0x80]]).astype(np.uint16)
+    mags = (np.exp2(g.uniform(-24.0, 7.0, shape)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    pick = g.random(shape) < 0.2
+    bits = np.where(pick, g.choice(pool, shape), mags)
+    return (bits | (g.integers(0, 2, shape, dtype=np.uint16) << 15)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,act,lim", [("fp32", "swiglu", float("inf")),
+                                          ("ue8m0", "swiglu_clamp", 7.0),
+                                          ("pow2", "swiglu_clamp", 0.3),
+                                          ("ue8m0", "swiglu_clamp_after_silu", 7.0)])
+def test_silu_mul_quant_table_path(fmt, act, lim):
+    """Launches large enough that every workgroup takes SiLU from its table of
+    BF16 gates (at least 128 groups each with two workgroups per CU): codes
+    and scales bit-exact, including gates outside the table's range and a
+    clamp limit that is not a BF16 value."""
+    cus = torch.cuda.get_device_properties(dev()).multi_processor_count
+    inter, e = 2048, 32
+    rows_needed = 128 * 2 * cus * 128 // inter
+    say(f"silu_mul_quant table path fmt={fmt} act={act} lim={lim} rows>={rows_needed}")
+    g = np.random.default_rng(7)
+    per = -(-rows_needed // e) + 24
+    counts = g.integers(per - 16, per + 16, e).astype(np.int32)
+    counts[3] = 0
+    offsets = np.concatenate([[0], np.cumsum(-(-counts // 16) * 16)]).astype(np.int32)
+    assert offsets[-1] >= rows_needed
+    row_cap = int(offsets[-1]) + 16
+    # Truncated float32 normals as BF16 inputs; a tenth of the gates special.
+    gu = (np.float32(3.0) * g.standard_normal((row_cap, 2 * inter), np.float32)).view(np.uint32)
+    gu = (gu >> 16).astype(np.uint16)
+    sp = g.random((row_cap, inter)) < 0.1
+    gu[:, :inter] = np.where(sp, _gate_specials(g, (row_cap, inter)), gu[:, :inter])
+    live = np.zeros(row_cap, bool)
+    for i in range(e):
+        live[offsets[i]:offsets[i] + counts[i]] = True
+    gu[~live] = POISON_BF16
+    sdt = torch.uint8 if fmt == "ue8m0" else torch.float32
+    hq = _full((row_cap, inter), POISON_U8, torch.uint8)
+    hs = _full((inter // 128, row_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
+    lim32 = float(np.float32(lim))
+    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32)
+    gq, gs = down(hq), down(hs)
+    bad = np.argwhere(gq[live] != rq)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+    assert np.all(gq[~live] == POISON_U8)
+    if fmt == "ue8m0":
+        assert np.array_equal(gs[:, live], rs)
+    else:
+        assert np.array_equal(_f32_bits(gs[:, live]), _f32_bits(rs))
+
+
 # ------------------------------------------------------------------ grouped GEMM
 
 EXACT_CODES = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], np.uint8)  # 0, +-.5, +-1, +-2
