@@ -9,9 +9,12 @@
 // One launch, no scratch memory. Block b owns pairs [b*kChunk, (b+1)*kChunk).
 // Every block counts all live pairs per expert in LDS (so every block knows
 // the endpoints) and, separately, the pairs before its chunk (so it knows
-// where its chunk starts inside each segment). Inside the chunk, pairs are
-// ranked stably: a wave groups its lanes by expert with ballots, and waves
-// are ordered by an exclusive sum over per-wave counts.
+// where its chunk starts inside each segment). Inside the chunk (one pair
+// per thread), pairs are ranked stably: each wave finds, per expert, the set
+// of its lanes holding it (a 64-bit lane mask in LDS built by one atomic OR
+// per lane when there are at most 256 experts, else a ballot loop over the
+// wave's distinct experts), and waves are ordered by an exclusive sum over
+// per-wave counts.
 #include "device_common.h"
 #include "kernels.h"
 #include "quant_device.h"
@@ -21,7 +24,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = 4096;
+constexpr int kChunk = kThreads;  // pairs ranked by a block: one per thread
+constexpr int kMaskExperts = 256;  // experts ranked by lane masks (32 KB of masks)
+constexpr int kBatch = 8;  // ids in flight per thread in the counting pass
 
 // The work of align block `block` (all kThreads threads of a block call it).
 __device__ __forceinline__ void align_block(
@@ -29,41 +34,58 @@ __device__ __forceinline__ void align_block(
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
     int32_t* __restrict__ pair_to_row) {
-  __shared__ int s_total[kMaxExperts];
-  __shared__ int s_before[kMaxExperts];
-  __shared__ int s_run[kMaxExperts];
+  // Per expert: live pairs (low word) and live pairs before the chunk (high).
+  __shared__ unsigned long long s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ uint16_t s_wave[kWaves][kMaxExperts];
+  // Per-wave ranking state, 32 KB: with at most kMaskExperts experts, bit l
+  // of mask [wave][e] is set when lane l holds expert e; otherwise 16-bit
+  // counts [wave][e] of the ballot loop.
+  __shared__ __attribute__((aligned(16))) unsigned long long s_rank[kWaves * kMaxExperts / 4];
   __shared__ int s_wsum[kWaves];
+  __shared__ int16_t s_chunk[kChunk];  // ids of this block's chunk (-1: dropped)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int E = num_experts;
-  // The first id this thread counts is loaded together with the live count
-  // (ids holds t_cap * topk entries, so the load is in bounds either way).
-  const int e_first = tid < static_cast<int64_t>(t_cap) * topk ? ids[tid] : -1;
+  const int64_t cap_pairs = static_cast<int64_t>(t_cap) * topk;
+  // kBatch ids per thread are loaded together, so their latencies overlap;
+  // the first batch is in flight together with the live count (ids holds
+  // t_cap * topk entries, so the loads are in bounds either way).
+  int ev[kBatch];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = p0 + i * kThreads + tid;
+      ev[i] = p < cap_pairs ? ids[p] : -1;
+    }
+  };
+  load_batch(0);
   const int n_pairs = clamp_live(t_live_dev, t_cap) * topk;
   const int c0 = block * kChunk;
   if (block > 0 && c0 >= n_pairs) return;
 
-  for (int e = tid; e < E; e += kThreads) {
-    s_total[e] = 0;
-    s_before[e] = 0;
-    s_run[e] = 0;
-  }
-  for (int i = tid; i < kWaves * E; i += kThreads) s_wave[i / E][i % E] = 0;
+  for (int e = tid; e < E; e += kThreads) s_cnt[e] = 0;
+  for (int i = tid; i < kWaves * kMaxExperts / 8; i += kThreads)
+    reinterpret_cast<uint4*>(s_rank)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  // Phase 1: per-expert counts of all live pairs and of pairs before the chunk.
-  for (int p = tid; p < n_pairs; p += kThreads) {
-    const int e = p == tid ? e_first : ids[p];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
-      atomicAdd(&s_total[e], 1);
-      if (p < c0) atomicAdd(&s_before[e], 1);
+  // Phase 1: per-expert counts of all live pairs and of pairs before the
+  // chunk (one 64-bit LDS add per pair); the chunk's own ids are kept in LDS
+  // for phase 3.
+  for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kThreads) {
+    if (p0 > 0) load_batch(p0);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int p = p0 + i * kThreads + tid;
+      const int e = ev[i];
+      const bool ok = p < n_pairs && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+      if (ok) atomicAdd(&s_cnt[e], p < c0 ? 0x100000001ull : 1ull);
+      if (p >= c0 && p < c0 + kChunk && p < n_pairs) s_chunk[p - c0] = static_cast<int16_t>(ok ? e : -1);
     }
   }
   __syncthreads();
+  auto total = [&](int e) { return static_cast<int>(static_cast<uint32_t>(s_cnt[e])); };
 
   // Phase 2: endpoints = exclusive prefix sum of counts rounded up to align_rows.
   // Thread t owns experts [t*per, t*per + per).
@@ -72,7 +94,7 @@ __device__ __forceinline__ void align_block(
     const int b = tid * per;
     int local = 0;
     for (int e = b; e < b + per && e < E; ++e)
-      local += (s_total[e] + align_rows - 1) / align_rows * align_rows;
+      local += (total(e) + align_rows - 1) / align_rows * align_rows;
     int incl = local;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -87,7 +109,7 @@ __device__ __forceinline__ void align_block(
     for (int w = 0; w < kWaves; ++w) run += w < wave ? s_wsum[w] : 0;
     for (int e = b; e < b + per && e < E; ++e) {
       s_off[e] = run;
-      run += (s_total[e] + align_rows - 1) / align_rows * align_rows;
+      run += (total(e) + align_rows - 1) / align_rows * align_rows;
     }
     if (b < E && b + per >= E) s_off[E] = run;
     __syncthreads();
@@ -95,22 +117,36 @@ __device__ __forceinline__ void align_block(
 
   if (block == 0) {
     for (int e = tid; e < E; e += kThreads) {
-      counts[e] = s_total[e];
+      counts[e] = total(e);
       offsets[e] = s_off[e];
-      for (int r = s_off[e] + s_total[e]; r < s_off[e + 1]; ++r) row_to_pair[r] = -1;
+      for (int r = s_off[e] + total(e); r < s_off[e + 1]; ++r) row_to_pair[r] = -1;
     }
     if (tid == 0) offsets[E] = s_off[E];
   }
 
-  // Phase 3: stable ranks inside the chunk, one round of kThreads pairs at a time.
-  const int c1 = min(c0 + kChunk, n_pairs);
-  for (int base = c0; base < c1; base += kThreads) {
-    const int p = base + tid;
-    const bool in_range = p < c1;
-    const int e = in_range ? (p == tid ? e_first : ids[p]) : -1;
-    const bool ok = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
-    const uint64_t below = (uint64_t(1) << lane) - 1;
-    int rank = 0;
+  // Phase 3: stable ranks inside the chunk (kChunk == kThreads: one pair per
+  // thread). The row of pair p is its segment's start + the pairs of its
+  // expert before the chunk + those in earlier waves + those in earlier
+  // lanes of its own wave.
+  const int p = c0 + tid;
+  const bool in_range = p < min(c0 + kChunk, n_pairs);
+  const int e = in_range ? s_chunk[tid] : -1;
+  const bool ok = e >= 0;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int rank = 0, prior = 0;
+  if (E <= kMaskExperts) {  // uniform
+    unsigned long long* mask = s_rank;  // [kWaves][kMaskExperts]
+    if (ok) atomicOr(&mask[wave * kMaskExperts + e], 1ull << lane);
+    // The LDS runs a wave's instructions in order, so the read sees the
+    // bits of every lane of this wave.
+    if (ok) rank = __popcll(mask[wave * kMaskExperts + e] & below);
+    __syncthreads();
+    if (ok) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) prior += w < wave ? __popcll(mask[w * kMaskExperts + e]) : 0;
+    }
+  } else {
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(s_rank);  // [kWaves][kMaxExperts]
     uint64_t active = __ballot(ok);
     while (active) {
       // The leader is uniform, so its expert is read with v_readlane (a
@@ -119,31 +155,21 @@ __device__ __forceinline__ void align_block(
       const int le = __builtin_amdgcn_readlane(e, leader);
       const uint64_t same = __ballot(ok && e == le);
       if (ok && e == le) rank = __popcll(same & below);
-      if (lane == leader) s_wave[wave][le] = static_cast<uint16_t>(__popcll(same));
+      if (lane == leader) cnt[wave * kMaxExperts + le] = static_cast<uint16_t>(__popcll(same));
       active &= ~same;
     }
     __syncthreads();
     if (ok) {
-      int prior = 0;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) prior += w < wave ? s_wave[w][e] : 0;
-      const int row = s_off[e] + s_before[e] + s_run[e] + prior + rank;
-      row_to_pair[row] = p;
-      pair_to_row[p] = row;
-    } else if (in_range) {
-      pair_to_row[p] = -1;
+      for (int w = 0; w < kWaves; ++w) prior += w < wave ? cnt[w * kMaxExperts + e] : 0;
     }
-    __syncthreads();
-    if (base + kThreads >= c1) break;  // last round: the running counts are not needed again
-    for (int x = tid; x < E; x += kThreads) {
-      int s = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        s += s_wave[w][x];
-        s_wave[w][x] = 0;
-      }
-      s_run[x] += s;
-    }
-    __syncthreads();
+  }
+  if (ok) {
+    const int row = s_off[e] + static_cast<int>(s_cnt[e] >> 32) + prior + rank;
+    row_to_pair[row] = p;
+    pair_to_row[p] = row;
+  } else if (in_range) {
+    pair_to_row[p] = -1;
   }
 }
 

@@ -48,6 +48,8 @@ ALIGN_CASES = [
     (1000, 999, 8, 1024, 7, 9, 0, 1024),
     (4096, 4096, 8, 256, 16, 10, 0, 3),  # three experts own every pair
     (1500, 1500, 1, 1, 1, 11, 0, 1),
+    (2048, 2000, 8, 256, 16, 12, -3, 259),  # the most experts ranked by lane masks
+    (300, 300, 8, 257, 16, 13, 0, 257),     # the fewest ranked by the ballot loop
 ]
 
 
