@@ -582,14 +582,15 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 }
 
 // Large-expert GEMM. A workgroup computes a 256 token x TNT weight tile
-// (TNT = 256, or 64 when the launch has too few 256-wide tiles to fill the
-// CUs) with 8 waves as 4 (tokens) x 2 (weights); wave (wm, wn) owns tokens
+// (TNT = 256, or 128 or 64 -- picked on the device, see PICK -- when wide
+// tiles would leave CUs idle) with 8 waves as 4 (tokens) x 2 (weights);
+// wave (wm, wn) owns tokens
 // [64 wm, 64 wm + 64) x weights [TNT/2 wn, TNT/2 (wn + 1)), as 2 x TNT/64
 // tiles of v_mfma_f32_32x32x64_f8f6f4 (weights are the MFMA "A" operand,
 // tokens "B"; lane l holds token l % 32 and 16 weight rows, so the token
 // scale is one value per lane and the weight block scale one value per
-// wave). The narrow variant keeps the stage layout: its W slab rows past 64
-// hold copies of the first 64 and are never read.
+// wave). The narrower variants keep the stage layout: W slab rows past TNT
+// are neither loaded nor read.
 //
 // K is walked in 64-byte stages: both operand slabs of a stage (256 x 64 B
 // each, 32 KB) are staged in LDS by direct-to-LDS loads through a ring of 4
@@ -602,9 +603,10 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // into it; the epilogue multiplies by the last s. One VALU multiply per
 // element and block, no temporaries, no wait on an MFMA result. Power-of-two
 // ratios are exact.
-template <bool UE8M0, bool GATHER, int TNT>
+template <bool UE8M0, bool GATHER, int TNT, bool PICK>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
-  static_assert(TNT == 256 || TNT == 64, "tile widths");
+  static_assert(TNT == 256 || TNT == 128 || TNT == 64, "tile widths");
+  static_assert(!PICK || TNT != 256, "the pick is between 64 and 128");
   constexpr int WN = TNT / 2;   // weight rows of a wave
   constexpr int WT = WN / 32;   // its 32-row MFMA tiles
   constexpr int LPS = TNT == 256 ? 4 : 3;  // direct-to-LDS loads per wave and stage
@@ -627,6 +629,16 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 
   const int n_list = build_expert_list<kTiledThreads>(p, WantLarge(), TiledUnits(), s_list,
                                                       s_pref, s_tmp);
+  if constexpr (PICK) {
+    // The 64- and 128-wide kernels are launched together on the same grid;
+    // both find the same row tiles and agree on which one runs: the fewer
+    // rounds of tiles over the grid times the relative time of one tile
+    // (measured at K = 6144: 64 -> 20, 128 -> 23; a tile streams 256 token
+    // rows and TNT weight rows per stage). The other exits here.
+    const int rows = s_pref[n_list], G = gridDim.x;
+    auto cost = [&](int w, int c) { return (rows * (p.n / w) + G - 1) / G * c; };
+    if ((cost(64, 20) < cost(128, 23)) != (TNT == 64)) return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -667,8 +679,9 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
     }
     // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
-    // instructions of 16 rows each (the narrow tile's 64 weight rows: rows
-    // [8 w, 8 w + 8) as one instruction of 32 lanes); lane l lands in slot
+    // instructions of 16 rows each (128 weight rows: rows [16 w, 16 w + 16)
+    // as one instruction; 64: rows [8 w, 8 w + 8) as one instruction of 32
+    // lanes); lane l lands in slot
     // l & 3 of row 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps
     // there.
     uint32_t aoff[2], woff[2];
@@ -678,7 +691,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
       const int ar = row < rows_here ? a_source_row<GATHER>(p, row0 + row) : -1;
       aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
-      const int wrow = TNT == 256 ? row : wave * 8 + (lane >> 2) % 8;
+      const int wrow = TNT == 256 ? row : TNT == 128 ? wave * 16 + (lane >> 2) : wave * 8 + (lane >> 2) % 8;
       const int wchunk = TNT == 256 ? chunk : ((lane & 3) ^ ((wrow >> 2) & 3)) << 4;
       const int wr = n0 + wrow < N ? n0 + wrow : n0;
       woff[i] = static_cast<uint32_t>(wr) * K + wchunk;
@@ -695,6 +708,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+      } else if constexpr (TNT == 128) {
+        __builtin_amdgcn_global_load_lds(wbase + (woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 16 * SK), 16, 0, 0);
       } else if (lane < 32) {
         __builtin_amdgcn_global_load_lds(wbase + (woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 8 * SK), 16, 0, 0);
       }
@@ -865,24 +880,32 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
     const int64_t large = rows / (kStreamMaxRows + 1) < live_bound ? rows / (kStreamMaxRows + 1) : live_bound;
     const int64_t row_tiles = (rows + TM - 1) / TM + large;
     const int64_t cap = device_cu_count();
-    // 64-wide tiles when 256-wide ones would leave CUs idle (few large
-    // experts on a narrow N, e.g. FC1 of a 256-intermediate layer).
-    const bool narrow = row_tiles * ((g.n + TN - 1) / TN) < 2 * cap && g.n % 64 == 0;
+    // 256-wide weight tiles, or, when those would leave CUs idle (few large
+    // experts on a narrow N, e.g. FC1 of a 256-intermediate layer), the 64-
+    // and 128-wide kernels together, of which the one that suits the actual
+    // row tiles runs (the pick needs the endpoints, which only the device
+    // has). The grid covers the most tiles a launch could have, up to one
+    // workgroup per CU.
+    const bool narrow = row_tiles * ((g.n + TN - 1) / TN) < 2 * cap;
     const int64_t tiles = row_tiles * (narrow ? g.n / 64 : (g.n + TN - 1) / TN);
     const int grid = static_cast<int>(tiles < cap ? tiles : cap);
     if (grid > 0) {
       const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
       const dim3 gr(grid), bl(kTiledThreads);
+      auto launch = [&](auto tnt, auto pick) {
+        constexpr int W = decltype(tnt)::value;
+        constexpr bool P = decltype(pick)::value;
+        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, W, P>), gr, bl, 0, stream, g);
+        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, W, P>), gr, bl, 0, stream, g);
+        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, W, P>), gr, bl, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, W, P>), gr, bl, 0, stream, g);
+      };
       if (narrow) {
-        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, 64>), gr, bl, 0, stream, g);
-        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, 64>), gr, bl, 0, stream, g);
-        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, 64>), gr, bl, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, 64>), gr, bl, 0, stream, g);
+        launch(std::integral_constant<int, 64>{}, std::true_type{});
+        if (hipGetLastError() == hipSuccess)
+          launch(std::integral_constant<int, 128>{}, std::true_type{});
       } else {
-        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, TN>), gr, bl, 0, stream, g);
-        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, TN>), gr, bl, 0, stream, g);
-        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, TN>), gr, bl, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, TN>), gr, bl, 0, stream, g);
+        launch(std::integral_constant<int, TN>{}, std::false_type{});
       }
       err = hipGetLastError();
     }

@@ -328,6 +328,8 @@ GEMM_SHAPES = [
     (7, 32, 1024, 256, _MANY, 0),                   # 64-row streaming tasks
     (8, 32, 1024, 384, _MANY, 8),                   # the same, gathered, K/128 = 3
     (9, 8, 8192, 256, [300] * 8, 0),                # enough tiles for 256-wide weight tiles
+    (10, 8, 2048, 256, [300] * 8, 0),               # 128-wide weight tiles
+    (11, 12, 1024, 512, [400] * 12, 8),             # 128-wide, gathered
 ]
 
 
