@@ -165,13 +165,20 @@ struct StreamLists {
 };
 
 // t is uniform over the wave; readfirstlane tells the compiler so, which
-// keeps the task bookkeeping in scalar registers and branches.
+// keeps the task bookkeeping in scalar registers and branches. The entry is
+// found by the whole wave at once: the prefixes are strictly increasing
+// from pref[0] = 0, so the last entry with pref <= key is the number of
+// entries i >= 1 with pref[i] <= key -- one LDS read per lane and a ballot
+// per 64 entries, instead of a chain of dependent reads.
 __device__ __forceinline__ StreamTask stream_task(const StreamLists& L, int n_rb, int t) {
   const int key = t / n_rb;
-  int lo = 0, hi = L.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(L.pref[mid]) <= key) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int lo = 0;
+  for (int base = 1; base < L.n; base += 64) {
+    const int i = base + lane;
+    const uint64_t le = __ballot(i < L.n && L.pref[i] <= key);
+    lo += __popcll(le);
+    if (~le != 0) break;  // an entry past the key (or the list's end) in this round
   }
   lo = __builtin_amdgcn_readfirstlane(lo);
   StreamTask r;
