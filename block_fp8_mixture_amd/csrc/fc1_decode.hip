@@ -349,8 +349,11 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const double lim = p.act_limit;
   for (int s = 0; s < total; ++s) {
+    // Stages issued after s: kF1Depth - 2, or max(kF1Depth - 2, total - 1) - s
+    // near the end (the start always issues kF1Depth - 1), as in
+    // fc2_stream_block.
     if (s + kF1Depth - 2 >= total)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wait_stages<kF1Loads>(max(kF1Depth - 2, total - 1) - s);
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kF1Loads * (kF1Depth - 2)));
     const int prev = slot == 0 ? kF1Depth - 1 : slot - 1;

@@ -188,7 +188,7 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int colg = col0 + g * kGroup;
-        if (colg >= I) break;  // uniform
+        const bool g_ok = colg < I;  // uniform; past I the loads hold stand-ins, never stored
         const u32x4 ra = vr[2 * g], rb = vr[2 * g + 1];
         float x[8];
 #pragma unroll
@@ -207,7 +207,7 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
         const uint32_t qb = cvt_pk_e4m3(scale_div(x[4], sc, inv, FMT), scale_div(x[5], sc, inv, FMT)) |
                             (cvt_pk_e4m3(scale_div(x[6], sc, inv, FMT), scale_div(x[7], sc, inv, FMT)) << 16);
         const int ca = col0 + 4 * (32 * g + l16), cb = ca + 64;
-        if (row_ok) {
+        if (row_ok && g_ok) {
           *reinterpret_cast<uint32_t*>(tok + c * TS + ca) = qa;
           *reinterpret_cast<uint32_t*>(tok + c * TS + cb) = qb;
           if (l16 == 0) sa[c * KB + colg / kGroup] = sc;
@@ -247,8 +247,13 @@ __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const De
 #pragma unroll
   for (int m = 0; m < kDecTiles; ++m) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int s = 0; s < st.total; ++s) {
+    // The start issued kDecDepth - 1 stages (stand-ins past the end) and
+    // every step one more while any remain, so the stages issued after s
+    // number kDecDepth - 2 in the steady state and max(kDecDepth - 2,
+    // total - 1) - s near the end; operations issued among them only make
+    // the wait stricter (they retire in order).
     if (s + kDecDepth - 2 >= st.total)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wait_stages<kDecLoads>(max(kDecDepth - 2, st.total - 1) - s);
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDecLoads * (kDecDepth - 2)));
     const int prev = slotn == 0 ? kDecDepth - 1 : slotn - 1;

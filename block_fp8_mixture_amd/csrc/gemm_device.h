@@ -49,6 +49,23 @@ __device__ __forceinline__ int scalar_load(const int* q) { return *(const const_
 // lgkmcnt left at their maxima).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Waits until at most n (uniform, 0..4) stages of L vector-memory operations
+// each are outstanding; s_waitcnt takes only an immediate.
+template <int L>
+__device__ __forceinline__ void wait_stages(int n) {
+  static_assert(4 * L <= 63, "vmcnt range");
+  if (n >= 4)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * L));
+  else if (n == 3)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * L));
+  else if (n == 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // Byte offset of 16-byte chunk c of row `row` in a slab of 128-byte rows.
 // Rows are written whole (8 lanes x 16 bytes each); chunk c of a row sits in
 // slot c ^ ((row >> 1) & 7), which gives the 16 lanes one ds_read_b128 cycle
