@@ -330,7 +330,7 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
 
   hipError_t e = hipSuccess;
   if (decode && moe::decode_layer_fits(p->t_cap, p->topk, p->hidden, p->inter) &&
-      moe::decode_layer_grid() > 0) {
+      moe::decode_layer_grid(moe::decode_layer_wide(p->t_cap, p->hidden)) > 0) {
     // The whole layer in one launch.
     moe::DecodeLayerArgs a;
     a.f1 = fc1_decode_args(p, t, L, ws);

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void down_combine_kernel(DownCombin
       lds_barrier();  // zeroed slots visible
       st.start(n0, 0, kDecDepth - 1);
     }
-    fc2_stream_block(st, n0, t, s_tok, s_sa, s_slot, lane);
+    fc2_stream_block<kDecDepth>(st, n0, t, s_tok, s_sa, s_slot, lane);
     lds_barrier();  // every slot of this column block written
     fc2_combine(t, s_slot, t_live, TK, p.row_cap, N, n0, p.out, p.y, tid);
     lds_barrier();  // slots free for the next column block

@@ -32,6 +32,8 @@
 //     fc2_decode.h describes, in the same LDS (token codes -> FC2 input
 //     codes, K-split partials -> pair slots, each wave's ring -> its FC2
 //     stream). The first FC2 stages go out before the barrier.
+#include <type_traits>
+
 #include "device_common.h"
 #include "fc2_decode.h"
 #include "gemm_device.h"
@@ -47,11 +49,9 @@ namespace {
 // share the ring geometry of fc2_decode.h.
 constexpr int kF1Threads = kDecThreads;
 constexpr int kF1Waves = kDecWaves;
-constexpr int kF1Depth = kDecDepth;          // stages in a wave's ring
 constexpr int kF1StageW = kDecStageW;        // 8 gate + 8 up rows x 128 bytes
 constexpr int kF1Stage = kDecStage;          // + the two weight scales (64 x 4-byte slots)
 constexpr int kF1Loads = kDecLoads;          // loads per wave and stage
-constexpr int kF1XLoads = kF1TokBytes / 8 / kF1Threads;  // 16-byte (8-value) activation loads per thread
 
 // Grid barrier of the one-launch layer: per workgroup the epoch (launch
 // count) it has reached, the epoch workgroup 0 has released, and a sticky
@@ -77,13 +77,20 @@ __device__ __forceinline__ void flag_wait(const unsigned* a, unsigned v) {
   }
 }
 
-template <int FMT, bool FUSED>
+// DEPTH: stages in a wave's ring, kDecDepth; or 4 in the wide variant of the
+// one-launch layer, whose LDS then holds kF1TokBytesWide of token codes.
+template <int FMT, bool FUSED, int DEPTH>
 __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerArgs a) {
+  constexpr bool kWide = DEPTH != kDecDepth;
+  static_assert(!kWide || (DEPTH == 4 && FUSED), "the wide variant: one-launch layer, 4 stages");
+  constexpr int kTokBytes = kWide ? kF1TokBytesWide : kF1TokBytes;
+  constexpr int kMaxScales = kWide ? kF1MaxScalesWide : kF1MaxScales;
+  constexpr int kXLoads = kTokBytes / 8 / kF1Threads;  // 16-byte (8-value) activation loads per thread
   const DecodeFc1Args& p = a.f1;
   const DownCombineArgs& q = a.f2;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kF1Waves * kF1Depth * kF1Stage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[kF1TokBytes];  // codes, row stride H + 16
-  __shared__ float s_xs[kF1MaxScales];    // token scale of (token, K block) at t * KB + kb
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kF1Waves * DEPTH * kF1Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[kTokBytes];  // codes, row stride H + 16
+  __shared__ float s_xs[kMaxScales];    // token scale of (token, K block) at t * KB + kb
   __shared__ int s_e[kDcMaxPairs];        // live entry (in expert order) -> expert
   __shared__ int s_cnt[kDcMaxPairs];      //   its live rows
   __shared__ int s_c0[kDcMaxPairs];       //   its first compact row
@@ -115,9 +122,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const unsigned epoch = FUSED ? flag_load(&g_dl_flag[blockIdx.x]) + 1u : 0u;
   const int t_live = p.t_live_dev ? min(max(scalar_load(p.t_live_dev), 0), p.t_cap) : p.t_cap;
   const int n_chunks = p.t_cap * H / 8;  // 16-byte chunks of x
-  uint4 xr[kF1XLoads];
+  uint4 xr[kXLoads];
 #pragma unroll
-  for (int k = 0; k < kF1XLoads; ++k) {
+  for (int k = 0; k < kXLoads; ++k) {
     const int ci = min(tid + k * kF1Threads, n_chunks - 1);
     xr[k] = *reinterpret_cast<const uint4*>(p.x + static_cast<int64_t>(ci) * 8);
   }
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const int kb_lo = (wave % S) * kbs, kb_hi = kb_lo + kbs;
   const int my_tasks = gl < t_hi - t_lo ? (t_hi - t_lo - 1 - gl) / NG + 1 : 0;
   const int total = my_tasks * kbs;  // stages of this wave
-  uint8_t* ring = s_ring + wave * (kF1Depth * kF1Stage);
+  uint8_t* ring = s_ring + wave * (DEPTH * kF1Stage);
   const int grow = lane >> 3;
   const int chunk_lo = ((lane & 7) ^ ((grow >> 1) & 7)) << 4;        // slab row grow
   const int chunk_hi = ((lane & 7) ^ (((grow + 8) >> 1) & 7)) << 4;  // slab row grow + 8
@@ -301,10 +308,10 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     }
   };
   if (total > 0) i_set();
-  // Stream start: always kF1Depth - 1 stages; past the wave's last stage the
+  // Stream start: always DEPTH - 1 stages; past the wave's last stage the
   // stand-ins repeat it (or the initial addresses) and are never read.
 #pragma unroll
-  for (int d = 0; d < kF1Depth - 1; ++d) {
+  for (int d = 0; d < DEPTH - 1; ++d) {
     issue_stage(ring + d * kF1Stage);
     if (d + 1 < total) advance();
   }
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   // them to the workspace); 16 lanes per group, as moe_act_quant
   const int l16 = tid & 15;
 #pragma unroll
-  for (int k = 0; k < kF1XLoads; ++k) {
+  for (int k = 0; k < kXLoads; ++k) {
     const int ci = tid + k * kF1Threads;
     if (ci >= n_chunks) break;  // whole 16-lane groups (512 is a multiple of 16)
     const int gid = ci >> 4;
@@ -349,15 +356,15 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const double lim = p.act_limit;
   for (int s = 0; s < total; ++s) {
-    // Stages issued after s: kF1Depth - 2, or max(kF1Depth - 2, total - 1) - s
-    // near the end (the start always issues kF1Depth - 1), as in
+    // Stages issued after s: DEPTH - 2, or max(DEPTH - 2, total - 1) - s
+    // near the end (the start always issues DEPTH - 1), as in
     // fc2_stream_block.
-    if (s + kF1Depth - 2 >= total)
-      wait_stages<kF1Loads>(max(kF1Depth - 2, total - 1) - s);
+    if (s + DEPTH - 2 >= total)
+      wait_stages<kF1Loads>(max(DEPTH - 2, total - 1) - s);
     else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kF1Loads * (kF1Depth - 2)));
-    const int prev = slot == 0 ? kF1Depth - 1 : slot - 1;
-    if (s + kF1Depth - 1 < total) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kF1Loads * (DEPTH - 2)));
+    const int prev = slot == 0 ? DEPTH - 1 : slot - 1;
+    if (s + DEPTH - 1 < total) {
       issue_stage(ring + prev * kF1Stage);
       advance();
     }
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
       ++c_iter;
       if (c_task < t_hi) c_set();
     }
-    slot = slot == kF1Depth - 1 ? 0 : slot + 1;
+    slot = slot == DEPTH - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
   if constexpr (FUSED) {
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     if (has_cb) {
       fc2_quant_rows<FMT, true>(t, wave, lane, p.act_out, I, s_tok, s_sa, blockIdx.x == 0, q.hq, q.hs,
                                 q.row_cap, nullptr, nullptr, nullptr);
-      st.start(cb * 16, kDecPreStages, kDecDepth - 1);
+      st.start(cb * 16, kDecPreStages, DEPTH - 1);
     }
     // ---- 6. stream and combine per column block
     for (; cb < n_cb; cb += G) {
@@ -488,9 +495,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
       if (cb != static_cast<int>(blockIdx.x)) {
         for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;
         lds_barrier();  // zeroed slots visible
-        st.start(n0, 0, kDecDepth - 1);
+        st.start(n0, 0, DEPTH - 1);
       }
-      fc2_stream_block(st, n0, t, s_tok, s_sa, s_slot, lane);
+      fc2_stream_block<DEPTH>(st, n0, t, s_tok, s_sa, s_slot, lane);
       lds_barrier();  // every slot of this column block written
       fc2_combine(t, s_slot, t_live, TK, p.row_cap, H, n0, q.out, q.y, tid);
       lds_barrier();  // slots free for the next column block
@@ -509,47 +516,56 @@ hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream) {
   l.f1 = a;
   const dim3 grid(static_cast<unsigned>(device_cu_count()));
   if (a.fmt == kFp32)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, false>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
   else if (a.fmt == kFp32Pow2)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, false>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
   else
-    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, false>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
   return hipGetLastError();
 }
 
 // The grid barrier needs every workgroup resident at once: one per CU, at
 // most kDlMaxGrid, and the same grid on every launch on a device (the
-// epochs count launches per workgroup).
-int decode_layer_grid() {
-  static std::atomic<int> cache[64];
+// epochs count launches per workgroup; both variants use that grid).
+int decode_layer_grid(bool wide) {
+  static std::atomic<int> cache[2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int v = cache[dev].load(std::memory_order_relaxed);
+  int v = cache[wide][dev].load(std::memory_order_relaxed);
   if (v != 0) return v > 0 ? v : 0;
   int cus = 0, occ = 0;
+  const hipError_t e =
+      wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, 4>, kF1Threads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, kDecDepth>, kF1Threads, 0);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true>, kF1Threads, 0) !=
-          hipSuccess ||
-      cus < 1 || cus > kDlMaxGrid || occ < 1)
+      e != hipSuccess || cus < 1 || cus > kDlMaxGrid || occ < 1)
     v = -1;
   else
     v = cus;
-  cache[dev].store(v, std::memory_order_relaxed);
+  cache[wide][dev].store(v, std::memory_order_relaxed);
   return v > 0 ? v : 0;
 }
 
 hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream) {
   if (a.f1.t_cap == 0) return hipSuccess;
-  const int grid = decode_layer_grid();
+  const bool wide = decode_layer_wide(a.f1.t_cap, a.f1.hidden);
+  const int grid = decode_layer_grid(wide);
   if (!decode_layer_fits(a.f1.t_cap, a.f1.topk, a.f1.hidden, a.f1.inter) || grid < 1 ||
       a.f1.num_experts > kMaxExperts || a.f1.num_experts < 1 || a.f1.align_rows < 1)
     return hipErrorInvalidValue;
-  if (a.f1.fmt == kFp32)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
-  else if (a.f1.fmt == kFp32Pow2)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+  auto launch = [&](auto depth) {
+    constexpr int D = decltype(depth)::value;
+    if (a.f1.fmt == kFp32)
+      hipLaunchKernelGGL((fc1_decode_kernel<kFp32, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+    else if (a.f1.fmt == kFp32Pow2)
+      hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+  };
+  if (wide)
+    launch(std::integral_constant<int, 4>{});
   else
-    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, true>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+    launch(std::integral_constant<int, kDecDepth>{});
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ struct DecodeTables {
 // One wave's FC2 weight stream over a column block: the 16 x I slab of every
 // kDecWaves-th entry, one stage per 128-wide K block. Stand-ins (valid
 // addresses) fill the stages past the wave's last one that the stream start
-// issues, so that it always issues kDecDepth - 1 stages.
+// issues, so that it always issues (ring depth) - 1 stages.
 struct Fc2Stream {
   const uint8_t* w;       // [E, H, I] E4M3
   const float* w_scales;  // [E, H/128, I/128]
@@ -112,7 +112,8 @@ struct Fc2Stream {
     }
   }
   // Stages d0..d1-1 of the stream start of column block n0 (d0 == 0 resets
-  // the stream); the start as a whole issues stages 0..kDecDepth-2.
+  // the stream); the start as a whole issues stages 0..DEPTH-2 of the ring
+  // it runs on (kDecDepth, or 4 in the wide one-launch layer).
   __device__ __forceinline__ void start(int n0, int d0, int d1) {
     if (d0 == 0) {
       ent = wave;
@@ -225,10 +226,12 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
   asm volatile("" ::: "memory");
 }
 
-// The stream of one column block (started with Fc2Stream::start): wait for
+// The stream of one column block (started with Fc2Stream::start on a ring of
+// DEPTH stages, so the start issued DEPTH - 1 of them): wait for
 // stage s, refill the slot of stage s - 1, compute s; after an entry's last
 // K block its live rows' BF16-rounded results go to their pairs' slots.
 // Ends with the wave's loads drained.
+template <int DEPTH>
 __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const DecodeTables& t,
                                                  const uint8_t* tok, const float* sa, float* slot,
                                                  int lane) {
@@ -247,17 +250,17 @@ __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const De
 #pragma unroll
   for (int m = 0; m < kDecTiles; ++m) acc[m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int s = 0; s < st.total; ++s) {
-    // The start issued kDecDepth - 1 stages (stand-ins past the end) and
+    // The start issued DEPTH - 1 stages (stand-ins past the end) and
     // every step one more while any remain, so the stages issued after s
-    // number kDecDepth - 2 in the steady state and max(kDecDepth - 2,
+    // number DEPTH - 2 in the steady state and max(DEPTH - 2,
     // total - 1) - s near the end; operations issued among them only make
     // the wait stricter (they retire in order).
-    if (s + kDecDepth - 2 >= st.total)
-      wait_stages<kDecLoads>(max(kDecDepth - 2, st.total - 1) - s);
+    if (s + DEPTH - 2 >= st.total)
+      wait_stages<kDecLoads>(max(DEPTH - 2, st.total - 1) - s);
     else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDecLoads * (kDecDepth - 2)));
-    const int prev = slotn == 0 ? kDecDepth - 1 : slotn - 1;
-    if (s + kDecDepth - 1 < st.total) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDecLoads * (DEPTH - 2)));
+    const int prev = slotn == 0 ? DEPTH - 1 : slotn - 1;
+    if (s + DEPTH - 1 < st.total) {
       st.issue(st.ring + prev * kDecStage);
       st.advance(n0);
     }
@@ -309,7 +312,7 @@ __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const De
         e_c0 = __builtin_amdgcn_readfirstlane(t.c0[e_ent]);
       }
     }
-    slotn = slotn == kDecDepth - 1 ? 0 : slotn + 1;
+    slotn = slotn == DEPTH - 1 ? 0 : slotn + 1;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
 }

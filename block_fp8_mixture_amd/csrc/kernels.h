@@ -154,8 +154,19 @@ hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream);
 // barrier's epochs live in device globals.
 constexpr int kDlMaxGrid = 1024;
 
+// Its variant for more token bytes: a 4-deep weight ring per wave instead
+// of 6 leaves room for t_cap x (H + 16) codes within kF1TokBytesWide and
+// t_cap x H/128 scales within kF1MaxScalesWide (e.g. 8 tokens of H = 7168).
+constexpr int kF1TokBytesWide = 61440;
+constexpr int kF1MaxScalesWide = 512;
+
+inline bool decode_layer_wide(int64_t t_cap, int64_t hidden) {
+  return t_cap * (hidden + 16) > kF1TokBytes || t_cap * (hidden / 128) > kF1MaxScales;
+}
+
 inline bool decode_layer_fits(int64_t t_cap, int64_t topk, int64_t hidden, int64_t inter) {
-  return fc1_decode_fits(t_cap, topk, hidden, inter) && hidden % 16 == 0;
+  return down_combine_fits(t_cap, topk, inter) && hidden % 16 == 0 &&
+         t_cap * (hidden + 16) <= kF1TokBytesWide && t_cap * (hidden / 128) <= kF1MaxScalesWide;
 }
 
 struct DecodeLayerArgs {
@@ -165,8 +176,9 @@ struct DecodeLayerArgs {
 
 hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream);
 // Grid of launch_decode_layer on the current device (one workgroup per CU),
-// or 0 where its workgroups cannot all be resident.
-int decode_layer_grid();
+// or 0 where its workgroups cannot all be resident; `wide`: the variant
+// decode_layer_wide selects.
+int decode_layer_grid(bool wide);
 // Waits at the grid barrier that gave up (sticky, per device).
 hipError_t decode_layer_timeouts(uint32_t* out);
 

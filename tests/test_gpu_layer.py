@@ -306,6 +306,53 @@ def test_one_launch_layer_wide_routing(t_live, fmt):
     say(f"  layer max err / max|ref| = {err:.3e}")
 
 
+# The one-launch layer's variant with a 4-deep weight ring, for token codes
+# beyond the 6-deep layout's 24 KB of LDS (up to 60 KB and 512 scales).
+MANY_TOKENS = [
+    # t_cap, t_live, E, H, I, topk, fmt, act, limit
+    (8, 8, 256, 6144, 256, 8, "fp32", "swiglu", float("inf")),      # the sweep shape at 8 tokens
+    (8, 7, 64, 7168, 256, 8, "ue8m0", "swiglu_clamp", 7.0),         # 56 KB of codes, 448 scales
+    (16, 13, 96, 3584, 256, 4, "pow2", "swiglu_clamp_after_silu", 7.0),  # 16 tokens
+]
+
+
+@pytest.mark.parametrize("t_cap,t_live,E,H,I,K,fmt,act,lim", MANY_TOKENS)
+def test_one_launch_layer_many_token_bytes(t_cap, t_live, E, H, I, K, fmt, act, lim):
+    assert t_cap * (H + 16) > 24576 and t_cap * (H + 16) <= 61440 and t_cap * (H // 128) <= 512
+    cfg = synth.Workload(name="many", index=10 + t_cap + H % 1000, num_experts=E, hidden=H, inter=I,
+                         topk=K, tokens=(t_cap,), t_cap=t_cap, align_rows=16, row_cap=0,
+                         scale_fmts=(fmt,))
+    say(f"one-launch layer, wide ring: t_cap={t_cap} t_live={t_live} E={E} H={H} I={I} top-{K} {fmt} {act}")
+    x, ids, w = synth.make_workload(cfg, t_cap)
+    ew = synth.ExpertWeights(cfg)
+    w1q = np.zeros((E, 2 * I, H), np.uint8)
+    w1s = np.zeros((E, 2 * I // 128, H // 128), np.float32)
+    w2q = np.zeros((E, H, I), np.uint8)
+    w2s = np.zeros((E, H // 128, I // 128), np.float32)
+    for e in np.unique(ids):  # only routed experts are ever read
+        (w1q[e], w1s[e]), (w2q[e], w2s[e]) = ew.fc1(e), ew.fc2(e)
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, cfg.align_rows, 0, fmt)
+    assert lay["act"] < lay["total"]  # the decode path
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    out = torch.full((t_cap, H), POISON_BF16, dtype=torch.int16, device=dev())
+    lim32 = float(np.float32(lim))
+    for rep in range(2):  # the barrier's epochs advance per launch
+        moe.moe_forward(up(x), up(ids), up(w), up(w1q), up(w1s), up(w2q), up(w2s), fmt, act=act,
+                        clamp_limit=lim32, align_rows=cfg.align_rows,
+                        t_live=up(np.array([t_live], np.int32)), out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert moe.moe_barrier_timeouts() == 0
+    al = oracle.align(ids, t_live, E, cfg.align_rows)
+    assert np.array_equal(_ws_view(ws, lay, "expert_counts", np.int32, (E,)), al["counts"])
+    assert np.array_equal(_ws_view(ws, lay, "expert_offsets", np.int32, (E + 1,)), al["offsets"])
+    got = down(out)
+    assert np.all(got[t_live:] == POISON_BF16)
+    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, t_live, fmt, act=act,
+                               clamp_limit=lim32)
+    err = assert_bf16_close(got[:t_live], ref, "wide-ring layer")
+    say(f"  layer max err / max|ref| = {err:.3e}")
+
+
 def test_padded_tiles_are_skipped():
     """On the 512-capacity / 16-live workload the FC1 GEMM visits exactly the
     tiles that hold live rows, far fewer than the capacity holds."""
