@@ -174,7 +174,7 @@ def traffic_from(args, fetch_dir, write_dir):
     if args.tokens is not None:
         t_cap = t_live = args.tokens
     want = f"<{'true' if fmt == 'ue8m0' else 'false'}, true"
-    want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true>"
+    want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true,"
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _counter_rows(d, counter)
@@ -356,17 +356,12 @@ def main():
     xs_raw = ws[lay["xs"]:lay["xs"] + (H // 128) * t_cap * sb]
     xs = (xs_raw if fmt == "ue8m0" else xs_raw.view(torch.float32)).view(H // 128, t_cap)
     c1 = torch.empty((R, 2 * I), dtype=torch.int16, device=dev)
-    # On the decode path the whole layer is one kernel (the decode FC1's
-    # limits hold, so moe_forward launches the one-launch layer); it is timed
+    # On the decode path the whole layer is one kernel (within the one-launch
+    # limits moe_forward launches the one-launch layer); it is timed
     # through moe_forward on a workspace of its own. Elsewhere the dominant
     # kernel is the FC1 grouped GEMM.
     ws_f = torch.empty_like(ws)
-    try:
-        moe.moe_fc1_decode(dx, dids, d_w[0], d_w[1], I, fmt, act, lim, cfg.align_rows, 0,
-                           t_live=dlive, workspace=ws_f)
-        fused = True
-    except moe.MoeError:
-        fused = False
+    fused = moe.decode_layer_applies(t_cap, K, H, I)
     out_f = torch.empty_like(out)
 
     # The kernel alone, back to back over rotating copies of its weights: the
@@ -411,7 +406,8 @@ def main():
     kname = ("gemm_tiled_kernel" if tiled else "gemm_stream_kernel") + \
         f"<{'true' if fmt == 'ue8m0' else 'false'}, true> (FC1)"
     if fused:
-        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true> "
+        wide = t_cap * (H + 16) > 24576 or t_cap * (H // 128) > 256  # the 4-deep ring variant
+        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true, {4 if wide else 6}> "
                  "(the whole decode layer: routing, activation quantization, FC1, SiLU, "
                  "grid barrier, FC2, top-k combine)")
     if tiled:

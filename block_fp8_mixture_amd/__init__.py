@@ -14,11 +14,12 @@ is missing, importing the binding's functions raises -- there is no fallback.
 from ._binding import (ACTS, SCALE_FMTS, MoeError, library_path, load_library, moe_act_quant,
                        moe_align, moe_barrier_timeouts, moe_fc1_decode, moe_forward, moe_grouped_gemm_fp8, moe_min_row_cap,
                        moe_silu_mul_quant, moe_status_string, moe_topk_combine,
-                       moe_workspace_bytes, moe_workspace_plan, GEMM_TILES)
+                       moe_workspace_bytes, moe_workspace_plan, GEMM_TILES, DECODE_LIMITS,
+                       decode_layer_applies)
 
 __all__ = [
     "ACTS", "SCALE_FMTS", "MoeError", "library_path", "load_library", "moe_act_quant",
     "moe_align", "moe_barrier_timeouts", "moe_fc1_decode", "moe_forward", "moe_grouped_gemm_fp8", "moe_min_row_cap",
     "moe_silu_mul_quant", "moe_status_string", "moe_topk_combine", "moe_workspace_bytes",
-    "moe_workspace_plan", "GEMM_TILES",
+    "moe_workspace_plan", "GEMM_TILES", "DECODE_LIMITS", "decode_layer_applies",
 ]

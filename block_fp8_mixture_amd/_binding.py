@@ -14,6 +14,19 @@ ACTS = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_clamp_after_silu": 2}
 # Row-tile geometry of the grouped GEMM (mirrors the header's macros), used to
 # interpret the tiles_visited counter.
 GEMM_TILES = {"stream_tile_m": 16, "stream_max_rows": 64, "tiled_tile_m": 256, "col_tile": 128}
+# Limits of moe_forward's decode path and of its one-launch form (mirrors the
+# header's MOE_DECODE_* macros).
+DECODE_LIMITS = {"max_pairs": 64, "fc2_row_bytes": 24576, "fc2_max_scales": 256,
+                 "layer_token_bytes": 61440, "layer_max_scales": 512}
+
+
+def decode_layer_applies(t_cap, topk, hidden, inter):
+    """Whether moe_forward runs this problem as its one-launch decode layer."""
+    d, p = DECODE_LIMITS, t_cap * topk
+    return (1 <= p <= d["max_pairs"] and p * (inter + 16) <= d["fc2_row_bytes"]
+            and p * (inter // 128) <= d["fc2_max_scales"] and hidden % 16 == 0
+            and t_cap * (hidden + 16) <= d["layer_token_bytes"]
+            and t_cap * (hidden // 128) <= d["layer_max_scales"])
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "capacity too small",
            4: "HIP runtime error"}

@@ -8,6 +8,12 @@
 #include "../../include/moe_fp8.h"
 #include "kernels.h"
 
+static_assert(MOE_DECODE_MAX_PAIRS == moe::kDcMaxPairs && MOE_DECODE_FC2_ROW_BYTES == moe::kDcTokBytes &&
+                  MOE_DECODE_FC2_MAX_SCALES == moe::kDcMaxScales &&
+                  MOE_DECODE_LAYER_TOKEN_BYTES == moe::kF1TokBytesWide &&
+                  MOE_DECODE_LAYER_MAX_SCALES == moe::kF1MaxScalesWide,
+              "the header's decode limits are the kernels'");
+
 namespace moe {
 
 int device_cu_count() {

@@ -255,17 +255,33 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* layout
 /* Bytes of workspace moe_forward needs for `p` (0 if `p` is invalid). */
 size_t moe_workspace_bytes(const moe_problem* p);
 
+/* Limits of moe_forward's decode path and of its one-launch form, on
+ * P = t_cap*topk routed pairs of capacity: the decode path needs
+ * P <= MOE_DECODE_MAX_PAIRS, P*(I+16) <= MOE_DECODE_FC2_ROW_BYTES and
+ * P*I/128 <= MOE_DECODE_FC2_MAX_SCALES (the quantized FC2 input rows in
+ * LDS); the one launch also needs t_cap*(H+16) <= MOE_DECODE_LAYER_TOKEN_BYTES,
+ * t_cap*H/128 <= MOE_DECODE_LAYER_MAX_SCALES (all tokens' codes and scales in
+ * LDS) and H a multiple of 16. moe_fc1_decode's token limits are 24576 bytes
+ * and 256 scales. */
+#define MOE_DECODE_MAX_PAIRS 64
+#define MOE_DECODE_FC2_ROW_BYTES 24576
+#define MOE_DECODE_FC2_MAX_SCALES 256
+#define MOE_DECODE_LAYER_TOKEN_BYTES 61440
+#define MOE_DECODE_LAYER_MAX_SCALES 512
+
 /* The whole expert layer: align -> act_quant -> FC1 -> silu_mul_quant -> FC2
  * -> topk_combine, enqueued on one stream with no host synchronization
  * (vLLM PR #59128, SM100 on B200: the full-expert benchmark scope; the layer
  * replays inside a captured graph with the token count on the device).
  * On the decode path (see moe_workspace_layout.act) the launches are fewer
  * (TensorRT-LLM PR #21250, description: at decode sizes each launch's fixed
- * cost counts). When moe_fc1_decode's limits hold and H is a multiple of 16,
+ * cost counts). Within the one-launch limits above (MOE_DECODE_LAYER_*),
  * the layer is ONE launch: one workgroup per CU runs routing, activation
  * quantization and FC1 with SiLU(gate)*up, meets the others at a barrier
  * across the grid, then runs FC2 with the top-k combine for its output
- * columns. That launch needs all its workgroups resident at once, so calls
+ * columns (beyond moe_fc1_decode's token limits, with a 4-deep instead of a
+ * 6-deep weight ring per wave). That launch needs all its workgroups
+ * resident at once, so calls
  * on one device must not overlap in time (one stream, or ordered streams),
  * and the GPU should not be shared with work that holds CUs for long (see
  * moe_barrier_timeouts). Otherwise the decode path takes two or three

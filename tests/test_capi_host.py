@@ -194,3 +194,34 @@ def test_decode_plan_lays_out_act_and_fc1_decode_validates(lib):
     l8 = B._Layout()
     assert lib.moe_workspace_plan(ctypes.byref(p8), ctypes.byref(l8)) == OK and l8.act < l8.total
     assert f(ctypes.byref(p8), ctypes.byref(t), FAKE, l8.total, NULL) == UNSUPPORTED
+
+
+def _header_macros(prefix):
+    return {m: int(v) for m, v in re.findall(r"#define (" + prefix + r"[A-Z0-9_]+) (\d+)", open(HEADER).read())}
+
+
+def test_python_mirrors_of_header_limits():
+    g = _header_macros("MOE_GEMM_")
+    assert moe.GEMM_TILES == {"stream_tile_m": g["MOE_GEMM_STREAM_TILE_M"],
+                              "stream_max_rows": g["MOE_GEMM_STREAM_MAX_ROWS"],
+                              "tiled_tile_m": g["MOE_GEMM_TILED_TILE_M"],
+                              "col_tile": g["MOE_GEMM_COL_TILE"]}
+    d = _header_macros("MOE_DECODE_")
+    assert moe.DECODE_LIMITS == {"max_pairs": d["MOE_DECODE_MAX_PAIRS"],
+                                 "fc2_row_bytes": d["MOE_DECODE_FC2_ROW_BYTES"],
+                                 "fc2_max_scales": d["MOE_DECODE_FC2_MAX_SCALES"],
+                                 "layer_token_bytes": d["MOE_DECODE_LAYER_TOKEN_BYTES"],
+                                 "layer_max_scales": d["MOE_DECODE_LAYER_MAX_SCALES"]}
+
+
+def test_decode_layer_applies_matches_the_workspace_plan(lib):
+    # The one-launch layer is a form of the decode path: whenever it applies,
+    # the plan lays out the decode path's act buffer.
+    for t_cap, k, h, i in [(4, 8, 4096, 512), (1, 8, 4096, 512), (8, 8, 6144, 256),
+                           (16, 4, 3584, 256), (8, 8, 7168, 256), (32, 2, 512, 128)]:
+        lay = moe.moe_workspace_plan(288, h, i, k, t_cap)
+        if moe.decode_layer_applies(t_cap, k, h, i):
+            assert lay["act"] < lay["total"], (t_cap, k, h, i)
+    assert moe.decode_layer_applies(8, 8, 6144, 256)       # 49 KB of token codes
+    assert not moe.decode_layer_applies(9, 7, 7168, 256)   # 64.6 KB
+    assert not moe.decode_layer_applies(4, 8, 4096, 2048)  # FC2 input rows too large
