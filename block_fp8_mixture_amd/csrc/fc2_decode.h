@@ -173,15 +173,13 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
     for (int col0 = 0; col0 < I; col0 += 512) {
       u32x4 vr[8];
       uint32_t pr = 0;
+      const void* av[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {  // columns past I (unused) load a valid stand-in
-        const float* a = act + static_cast<int64_t>(r) * I + min(col0 + 4 * (16 * u + l16), I - 4);
-        vr[u] = DEVICE_SCOPE ? gload_b128_dev(a) : gload_b128(a);
-      }
-      if (row_to_pair && col0 == 0) pr = gload_b32(row_to_pair + r);
-      asm volatile("s_waitcnt vmcnt(0)"
-                   : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]),
-                     "+v"(vr[6]), "+v"(vr[7]), "+v"(pr));
+      for (int u = 0; u < 8; ++u)  // columns past I (unused) load a valid stand-in
+        av[u] = act + static_cast<int64_t>(r) * I + min(col0 + 4 * (16 * u + l16), I - 4);
+      // The row's pair, or a stand-in (the row's first value, never used).
+      const void* pv = row_to_pair && col0 == 0 ? static_cast<const void*>(row_to_pair + r) : av[0];
+      gload9_wait<DEVICE_SCOPE>(av, pv, vr, pr);
       if (row_to_pair && col0 == 0 && row_ok && l16 == 0) {
         row[c] = r;
         pair[c] = static_cast<int>(pr);

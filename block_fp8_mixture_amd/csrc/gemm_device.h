@@ -127,32 +127,59 @@ __device__ __forceinline__ void lds_read_tile(uint32_t t0, uint32_t t1, uint32_t
 // Global loads the compiler does not track. Its wait insertion does not
 // count direct-to-LDS loads as later vector-memory operations, so a register
 // load issued before them would be waited for with vmcnt(0), draining the
-// weight stream; these are waited for by an explicit s_waitcnt in assembly
-// that names their registers.
+// weight stream; these are issued and waited for inside assembly instead.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x4 gload_b128(const void* a) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(a));
-  return r;
-}
-__device__ __forceinline__ uint32_t gload_b32(const void* a) {
-  uint32_t r;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(a));
-  return r;
+
+// Eight 16-byte loads and one 4-byte load that have all landed when the
+// statement ends: issued and waited for (vmcnt(0)) in one assembly
+// statement, so no compiler-scheduled code can move or reuse their
+// registers while they are in flight. DEVICE: read at device scope (sc1).
+template <bool DEVICE>
+__device__ __forceinline__ void gload9_wait(const void* const (&a)[8], const void* b, u32x4 (&v)[8],
+                                            uint32_t& w) {
+  if constexpr (DEVICE)
+    asm volatile(
+        "global_load_dwordx4 %0, %9, off sc1\n\t"
+        "global_load_dwordx4 %1, %10, off sc1\n\t"
+        "global_load_dwordx4 %2, %11, off sc1\n\t"
+        "global_load_dwordx4 %3, %12, off sc1\n\t"
+        "global_load_dwordx4 %4, %13, off sc1\n\t"
+        "global_load_dwordx4 %5, %14, off sc1\n\t"
+        "global_load_dwordx4 %6, %15, off sc1\n\t"
+        "global_load_dwordx4 %7, %16, off sc1\n\t"
+        "global_load_dword %8, %17, off\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(w)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(b)
+        : "memory");
+  else
+    asm volatile(
+        "global_load_dwordx4 %0, %9, off\n\t"
+        "global_load_dwordx4 %1, %10, off\n\t"
+        "global_load_dwordx4 %2, %11, off\n\t"
+        "global_load_dwordx4 %3, %12, off\n\t"
+        "global_load_dwordx4 %4, %13, off\n\t"
+        "global_load_dwordx4 %5, %14, off\n\t"
+        "global_load_dwordx4 %6, %15, off\n\t"
+        "global_load_dwordx4 %7, %16, off\n\t"
+        "global_load_dword %8, %17, off\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7]), "=&v"(w)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(b)
+        : "memory");
 }
 
 // Data handed from one workgroup to another inside a launch, across XCDs
 // whose L2 caches are not coherent with each other: the store writes
-// through to memory (system scope), the load reads at device scope (the
-// cache bits of relaxed atomics of those scopes). Untracked, like the loads
-// above.
+// through to memory (system scope), the reader loads at device scope
+// (gload9_wait<true>) -- the cache bits of relaxed atomics of those scopes.
+// Untracked: the writer waits for it explicitly.
 __device__ __forceinline__ void gstore_b128_wt(void* a, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" ::"v"(a), "v"(v) : "memory");
-}
-__device__ __forceinline__ u32x4 gload_b128_dev(const void* a) {
-  u32x4 r;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(r) : "v"(a));
-  return r;
 }
 
 }  // namespace moe
