@@ -21,7 +21,9 @@
 //     tasks' 2 KB weight stages and their two weight block scales through a
 //     private LDS ring by direct-to-LDS loads (whole 128-byte lines); a wave
 //     only waits for its own loads, so the loop has no workgroup barrier.
-//     Token fragments come from the resident LDS copy.
+//     Token fragments come from the resident LDS copy. The ring is 6 stages
+//     deep, or 4 in the one-launch layer's variant for up to 60 KB of token
+//     codes (the LDS the two stages free holds them).
 //  3. Epilogue of a task. One cross-lane swap pairs gate and up values; C1
 //     gets both BF16 halves, and act the fp32 SiLU(gate) * up of the
 //     BF16-rounded pair (fp64 inside, rounded once).

@@ -25,10 +25,11 @@
 //    K-split partial sums are added in a fixed order through LDS. This is the
 //    weight-streaming (HBM-bound) path.
 //  * gemm_tiled_kernel -- experts with more rows: persistent, XCD-grouped
-//    256 x 256 tiles on v_mfma_f32_32x32x64_f8f6f4, operands staged through
-//    a 4-deep LDS ring of 64-byte K stages by direct-to-LDS loads, scales
-//    applied by rescaling the accumulator once per 128-wide block (details at
-//    the kernel).
+//    256 x 256 tiles (256 x 128 or 256 x 64 when wide tiles would leave CUs
+//    idle, picked on the device) on v_mfma_f32_32x32x64_f8f6f4, operands
+//    staged through a 4-deep LDS ring of 64-byte K stages by direct-to-LDS
+//    loads, scales applied by rescaling the accumulator once per 128-wide
+//    block (details at the kernel).
 #include <type_traits>
 
 #include "device_common.h"
