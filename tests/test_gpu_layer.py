@@ -353,6 +353,34 @@ def test_one_launch_layer_many_token_bytes(t_cap, t_live, E, H, I, K, fmt, act, 
     say(f"  layer max err / max|ref| = {err:.3e}")
 
 
+def test_one_launch_variants_alternate():
+    """The 6-deep and 4-deep ring variants of the one-launch layer share the
+    grid barrier's epochs: launches alternating between them (and repeated)
+    stay correct and no barrier wait gives up."""
+    cases = []
+    for t_cap, H, idx in [(2, 1024, 30), (8, 4096, 31)]:  # 2 x 1040 B / 8 x 4112 B of codes
+        cfg = synth.Workload(name="alt", index=idx, num_experts=16, hidden=H, inter=256, topk=8,
+                             tokens=(t_cap,), t_cap=t_cap, align_rows=16, row_cap=0,
+                             scale_fmts=("fp32",))
+        x, ids, w = synth.make_workload(cfg, t_cap)
+        ew = synth.ExpertWeights(cfg)
+        (w1q, w1s), (w2q, w2s) = ew.stacked()
+        lay = moe.moe_workspace_plan(16, H, 256, 8, t_cap)
+        assert moe.decode_layer_applies(t_cap, 8, H, 256)
+        ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), 16, t_cap, "fp32")
+        dev_in = [up(a) for a in (x, ids, w, w1q, w1s, w2q, w2s)]
+        ws = torch.empty((lay["total"],), dtype=torch.uint8, device=dev())
+        cases.append((t_cap, H, dev_in, ws, ref))
+    say("one-launch layer: 6-deep and 4-deep ring launches alternating")
+    for order in (0, 1, 0, 0, 1, 1, 0):
+        t_cap, H, dev_in, ws, ref = cases[order]
+        out = torch.full((t_cap, H), POISON_BF16, dtype=torch.int16, device=dev())
+        moe.moe_forward(*dev_in, "fp32", out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert moe.moe_barrier_timeouts() == 0
+        assert_bf16_close(down(out), ref, f"one-launch layer t_cap={t_cap} H={H}")
+
+
 def test_padded_tiles_are_skipped():
     """On the 512-capacity / 16-live workload the FC1 GEMM visits exactly the
     tiles that hold live rows, far fewer than the capacity holds."""
