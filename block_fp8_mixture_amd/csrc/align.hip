@@ -139,7 +139,9 @@ __device__ __forceinline__ void align_block(
     if (ok) atomicOr(&mask[wave * kMaskExperts + e], 1ull << lane);
     // The LDS runs a wave's instructions in order, so the read sees the
     // bits of every lane of this wave.
-    if (ok) rank = __popcll(mask[wave * kMaskExperts + e] & below);
+    if (ok)
+      rank = __popcll(__hip_atomic_load(&mask[wave * kMaskExperts + e], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP) & below);
     __syncthreads();
     if (ok) {
 #pragma unroll
