@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--config", default="decode",
                     choices=["tiny", "decode", "padded", "full", "sweep"])
     ap.add_argument("--tokens", type=int, default=None, help="live tokens (default per config)")
+    ap.add_argument("--t-cap", type=int, default=None,
+                    help="token capacity (default: the config's, or --tokens); live tokens are capped by it")
     ap.add_argument("--fmt", default=None, help="activation scale format")
     ap.add_argument("--act", default="swiglu")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,6 +175,9 @@ def traffic_from(args, fetch_dir, write_dir):
     t_cap, t_live = DEFAULT_TOKENS[args.config]
     if args.tokens is not None:
         t_cap = t_live = args.tokens
+    if args.t_cap is not None:
+        t_cap = args.t_cap
+        t_live = min(t_live, t_cap)
     want = f"<{'true' if fmt == 'ue8m0' else 'false'}, true"
     want_dec = f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true,"
     out = {}
@@ -247,6 +252,9 @@ def main():
     t_cap, t_live = DEFAULT_TOKENS[args.config]
     if args.tokens is not None:
         t_cap = t_live = args.tokens
+    if args.t_cap is not None:
+        t_cap = args.t_cap
+        t_live = min(t_live, t_cap)
     fmt = args.fmt or cfg.scale_fmts[0]
     act = args.act
     lim = 7.0 if act != "swiglu" else float("inf")
