@@ -228,7 +228,13 @@ def cpu_baseline(cfg, x, ids, w, t_live, fmt, act, weights):
         oracle.forward(x, ids, w, (w1q, w1s), (w2q, w2s), t_live, cfg.align_rows, fmt, act)
         runs.append(time.perf_counter() - t0)
     med = statistics.median(runs)
+    try:  # the BLAS the oracle's fp64 GEMMs ran on
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # an older numpy without the dict form
+        blas = "unknown"
     return {"value": med * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
+            "blas": blas,
             "sample": f"whole layer, {t_live} tokens of the benchmarked workload, median of "
                       f"{len(runs)} run(s) of oracle.forward (numpy fp64)"}
 
