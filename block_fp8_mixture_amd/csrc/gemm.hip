@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads, kSGroupsPerCu) void gemm_stream_kernel(Ge
       int ra = k.row0 + first + ta, rb = k.row0 + first + tb, rs = k.row0 + first + tok;
       if constexpr (GATHER) {
         int ma = 0, mb = 0, ms = 0;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kStreamTileM; ++i) {
           const int r = k.row0 + first + i < last ? k.row0 + first + i : last;
           const int v = scalar_load(p.a_row_map + r);
@@ -547,6 +547,11 @@ constexpr int TM = kTiledTileM;   // token rows per tile (256)
 constexpr int TN = 256;           // weight rows per tile (the narrow variant: 64)
 constexpr int SK = 64;            // K bytes per pipeline stage (half a scale block)
 constexpr int kTiledThreads = 512;
+// Largest K whose 256-wide tiles stage their output through LDS before
+// storing it (whole 16-byte row chunks instead of 8-byte pieces spread over
+// 32 rows). Measured on the 7168 x 2048 layer: K = 2048 tiles 9% faster,
+// K = 7168 tiles 4% slower (the main loop schedules worse with it).
+constexpr int kStagedOutMaxK = 4096;
 constexpr int kStageA = TM * SK;              // token part of a stage (16 KB)
 constexpr int kStageBytes = (TM + TN) * SK;   // 32 KB
 constexpr int kGroupN = 8;                    // n-tiles per scheduling group
@@ -611,7 +616,7 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // into it; the epilogue multiplies by the last s. One VALU multiply per
 // element and block, no temporaries, no wait on an MFMA result. Power-of-two
 // ratios are exact.
-template <bool UE8M0, bool GATHER, int TNT, bool PICK>
+template <bool UE8M0, bool GATHER, int TNT, bool PICK, bool SOUT>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
   static_assert(TNT == 256 || TNT == 128 || TNT == 64, "tile widths");
   static_assert(!PICK || TNT != 256, "the pick is between 64 and 128");
@@ -849,22 +854,83 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     __builtin_amdgcn_s_waitcnt(0);  // trailing loads of this tile done before any stage is reused
     __syncthreads();
 
-    if (wave_on) {
-      const float f = sw_norm;
-      const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
-      const float fs[2] = {sl.x * f, sl.y * f};
+    if constexpr (!SOUT) {
+      // Each lane stores its 4-column pieces straight from the accumulator.
+      if (wave_on) {
+        const float f = sw_norm;
+        const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
+        const float fs[2] = {sl.x * f, sl.y * f};
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int j = wm * 64 + tt * 32 + (lane & 31);
-        if (j < rows_here) {
-          uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * WN + 4 * (lane >> 5);
+        for (int tt = 0; tt < 2; ++tt) {
+          const int j = wm * 64 + tt * 32 + (lane & 31);
+          if (j < rows_here) {
+            uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + wn * WN + 4 * (lane >> 5);
+#pragma unroll
+            for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                v4f v = {acc[wt][tt][4 * g], acc[wt][tt][4 * g + 1], acc[wt][tt][4 * g + 2], acc[wt][tt][4 * g + 3]};
+                *reinterpret_cast<uint2*>(crow + wt * 32 + g * 8) = pack_bf16x4(v * fs[tt]);
+              }
+          }
+        }
+      }
+    } else {
+      // Output tile through the free stage buffers: each wave writes its
+      // scaled BF16 results there (row j in buffer j / kRowsPerBuf, 16-byte
+      // chunk q of the row at slot q ^ (j % kChunks), so the 32 rows of one
+      // write spread over the banks), then every wave stores whole 16-byte
+      // row chunks, 8 lanes to a 128-byte line.
+      constexpr int kRowBytes = TNT * 2;
+      constexpr int kChunks = kRowBytes / 16;
+      constexpr int kRowsPerBuf = kStageBytes / kRowBytes;
+      auto out_row = [&](int j) -> uint8_t* {
+        const int b = j / kRowsPerBuf;
+        uint8_t* base = b == 0 ? s_st0 : b == 1 ? s_st1 : b == 2 ? s_st2 : s_st3;
+        return base + (j % kRowsPerBuf) * kRowBytes;
+      };
+      if (wave_on) {
+        const float f = sw_norm;
+        const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
+        const float fs[2] = {sl.x * f, sl.y * f};
+        // j % kChunks below equals lane % min(32, kChunks); formed here behind
+        // an opaque move so the compiler does not hoist the per-chunk slot
+        // offsets out of the tile loop (they would stay live across it).
+        int sw = lane & 31 & (kChunks - 1);
+        asm volatile("" : "+v"(sw));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int j = wm * 64 + tt * 32 + (lane & 31);
+          uint8_t* row = out_row(j);
 #pragma unroll
           for (int wt = 0; wt < WT; ++wt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               v4f v = {acc[wt][tt][4 * g], acc[wt][tt][4 * g + 1], acc[wt][tt][4 * g + 2], acc[wt][tt][4 * g + 3]};
-              *reinterpret_cast<uint2*>(crow + wt * 32 + g * 8) = pack_bf16x4(v * fs[tt]);
+              const int q = (wn * WN + wt * 32 + g * 8) / 8;  // chunk of these 8 columns
+              *reinterpret_cast<uint2*>(row + ((q ^ sw) << 4) + 8 * (lane >> 5)) = pack_bf16x4(v * fs[tt]);
             }
+        }
+      }
+      __syncthreads();
+      {
+        // Pass `it` stores rows it * RPI + tr; thread (tr, tq) takes chunk tq.
+        // The row's swizzle (it * RPI + tr) % kChunks is the XOR of the two
+        // terms (RPI and kChunks are powers of two, tr < RPI).
+        constexpr int RPI = kTiledThreads / kChunks;
+        const int tq = tid % kChunks, tr = tid / kChunks;
+        int lb = tr * kRowBytes + ((tq ^ (tr % kChunks)) << 4);
+        asm volatile("" : "+v"(lb));
+        uint16_t* gc = p.c + static_cast<int64_t>(row0 + tr) * N + n0 + tq * 8;
+        int step = RPI * N;  // opaque, so per-pass offsets are not hoisted
+        asm volatile("" : "+s"(step));
+        const bool col_ok = n0 + tq * 8 < N;
+#pragma unroll
+        for (int it = 0; it < TM / RPI; ++it, gc += step) {
+          const int j0 = it * RPI;  // first row of the pass
+          const uint8_t* src = out_row(j0) + (lb ^ (((j0 % kChunks)) << 4));
+          if (col_ok && j0 + tr < rows_here)
+            *reinterpret_cast<uint4*>(gc) = *reinterpret_cast<const uint4*>(src);
         }
       }
     }
@@ -900,20 +966,22 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
     if (grid > 0) {
       const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
       const dim3 gr(grid), bl(kTiledThreads);
-      auto launch = [&](auto tnt, auto pick) {
+      auto launch = [&](auto tnt, auto pick, auto sout) {
         constexpr int W = decltype(tnt)::value;
-        constexpr bool P = decltype(pick)::value;
-        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, W, P>), gr, bl, 0, stream, g);
-        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, W, P>), gr, bl, 0, stream, g);
-        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, W, P>), gr, bl, 0, stream, g);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, W, P>), gr, bl, 0, stream, g);
+        constexpr bool P = decltype(pick)::value, S = decltype(sout)::value;
+        if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, W, P, S>), gr, bl, 0, stream, g);
+        else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, W, P, S>), gr, bl, 0, stream, g);
+        else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, W, P, S>), gr, bl, 0, stream, g);
+        else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, W, P, S>), gr, bl, 0, stream, g);
       };
       if (narrow) {
-        launch(std::integral_constant<int, 64>{}, std::true_type{});
+        launch(std::integral_constant<int, 64>{}, std::true_type{}, std::false_type{});
         if (hipGetLastError() == hipSuccess)
-          launch(std::integral_constant<int, 128>{}, std::true_type{});
+          launch(std::integral_constant<int, 128>{}, std::true_type{}, std::false_type{});
+      } else if (g.k <= kStagedOutMaxK) {
+        launch(std::integral_constant<int, TN>{}, std::false_type{}, std::true_type{});
       } else {
-        launch(std::integral_constant<int, TN>{}, std::false_type{});
+        launch(std::integral_constant<int, TN>{}, std::false_type{}, std::false_type{});
       }
       err = hipGetLastError();
     }

@@ -330,6 +330,7 @@ GEMM_SHAPES = [
     (9, 8, 8192, 256, [300] * 8, 0),                # enough tiles for 256-wide weight tiles
     (10, 8, 2048, 256, [300] * 8, 0),               # 128-wide weight tiles
     (11, 12, 1024, 512, [400] * 12, 8),             # 128-wide, gathered
+    (12, 8, 8320, 256, [300] * 7 + [211], 8),       # 256-wide, output staged in LDS; N % 256 = 128
 ]
 
 
