@@ -190,6 +190,7 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   if (need > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   const int64_t rc = p->row_cap == 0 ? need : p->row_cap;
   if (rc < need) return MOE_ERR_CAPACITY;
+  if (rc * (p->inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;  // as moe_silu_mul_quant
   if (!gemm_shape_ok(p->t_cap, 2 * static_cast<int64_t>(p->inter), p->hidden) ||
       !gemm_shape_ok(rc, p->hidden, p->inter))
     return MOE_ERR_UNSUPPORTED;

@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int64_t q = gid + k * stride < n ? gid + k * stride : gid;  // in-range stand-in
-        rows[k] = q / groups;
-        gs[k] = static_cast<int>(q % groups);
+        rows[k] = static_cast<uint32_t>(q) / static_cast<uint32_t>(groups);  // q < 2^31 (host check)
+        gs[k] = static_cast<int>(static_cast<uint32_t>(q) - static_cast<uint32_t>(rows[k]) * groups);
         const int64_t src = rows[k] * (2 * inter) + gs[k] * kGroup + l16 * 8;
         gr[k] = *reinterpret_cast<const uint4*>(gate_up + src);
         ur[k] = *reinterpret_cast<const uint4*>(gate_up + src + inter);
@@ -125,6 +125,7 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
                       uint8_t* hq, void* hs, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
+  if (groups > INT32_MAX) return hipErrorInvalidValue;  // the kernel divides 32-bit group indices
   const int64_t need = (groups + 2 * kSmqGroupsPerBlock - 1) / (2 * kSmqGroupsPerBlock);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
   const int blocks = static_cast<int>(need < cap ? need : cap);

@@ -178,7 +178,7 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
  *   gate_up  device BF16 [row_cap, 2*inter]
  *   hq       device uint8 [row_cap, inter]; hs device [inter/128][row_cap]
  *   clamp_limit  used by the clamp variants; must be > 0 there
- * Errors: INVALID_ARG. */
+ * Errors: INVALID_ARG (also when row_cap * inter / 128 exceeds 2^31 - 1). */
 moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               const int32_t* expert_counts, const int32_t* expert_offsets,
                               int32_t num_experts, int32_t row_cap, moe_act act,
