@@ -113,6 +113,7 @@ def test_silu_mul_quant_validation(lib):
     assert call(act=1, lim=float("nan")) == INVALID
     assert call(fmt=5) == INVALID
     assert call(gu=NULL) == INVALID
+    assert call(rc=1 << 24, inter=1 << 15) == INVALID  # 2^32 groups
     assert call(rc=0, gu=NULL) == OK
 
 
@@ -160,6 +161,9 @@ def test_forward_validation(lib):
     assert lib.moe_workspace_plan(ctypes.byref(_problem(num_experts=4096)),
                                   ctypes.byref(lay)) == UNSUPPORTED
     assert lib.moe_workspace_bytes(ctypes.byref(_problem(inter=0))) == 0
+    # FC2-input groups (row_cap * inter / 128) are indexed in 32 bits
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(row_cap=1 << 24, inter=1 << 15)),
+                                  ctypes.byref(lay)) == INVALID
     p = _problem()
     t = B._Tensors(*([FAKE.value] * 9))
     need = lib.moe_workspace_bytes(ctypes.byref(p))
