@@ -547,11 +547,6 @@ constexpr int TM = kTiledTileM;   // token rows per tile (256)
 constexpr int TN = 256;           // weight rows per tile (the narrow variant: 64)
 constexpr int SK = 64;            // K bytes per pipeline stage (half a scale block)
 constexpr int kTiledThreads = 512;
-// Largest K whose 256-wide tiles stage their output through LDS before
-// storing it (whole 16-byte row chunks instead of 8-byte pieces spread over
-// 32 rows). Measured on the 7168 x 2048 layer: K = 2048 tiles 9% faster,
-// K = 7168 tiles 4% slower (the main loop schedules worse with it).
-constexpr int kStagedOutMaxK = 4096;
 constexpr int kStageA = TM * SK;              // token part of a stage (16 KB)
 constexpr int kStageBytes = (TM + TN) * SK;   // 32 KB
 constexpr int kGroupN = 8;                    // n-tiles per scheduling group
@@ -616,6 +611,10 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // into it; the epilogue multiplies by the last s. One VALU multiply per
 // element and block, no temporaries, no wait on an MFMA result. Power-of-two
 // ratios are exact.
+//
+// Output (SOUT): the 256-wide kernel stages the BF16 tile in LDS and stores
+// whole 16-byte row chunks; the narrow kernels store each lane's 8-byte
+// pieces straight from the accumulators.
 template <bool UE8M0, bool GATHER, int TNT, bool PICK, bool SOUT>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
   static_assert(TNT == 256 || TNT == 128 || TNT == 64, "tile widths");
@@ -878,9 +877,11 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     } else {
       // Output tile through the free stage buffers: each wave writes its
       // scaled BF16 results there (row j in buffer j / kRowsPerBuf, 16-byte
-      // chunk q of the row at slot q ^ (j % kChunks), so the 32 rows of one
-      // write spread over the banks), then every wave stores whole 16-byte
-      // row chunks, 8 lanes to a 128-byte line.
+      // chunk q of the row at slot q ^ (j % 4), so the 32 rows of one write
+      // spread over 4 bank groups), then every wave stores whole 16-byte row
+      // chunks, 8 lanes to a 128-byte line. A wider swizzle would spread the
+      // writes further but needs a write address per chunk and lane, and
+      // those registers cost the main loop more than the bank conflicts.
       constexpr int kRowBytes = TNT * 2;
       constexpr int kChunks = kRowBytes / 16;
       constexpr int kRowsPerBuf = kStageBytes / kRowBytes;
@@ -893,10 +894,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         const float f = sw_norm;
         const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
         const float fs[2] = {sl.x * f, sl.y * f};
-        // j % kChunks below equals lane % min(32, kChunks); formed here behind
-        // an opaque move so the compiler does not hoist the per-chunk slot
-        // offsets out of the tile loop (they would stay live across it).
-        int sw = lane & 31 & (kChunks - 1);
+        // j % 4 equals lane % 4; formed here behind an opaque move so the
+        // compiler does not hoist the slot offsets out of the tile loop (they
+        // would stay live across it).
+        int sw = lane & 3;
         asm volatile("" : "+v"(sw));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -907,28 +908,30 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               v4f v = {acc[wt][tt][4 * g], acc[wt][tt][4 * g + 1], acc[wt][tt][4 * g + 2], acc[wt][tt][4 * g + 3]};
-              const int q = (wn * WN + wt * 32 + g * 8) / 8;  // chunk of these 8 columns
-              *reinterpret_cast<uint2*>(row + ((q ^ sw) << 4) + 8 * (lane >> 5)) = pack_bf16x4(v * fs[tt]);
+              // chunk of these 8 columns: q % 4 == g, so q ^ sw keeps q's
+              // upper bits (an immediate offset) and swizzles g
+              const int q = (wn * WN + wt * 32 + g * 8) / 8;
+              *reinterpret_cast<uint2*>(row + (((q & ~3) | (g ^ sw)) << 4) + 8 * (lane >> 5)) = pack_bf16x4(v * fs[tt]);
             }
         }
       }
       __syncthreads();
       {
         // Pass `it` stores rows it * RPI + tr; thread (tr, tq) takes chunk tq.
-        // The row's swizzle (it * RPI + tr) % kChunks is the XOR of the two
-        // terms (RPI and kChunks are powers of two, tr < RPI).
+        // RPI is a multiple of 4, so the row's swizzle is tr % 4 in every pass.
         constexpr int RPI = kTiledThreads / kChunks;
+        static_assert(RPI % 4 == 0, "passes start at rows divisible by 4");
         const int tq = tid % kChunks, tr = tid / kChunks;
-        int lb = tr * kRowBytes + ((tq ^ (tr % kChunks)) << 4);
+        int lb = tr * kRowBytes + ((tq ^ (tr & 3)) << 4);
         asm volatile("" : "+v"(lb));
         uint16_t* gc = p.c + static_cast<int64_t>(row0 + tr) * N + n0 + tq * 8;
         int step = RPI * N;  // opaque, so per-pass offsets are not hoisted
         asm volatile("" : "+s"(step));
         const bool col_ok = n0 + tq * 8 < N;
-#pragma unroll
+#pragma unroll 1  // unrolled, the passes' LDS reads are batched and hold more registers
         for (int it = 0; it < TM / RPI; ++it, gc += step) {
           const int j0 = it * RPI;  // first row of the pass
-          const uint8_t* src = out_row(j0) + (lb ^ (((j0 % kChunks)) << 4));
+          const uint8_t* src = out_row(j0) + lb;
           if (col_ok && j0 + tr < rows_here)
             *reinterpret_cast<uint4*>(gc) = *reinterpret_cast<const uint4*>(src);
         }
@@ -978,10 +981,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
         launch(std::integral_constant<int, 64>{}, std::true_type{}, std::false_type{});
         if (hipGetLastError() == hipSuccess)
           launch(std::integral_constant<int, 128>{}, std::true_type{}, std::false_type{});
-      } else if (g.k <= kStagedOutMaxK) {
-        launch(std::integral_constant<int, TN>{}, std::false_type{}, std::true_type{});
       } else {
-        launch(std::integral_constant<int, TN>{}, std::false_type{}, std::false_type{});
+        launch(std::integral_constant<int, TN>{}, std::false_type{}, std::true_type{});
       }
       err = hipGetLastError();
     }
