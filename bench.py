@@ -1,14 +1,15 @@
 """Benchmark of the block-scaled FP8 expert layer on one MI355X.
 
-Default workload: decode-sized layer, 288 experts, top-8, hidden 4096,
-intermediate 512, 4 tokens, fp32 activation scales, plain SwiGLU, the weights
-FP8 E4M3 with 128x128 fp32 block scales (TensorRT-LLM PR #21250,
-Performance). One step is one whole forward of the layer (align, act quant,
-FC1, SiLU*up+quant, FC2, top-k combine), replayed from a captured HIP graph
-with all inputs resident in HBM. Before every step the L2 and the 256 MB
-Infinity Cache are flushed by reading 1 GiB of unrelated data, so weights
-stream from HBM (the pages time with a cold L2, vLLM PR #59128, SM100 on
-B200). A read leaves the caches clean: flushing by writing would leave
+Default workload: the fully occupied layer, 32 experts, hidden 7168,
+intermediate 2048, top-8, 4096 live of 4096 tokens, fp32 activation scales,
+plain SwiGLU, weights FP8 E4M3 with 128x128 fp32 block scales: the
+full-expert benchmark shape of vLLM PR #59128 (SM100 on B200), the
+compute-bound case. One step is one whole forward of the layer (align, act
+quant, FC1, SiLU*up+quant, FC2, top-k combine), replayed from a captured HIP
+graph with all inputs resident in HBM. Before every step the L2 and the
+256 MB Infinity Cache are flushed by reading 1 GiB of unrelated data, so
+weights stream from HBM (the pages time with a cold L2, vLLM PR #59128, SM100
+on B200). A read leaves the caches clean: flushing by writing would leave
 dirty lines whose write-back competes with the layer's own reads.
 
 Printed: one JSON line. `value` is the median cold layer latency in
@@ -21,8 +22,10 @@ wall clock of the bracketed timed loop divided by the steps (it includes the
 flush). `roofline` describes the dominant kernel, timed on its own with HIP
 events on the stream it runs on: on the decode path the layer is one kernel
 (routing, quantization, FC1, SiLU, a grid barrier, FC2 and the combine), so
-it is that kernel; elsewhere it is the FC1 grouped GEMM.
-`cpu_baseline` is the CPU oracle on the same workload.
+it is that kernel; elsewhere it is the FC1 grouped GEMM. `per_config` holds
+the same layer span for every workload and variant, each with its live-row
+TFLOP/s and minimum-bytes HBM rate as fractions of the peaks. `cpu_baseline`
+is the CPU oracle on a bounded sample of the headline workload.
 """
 
 import argparse
@@ -38,7 +41,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
-PAGES_DECODE_T4_US = 64.7    # TensorRT-LLM PR #21250, Performance (H200, context only)
+# The pages' own latencies, other GPUs: context only, never a target.
+PAGES_CONTEXT_US = {
+    "full:4096": {"B200": 1509.025, "H200": 2646.141, "source": "vLLM PR #59128, SM100 on B200 / SM90 on H200"},
+    "padded:16": {"B200": 347.456, "H200": 438.144, "source": "vLLM PR #59128, SM100 on B200 / SM90 on H200"},
+    "decode:4": {"H200": 64.7, "source": "TensorRT-LLM PR #21250, Performance"},
+    "decode:1": {"H200": 28.7, "source": "TensorRT-LLM PR #21250, Performance"},
+    "sweep:1": {"Hopper": 36.9, "source": "vLLM PR #65794, layer-time table"},
+    "sweep:8": {"Hopper": 92.4, "source": "vLLM PR #65794, layer-time table"},
+    "sweep:64": {"Hopper": 280.9, "source": "vLLM PR #65794, layer-time table"},
+    "sweep:256": {"Hopper": 337.8, "source": "vLLM PR #65794, layer-time table"},
+    "sweep:1024": {"Hopper": 438.0, "source": "vLLM PR #65794, layer-time table"},
+    "sweep:4096": {"Hopper": 947.7, "source": "vLLM PR #65794, layer-time table"},
+}
 FLUSH_BYTES = 1 << 30
 MALL_BYTES = 256 << 20       # MI355X Infinity Cache
 CAL_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
@@ -55,7 +70,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode",
+    ap.add_argument("--config", default="full",
                     choices=["tiny", "decode", "padded", "full", "sweep"])
     ap.add_argument("--tokens", type=int, default=None, help="live tokens (default per config)")
     ap.add_argument("--t-cap", type=int, default=None,
@@ -63,6 +78,10 @@ def parse():
     ap.add_argument("--fmt", default=None, help="activation scale format")
     ap.add_argument("--act", default="swiglu")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-config latency table")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed replays per entry of the per-config table")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -211,32 +230,135 @@ def traffic_from(args, fetch_dir, write_dir):
     print(json.dumps(res))
 
 
-def cpu_baseline(cfg, x, ids, w, t_live, fmt, act, weights):
+def cpu_baseline(cfg, x, ids, w, t_live, fmt, act, lim, weights):
+    """The oracle on a bounded sample of the workload, on the host's cores.
+
+    The whole 4096-token layer would keep the oracle busy for minutes, so it
+    runs on the first S1 and S2 tokens of the same inputs (S2 = 4 S1, each
+    about 5-15 s) and the time of the full token count is extrapolated
+    linearly from those two points (the oracle's per-expert weight decoding is
+    a fixed cost, its GEMMs grow with the tokens). Small workloads run whole.
+    The BLAS threads are the process's CPU affinity set.
+    """
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     import oracle
+    cores = len(os.sched_getaffinity(0))
     (w1q, w1s), (w2q, w2s) = weights
-    runs = []
-    budget = 25.0
-    t_start = time.perf_counter()
-    while len(runs) < 3 and (time.perf_counter() - t_start) < budget:
+
+    def run(n):
         t0 = time.perf_counter()
-        oracle.forward(x, ids, w, (w1q, w1s), (w2q, w2s), t_live, cfg.align_rows, fmt, act)
-        runs.append(time.perf_counter() - t0)
-    med = statistics.median(runs)
+        oracle.forward(x[:n], ids[:n], w[:n], (w1q, w1s), (w2q, w2s), n, cfg.align_rows, fmt, act,
+                       lim)
+        return time.perf_counter() - t0
+
+    if t_live <= 64:
+        runs = [run(t_live) for _ in range(3)]
+        value = statistics.median(runs)
+        sample = (f"whole layer, all {t_live} tokens of the benchmarked workload, median of 3 runs "
+                  f"of oracle.forward (numpy fp64)")
+    else:
+        s1 = max(t_live // 32, 16)
+        s2 = 4 * s1
+        t1, t2 = run(s1), run(s2)
+        slope = (t2 - t1) / (s2 - s1)
+        value = t2 + slope * (t_live - s2)
+        sample = (f"oracle.forward (numpy fp64) on the first {s1} and {s2} of the {t_live} tokens "
+                  f"({t1:.1f} s and {t2:.1f} s), extrapolated linearly to {t_live} tokens")
     try:  # the BLAS the oracle's fp64 GEMMs ran on
         b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
         blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
     except Exception:  # an older numpy without the dict form
         blas = "unknown"
-    return {"value": med * 1e6, "unit": "us", "cores": int(threads), "kind": "oracle",
-            "blas": blas,
-            "sample": f"whole layer, {t_live} tokens of the benchmarked workload, median of "
-                      f"{len(runs)} run(s) of oracle.forward (numpy fp64)"}
+    return {"value": round(value * 1e6, 1), "unit": "us", "cores": cores, "kind": "oracle",
+            "blas": blas, "sample": sample}
+
+
+class Marks:
+    """Device-clock marks around a captured layer (bench_clock.hip)."""
+
+    def __init__(self, torch, cap):
+        import ctypes
+        self.torch = torch
+        self.lib = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
+        self.lib.moe_bench_mark.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                            ctypes.c_int, ctypes.c_void_p]
+        self.lib.moe_bench_clock_hz.restype = ctypes.c_int64
+        self.cap = cap
+        dev = torch.device("cuda", 0)
+        self.slots = torch.zeros(cap, dtype=torch.int64, device=dev)
+        self.ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def mark(self, closing):
+        if self.lib.moe_bench_mark(self.slots.data_ptr(), self.ctr.data_ptr(), self.cap,
+                                   int(closing), self.torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("device-clock mark launch failed")
+
+    def spans_us(self, n):
+        hz = self.lib.moe_bench_clock_hz()
+        m = self.slots[:2 * n].cpu().numpy().reshape(-1, 2)
+        if hz <= 0 or int(self.ctr.item()) != 2 * n or (m[:, 1] <= m[:, 0]).any():
+            raise RuntimeError("device-clock marks incomplete")
+        return sorted(((m[:, 1] - m[:, 0]) * 1e6 / hz).tolist())
+
+
+def time_layer(torch, fwd, steps, warmup, flush_caches, record_events=True):
+    """Captures fwd() between two device-clock marks and replays it `steps`
+    times after `warmup` replays, flushing the caches before each. Returns the
+    sorted spans (us), the sorted HIP-event times (us) and the wall time (s)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    marks = Marks(torch, 2 * (steps + warmup + 8))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        marks.mark(False)
+        fwd()
+        marks.mark(True)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        flush_caches()
+        graph.replay()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    marks.ctr.zero_()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(steps):
+        flush_caches()
+        starts[i].record(stream)
+        graph.replay()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ev = sorted(a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends))
+    spans = marks.spans_us(steps)
+    del graph
+    return spans, ev, wall
+
+
+def pct(v, q):
+    return v[int(q * (len(v) - 1))]
+
+
+# Entries of the per-config table: (workload, token capacity, live tokens,
+# activation scale format, activation, clamp limit).
+PER_CONFIG = [
+    ("tiny", 8, 8, "fp32", "swiglu", float("inf")),
+    ("decode", 1, 1, "fp32", "swiglu", float("inf")),
+    ("decode", 4, 4, "fp32", "swiglu", float("inf")),
+    ("decode", 4, 4, "fp32", "swiglu_clamp", 7.0),
+    ("padded", 512, 16, "fp32", "swiglu", float("inf")),
+    ("padded", 512, 16, "ue8m0", "swiglu", float("inf")),
+    ("full", 4096, 4096, "fp32", "swiglu", float("inf")),
+    ("full", 4096, 4096, "ue8m0", "swiglu", float("inf")),
+] + [("sweep", m, m, f, "swiglu", float("inf"))
+     for m in (1, 8, 64, 256, 1024, 4096) for f in ("fp32", "pow2")]
 
 
 def main():
@@ -245,8 +367,9 @@ def main():
         traffic_from(args, *args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the expert layer here is "
-              f"a single-GPU kernel library", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
+              f"expert layer on a single MI355X; how it would shard is described in DESIGN.md",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -254,6 +377,57 @@ def main():
     import block_fp8_mixture_amd as moe
     import synth
 
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush_caches():
+        if not args.no_flush:
+            torch.sum(flush, dim=0, out=flush_sink)
+
+    weights_cache = {}
+
+    def weights_for(name):
+        if name not in weights_cache:
+            weights_cache.clear()
+            torch.cuda.empty_cache()
+            cfg_w = synth.get(name)
+            host = synth.ExpertWeights(cfg_w).stacked(threads=min(16, len(os.sched_getaffinity(0))))
+            weights_cache[name] = (host, [up(a) for a in (host[0][0], host[0][1], host[1][0], host[1][1])])
+        return weights_cache[name]
+
+    def layer_inputs(name, t_cap, t_live, fmt, act, lim):
+        cfg_l = synth.get(name)
+        x_l, ids_l, w_l = synth.make_workload(cfg_l, t_cap)
+        _, d_w_l = weights_for(name)
+        E_l, H_l, I_l, K_l = cfg_l.num_experts, cfg_l.hidden, cfg_l.inter, cfg_l.topk
+        lay_l = moe.moe_workspace_plan(E_l, H_l, I_l, K_l, t_cap, cfg_l.align_rows, 0, fmt, act, lim)
+        ws_l = torch.zeros(lay_l["total"], dtype=torch.uint8, device=dev)
+        out_l = torch.zeros((t_cap, H_l), dtype=torch.int16, device=dev)
+        dx_l, dids_l, dw_l = up(x_l), up(ids_l), up(w_l)
+        dlive_l = up(np.array([t_live], np.int32))
+
+        def fwd():
+            moe.moe_forward(dx_l, dids_l, dw_l, *d_w_l, fmt, act, lim, cfg_l.align_rows, 0,
+                            t_live=dlive_l, out=out_l, workspace=ws_l)
+        return cfg_l, (x_l, ids_l, w_l), fwd, lay_l, ws_l, (dx_l, dids_l, dw_l, dlive_l), out_l
+
+    def rates(cfg_l, ids_l, t_live, span_us):
+        n_e, pairs_l = live_stats(ids_l, t_live, cfg_l.num_experts)
+        bmin_l, flops_l = algorithmic(cfg_l, n_e, pairs_l, t_live)
+        return {"live_experts": n_e, "live_pairs": pairs_l,
+                "live_tflops": round(flops_l / (span_us * 1e-6) / 1e12, 3),
+                "frac_fp8_peak": round(flops_l / (span_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                "hbm_gbs_min_bytes": round(bmin_l / (span_us * 1e-6) / 1e9, 1),
+                "frac_hbm_peak": round(bmin_l / (span_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "min_bytes": bmin_l, "live_flops": flops_l}
+
+    # ---- the headline workload
     cfg = synth.get(args.config)
     t_cap, t_live = DEFAULT_TOKENS[args.config]
     if args.tokens is not None:
@@ -264,100 +438,20 @@ def main():
     fmt = args.fmt or cfg.scale_fmts[0]
     act = args.act
     lim = 7.0 if act != "swiglu" else float("inf")
-    dev = torch.device("cuda", 0)
     E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk
-
-    def up(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
-
     t0 = time.perf_counter()
-    x, ids, w = synth.make_workload(cfg, t_cap)
-    weights = synth.ExpertWeights(cfg).stacked(threads=16)
-    (w1q, w1s), (w2q, w2s) = weights
-    d_w = [up(a) for a in (w1q, w1s, w2q, w2s)]
-    dx, dids, dw = up(x), up(ids), up(w)
-    dlive = up(np.array([t_live], np.int32))
+    cfg, (x, ids, w), fwd, lay, ws, (dx, dids, dw, dlive), out = layer_inputs(
+        args.config, t_cap, t_live, fmt, act, lim)
+    weights, d_w = weights_for(args.config)
     print(f"# inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
-
-    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, cfg.align_rows, 0, fmt, act, lim)
-    ws = torch.zeros(lay["total"], dtype=torch.uint8, device=dev)
-    out = torch.zeros((t_cap, H), dtype=torch.int16, device=dev)
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
-
-    def flush_caches():
-        torch.sum(flush, dim=0, out=flush_sink)
-
-    def fwd():
-        moe.moe_forward(dx, dids, dw, *d_w, fmt, act, lim, cfg.align_rows, 0, t_live=dlive,
-                        out=out, workspace=ws)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for _ in range(3):
-            fwd()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    # Device-clock marks at both ends of the graph: each replay's kernel span
-    # (first kernel start to last kernel end, plus the two one-thread marks)
-    # on the GPU timeline, as a kernel trace measures it.
-    import ctypes
-    bl = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
-    bl.moe_bench_mark.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
-                                  ctypes.c_void_p]
-    bl.moe_bench_clock_hz.restype = ctypes.c_int64
-    mark_cap = 2 * (args.steps + args.warmup + 8)
-    mark_slots = torch.zeros(mark_cap, dtype=torch.int64, device=dev)
-    mark_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    def mark(closing):
-        if bl.moe_bench_mark(mark_slots.data_ptr(), mark_ctr.data_ptr(), mark_cap, int(closing),
-                             torch.cuda.current_stream().cuda_stream) != 0:
-            raise RuntimeError("device-clock mark launch failed")
-
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        mark(False)
-        fwd()
-        mark(True)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    for i in range(args.warmup):
-        if not args.no_flush:
-            flush_caches()
-        graph.replay()
-    torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    mark_ctr.zero_()
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush_caches()
-        starts[i].record(stream)
-        graph.replay()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ev_us = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))
-    ev_med = statistics.median(ev_us)
-    hz = bl.moe_bench_clock_hz()
-    marks = mark_slots[:2 * args.steps].cpu().numpy().reshape(-1, 2)
-    if hz <= 0 or int(mark_ctr.item()) != 2 * args.steps or (marks[:, 1] <= marks[:, 0]).any():
-        raise RuntimeError("device-clock marks incomplete")
-    lat_us = sorted(((marks[:, 1] - marks[:, 0]) * 1e6 / hz).tolist())
-    med = statistics.median(lat_us)
-    p10 = lat_us[int(0.1 * (len(lat_us) - 1))]
-    p90 = lat_us[int(0.9 * (len(lat_us) - 1))]
+    lat_us, ev_us, wall = time_layer(torch, fwd, args.steps, args.warmup, flush_caches)
+    med, ev_med = statistics.median(lat_us), statistics.median(ev_us)
+    p10, p90 = pct(lat_us, 0.1), pct(lat_us, 0.9)
     print(f"# layer kernel span median {med:.2f} us (p10 {p10:.2f}, p90 {p90:.2f}); events around "
           f"the replay {ev_med:.2f} us; over {args.steps} steps", file=sys.stderr, flush=True)
 
     # ---- dominant kernel alone: FC1 grouped GEMM on the forward's intermediates
+    stream = torch.cuda.current_stream()
     n_live_e, pairs = live_stats(ids, t_live, E)
     R = lay["row_cap"]
 
@@ -434,6 +528,8 @@ def main():
                 "unit": "GB/s", "frac": round(fc1_b / (k_avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     roof.update({"traffic": traffic, "kernel_avg_us": round(k_avg, 3),
                  "algorithmic_bytes": fc1_b, "algorithmic_flops": fc1_flops})
+    print(f"# dominant kernel alone: {k_avg:.2f} us, {roof['achieved']} {roof['unit']} "
+          f"({roof['frac']:.3f} of peak)", file=sys.stderr, flush=True)
 
     # A plain 256 MiB device copy, so counter runs (FETCH_SIZE / WRITE_SIZE)
     # can be scaled by what the counters read for a copy of known size.
@@ -442,9 +538,10 @@ def main():
     for _ in range(3):
         cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
-    del cal_src, cal_dst
+    del cal_src, cal_dst, ws_f, out_f, c1
 
-    bmin, flops = algorithmic(cfg, n_live_e, pairs, t_live)
+    head_rates = rates(cfg, ids, t_live, med)
+    ctx = PAGES_CONTEXT_US.get(f"{args.config}:{t_live}")
     res = {
         "metric": "MoE layer latency (us) + live-row TFLOP/s and HBM GB/s vs roofline",
         "value": round(med, 3),
@@ -455,9 +552,7 @@ def main():
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": False,
         "scaling": "weak",
-        "vs_baseline": (round(med / PAGES_DECODE_T4_US, 4)
-                        if (args.config, t_live, fmt, act) == ("decode", 4, "fp32", "swiglu")
-                        else None),
+        "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {
@@ -469,16 +564,45 @@ def main():
         },
         "latency_us": {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3),
                        "events_median": round(ev_med, 3)},
-        "live_experts": n_live_e,
-        "live_pairs": pairs,
-        "live_tflops": round(flops / (med * 1e-6) / 1e12, 4),
-        "hbm_gbs_min_bytes": round(bmin / (med * 1e-6) / 1e9, 1),
-        "frac_fp8_peak": round(flops / (med * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 5),
-        "frac_hbm_peak": round(bmin / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "live_experts": head_rates["live_experts"],
+        "live_pairs": head_rates["live_pairs"],
+        "live_tflops": head_rates["live_tflops"],
+        "hbm_gbs_min_bytes": head_rates["hbm_gbs_min_bytes"],
+        "frac_fp8_peak": head_rates["frac_fp8_peak"],
+        "frac_hbm_peak": head_rates["frac_hbm_peak"],
         "roofline": roof,
+        "pages_context_us": ctx,
     }
+    del fwd, ws, out, dx, dids, dw, dlive, d_w
+
+    # ---- every workload and variant, the same protocol with fewer replays
+    if not args.no_per_config:
+        table = []
+        for name, tc, tl, f, ac, li in PER_CONFIG:
+            cfg_l, (xl, idsl, wl), fwd_l, _, ws_l, _, out_l = layer_inputs(name, tc, tl, f, ac, li)
+            spans, evs, _ = time_layer(torch, fwd_l, args.config_steps, 3, flush_caches)
+            m = statistics.median(spans)
+            ent = {"workload": name, "tokens": tl, "token_capacity": tc, "act_scale_fmt": f,
+                   "activation": ac, "span_us": round(m, 2), "p10_us": round(pct(spans, 0.1), 2),
+                   "p90_us": round(pct(spans, 0.9), 2), "events_us": round(statistics.median(evs), 2),
+                   "path": ("one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter)
+                            else "general")}
+            ent.update(rates(cfg_l, idsl, tl, m))
+            # the bars: HBM at <= 32 tokens, FP8 MFMA at the fully occupied
+            # layer; the tiny layer is launch-bound and reported only
+            bar = None if name == "tiny" else ("hbm" if tl <= 32 else ("mfma" if name == "full" else None))
+            ent["bar"] = bar
+            c = PAGES_CONTEXT_US.get(f"{name}:{tl}")
+            if c:
+                ent["pages_context_us"] = c
+            table.append(ent)
+            print(f"# per-config {name} T={tl}/{tc} {f} {ac}: {m:.1f} us, "
+                  f"{ent['frac_fp8_peak']:.3f} FP8, {ent['frac_hbm_peak']:.3f} HBM",
+                  file=sys.stderr, flush=True)
+            del fwd_l, ws_l, out_l
+        res["per_config"] = table
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, x, ids, w, t_live, fmt, act, weights)
+        res["cpu_baseline"] = cpu_baseline(cfg, x, ids, w, t_live, fmt, act, lim, weights)
     print(json.dumps(res), flush=True)
 
 

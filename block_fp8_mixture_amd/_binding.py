@@ -62,7 +62,8 @@ class _Layout(ctypes.Structure):
                 ("row_to_pair", ctypes.c_size_t), ("pair_to_row", ctypes.c_size_t),
                 ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t), ("c1", ctypes.c_size_t),
                 ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t), ("y", ctypes.c_size_t),
-                ("act", ctypes.c_size_t), ("total", ctypes.c_size_t), ("row_cap", _i32)]
+                ("act", ctypes.c_size_t), ("status", ctypes.c_size_t), ("total", ctypes.c_size_t),
+                ("row_cap", _i32)]
 
 
 _SIGNATURES = {
@@ -83,6 +84,7 @@ _SIGNATURES = {
     "moe_fc1_decode": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
                                       ctypes.c_size_t, _vp]),
     "moe_barrier_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
+    "moe_barrier_spin_limit": (_i32, [_i32]),
 }
 
 
@@ -127,11 +129,32 @@ def _need(t, name, dtype, device=None, ndim=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims")
     return t
+
+
+def _shape(t, name, shape):
+    """Raises ValueError unless tensor ``t`` has exactly ``shape``."""
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _min_numel(t, name, n):
+    if t.numel() < n:
+        raise ValueError(f"{name} needs at least {n} elements, has {t.numel()}")
+    return t
+
+
+def _same_device(*tensors):
+    """All given tensors on one GPU (checked after every shape, so shape errors
+    are reported first)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors live on different devices: {sorted(map(str, devs))}")
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("tensors must be GPU tensors")
 
 
 def _fmt(fmt):
@@ -147,7 +170,10 @@ def _scale_dtype(fmt):
 def _live(t_live):
     if t_live is None:
         return None
-    return _ptr(_need(t_live, "t_live", torch.int32))
+    _need(t_live, "t_live", torch.int32)
+    if t_live.numel() != 1 or not t_live.is_cuda:
+        raise ValueError("t_live must be a one-element int32 GPU tensor")
+    return _ptr(t_live)
 
 
 def _bf16_view(t, name):
@@ -179,8 +205,10 @@ def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, o
             "row_to_pair": torch.empty(max(row_cap, 1), dtype=torch.int32, device=dev),
             "pair_to_row": torch.empty(max(t_cap * topk, 1), dtype=torch.int32, device=dev),
         }
-    for k in ("counts", "offsets", "row_to_pair", "pair_to_row"):
-        _need(out[k], k, torch.int32)
+    for k, n in (("counts", num_experts), ("offsets", num_experts + 1),
+                 ("row_to_pair", row_cap), ("pair_to_row", t_cap * topk)):
+        _min_numel(_need(out[k], k, torch.int32), k, n)
+    _same_device(ids, *out.values())
     st = lib.moe_align(_ptr(ids), t_cap, _live(t_live), topk, num_experts, align_rows, row_cap,
                        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_to_pair"]),
                        _ptr(out["pair_to_row"]), _stream())
@@ -192,13 +220,16 @@ def moe_act_quant(x, fmt="fp32", t_live=None, xq=None, xs=None):
     """Per-token 1x128 quantization. Returns (xq uint8 [t_cap, H], xs [H/128, t_cap])."""
     lib = load_library()
     xb = _bf16_view(x, "x")
+    if xb.dim() != 2:
+        raise ValueError("x must be [t_cap, hidden]")
     t_cap, hidden = xb.shape
     if xq is None:
         xq = torch.empty((t_cap, hidden), dtype=torch.uint8, device=xb.device)
     if xs is None:
         xs = torch.empty((hidden // 128, t_cap), dtype=_scale_dtype(fmt), device=xb.device)
-    _need(xq, "xq", torch.uint8)
-    _need(xs, "xs", _scale_dtype(fmt))
+    _shape(_need(xq, "xq", torch.uint8), "xq", (t_cap, hidden))
+    _shape(_need(xs, "xs", _scale_dtype(fmt)), "xs", (hidden // 128, t_cap))
+    _same_device(xb, xq, xs)
     st = lib.moe_act_quant(_ptr(xb), t_cap, _live(t_live), hidden, _fmt(fmt), _ptr(xq), _ptr(xs),
                            _stream())
     _check("moe_act_quant", st)
@@ -215,23 +246,30 @@ def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap
     _need(a_scales, "a_scales", _scale_dtype(fmt), ndim=2)
     _need(w, "w", torch.uint8, ndim=3)
     _need(w_scales, "w_scales", torch.float32, ndim=3)
-    _need(counts, "counts", torch.int32)
-    _need(offsets, "offsets", torch.int32)
     num_experts, n, k = w.shape
+    a_rows = a.shape[0]
     if a.shape[1] != k:
         raise ValueError("a and w disagree on K")
-    a_rows = a_scales.shape[1]
+    _shape(a_scales, "a_scales", (k // 128, a_rows))
+    _shape(w_scales, "w_scales", (num_experts, n // 128, k // 128))
+    _shape(_need(counts, "counts", torch.int32), "counts", (num_experts,))
+    _shape(_need(offsets, "offsets", torch.int32), "offsets", (num_experts + 1,))
     if out is None:
         out = torch.empty((max(row_cap, 1), n), dtype=torch.int16, device=a.device)
-    _bf16_view(out, "out")
+    ob = _bf16_view(out, "out")
+    if ob.dim() != 2 or ob.shape[1] != n or ob.shape[0] < row_cap:
+        raise ValueError(f"out must be [>= {row_cap}, {n}], got {tuple(ob.shape)}")
     if a_row_map is not None:
-        _need(a_row_map, "a_row_map", torch.int32)
+        _min_numel(_need(a_row_map, "a_row_map", torch.int32), "a_row_map", row_cap)
+    elif a_rows < row_cap:
+        raise ValueError("without a row map, a needs row_cap rows")
     if tiles_visited is not None:
-        _need(tiles_visited, "tiles_visited", torch.int32)
+        _min_numel(_need(tiles_visited, "tiles_visited", torch.int32), "tiles_visited", 1)
+    _same_device(a, a_scales, w, w_scales, counts, offsets, ob, a_row_map, tiles_visited)
     st = lib.moe_grouped_gemm_fp8(_ptr(a), _ptr(a_scales), _fmt(fmt), a_rows, _ptr(a_row_map),
                                   a_row_div, _ptr(w), _ptr(w_scales), _ptr(counts),
                                   _ptr(offsets), num_experts, row_cap, max_rows_per_expert, n, k,
-                                  _ptr(out), _ptr(tiles_visited), _stream())
+                                  _ptr(ob), _ptr(tiles_visited), _stream())
     _check("moe_grouped_gemm_fp8", st)
     return out
 
@@ -242,15 +280,20 @@ def moe_silu_mul_quant(gate_up, counts, offsets, act="swiglu", clamp_limit=float
     Returns (hq uint8 [row_cap, I], hs [I/128, row_cap])."""
     lib = load_library()
     gu = _bf16_view(gate_up, "gate_up")
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gate_up must be [row_cap, 2 * inter]")
     row_cap, two_i = gu.shape
     inter = two_i // 2
+    _need(counts, "counts", torch.int32, ndim=1)
     num_experts = counts.shape[0]
+    _shape(_need(offsets, "offsets", torch.int32), "offsets", (num_experts + 1,))
     if hq is None:
         hq = torch.empty((row_cap, inter), dtype=torch.uint8, device=gu.device)
     if hs is None:
         hs = torch.empty((inter // 128, row_cap), dtype=_scale_dtype(fmt), device=gu.device)
-    _need(hq, "hq", torch.uint8)
-    _need(hs, "hs", _scale_dtype(fmt))
+    _shape(_need(hq, "hq", torch.uint8), "hq", (row_cap, inter))
+    _shape(_need(hs, "hs", _scale_dtype(fmt)), "hs", (inter // 128, row_cap))
+    _same_device(gu, counts, offsets, hq, hs)
     if act not in ACTS:
         raise ValueError(f"act must be one of {list(ACTS)}")
     st = lib.moe_silu_mul_quant(_ptr(gu), inter, _ptr(counts), _ptr(offsets), num_experts,
@@ -264,13 +307,16 @@ def moe_topk_combine(y, pair_to_row, topk_w, t_live=None, out=None):
     """Top-k weighted sum of expert rows. Returns BF16 bits (int16) [t_cap, H]."""
     lib = load_library()
     yb = _bf16_view(y, "y")
+    if yb.dim() != 2:
+        raise ValueError("y must be [row_cap, hidden]")
     row_cap, hidden = yb.shape
-    _need(pair_to_row, "pair_to_row", torch.int32)
     w = _need(topk_w, "topk_w", torch.float32, ndim=2)
     t_cap, topk = w.shape
+    _min_numel(_need(pair_to_row, "pair_to_row", torch.int32), "pair_to_row", t_cap * topk)
     if out is None:
         out = torch.empty((t_cap, hidden), dtype=torch.int16, device=yb.device)
-    ob = _bf16_view(out, "out")
+    ob = _shape(_bf16_view(out, "out"), "out", (t_cap, hidden))
+    _same_device(yb, pair_to_row, w, ob)
     st = lib.moe_topk_combine(_ptr(yb), row_cap, _ptr(pair_to_row), _ptr(w), t_cap, _live(t_live),
                               topk, hidden, _ptr(ob), _stream())
     _check("moe_topk_combine", st)
@@ -303,24 +349,41 @@ def moe_workspace_bytes(num_experts, hidden, inter, topk, t_cap, align_rows=16, 
     return int(lib.moe_workspace_bytes(ctypes.byref(prob)))
 
 
+def _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2=None, w2_scales=None):
+    """Shapes and devices of the layer's inputs; returns (num_experts, inter, topk)."""
+    t_cap, hidden = xb.shape
+    _need(topk_ids, "topk_ids", torch.int32, ndim=2)
+    if topk_ids.shape[0] != t_cap:
+        raise ValueError(f"topk_ids has {topk_ids.shape[0]} rows, x has {t_cap}")
+    _need(w1, "w1", torch.uint8, ndim=3)
+    num_experts, two_i, h1 = w1.shape
+    if h1 != hidden or two_i % 256:
+        raise ValueError(f"w1 must be [E, 2*inter, {hidden}], got {tuple(w1.shape)}")
+    inter = two_i // 2
+    _shape(_need(w1_scales, "w1_scales", torch.float32), "w1_scales",
+           (num_experts, two_i // 128, hidden // 128))
+    if w2 is not None:
+        _shape(_need(w2, "w2", torch.uint8), "w2", (num_experts, hidden, inter))
+        _shape(_need(w2_scales, "w2_scales", torch.float32), "w2_scales",
+               (num_experts, hidden // 128, inter // 128))
+    return num_experts, inter, topk_ids.shape[1]
+
+
 def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", act="swiglu",
                 clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None, out=None,
                 workspace=None):
-    """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8)."""
+    """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8).
+    ``topk_w=None`` weights every routed pair by one."""
     lib = load_library()
     xb = _bf16_view(x, "x")
+    if xb.dim() != 2:
+        raise ValueError("x must be [t_cap, hidden]")
     t_cap, hidden = xb.shape
-    _need(topk_ids, "topk_ids", torch.int32, ndim=2)
-    _need(topk_w, "topk_w", torch.float32, ndim=2)
-    _need(w1, "w1", torch.uint8, ndim=3)
-    _need(w1_scales, "w1_scales", torch.float32, ndim=3)
-    _need(w2, "w2", torch.uint8, ndim=3)
-    _need(w2_scales, "w2_scales", torch.float32, ndim=3)
-    num_experts, two_i, h1 = w1.shape
-    topk = topk_ids.shape[1]
-    if h1 != hidden or tuple(w2.shape) != (num_experts, hidden, two_i // 2):
-        raise ValueError("weight shapes disagree with x")
-    prob = _problem(num_experts, hidden, two_i // 2, topk, t_cap, align_rows, row_cap, fmt, act,
+    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales)
+    if topk_w is None:
+        topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
+    _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
+    prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
                     clamp_limit)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if need == 0:
@@ -331,7 +394,10 @@ def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", a
     _need(workspace, "workspace", torch.uint8)
     if out is None:
         out = torch.empty((t_cap, hidden), dtype=torch.int16, device=xb.device)
-    ob = _bf16_view(out, "out")
+    ob = _shape(_bf16_view(out, "out"), "out", (t_cap, hidden))
+    if t_live is not None:
+        _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
+    _same_device(xb, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, ob, workspace, t_live)
     tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
                     _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
     st = lib.moe_forward(ctypes.byref(prob), ctypes.byref(tens), _ptr(workspace),
@@ -347,19 +413,21 @@ def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
     FC1 with SiLU(gate)*up), writing moe_forward's workspace. Returns the workspace."""
     lib = load_library()
     xb = _bf16_view(x, "x")
+    if xb.dim() != 2:
+        raise ValueError("x must be [t_cap, hidden]")
     t_cap, hidden = xb.shape
-    _need(topk_ids, "topk_ids", torch.int32, ndim=2)
-    _need(w1, "w1", torch.uint8, ndim=3)
-    _need(w1_scales, "w1_scales", torch.float32, ndim=3)
-    num_experts, two_i, h1 = w1.shape
-    if h1 != hidden or two_i != 2 * inter:
-        raise ValueError("w1 shape disagrees with x / inter")
-    prob = _problem(num_experts, hidden, inter, topk_ids.shape[1], t_cap, align_rows, row_cap,
+    num_experts, w_inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales)
+    if w_inter != inter:
+        raise ValueError("w1 shape disagrees with inter")
+    prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap,
                     fmt, act, clamp_limit)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xb.device)
     _need(workspace, "workspace", torch.uint8)
+    if t_live is not None:
+        _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
+    _same_device(xb, topk_ids, w1, w1_scales, workspace, t_live)
     tens = _Tensors(_ptr(xb), _ptr(topk_ids), None, _live(t_live), _ptr(w1), _ptr(w1_scales),
                     None, None, None)
     st = lib.moe_fc1_decode(ctypes.byref(prob), ctypes.byref(tens), _ptr(workspace),
@@ -375,3 +443,9 @@ def moe_barrier_timeouts():
     n = ctypes.c_uint32(0)
     _check("moe_barrier_timeouts", lib.moe_barrier_timeouts(ctypes.byref(n)))
     return int(n.value)
+
+
+def moe_barrier_spin_limit(polls):
+    """Sets the polls per wait of the one-launch decode layer's grid barrier for
+    later launches (negative: every wait gives up at once); returns the old value."""
+    return int(load_library().moe_barrier_spin_limit(int(polls)))

@@ -214,8 +214,9 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   L->y = take(R * H * 2);
   const bool decode = moe::down_combine_fits(p->t_cap, p->topk, p->inter);
   L->act = decode ? take(R * I * 4) : 0;
+  L->status = take(static_cast<size_t>(moe::kDlMaxGrid) * 4);
   L->total = off;
-  if (!decode) L->act = off;
+  if (!decode) L->act = L->status;
   L->row_cap = static_cast<int32_t>(rc);
   return MOE_OK;
 }
@@ -291,7 +292,7 @@ moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* work
   moe_workspace_layout L;
   const moe_status st = moe_workspace_plan(p, &L);
   if (st != MOE_OK) return st;
-  if (!(L.act < L.total) || !moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter))
+  if (!(L.act < L.status) || !moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter))
     return MOE_ERR_UNSUPPORTED;
   if (!t || !workspace) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
@@ -303,6 +304,12 @@ moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* work
 moe_status moe_barrier_timeouts(uint32_t* count) {
   if (!count) return MOE_ERR_INVALID_ARG;
   return from_hip(moe::decode_layer_timeouts(count));
+}
+
+int32_t moe_barrier_spin_limit(int32_t polls) {
+  const int32_t old = moe::decode_layer_spin_limit();
+  moe::set_decode_layer_spin_limit(polls);
+  return old;
 }
 
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
@@ -328,7 +335,7 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   auto* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
   void* hs = ws + L.hs;
   auto* y = reinterpret_cast<uint16_t*>(ws + L.y);
-  const bool decode = L.act < L.total;  // fused decode path (the plan lays out act)
+  const bool decode = L.act < L.status;  // fused decode path (the plan lays out act)
   auto* act = reinterpret_cast<float*>(ws + L.act);
   const hipStream_t s = as_stream(stream);
   const int R = L.row_cap;
@@ -342,6 +349,8 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
     moe::DecodeLayerArgs a;
     a.f1 = fc1_decode_args(p, t, L, ws);
     a.f2 = down_combine_args(p, t, L, ws);
+    a.status = reinterpret_cast<int32_t*>(ws + L.status);
+    a.spin_limit = moe::decode_layer_spin_limit();
     return from_hip(moe::launch_decode_layer(a, s));
   }
   if (decode && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {

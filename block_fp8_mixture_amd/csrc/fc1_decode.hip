@@ -56,12 +56,14 @@ constexpr int kF1Stage = kDecStage;          // + the two weight scales (64 x 4-
 constexpr int kF1Loads = kDecLoads;          // loads per wave and stage
 
 // Grid barrier of the one-launch layer: per workgroup the epoch (launch
-// count) it has reached, the epoch workgroup 0 has released, and a sticky
-// count of waits that gave up (a workgroup that was not resident).
+// count) it has reached, the epoch workgroup 0 has released (with
+// kDlFailBit set when one of its waits gave up), and a sticky count of waits
+// that gave up (a workgroup that was not resident).
 __device__ unsigned g_dl_flag[kDlMaxGrid];
 __device__ unsigned g_dl_release;
 __device__ unsigned g_dl_timeouts;
-constexpr int kDlSpinLimit = 1 << 21;  // polls (about a microsecond each) before a wait gives up
+constexpr unsigned kDlFailBit = 0x80000000u;
+constexpr unsigned kDlEpochMask = ~kDlFailBit;
 
 __device__ __forceinline__ unsigned flag_load(const unsigned* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,14 +71,21 @@ __device__ __forceinline__ unsigned flag_load(const unsigned* a) {
 __device__ __forceinline__ void flag_store(unsigned* a, unsigned v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
-__device__ __forceinline__ void flag_wait(const unsigned* a, unsigned v) {
-  for (int it = 0; flag_load(a) != v; ++it) {
-    if (it == kDlSpinLimit) {
+// Waits until (*a & mask) == v; after `limit` polls (or at once when limit
+// is negative) it gives up, counts itself and returns false.
+__device__ __forceinline__ bool flag_wait(const unsigned* a, unsigned v, int limit, unsigned mask = ~0u) {
+  if (limit < 0) {
+    atomicAdd(&g_dl_timeouts, 1u);
+    return false;
+  }
+  for (int it = 0; (flag_load(a) & mask) != v; ++it) {
+    if (it == limit) {
       atomicAdd(&g_dl_timeouts, 1u);
-      return;
+      return false;
     }
     __builtin_amdgcn_s_sleep(2);
   }
+  return true;
 }
 
 // DEPTH: stages in a wave's ring, kDecDepth; or 4 in the wide variant of the
@@ -470,19 +479,42 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     // ---- grid barrier. Every wave has waited for its act stores (write-
     // through) above; after the workgroup barrier thread 0 publishes the
     // workgroup's epoch, workgroup 0 waits for every workgroup's epoch and
-    // releases the epoch. Waits are bounded: one that gives up is counted and
-    // the launch goes on.
+    // releases the epoch. Waits are bounded: one that gives up is counted,
+    // workgroup 0 then releases with the failure bit, and every workgroup
+    // that gave up or saw that bit writes NaN to its output columns of the
+    // live tokens instead of computing them (the act rows it would read may
+    // be incomplete) and reports it in its status slot.
+    __shared__ int s_failed;
     lds_barrier();
-    if (tid == 0) flag_store(&g_dl_flag[blockIdx.x], epoch);
+    if (tid == 0) {
+      s_failed = 0;
+      flag_store(&g_dl_flag[blockIdx.x], epoch);
+    }
+    lds_barrier();
+    const int limit = a.spin_limit;
     if (blockIdx.x == 0) {
-      for (int j = tid; j < G; j += kF1Threads) flag_wait(&g_dl_flag[j], epoch);
+      bool ok = true;
+      for (int j = tid; j < G; j += kF1Threads) ok &= flag_wait(&g_dl_flag[j], epoch, limit);
+      if (!ok) s_failed = 1;
       lds_barrier();
-      if (tid == 0) flag_store(&g_dl_release, epoch);
+      if (tid == 0) flag_store(&g_dl_release, s_failed ? (epoch | kDlFailBit) : epoch);
     } else if (tid == 0) {
-      flag_wait(&g_dl_release, epoch);
+      if (!flag_wait(&g_dl_release, epoch, limit, kDlEpochMask) || (flag_load(&g_dl_release) & kDlFailBit))
+        s_failed = 1;
     }
     for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;  // the K-split partials are done
     lds_barrier();
+    const bool failed = s_failed != 0;  // uniform
+    if (tid == 0 && a.status) a.status[blockIdx.x] = failed ? 1 : 0;
+    if (failed) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the FC2 stages issued above
+      for (int c = cb; c < n_cb; c += G)
+        for (int x = tid; x < t_live * 2; x += kF1Threads) {
+          const uint4 nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+          *reinterpret_cast<uint4*>(q.out + static_cast<int64_t>(x >> 1) * H + c * 16 + 8 * (x & 1)) = nan;
+        }
+      return;
+    }
 
     // ---- 5. this wave's FC2 input rows, read at device scope (other
     // workgroups wrote them), then the rest of the stream start
@@ -570,6 +602,13 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream) {
     launch(std::integral_constant<int, kDecDepth>{});
   return hipGetLastError();
 }
+
+namespace {
+std::atomic<int> g_spin_limit{kDlSpinDefault};
+}  // namespace
+
+void set_decode_layer_spin_limit(int polls) { g_spin_limit.store(polls, std::memory_order_relaxed); }
+int decode_layer_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
 hipError_t decode_layer_timeouts(uint32_t* out) {
   return hipMemcpyFromSymbol(out, HIP_SYMBOL(g_dl_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);

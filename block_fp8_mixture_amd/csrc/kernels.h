@@ -172,7 +172,21 @@ inline bool decode_layer_fits(int64_t t_cap, int64_t topk, int64_t hidden, int64
 struct DecodeLayerArgs {
   DecodeFc1Args f1;
   DownCombineArgs f2;
+  // Per-workgroup outcome of the grid barrier ([grid] int32, the workspace's
+  // status slots): 0 = it opened, 1 = a wait gave up and the workgroup wrote
+  // NaN to its output columns instead of computing them.
+  int32_t* status;
+  // Polls per barrier wait before it gives up; below 0: give up at once
+  // (a host-forced timeout, for tests).
+  int spin_limit;
 };
+
+// Polls per wait of the one-launch layer's grid barrier (about a microsecond
+// each) used by subsequent launches in this process; below 0, every wait
+// gives up at once. Default kDlSpinDefault.
+constexpr int kDlSpinDefault = 1 << 21;
+void set_decode_layer_spin_limit(int polls);
+int decode_layer_spin_limit();
 
 hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream);
 // Grid of launch_decode_layer on the current device (one workgroup per CU),

@@ -242,7 +242,14 @@ typedef struct {
   size_t y;              /* BF16 [row_cap, H] */
   size_t act;            /* fp32 [row_cap, I] SiLU(gate)*up before quantization; laid out
                             only on the decode path (t_cap*topk <= 64 and the quantized
-                            FC2 input rows fit 24 KiB of LDS), else equal to total */
+                            FC2 input rows fit 24 KiB of LDS), else equal to status */
+  size_t status;         /* int32 [1024] per-launch outcome of the one-launch decode
+                            layer's grid barrier: every launch of that path writes slot b
+                            for each of its workgroups b < grid (one per CU): 0 = the
+                            barrier opened, 1 = a wait gave up (see moe_barrier_timeouts)
+                            and workgroup b wrote NaN (0x7FC0) to its output columns
+                            16*(b + grid*j) .. +15 of the live tokens instead of computing
+                            them. Other paths do not write it. */
   size_t total;          /* bytes required */
   int32_t row_cap;       /* effective row capacity */
 } moe_workspace_layout;
@@ -281,10 +288,14 @@ size_t moe_workspace_bytes(const moe_problem* p);
  * across the grid, then runs FC2 with the top-k combine for its output
  * columns (beyond moe_fc1_decode's token limits, with a 4-deep instead of a
  * 6-deep weight ring per wave). That launch needs all its workgroups
- * resident at once, so calls
+ * resident at once and keeps its barrier epochs in device globals, so on
+ * that path moe_forward drops thread safety across overlapping calls: calls
  * on one device must not overlap in time (one stream, or ordered streams),
- * and the GPU should not be shared with work that holds CUs for long (see
- * moe_barrier_timeouts). Otherwise the decode path takes two or three
+ * and the GPU should not be shared with work that holds CUs for long. A
+ * barrier wait that gives up never hangs the launch; it is reported in the
+ * workspace's status slots and as NaN output columns (see
+ * moe_barrier_timeouts). Every other path keeps no state between calls.
+ * Otherwise the decode path takes two or three
  * launches: [align + act_quant, then FC1 with SiLU(gate)*up] or the fused
  * FC1 of moe_fc1_decode, then FC2 with the top-k combine. The workspace then
  * holds the same alignment, codes and scales, bit for bit, and FC1/FC2 rows
@@ -315,10 +326,21 @@ moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* work
  * path that gave up on the current device since the library was loaded
  * (sticky). A wait gives up after about two seconds without the other
  * workgroups, which only happens when some of them could not become resident
- * (CUs held by other work); that launch's outputs are then unreliable. Reads
- * device memory synchronously.
+ * (CUs held by other work). The launch then still finishes: every workgroup
+ * that gave up, or whose release carried the failure mark, writes NaN to its
+ * output columns and 1 to its slot of moe_workspace_layout.status, so the
+ * failure is visible in that launch's own outputs without a host poll. This
+ * call reads device memory synchronously.
  * Errors: INVALID_ARG (count NULL), HIP. */
 moe_status moe_barrier_timeouts(uint32_t* count);
+
+/* Sets how many polls (about a microsecond each) a wait at the one-launch
+ * decode layer's grid barrier makes before it gives up, for launches enqueued
+ * after the call, process-wide; returns the previous value. Default 2^21.
+ * A negative value makes every wait give up at once: a host-forced timeout,
+ * so that tests can exercise the failure report above while every kernel
+ * still exits normally. Not thread-safe against concurrent launches. */
+int32_t moe_barrier_spin_limit(int32_t polls);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

@@ -184,7 +184,7 @@ def test_decode_plan_lays_out_act_and_fc1_decode_validates(lib):
     # 4096 tokens: no act buffer (act == total)
     big = B._Layout()
     assert lib.moe_workspace_plan(ctypes.byref(_problem()), ctypes.byref(big)) == OK
-    assert big.act == big.total
+    assert big.act == big.status
     need = lib.moe_workspace_bytes(ctypes.byref(p))
     t = B._Tensors(*([FAKE.value] * 9))
     f = lib.moe_fc1_decode
@@ -196,7 +196,7 @@ def test_decode_plan_lays_out_act_and_fc1_decode_validates(lib):
     # 8 tokens at H = 6144 fit the decode path but not FC1's resident activations
     p8 = _problem(num_experts=256, hidden=6144, inter=256, topk=8, t_cap=8)
     l8 = B._Layout()
-    assert lib.moe_workspace_plan(ctypes.byref(p8), ctypes.byref(l8)) == OK and l8.act < l8.total
+    assert lib.moe_workspace_plan(ctypes.byref(p8), ctypes.byref(l8)) == OK and l8.act < l8.status
     assert f(ctypes.byref(p8), ctypes.byref(t), FAKE, l8.total, NULL) == UNSUPPORTED
 
 
@@ -225,7 +225,7 @@ def test_decode_layer_applies_matches_the_workspace_plan(lib):
                            (16, 4, 3584, 256), (8, 8, 7168, 256), (32, 2, 512, 128)]:
         lay = moe.moe_workspace_plan(288, h, i, k, t_cap)
         if moe.decode_layer_applies(t_cap, k, h, i):
-            assert lay["act"] < lay["total"], (t_cap, k, h, i)
+            assert lay["act"] < lay["status"], (t_cap, k, h, i)
     assert moe.decode_layer_applies(8, 8, 6144, 256)       # 49 KB of token codes
     assert not moe.decode_layer_applies(9, 7, 7168, 256)   # 64.6 KB
     assert not moe.decode_layer_applies(4, 8, 4096, 2048)  # FC2 input rows too large

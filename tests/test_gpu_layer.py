@@ -288,7 +288,7 @@ def test_one_launch_layer_wide_routing(t_live, fmt):
     for e in np.unique(ids):  # only routed experts are ever read
         (w1q[e], w1s[e]), (w2q[e], w2s[e]) = ew.fc1(e), ew.fc2(e)
     lay = moe.moe_workspace_plan(E, H, I, K, 4, cfg.align_rows, 0, fmt)
-    assert lay["act"] < lay["total"]  # the decode path
+    assert lay["act"] < lay["status"]  # the decode path
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     out = torch.full((4, H), POISON_BF16, dtype=torch.int16, device=dev())
     moe.moe_forward(up(x), up(ids), up(w), up(w1q), up(w1s), up(w2q), up(w2s), fmt,
@@ -332,7 +332,7 @@ def test_one_launch_layer_many_token_bytes(t_cap, t_live, E, H, I, K, fmt, act, 
     for e in np.unique(ids):  # only routed experts are ever read
         (w1q[e], w1s[e]), (w2q[e], w2s[e]) = ew.fc1(e), ew.fc2(e)
     lay = moe.moe_workspace_plan(E, H, I, K, t_cap, cfg.align_rows, 0, fmt)
-    assert lay["act"] < lay["total"]  # the decode path
+    assert lay["act"] < lay["status"]  # the decode path
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     out = torch.full((t_cap, H), POISON_BF16, dtype=torch.int16, device=dev())
     lim32 = float(np.float32(lim))
@@ -434,7 +434,7 @@ def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
     lim32 = float(np.float32(lim))
     row_cap = cfg.row_cap or 0
     lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32)
-    assert lay["act"] < lay["total"]
+    assert lay["act"] < lay["status"]
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     moe.moe_fc1_decode(up(x), up(ids), d_w1q, d_w1s, I, fmt, act, lim32, A, row_cap,
                        t_live=up(np.array([t_live], np.int32)), workspace=ws)
@@ -472,3 +472,58 @@ def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
         assert np.array_equal(act_rows[seg].view(np.uint32), ref_act.view(np.uint32)), e
     dead = np.setdiff1d(np.arange(R), live_rows)
     assert np.all(c1[dead] == (POISON_U8 << 8 | POISON_U8))
+
+
+def test_barrier_timeout_is_reported_in_the_launch_outputs():
+    """A grid-barrier wait of the one-launch layer that gives up (forced from
+    the host: a negative spin limit makes every wait give up at once, and every
+    kernel still exits normally) shows in that launch's own outputs: each
+    workgroup's status slot says so and its output columns of the live tokens
+    are NaN. With the limit restored the next launch is correct again and all
+    slots read 0."""
+    name = "decode"
+    cfg = synth.get(name)
+    E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk
+    x, ids, w = synth.make_workload(cfg, 4, 7)
+    (w1q, w1s), (w2q, w2s) = host_weights(name)
+    d = device_weights(name)
+    assert moe.decode_layer_applies(4, K, H, I)
+    lay = moe.moe_workspace_plan(E, H, I, K, 4)
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    out = torch.full((4, H), POISON_BF16, dtype=torch.int16, device=dev())
+    live = up(np.array([3], np.int32))
+    before = moe.moe_barrier_timeouts()
+    old = moe.moe_barrier_spin_limit(-1)
+    try:
+        say("one-launch layer with every barrier wait forced to give up")
+        moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_barrier_spin_limit(old)
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    status = _ws_view(ws, lay, "status", np.int32, (1024,))
+    assert np.all(status[:grid] == 1)
+    assert np.all(status[grid:].view(np.uint32) == np.uint32(POISON_U8 * 0x01010101))
+    got = down(out)
+    assert np.all(got[:3] == 0x7FC0), "output columns of a failed workgroup must be NaN"
+    assert np.all(got[3:] == POISON_BF16)
+    assert moe.moe_barrier_timeouts() >= before + grid
+    # the next launch, with the default limit, is whole again
+    say("one-launch layer with the default spin limit")
+    moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(_ws_view(ws, lay, "status", np.int32, (1024,))[:grid] == 0)
+    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, 3, "fp32")
+    assert_bf16_close(down(out)[:3], ref, "after a forced timeout")
+
+
+@pytest.mark.parametrize("name,t_cap", [("decode", 4), ("tiny", 8), ("sweep", 64)])
+def test_missing_routing_weights_mean_ones(name, t_cap):
+    cfg = synth.get(name)
+    x, ids, _ = synth.make_workload(cfg, t_cap, 8)
+    d = device_weights(name)
+    ones = np.ones(ids.shape, np.float32)
+    a, _ = moe.moe_forward(up(x), up(ids), None, *d, align_rows=cfg.align_rows)
+    b, _ = moe.moe_forward(up(x), up(ids), up(ones), *d, align_rows=cfg.align_rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(a), down(b))
