@@ -83,6 +83,7 @@ _SIGNATURES = {
                                    ctypes.c_size_t, _vp]),
     "moe_fc1_decode": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp,
                                       ctypes.c_size_t, _vp]),
+    "moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Tensors), _vp]),
     "moe_barrier_timeouts": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
     "moe_barrier_spin_limit": (_i32, [_i32]),
 }
@@ -404,6 +405,42 @@ def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", a
                          workspace.numel(), _stream())
     _check("moe_forward", st)
     return out, workspace
+
+
+# Bytes of the library's static workspace behind moe_forward_noalloc (mirrors
+# the header's MOE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32",
+                        act="swiglu", clamp_limit=float("inf"), align_rows=16, row_cap=0,
+                        t_live=None, out=None):
+    """moe_forward with the library's static per-device workspace instead of a
+    caller buffer (for callers that cannot allocate; the call allocates nothing
+    when ``out`` and ``topk_w`` are given). Calls on one device must not overlap.
+    Returns out (BF16 bits int16 [t_cap, H])."""
+    lib = load_library()
+    xb = _bf16_view(x, "x")
+    if xb.dim() != 2:
+        raise ValueError("x must be [t_cap, hidden]")
+    t_cap, hidden = xb.shape
+    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales)
+    if topk_w is None:
+        topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
+    _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
+    if out is None:
+        out = torch.empty((t_cap, hidden), dtype=torch.int16, device=xb.device)
+    ob = _shape(_bf16_view(out, "out"), "out", (t_cap, hidden))
+    if t_live is not None:
+        _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
+    _same_device(xb, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, ob, t_live)
+    prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
+                    clamp_limit)
+    tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
+                    _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
+    _check("moe_forward_noalloc", lib.moe_forward_noalloc(ctypes.byref(prob), ctypes.byref(tens),
+                                                          _stream()))
+    return out
 
 
 def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",

@@ -4,6 +4,7 @@
 // invalid request returns an error with nothing enqueued.
 #include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "../../include/moe_fp8.h"
 #include "kernels.h"
@@ -30,9 +31,34 @@ int device_cu_count() {
 
 }  // namespace moe
 
+// Workspace of moe_forward_noalloc: one copy per device, held until the
+// process ends. Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxTopk = 64;
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup failed.
+void* scratch_address() {
+  static std::atomic<void*> cache[kMaxDevices];
+  static std::mutex lock;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> g(lock);
+  ptr = cache[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
 
 bool fmt_ok(int f) { return f == MOE_SCALE_FP32 || f == MOE_SCALE_FP32_POW2 || f == MOE_SCALE_UE8M0; }
 bool act_ok(int a) {
@@ -312,6 +338,9 @@ int32_t moe_barrier_spin_limit(int32_t polls) {
   return old;
 }
 
+static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout& L,
+                               const moe_tensors* t, void* workspace, void* stream);
+
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
                        size_t workspace_bytes, void* stream) {
   moe_workspace_layout L;
@@ -319,6 +348,23 @@ moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspa
   if (st != MOE_OK) return st;
   if (!t || !workspace) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
+  return forward_impl(p, L, t, workspace, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_problem* p, const moe_tensors* t, void* stream) {
+  moe_workspace_layout L;
+  const moe_status st = moe_workspace_plan(p, &L);
+  if (st != MOE_OK) return st;
+  if (!t) return MOE_ERR_INVALID_ARG;
+  if (L.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_CAPACITY;
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_HIP;
+  return forward_impl(p, L, t, ws, stream);
+}
+
+static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout& L,
+                               const moe_tensors* t, void* workspace, void* stream) {
+  if (!t || !workspace) return MOE_ERR_INVALID_ARG;
   if (p->t_cap > 0 && (!t->x || !t->topk_ids || !t->topk_w || !t->w1 || !t->w1_scales ||
                        !t->w2 || !t->w2_scales || !t->out))
     return MOE_ERR_INVALID_ARG;

@@ -306,6 +306,27 @@ size_t moe_workspace_bytes(const moe_problem* p);
 moe_status moe_forward(const moe_problem* p, const moe_tensors* t, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * layer as moe_forward computes it, with the workspace taken from a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library instead of a
+ * caller buffer. The array exists once per device (its address is looked up
+ * on the first call on that device, with that device current) and is held
+ * until the process ends. Nothing is allocated or freed by any call.
+ * The caller still passes all inputs and `t->out`. The workspace layout is
+ * moe_workspace_plan's; the array keeps the last call's contents, and since
+ * moe_forward does not depend on prior workspace contents nothing needs
+ * clearing. Every call on one device shares that device's array, so calls on
+ * one device that overlap in time (different streams without ordering, or
+ * several host threads) race and give wrong results; order them.
+ * Errors: as moe_forward, and CAPACITY when moe_workspace_bytes(p) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB: every decode-sized problem of the
+ * one-launch path, the tiny layer, and general-path layers up to about
+ * 64 tokens of the 256-expert sweep shape), HIP if the array's address
+ * cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES 67108864
+moe_status moe_forward_noalloc(const moe_problem* p, const moe_tensors* t, void* stream);
+
 /* The first launch of moe_forward's decode path, on its own: routing
  * alignment, activation quantization and FC1 with SiLU(gate)*up in one
  * kernel (vLLM PR #59128, Purpose; vLLM PR #65794, Details; TensorRT-LLM

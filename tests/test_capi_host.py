@@ -229,3 +229,16 @@ def test_decode_layer_applies_matches_the_workspace_plan(lib):
     assert moe.decode_layer_applies(8, 8, 6144, 256)       # 49 KB of token codes
     assert not moe.decode_layer_applies(9, 7, 7168, 256)   # 64.6 KB
     assert not moe.decode_layer_applies(4, 8, 4096, 2048)  # FC2 input rows too large
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(B._Problem), ctypes.POINTER(B._Tensors),
+                                        ctypes.c_void_p]
+    t = B._Tensors(*([FAKE.value] * 9))
+    big = _problem()  # the 4096-token layer needs about 1 GB of workspace
+    assert lib.moe_workspace_bytes(ctypes.byref(big)) > _header_macros("MOE_NOALLOC_")["MOE_NOALLOC_SCRATCH_BYTES"]
+    assert lib.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(t), NULL) == CAPACITY
+    assert lib.moe_forward_noalloc(ctypes.byref(_problem(hidden=100)), ctypes.byref(t), NULL) == INVALID
+    assert lib.moe_forward_noalloc(ctypes.byref(_problem(t_cap=4)), None, NULL) == INVALID
+    assert moe.NOALLOC_SCRATCH_BYTES == _header_macros("MOE_NOALLOC_")["MOE_NOALLOC_SCRATCH_BYTES"]
