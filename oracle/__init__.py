@@ -16,8 +16,9 @@ Sources (three web pages, cited by title and section):
 * vLLM PR #65794 (per-layer activation-scale format, fused SiLU+quant) --
   Overview; Claims; Details (fused-kernel and sorted-A bullets).
 * TensorRT-LLM PR #21250 "Triton FP8-activation MoE for decode-sized
-  batches on Hopper" -- description; rounding-fix commit message; review
-  comments on expert-parallel ids and block-scale order.
+  batches on Hopper" -- description; rounding-fix commit message (the
+  ``reciprocal`` rounding convention); review comments on expert-parallel
+  ids and block-scale order.
 
 Pins (tests/test_oracle_*.py) tie every function here to something other
 than itself: closed forms, exhaustive codec checks, exact rational
@@ -29,15 +30,16 @@ pages name the variants without giving a formula (see ``moe.swiglu``).
 
 from .fp_formats import (E4M3_MAX, bf16_bits_to_f64, bf16_from_f64,
                          e4m3_decode, e4m3_encode)
-from .quant import (SCALE_FMTS, group_scales, quantize_groups,
-                    scales_to_f64)
+from .quant import (ROUNDINGS, SCALE_FMTS, group_scales, quantize_groups,
+                    reciprocal_multiplier, scales_to_f64)
 from .align import align
 from .moe import (ACTS, combine, forward, grouped_gemm, silu_mul_quant,
                   swiglu, token_forward, unquantized_reference)
 
 __all__ = [
     "E4M3_MAX", "bf16_bits_to_f64", "bf16_from_f64", "e4m3_decode",
-    "e4m3_encode", "SCALE_FMTS", "group_scales", "quantize_groups",
+    "e4m3_encode", "ROUNDINGS", "SCALE_FMTS", "group_scales", "quantize_groups",
+    "reciprocal_multiplier",
     "scales_to_f64", "align", "ACTS", "combine", "forward", "grouped_gemm",
     "silu_mul_quant", "swiglu", "token_forward", "unquantized_reference",
 ]

@@ -20,6 +20,13 @@ Stages and the passages they follow:
   columns, up the second half (the pages leave the order open; the weight
   layout [E, 2I, H] puts gate rows first here). SiLU is evaluated in fp64 as
   g / (1 + exp(-g)), times u in fp64, and rounded once to float32.
+* ``rounding="reciprocal"`` -- the convention of the fused CUTLASS op that
+  TensorRT-LLM PR #21250 follows (rounding-fix commit message; review comment
+  on the block-scale order): both quantizers multiply by fl32(448 / amax)
+  (see ``quant``), the SwiGLU output is rounded to BF16 before its FP8
+  quantization, and each K block's scale is the float32 product
+  fl32(sa * sw), formed before it multiplies the block's dot product. The
+  default ``divide`` is vLLM PR #65794's arithmetic described above.
 * ``combine`` -- the routing weights scale the BF16 expert outputs, in top-k
   order, not the FC2 accumulators (TensorRT-LLM PR #21250, rounding-fix
   commit message). Accumulated in fp64, rounded once to BF16. A token with
@@ -36,7 +43,7 @@ import numpy as np
 
 from .align import align
 from .fp_formats import bf16_bits_to_f64, bf16_from_f64, e4m3_decode
-from .quant import GROUP, quantize_groups, scales_to_f64
+from .quant import GROUP, ROUNDINGS, quantize_groups, scales_to_f64
 
 ACTS = ("swiglu", "swiglu_clamp", "swiglu_clamp_after_silu")
 
@@ -47,13 +54,16 @@ def _dec(codes):
     return _DECODE_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def gemm_rows(a_codes, a_scales, w_codes, w_scales):
+def gemm_rows(a_codes, a_scales, w_codes, w_scales, rounding="divide"):
     """C[m, n] = bf16( sum_kb (sa[kb, m] * sw[n/128, kb]) * sum_{j<128} a*w ).
 
     ``a_codes`` [m, Kd] uint8, ``a_scales`` [Kd/128, m] float64 (decoded),
     ``w_codes`` [N, Kd] uint8, ``w_scales`` [N/128, Kd/128] float32.
+    Under ``rounding="reciprocal"`` the block factor is fl32(sa * sw).
     Returns BF16 bits [m, N].
     """
+    if rounding not in ROUNDINGS:
+        raise ValueError(rounding)
     a = _dec(a_codes)
     w = _dec(w_codes)
     m, kd = a.shape
@@ -65,6 +75,9 @@ def gemm_rows(a_codes, a_scales, w_codes, w_scales):
         cols = slice(kb * GROUP, (kb + 1) * GROUP)
         part = a[:, cols] @ w[:, cols].T  # exact (see module docstring)
         scale = a_scales[kb][:, None] * sw[:, kb][None, :]  # exact in fp64
+        if rounding == "reciprocal":  # the float32 product of the two scales
+            scale = (a_scales[kb].astype(np.float32)[:, None]
+                     * sw[:, kb].astype(np.float32)[None, :]).astype(np.float64)
         acc = acc + scale * part
     return bf16_from_f64(acc)
 
@@ -73,7 +86,8 @@ def _expert(weights, e):
     return weights(e) if callable(weights) else (weights[0][e], weights[1][e])
 
 
-def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=None):
+def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=None,
+                 rounding="divide"):
     """Grouped FP8 GEMM over the live rows of every expert segment.
 
     ``a_codes``/``a_scales`` are indexed by A row; row r of the output reads
@@ -95,7 +109,7 @@ def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=Non
         w_codes, w_scales = _expert(weights, e)
         rows = np.arange(int(offsets[e]), int(offsets[e]) + cnt)
         src = rows if row_index is None else np.asarray(row_index)[rows]
-        out = gemm_rows(a_codes[src], sa_all[:, src], w_codes, w_scales)
+        out = gemm_rows(a_codes[src], sa_all[:, src], w_codes, w_scales, rounding)
         if c is None:
             c = np.zeros((total, out.shape[1]), dtype=np.uint16)
         c[rows] = out
@@ -105,8 +119,9 @@ def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=Non
     return c, live
 
 
-def swiglu(g, u, act="swiglu", clamp_limit=np.inf):
-    """SiLU(gate) * up in fp64, rounded once to float32.
+def swiglu(g, u, act="swiglu", clamp_limit=np.inf, rounding="divide"):
+    """SiLU(gate) * up in fp64, rounded once to float32 (and then to BF16,
+    held in float32, under ``rounding="reciprocal"``).
 
     Clamp variants (TensorRT-LLM PR #21250, Test Coverage, names "clamp" and
     "clamp after SiLU"; vLLM PR #65794, Details, ``clamp_limit``). The pages
@@ -117,6 +132,8 @@ def swiglu(g, u, act="swiglu", clamp_limit=np.inf):
     * ``swiglu_clamp_after_silu``: SiLU(gate) clamped above at L, times up
       clamped to [-L, L].
     """
+    if rounding not in ROUNDINGS:
+        raise ValueError(rounding)
     g = np.asarray(g, dtype=np.float64)
     u = np.asarray(u, dtype=np.float64)
     lim = np.float64(clamp_limit)
@@ -131,15 +148,18 @@ def swiglu(g, u, act="swiglu", clamp_limit=np.inf):
         u = np.clip(u, -lim, lim)
     else:
         raise ValueError(act)
-    return (s * u).astype(np.float32)
+    y = (s * u).astype(np.float32)
+    if rounding == "reciprocal":  # the fused op's epilogue rounds to BF16 first
+        y = bf16_bits_to_f64(bf16_from_f64(y.astype(np.float64))).astype(np.float32)
+    return y
 
 
-def silu_mul_quant(c1_bits, fmt, act="swiglu", clamp_limit=np.inf):
+def silu_mul_quant(c1_bits, fmt, act="swiglu", clamp_limit=np.inf, rounding="divide"):
     """FC1 output rows [rows, 2I] (BF16 bits) -> (codes [rows, I], scales [I/128, rows])."""
     c1 = bf16_bits_to_f64(c1_bits)
     inter = c1.shape[1] // 2
-    y = swiglu(c1[:, :inter], c1[:, inter:], act, clamp_limit)
-    return quantize_groups(y, fmt)
+    y = swiglu(c1[:, :inter], c1[:, inter:], act, clamp_limit, rounding)
+    return quantize_groups(y, fmt, rounding)
 
 
 def combine(y_bits, pair_to_row, topk_w, t_live, hidden=None):
@@ -163,7 +183,7 @@ def combine(y_bits, pair_to_row, topk_w, t_live, hidden=None):
 
 
 def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
-            act="swiglu", clamp_limit=np.inf, num_experts=None):
+            act="swiglu", clamp_limit=np.inf, num_experts=None, rounding="divide"):
     """The whole layer on the aligned, per-expert-contiguous row layout.
 
     ``x_bits`` [t_cap, H] BF16 bits; ``topk_ids``/``topk_w`` [t_cap, K];
@@ -175,26 +195,26 @@ def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
     if num_experts is None:
         num_experts = w1[0].shape[0]
     return forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live,
-                     align_rows, fmt, act, clamp_limit)
+                     align_rows, fmt, act, clamp_limit, rounding)
 
 
 def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
-              fmt, act="swiglu", clamp_limit=np.inf):
+              fmt, act="swiglu", clamp_limit=np.inf, rounding="divide"):
     """``forward`` with an explicit expert count (for callable weights)."""
     k = np.asarray(topk_ids).shape[1]
     al = align(topk_ids, t_live, num_experts, align_rows)
     x = bf16_bits_to_f64(np.asarray(x_bits)[:t_live]).astype(np.float32)
-    xq, xs = quantize_groups(x, fmt)
+    xq, xs = quantize_groups(x, fmt, rounding)
     token_of_row = np.where(al["row_to_pair"] >= 0, al["row_to_pair"] // k, 0)
-    c1, live = grouped_gemm(xq, xs, fmt, w1, al["counts"], al["offsets"], token_of_row)
-    hq, hs = silu_mul_quant(c1[live], fmt, act, clamp_limit)
+    c1, live = grouped_gemm(xq, xs, fmt, w1, al["counts"], al["offsets"], token_of_row, rounding)
+    hq, hs = silu_mul_quant(c1[live], fmt, act, clamp_limit, rounding)
     total = int(al["offsets"][-1])
     inter = c1.shape[1] // 2
     hq_full = np.zeros((total, inter), dtype=np.uint8)
     hq_full[live] = hq
     hs_full = np.zeros((inter // GROUP, total), dtype=hs.dtype)
     hs_full[:, live] = hs
-    y, _ = grouped_gemm(hq_full, hs_full, fmt, w2, al["counts"], al["offsets"])
+    y, _ = grouped_gemm(hq_full, hs_full, fmt, w2, al["counts"], al["offsets"], rounding=rounding)
     out = combine(y, al["pair_to_row"], topk_w, t_live, np.asarray(x_bits).shape[1])
     res = dict(al)
     res.update(xq=xq, xs=xs, c1=c1, live=live, hq=hq_full, hs=hs_full, y=y, out=out)
@@ -202,7 +222,7 @@ def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
 
 
 def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
-                  act="swiglu", clamp_limit=np.inf, tokens=None):
+                  act="swiglu", clamp_limit=np.inf, tokens=None, rounding="divide"):
     """Dense per-token brute force: no alignment, no row maps, one token at a time.
 
     ``tokens`` selects which tokens to evaluate (default: all t < t_live);
@@ -214,7 +234,7 @@ def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
     rows = []
     for t in tokens:
         x = bf16_bits_to_f64(np.asarray(x_bits)[t:t + 1]).astype(np.float32)
-        xq, xs = quantize_groups(x, fmt)
+        xq, xs = quantize_groups(x, fmt, rounding)
         hidden = np.asarray(x_bits).shape[1]
         acc = np.zeros(hidden, dtype=np.float64)
         for kk in range(ids.shape[1]):
@@ -223,9 +243,9 @@ def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
                 continue
             w1c, w1s = _expert(w1, e)
             w2c, w2s = _expert(w2, e)
-            c1 = gemm_rows(xq, scales_to_f64(xs, fmt), w1c, w1s)
-            hq, hs = silu_mul_quant(c1, fmt, act, clamp_limit)
-            y = gemm_rows(hq, scales_to_f64(hs, fmt), w2c, w2s)
+            c1 = gemm_rows(xq, scales_to_f64(xs, fmt), w1c, w1s, rounding)
+            hq, hs = silu_mul_quant(c1, fmt, act, clamp_limit, rounding)
+            y = gemm_rows(hq, scales_to_f64(hs, fmt), w2c, w2s, rounding)
             acc = acc + np.float64(topk_w[t, kk]) * bf16_bits_to_f64(y[0])
         rows.append(bf16_from_f64(acc))
     hidden = np.asarray(x_bits).shape[1]
