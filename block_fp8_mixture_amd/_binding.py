@@ -10,6 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoefp8.so"
 
 SCALE_FMTS = {"fp32": 0, "pow2": 1, "ue8m0": 2}
+ROUNDINGS = {"divide": 0, "reciprocal": 1}
 ACTS = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_clamp_after_silu": 2}
 # Row-tile geometry of the grouped GEMM (mirrors the header's macros), used to
 # interpret the tiles_visited counter.
@@ -48,7 +49,8 @@ class MoeError(RuntimeError):
 class _Problem(ctypes.Structure):
     _fields_ = [("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("topk", _i32),
                 ("t_cap", _i32), ("align_rows", _i32), ("row_cap", _i32),
-                ("scale_fmt", ctypes.c_int), ("act", ctypes.c_int), ("clamp_limit", _f32)]
+                ("scale_fmt", ctypes.c_int), ("act", ctypes.c_int), ("clamp_limit", _f32),
+                ("rounding", ctypes.c_int)]
 
 
 class _Tensors(ctypes.Structure):
@@ -70,12 +72,13 @@ _SIGNATURES = {
     "moe_min_row_cap": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_align": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
-    "moe_act_quant": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.c_int, _vp, _vp, _vp]),
+    "moe_act_quant": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                     _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp, _vp,
                                             _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                             _vp]),
     "moe_silu_mul_quant": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, ctypes.c_int, _f32,
-                                          ctypes.c_int, _vp, _vp, _vp]),
+                                          ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_topk_combine": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]),
     "moe_workspace_plan": (ctypes.c_int, [ctypes.POINTER(_Problem), ctypes.POINTER(_Layout)]),
     "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Problem)]),
@@ -164,6 +167,12 @@ def _fmt(fmt):
     return SCALE_FMTS[fmt]
 
 
+def _rounding(rounding):
+    if rounding not in ROUNDINGS:
+        raise ValueError(f"rounding must be one of {list(ROUNDINGS)}")
+    return ROUNDINGS[rounding]
+
+
 def _scale_dtype(fmt):
     return torch.uint8 if fmt == "ue8m0" else torch.float32
 
@@ -217,7 +226,7 @@ def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, o
     return out
 
 
-def moe_act_quant(x, fmt="fp32", t_live=None, xq=None, xs=None):
+def moe_act_quant(x, fmt="fp32", t_live=None, xq=None, xs=None, rounding="divide"):
     """Per-token 1x128 quantization. Returns (xq uint8 [t_cap, H], xs [H/128, t_cap])."""
     lib = load_library()
     xb = _bf16_view(x, "x")
@@ -231,8 +240,8 @@ def moe_act_quant(x, fmt="fp32", t_live=None, xq=None, xs=None):
     _shape(_need(xq, "xq", torch.uint8), "xq", (t_cap, hidden))
     _shape(_need(xs, "xs", _scale_dtype(fmt)), "xs", (hidden // 128, t_cap))
     _same_device(xb, xq, xs)
-    st = lib.moe_act_quant(_ptr(xb), t_cap, _live(t_live), hidden, _fmt(fmt), _ptr(xq), _ptr(xs),
-                           _stream())
+    st = lib.moe_act_quant(_ptr(xb), t_cap, _live(t_live), hidden, _fmt(fmt), _rounding(rounding),
+                           _ptr(xq), _ptr(xs), _stream())
     _check("moe_act_quant", st)
     return xq, xs
 
@@ -276,7 +285,7 @@ def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap
 
 
 def moe_silu_mul_quant(gate_up, counts, offsets, act="swiglu", clamp_limit=float("inf"),
-                       fmt="fp32", hq=None, hs=None):
+                       fmt="fp32", hq=None, hs=None, rounding="divide"):
     """SiLU(gate)*up + 1x128 FP8 quantization of live rows.
     Returns (hq uint8 [row_cap, I], hs [I/128, row_cap])."""
     lib = load_library()
@@ -298,8 +307,8 @@ def moe_silu_mul_quant(gate_up, counts, offsets, act="swiglu", clamp_limit=float
     if act not in ACTS:
         raise ValueError(f"act must be one of {list(ACTS)}")
     st = lib.moe_silu_mul_quant(_ptr(gu), inter, _ptr(counts), _ptr(offsets), num_experts,
-                                row_cap, ACTS[act], float(clamp_limit), _fmt(fmt), _ptr(hq),
-                                _ptr(hs), _stream())
+                                row_cap, ACTS[act], float(clamp_limit), _fmt(fmt),
+                                _rounding(rounding), _ptr(hq), _ptr(hs), _stream())
     _check("moe_silu_mul_quant", st)
     return hq, hs
 
@@ -324,29 +333,30 @@ def moe_topk_combine(y, pair_to_row, topk_w, t_live=None, out=None):
     return out
 
 
-def _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act, clamp_limit):
+def _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act, clamp_limit,
+             rounding="divide"):
     if act not in ACTS:
         raise ValueError(f"act must be one of {list(ACTS)}")
     return _Problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap or 0, _fmt(fmt),
-                    ACTS[act], float(clamp_limit))
+                    ACTS[act], float(clamp_limit), _rounding(rounding))
 
 
 def moe_workspace_plan(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
-                       fmt="fp32", act="swiglu", clamp_limit=float("inf")):
+                       fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide"):
     """Byte offsets of every intermediate in the forward workspace (dict)."""
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit)
+                    clamp_limit, rounding)
     lay = _Layout()
     _check("moe_workspace_plan", lib.moe_workspace_plan(ctypes.byref(prob), ctypes.byref(lay)))
     return {name: getattr(lay, name) for name, _ in _Layout._fields_}
 
 
 def moe_workspace_bytes(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
-                        fmt="fp32", act="swiglu", clamp_limit=float("inf")):
+                        fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide"):
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit)
+                    clamp_limit, rounding)
     return int(lib.moe_workspace_bytes(ctypes.byref(prob)))
 
 
@@ -372,7 +382,7 @@ def _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2=None, w2_scales=None):
 
 def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", act="swiglu",
                 clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None, out=None,
-                workspace=None):
+                workspace=None, rounding="divide"):
     """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8).
     ``topk_w=None`` weights every routed pair by one."""
     lib = load_library()
@@ -385,7 +395,7 @@ def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", a
         topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
     _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit)
+                    clamp_limit, rounding)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if need == 0:
         lay = _Layout()
@@ -414,7 +424,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32",
                         act="swiglu", clamp_limit=float("inf"), align_rows=16, row_cap=0,
-                        t_live=None, out=None):
+                        t_live=None, out=None, rounding="divide"):
     """moe_forward with the library's static per-device workspace instead of a
     caller buffer (for callers that cannot allocate; the call allocates nothing
     when ``out`` and ``topk_w`` are given). Calls on one device must not overlap.
@@ -435,7 +445,7 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
         _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
     _same_device(xb, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, ob, t_live)
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit)
+                    clamp_limit, rounding)
     tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
                     _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
     _check("moe_forward_noalloc", lib.moe_forward_noalloc(ctypes.byref(prob), ctypes.byref(tens),
@@ -445,7 +455,7 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
 
 def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
                    clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None,
-                   workspace=None):
+                   workspace=None, rounding="divide"):
     """The decode path's first launch alone (routing, activation quantization and
     FC1 with SiLU(gate)*up), writing moe_forward's workspace. Returns the workspace."""
     lib = load_library()
@@ -457,7 +467,7 @@ def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
     if w_inter != inter:
         raise ValueError("w1 shape disagrees with inter")
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap,
-                    fmt, act, clamp_limit)
+                    fmt, act, clamp_limit, rounding)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xb.device)

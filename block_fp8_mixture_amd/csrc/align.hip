@@ -194,14 +194,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
     int32_t* __restrict__ pair_to_row, int n_align, const uint16_t* __restrict__ x, int hidden,
-    uint8_t* __restrict__ xq, void* __restrict__ xs) {
+    uint8_t* __restrict__ xq, void* __restrict__ xs, int rnd) {
   if (static_cast<int>(blockIdx.x) < n_align) {
     align_block(blockIdx.x, ids, t_cap, t_live_dev, topk, num_experts, align_rows, counts,
                 offsets, row_to_pair, pair_to_row);
     return;
   }
   const int64_t gid = static_cast<int64_t>(blockIdx.x - n_align) * (kThreads / 16) + (threadIdx.x >> 4);
-  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15);
+  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15, rnd);
 }
 
 int align_blocks(int t_cap, int topk) {
@@ -224,7 +224,7 @@ hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev
 hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                        int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                        int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
-                       int fmt, uint8_t* xq, void* xs, hipStream_t stream) {
+                       int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream) {
   const int n_align = align_blocks(t_cap, topk);
   const int64_t groups = static_cast<int64_t>(t_cap) * (hidden / kGroup);
   const int64_t n_quant = (groups + kThreads / 16 - 1) / (kThreads / 16);
@@ -233,15 +233,15 @@ hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev,
   if (fmt == kFp32)
     hipLaunchKernelGGL(prep_kernel<kFp32>, grid, dim3(kThreads), 0, stream, ids, t_cap, t_live_dev,
                        topk, num_experts, align_rows, counts, offsets, row_to_pair, pair_to_row,
-                       n_align, x, hidden, xq, xs);
+                       n_align, x, hidden, xq, xs, rounding);
   else if (fmt == kFp32Pow2)
     hipLaunchKernelGGL(prep_kernel<kFp32Pow2>, grid, dim3(kThreads), 0, stream, ids, t_cap,
                        t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
-                       pair_to_row, n_align, x, hidden, xq, xs);
+                       pair_to_row, n_align, x, hidden, xq, xs, rounding);
   else
     hipLaunchKernelGGL(prep_kernel<kUe8m0>, grid, dim3(kThreads), 0, stream, ids, t_cap,
                        t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
-                       pair_to_row, n_align, x, hidden, xq, xs);
+                       pair_to_row, n_align, x, hidden, xq, xs, rounding);
   return hipGetLastError();
 }
 

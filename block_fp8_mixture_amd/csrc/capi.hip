@@ -64,6 +64,7 @@ bool fmt_ok(int f) { return f == MOE_SCALE_FP32 || f == MOE_SCALE_FP32_POW2 || f
 bool act_ok(int a) {
   return a == MOE_ACT_SWIGLU || a == MOE_ACT_SWIGLU_CLAMP || a == MOE_ACT_SWIGLU_CLAMP_AFTER_SILU;
 }
+bool rounding_ok(int r) { return r == MOE_ROUND_DIVIDE || r == MOE_ROUND_RECIPROCAL; }
 bool dim128(int32_t d) { return d > 0 && d % 128 == 0; }
 // Limits of the GEMM kernels: k <= 32768 (per-tile weight scale table in
 // LDS) and 32-bit byte offsets within one operand (a_rows * k and one
@@ -123,12 +124,14 @@ moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_li
 }
 
 moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live_dev,
-                         int32_t hidden, moe_scale_fmt fmt, uint8_t* xq, void* xs, void* stream) {
-  if (t_cap < 0 || !dim128(hidden) || !fmt_ok(fmt)) return MOE_ERR_INVALID_ARG;
+                         int32_t hidden, moe_scale_fmt fmt, moe_rounding rounding, uint8_t* xq,
+                         void* xs, void* stream) {
+  if (t_cap < 0 || !dim128(hidden) || !fmt_ok(fmt) || !rounding_ok(rounding))
+    return MOE_ERR_INVALID_ARG;
   if (t_cap > 0 && (!x || !xq || !xs)) return MOE_ERR_INVALID_ARG;
   if (static_cast<int64_t>(t_cap) * (hidden / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (t_cap == 0) return MOE_OK;
-  return from_hip(moe::launch_act_quant(x, t_cap, t_live_dev, hidden, fmt, xq, xs,
+  return from_hip(moe::launch_act_quant(x, t_cap, t_live_dev, hidden, fmt, rounding, xq, xs,
                                         as_stream(stream)));
 }
 
@@ -178,9 +181,10 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
 moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               const int32_t* expert_counts, const int32_t* expert_offsets,
                               int32_t num_experts, int32_t row_cap, moe_act act,
-                              float clamp_limit, moe_scale_fmt fmt, uint8_t* hq, void* hs,
-                              void* stream) {
-  if (!dim128(inter) || num_experts < 1 || row_cap < 0 || !fmt_ok(fmt) || !act_ok(act))
+                              float clamp_limit, moe_scale_fmt fmt, moe_rounding rounding,
+                              uint8_t* hq, void* hs, void* stream) {
+  if (!dim128(inter) || num_experts < 1 || row_cap < 0 || !fmt_ok(fmt) || !act_ok(act) ||
+      !rounding_ok(rounding))
     return MOE_ERR_INVALID_ARG;
   if (act != MOE_ACT_SWIGLU && !(clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
@@ -188,8 +192,8 @@ moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
   if (static_cast<int64_t>(row_cap) * (inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (row_cap == 0) return MOE_OK;
   return from_hip(moe::launch_silu_mul_quant(gate_up, inter, expert_counts, expert_offsets,
-                                             num_experts, row_cap, act, clamp_limit, fmt, hq,
-                                             hs, as_stream(stream)));
+                                             num_experts, row_cap, act, clamp_limit, fmt,
+                                             rounding, hq, hs, as_stream(stream)));
 }
 
 moe_status moe_topk_combine(const uint16_t* y, int32_t row_cap, const int32_t* pair_to_row,
@@ -208,7 +212,7 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   if (!p || !L) return MOE_ERR_INVALID_ARG;
   if (p->num_experts < 1 || !dim128(p->hidden) || !dim128(p->inter) || p->topk < 1 ||
       p->topk > kMaxTopk || p->t_cap < 0 || p->align_rows < 1 || p->row_cap < 0 ||
-      !fmt_ok(p->scale_fmt) || !act_ok(p->act))
+      !fmt_ok(p->scale_fmt) || !act_ok(p->act) || !rounding_ok(p->rounding))
     return MOE_ERR_INVALID_ARG;
   if (p->act != MOE_ACT_SWIGLU && !(p->clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (p->num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -278,6 +282,7 @@ moe::DownCombineArgs down_combine_args(const moe_problem* p, const moe_tensors* 
   d.hs = ws + L.hs;
   d.y = reinterpret_cast<uint16_t*>(ws + L.y);
   d.out = t->out;
+  d.rounding = p->rounding;
   return d;
 }
 
@@ -308,6 +313,7 @@ moe::DecodeFc1Args fc1_decode_args(const moe_problem* p, const moe_tensors* t,
   f.xs = ws + L.xs;
   f.c1 = reinterpret_cast<uint16_t*>(ws + L.c1);
   f.act_out = reinterpret_cast<float*>(ws + L.act);
+  f.rounding = p->rounding;
   return f;
 }
 
@@ -408,8 +414,8 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   }
   // Alignment and activation quantization share one launch (independent work).
   e = moe::launch_prep(t->topk_ids, p->t_cap, t->t_live_dev, p->topk, p->num_experts,
-                       p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden, p->scale_fmt, xq,
-                       xs, s);
+                       p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden, p->scale_fmt,
+                       p->rounding, xq, xs, s);
 
   moe::GemmArgs g;
   g.fmt = p->scale_fmt;
@@ -420,6 +426,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   g.max_rows_per_expert = pairs < R ? pairs : R;
   g.max_live_experts = pairs < p->num_experts ? pairs : p->num_experts;
   g.tiles_visited = nullptr;
+  g.rounding = p->rounding;
   if (e == hipSuccess) {  // FC1: A rows gathered from the token-major quantized activations
     g.a = xq;
     g.a_scales = xs;
@@ -445,7 +452,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   }
   if (e == hipSuccess)
     e = moe::launch_silu_mul_quant(c1, p->inter, counts, offsets, p->num_experts, R, p->act,
-                                   p->clamp_limit, p->scale_fmt, hq, hs, s);
+                                   p->clamp_limit, p->scale_fmt, p->rounding, hq, hs, s);
   if (e == hipSuccess) {  // FC2
     g.a = hq;
     g.a_scales = hs;

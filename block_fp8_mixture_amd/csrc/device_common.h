@@ -29,18 +29,50 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 enum ScaleFmt : int { kFp32 = 0, kFp32Pow2 = 1, kUe8m0 = 2 };
 
-// The float32 scale a group is divided by. amax/448 is an IEEE division (the
-// library is built without fast-math, so it is correctly rounded); the floor
-// constant 1/229376 is folded by the compiler with correct rounding. The
-// power-of-two forms round up: a non-zero mantissa bumps the exponent.
-__device__ __forceinline__ float group_scale(float amax, int fmt) {
-  float s = fmaxf(amax / 448.0f, 1.0f / 229376.0f);
-  if (fmt != kFp32) {
-    uint32_t u = __float_as_uint(s);
-    if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
-    s = __uint_as_float(u);
+// Rounding conventions of the quantizers. kDivide: the rule above, scale =
+// max(fl32(amax/448), fl32(1/229376)) and codes from fl32(x / scale).
+// kReciprocal: the fused CUTLASS op's convention that TensorRT-LLM PR #21250
+// follows (rounding-fix commit message): multiply by inv = fl32(448 / amax),
+// store fl32(1 / inv), with amax floored at 2^-9 (= 448 / (448*512), where the
+// divide rule's floor starts to bind) so that an all-zero group stays finite;
+// the SwiGLU output is rounded to BF16 before its quantization.
+enum Rounding : int { kDivide = 0, kReciprocal = 1 };
+
+// Rounds a power-of-two format's scale up: a non-zero mantissa bumps the exponent.
+__device__ __forceinline__ float pow2_ceil(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u & 0x007FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
+  return __uint_as_float(u);
+}
+
+// The stored (float) scale of a group with this amax, and in *inv the factor
+// its elements are multiplied by. Divisions are IEEE (the library is built
+// without fast-math, so they are correctly rounded); the constants are folded
+// by the compiler with correct rounding. Under kDivide *inv = 1/s, which
+// scale_apply refines to the correctly rounded quotient; under kReciprocal
+// with fp32 scales *inv is the convention's multiplier itself. Power-of-two
+// scales give an exact *inv either way.
+__device__ __forceinline__ float group_scale_inv(float amax, int fmt, int rnd, float* inv) {
+  float s;
+  if (rnd == kReciprocal) {
+    const float m = 448.0f / fmaxf(amax, 0x1p-9f);
+    s = 1.0f / m;
+    if (fmt == kFp32) {
+      *inv = m;
+      return s;
+    }
+  } else {
+    s = fmaxf(amax / 448.0f, 1.0f / 229376.0f);
   }
+  if (fmt != kFp32) s = pow2_ceil(s);
+  *inv = 1.0f / s;
   return s;
+}
+
+// The divide convention's scale alone.
+__device__ __forceinline__ float group_scale(float amax, int fmt) {
+  float inv;
+  return group_scale_inv(amax, fmt, kDivide, &inv);
 }
 
 // Stored scale -> float (UE8M0 byte b is 2^(b-127); b >= 1 here).
@@ -74,6 +106,16 @@ __device__ __forceinline__ float scale_div(float x, float s, float inv, int fmt)
   const float r = __builtin_fmaf(-q0, s, x);
   return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
 }
+
+// One element's value before its E4M3 rounding, as the convention defines it
+// (s and inv from group_scale_inv): fl32(x / s) under kDivide, fl32(x * inv)
+// under kReciprocal.
+__device__ __forceinline__ float scale_apply(float x, float s, float inv, int fmt, int rnd) {
+  return rnd == kReciprocal ? x * inv : scale_div(x, s, inv, fmt);
+}
+
+// A float rounded to the nearest BF16 value (ties to even), kept as float.
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
 // Two float32 values -> two E4M3 codes (low 16 bits: a in byte 0, b in byte 1).
 // gfx950's v_cvt_pk_fp8_f32 rounds to nearest even in the OCP E4M3 format and

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void down_combine_kernel(DownCombin
   st.start(cb * 16, 0, kDecPreStages);
   // The rows' pairs come with them (row_to_pair), filling s_row / s_pair.
   fc2_quant_rows<FMT, false>(t, wave, lane, p.act, I, s_tok, s_sa, blockIdx.x == 0, p.hq, p.hs,
-                             p.row_cap, p.row_to_pair, s_row, s_pair);
+                             p.row_cap, p.row_to_pair, s_row, s_pair, p.rounding);
   st.start(cb * 16, kDecPreStages, kDecDepth - 1);
   for (; cb < n_cb; cb += G) {
     const int n0 = cb * 16;

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     const int t = gid / gpr, g = gid % gpr;
     if (t >= t_live) continue;  // tokens past the live count: not written
     float sc;
-    const uint2 codes = quantize8<FMT>(unpack_bf16x8(xr[k]), &sc);
+    const uint2 codes = quantize8<FMT>(unpack_bf16x8(xr[k]), &sc, p.rounding);
     *reinterpret_cast<uint2*>(s_x + t * XS + g * kGroup + l16 * 8) = codes;
     if (l16 == 0) s_xs[t * KB + g] = sc;
     if (blockIdx.x == 0) {
@@ -426,10 +426,10 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
         *reinterpret_cast<uint2*>(p.c1 + row * N + col) = packed;
         if (lane < 32) {
           float4 av;
-          av.x = swiglu_any(p.act, bf16_to_f32(packed.x & 0xFFFFu), bf16_to_f32(other.x & 0xFFFFu), lim);
-          av.y = swiglu_any(p.act, bf16_to_f32(packed.x >> 16), bf16_to_f32(other.x >> 16), lim);
-          av.z = swiglu_any(p.act, bf16_to_f32(packed.y & 0xFFFFu), bf16_to_f32(other.y & 0xFFFFu), lim);
-          av.w = swiglu_any(p.act, bf16_to_f32(packed.y >> 16), bf16_to_f32(other.y >> 16), lim);
+          av.x = swiglu_any(p.act, bf16_to_f32(packed.x & 0xFFFFu), bf16_to_f32(other.x & 0xFFFFu), lim, p.rounding);
+          av.y = swiglu_any(p.act, bf16_to_f32(packed.x >> 16), bf16_to_f32(other.x >> 16), lim, p.rounding);
+          av.z = swiglu_any(p.act, bf16_to_f32(packed.y & 0xFFFFu), bf16_to_f32(other.y & 0xFFFFu), lim, p.rounding);
+          av.w = swiglu_any(p.act, bf16_to_f32(packed.y >> 16), bf16_to_f32(other.y >> 16), lim, p.rounding);
           if constexpr (FUSED)  // read by other workgroups after the grid barrier
             gstore_b128_wt(p.act_out + row * I + col, u32x4{__float_as_uint(av.x), __float_as_uint(av.y),
                                                             __float_as_uint(av.z), __float_as_uint(av.w)});
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     // workgroups wrote them), then the rest of the stream start
     if (has_cb) {
       fc2_quant_rows<FMT, true>(t, wave, lane, p.act_out, I, s_tok, s_sa, blockIdx.x == 0, q.hq, q.hs,
-                                q.row_cap, nullptr, nullptr, nullptr);
+                                q.row_cap, nullptr, nullptr, nullptr, q.rounding);
       st.start(cb * 16, kDecPreStages, DEPTH - 1);
     }
     // ---- 6. stream and combine per column block

@@ -162,7 +162,7 @@ template <int FMT, bool DEVICE_SCOPE>
 __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, int lane, const float* act,
                                                int I, uint8_t* tok, float* sa, bool writer, uint8_t* hq,
                                                void* hs, int row_cap, const int32_t* row_to_pair,
-                                               int* row, int* pair) {
+                                               int* row, int* pair, int rnd) {
   const int KB = I / kGroup, TS = I + 16;
   const int l16 = lane & 15, lg = lane >> 4;
   const int my_rows = wave_rows(t, wave);
@@ -199,12 +199,11 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
 #pragma unroll
         for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
         amax = group_max<16>(amax);
-        const float sc = group_scale(amax, FMT);
-        const float inv = 1.0f / sc;  // IEEE division, once per group
-        const uint32_t qa = cvt_pk_e4m3(scale_div(x[0], sc, inv, FMT), scale_div(x[1], sc, inv, FMT)) |
-                            (cvt_pk_e4m3(scale_div(x[2], sc, inv, FMT), scale_div(x[3], sc, inv, FMT)) << 16);
-        const uint32_t qb = cvt_pk_e4m3(scale_div(x[4], sc, inv, FMT), scale_div(x[5], sc, inv, FMT)) |
-                            (cvt_pk_e4m3(scale_div(x[6], sc, inv, FMT), scale_div(x[7], sc, inv, FMT)) << 16);
+        float inv;
+        const float sc = group_scale_inv(amax, FMT, rnd, &inv);  // IEEE divisions, once per group
+        auto q = [&](int j) { return scale_apply(x[j], sc, inv, FMT, rnd); };
+        const uint32_t qa = cvt_pk_e4m3(q(0), q(1)) | (cvt_pk_e4m3(q(2), q(3)) << 16);
+        const uint32_t qb = cvt_pk_e4m3(q(4), q(5)) | (cvt_pk_e4m3(q(6), q(7)) << 16);
         const int ca = col0 + 4 * (32 * g + l16), cb = ca + 64;
         if (row_ok && g_ok) {
           *reinterpret_cast<uint32_t*>(tok + c * TS + ca) = qa;

@@ -17,17 +17,18 @@ hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev
                         int32_t* row_to_pair, int32_t* pair_to_row, hipStream_t stream);
 
 // moe_align and moe_act_quant of one layer in a single launch.
+// `rounding` below is the quantizers' convention (Rounding in device_common.h).
 hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                        int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                        int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
-                       int fmt, uint8_t* xq, void* xs, hipStream_t stream);
+                       int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream);
 
 hipError_t launch_act_quant(const uint16_t* x, int t_cap, const int32_t* t_live_dev, int hidden,
-                            int fmt, uint8_t* xq, void* xs, hipStream_t stream);
+                            int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream);
 
 hipError_t launch_silu_mul_quant(const uint16_t* gate_up, int inter, const int32_t* counts,
                                  const int32_t* offsets, int num_experts, int row_cap, int act,
-                                 float clamp_limit, int fmt, uint8_t* hq, void* hs,
+                                 float clamp_limit, int fmt, int rounding, uint8_t* hq, void* hs,
                                  hipStream_t stream);
 
 hipError_t launch_topk_combine(const uint16_t* y, int row_cap, const int32_t* pair_to_row,
@@ -62,6 +63,7 @@ struct GemmArgs {
   float* act_out = nullptr;
   int act = 0;
   float act_limit = 0.0f;
+  int rounding = 0;  // act_out is BF16-rounded under the reciprocal convention
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
@@ -102,6 +104,7 @@ struct DownCombineArgs {
   void* hs;                   // [I/128][row_cap] its scales
   uint16_t* y;                // [row_cap, H] FC2 output rows (workspace copy)
   uint16_t* out;              // [t_cap, H]
+  int rounding;               // quantizer convention of the FC2 input
 };
 
 hipError_t launch_down_combine(const DownCombineArgs& a, hipStream_t stream);
@@ -142,6 +145,7 @@ struct DecodeFc1Args {
   void* xs;
   uint16_t* c1;               // [row_cap, 2I] BF16
   float* act_out;             // [row_cap, I] fp32 SiLU(gate) * up
+  int rounding;               // quantizer convention (and BF16-rounded act when reciprocal)
 };
 
 hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream);

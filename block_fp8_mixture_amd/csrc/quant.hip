@@ -24,9 +24,9 @@ constexpr int kGroupsPerBlock = kThreads / 16;
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(
     const uint16_t* __restrict__ x, int t_cap, const int32_t* __restrict__ t_live_dev,
-    int hidden, uint8_t* __restrict__ xq, void* __restrict__ xs) {
+    int hidden, uint8_t* __restrict__ xq, void* __restrict__ xs, int rnd) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * kGroupsPerBlock + (threadIdx.x >> 4);
-  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15);
+  act_quant_group<FMT>(x, t_cap, t_live_dev, hidden, xq, xs, gid, threadIdx.x & 15, rnd);
 }
 
 
@@ -48,7 +48,7 @@ template <int FMT, int ACT>
 __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gate_up, int inter, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int num_experts, int row_cap, float clamp_limit,
-    uint8_t* __restrict__ hq, void* __restrict__ hs) {
+    uint8_t* __restrict__ hq, void* __restrict__ hs, int rnd) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ double s_lut[kSiluLutSize];
@@ -93,8 +93,12 @@ __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
           else
             y.v[i] = swiglu<ACT>(g8.v[i], u8.v[i], lim);
         }
+        if (rnd == kReciprocal) {  // the SwiGLU output rounded to BF16 first
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y.v[i] = round_bf16(y.v[i]);
+        }
         float sc;
-        const uint2 codes = quantize8<FMT>(y, &sc);
+        const uint2 codes = quantize8<FMT>(y, &sc, rnd);
         *reinterpret_cast<uint2*>(hq + static_cast<int64_t>(r) * inter + gs[k] * kGroup + l16 * 8) = codes;
         if (l16 == 0) store_scale(hs, FMT, static_cast<int64_t>(gs[k]) * row_cap + r, sc);
       }
@@ -111,19 +115,19 @@ __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
 
 template <int FMT>
 hipError_t act_quant_fmt(const uint16_t* x, int t_cap, const int32_t* t_live_dev, int hidden,
-                         uint8_t* xq, void* xs, hipStream_t stream) {
+                         uint8_t* xq, void* xs, int rnd, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(t_cap) * (hidden / kGroup);
   const int blocks = static_cast<int>((groups + kGroupsPerBlock - 1) / kGroupsPerBlock);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(act_quant_kernel<FMT>, dim3(blocks), dim3(kThreads), 0, stream, x, t_cap,
-                     t_live_dev, hidden, xq, xs);
+                     t_live_dev, hidden, xq, xs, rnd);
   return hipGetLastError();
 }
 
 template <int FMT, int ACT>
 hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
-                      uint8_t* hq, void* hs, hipStream_t stream) {
+                      uint8_t* hq, void* hs, int rnd, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
   if (groups > INT32_MAX) return hipErrorInvalidValue;  // the kernel divides 32-bit group indices
   const int64_t need = (groups + 2 * kSmqGroupsPerBlock - 1) / (2 * kSmqGroupsPerBlock);
@@ -131,53 +135,55 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
   const int blocks = static_cast<int>(need < cap ? need : cap);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((silu_mul_quant_kernel<FMT, ACT>), dim3(blocks), dim3(kSmqThreads), 0, stream,
-                     gate_up, inter, counts, offsets, num_experts, row_cap, clamp_limit, hq, hs);
+                     gate_up, inter, counts, offsets, num_experts, row_cap, clamp_limit, hq, hs, rnd);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t smq_fmt(const uint16_t* gate_up, int inter, const int32_t* counts,
                    const int32_t* offsets, int num_experts, int row_cap, int act,
-                   float clamp_limit, uint8_t* hq, void* hs, hipStream_t stream) {
+                   float clamp_limit, uint8_t* hq, void* hs, int rnd, hipStream_t stream) {
   switch (act) {
     case kSwiglu:
       return smq_launch<FMT, kSwiglu>(gate_up, inter, counts, offsets, num_experts, row_cap,
-                                      clamp_limit, hq, hs, stream);
+                                      clamp_limit, hq, hs, rnd, stream);
     case kSwigluClamp:
       return smq_launch<FMT, kSwigluClamp>(gate_up, inter, counts, offsets, num_experts,
-                                           row_cap, clamp_limit, hq, hs, stream);
+                                           row_cap, clamp_limit, hq, hs, rnd, stream);
     default:
       return smq_launch<FMT, kSwigluClampAfterSilu>(gate_up, inter, counts, offsets,
                                                     num_experts, row_cap, clamp_limit, hq, hs,
-                                                    stream);
+                                                    rnd, stream);
   }
 }
 
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t* x, int t_cap, const int32_t* t_live_dev, int hidden,
-                            int fmt, uint8_t* xq, void* xs, hipStream_t stream) {
+                            int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream) {
   switch (fmt) {
-    case kFp32: return act_quant_fmt<kFp32>(x, t_cap, t_live_dev, hidden, xq, xs, stream);
-    case kFp32Pow2: return act_quant_fmt<kFp32Pow2>(x, t_cap, t_live_dev, hidden, xq, xs, stream);
-    default: return act_quant_fmt<kUe8m0>(x, t_cap, t_live_dev, hidden, xq, xs, stream);
+    case kFp32: return act_quant_fmt<kFp32>(x, t_cap, t_live_dev, hidden, xq, xs, rounding, stream);
+    case kFp32Pow2:
+      return act_quant_fmt<kFp32Pow2>(x, t_cap, t_live_dev, hidden, xq, xs, rounding, stream);
+    default: return act_quant_fmt<kUe8m0>(x, t_cap, t_live_dev, hidden, xq, xs, rounding, stream);
   }
 }
 
 hipError_t launch_silu_mul_quant(const uint16_t* gate_up, int inter, const int32_t* counts,
                                  const int32_t* offsets, int num_experts, int row_cap, int act,
-                                 float clamp_limit, int fmt, uint8_t* hq, void* hs,
+                                 float clamp_limit, int fmt, int rounding, uint8_t* hq, void* hs,
                                  hipStream_t stream) {
+  const int rnd = rounding;
   switch (fmt) {
     case kFp32:
       return smq_fmt<kFp32>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                            clamp_limit, hq, hs, stream);
+                            clamp_limit, hq, hs, rnd, stream);
     case kFp32Pow2:
       return smq_fmt<kFp32Pow2>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                                clamp_limit, hq, hs, stream);
+                                clamp_limit, hq, hs, rnd, stream);
     default:
       return smq_fmt<kUe8m0>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                             clamp_limit, hq, hs, stream);
+                             clamp_limit, hq, hs, rnd, stream);
   }
 }
 

@@ -29,16 +29,16 @@ __device__ __forceinline__ Vals8 unpack_bf16x8(uint4 raw) {
 // Quantizes the 8 values this lane holds against the group's scale; returns
 // the 8 codes packed little-endian and writes the stored scale when asked.
 template <int FMT>
-__device__ __forceinline__ uint2 quantize8(const Vals8& x, float* scale_out) {
+__device__ __forceinline__ uint2 quantize8(const Vals8& x, float* scale_out, int rnd) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x.v[i]));
   amax = group_max<16>(amax);
-  const float s = group_scale(amax, FMT);
-  const float inv = 1.0f / s;  // IEEE division, once per group
+  float inv;
+  const float s = group_scale_inv(amax, FMT, rnd, &inv);  // IEEE divisions, once per group
   float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = scale_div(x.v[i], s, inv, FMT);
+  for (int i = 0; i < 8; ++i) q[i] = scale_apply(x.v[i], s, inv, FMT, rnd);
   uint2 out;
   out.x = cvt_pk_e4m3(q[0], q[1]) | (cvt_pk_e4m3(q[2], q[3]) << 16);
   out.y = cvt_pk_e4m3(q[4], q[5]) | (cvt_pk_e4m3(q[6], q[7]) << 16);
@@ -53,7 +53,7 @@ template <int FMT>
 __device__ __forceinline__ void act_quant_group(const uint16_t* __restrict__ x, int t_cap,
                                                 const int32_t* __restrict__ t_live_dev, int hidden,
                                                 uint8_t* __restrict__ xq, void* __restrict__ xs,
-                                                int64_t gid, int l16) {
+                                                int64_t gid, int l16, int rnd) {
   const int groups = hidden / kGroup;
   if (gid >= static_cast<int64_t>(t_cap) * groups) return;  // whole 16-lane groups exit
   const int t = static_cast<int>(gid / groups);
@@ -65,7 +65,7 @@ __device__ __forceinline__ void act_quant_group(const uint16_t* __restrict__ x, 
   if (t >= clamp_live(t_live_dev, t_cap)) return;
   const Vals8 v = unpack_bf16x8(raw);
   float s;
-  const uint2 codes = quantize8<FMT>(v, &s);
+  const uint2 codes = quantize8<FMT>(v, &s, rnd);
   *reinterpret_cast<uint2*>(xq + base) = codes;
   if (l16 == 0) store_scale(xs, FMT, static_cast<int64_t>(g) * t_cap + t, s);
 }
@@ -146,11 +146,19 @@ __device__ __forceinline__ float swiglu_lut(float gf, float uf, double lim, cons
   return static_cast<float>(s * u);
 }
 
-// The activation chosen at run time (a uniform branch).
-__device__ __forceinline__ float swiglu_any(int act, float g, float u, double lim) {
-  if (act == kSwigluClamp) return swiglu<kSwigluClamp>(g, u, lim);
-  if (act == kSwigluClampAfterSilu) return swiglu<kSwigluClampAfterSilu>(g, u, lim);
-  return swiglu<kSwiglu>(g, u, lim);
+// The activation chosen at run time (a uniform branch); under the
+// reciprocal convention the result is rounded to BF16 (TensorRT-LLM PR
+// #21250, rounding-fix commit message: the fused op's epilogue rounds the
+// SwiGLU output to BF16 before its FP8 quantization).
+__device__ __forceinline__ float swiglu_any(int act, float g, float u, double lim, int rnd) {
+  float y;
+  if (act == kSwigluClamp)
+    y = swiglu<kSwigluClamp>(g, u, lim);
+  else if (act == kSwigluClampAfterSilu)
+    y = swiglu<kSwigluClampAfterSilu>(g, u, lim);
+  else
+    y = swiglu<kSwiglu>(g, u, lim);
+  return rnd == kReciprocal ? round_bf16(y) : y;
 }
 
 }  // namespace moe

@@ -65,6 +65,28 @@ typedef enum {
   MOE_SCALE_UE8M0 = 2
 } moe_scale_fmt;
 
+/* Rounding conventions of the FP8 quantizers.
+ *   MOE_ROUND_DIVIDE      scale = max(fl32(amax / 448), fl32(1 / (448*512))),
+ *                         codes from fl32(x / scale) (vLLM PR #65794, Details);
+ *                         the SwiGLU output is quantized from float32.
+ *   MOE_ROUND_RECIPROCAL  the fused CUTLASS op's convention that TensorRT-LLM
+ *                         PR #21250 follows (rounding-fix commit message):
+ *                         inv = fl32(448 / max(amax, 2^-9)), stored scale
+ *                         fl32(1 / inv), codes from fl32(x * inv) (with a
+ *                         power-of-two format: the stored scale rounded up to
+ *                         a power of two, and x divided by it exactly); the
+ *                         SwiGLU output is rounded to BF16 before it is
+ *                         quantized. The 2^-9 floor (where the divide rule's
+ *                         floor starts to bind) is this library's reading.
+ * The grouped GEMM accumulates sa * sw * dot in fp32 either way; the review of
+ * TensorRT-LLM PR #21250 (block-scale order) notes that forming sa * sw first
+ * is that op's order, and the GEMM results match either convention within the
+ * GEMM tolerance. */
+typedef enum {
+  MOE_ROUND_DIVIDE = 0,
+  MOE_ROUND_RECIPROCAL = 1
+} moe_rounding;
+
 /* Gated activations (TensorRT-LLM PR #21250, Test Coverage: no clamp, clamp,
  * clamp after SiLU; vLLM PR #65794, Details: clamp_limit). With limit L:
  *   SWIGLU                   y = silu(g) * u
@@ -118,11 +140,12 @@ moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_li
  *   x     device BF16 [t_cap, hidden]
  *   xq    device uint8 [t_cap, hidden]; rows t >= t_live untouched
  *   xs    device scales [hidden/128][t_cap] (float or uint8, per `fmt`)
+ *   rounding  the quantizer's convention (moe_rounding)
  * Errors: INVALID_ARG (hidden not a positive multiple of 128, null pointers,
- * unknown fmt). */
+ * unknown fmt or rounding). */
 moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live_dev,
-                         int32_t hidden, moe_scale_fmt fmt, uint8_t* xq, void* xs,
-                         void* stream);
+                         int32_t hidden, moe_scale_fmt fmt, moe_rounding rounding, uint8_t* xq,
+                         void* xs, void* stream);
 
 /* Grouped FP8 x FP8 GEMM with per-block scales, over the live rows of every
  * expert segment only (vLLM PR #59128, Purpose and SM90-on-H200: both grouped
@@ -178,12 +201,14 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
  *   gate_up  device BF16 [row_cap, 2*inter]
  *   hq       device uint8 [row_cap, inter]; hs device [inter/128][row_cap]
  *   clamp_limit  used by the clamp variants; must be > 0 there
+ *   rounding  moe_rounding; MOE_ROUND_RECIPROCAL rounds SiLU(gate)*up to BF16
+ *             before quantizing it
  * Errors: INVALID_ARG (also when row_cap * inter / 128 exceeds 2^31 - 1). */
 moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               const int32_t* expert_counts, const int32_t* expert_offsets,
                               int32_t num_experts, int32_t row_cap, moe_act act,
-                              float clamp_limit, moe_scale_fmt fmt, uint8_t* hq, void* hs,
-                              void* stream);
+                              float clamp_limit, moe_scale_fmt fmt, moe_rounding rounding,
+                              uint8_t* hq, void* hs, void* stream);
 
 /* Top-k weighted unpermute/sum (TensorRT-LLM PR #21250, rounding-fix commit:
  * the routing weights scale the BF16 expert outputs in fp32 in the top-k sum,
@@ -213,6 +238,7 @@ typedef struct {
   moe_scale_fmt scale_fmt;
   moe_act act;
   float clamp_limit;
+  moe_rounding rounding; /* quantizer convention of both activation quantizations */
 } moe_problem;
 
 typedef struct {

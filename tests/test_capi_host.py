@@ -77,11 +77,12 @@ def test_align_validation(lib):
 
 def test_act_quant_validation(lib):
     f = lib.moe_act_quant
-    assert f(FAKE, 4, NULL, 100, 0, FAKE, FAKE, NULL) == INVALID    # hidden not a multiple of 128
-    assert f(FAKE, 4, NULL, 256, 3, FAKE, FAKE, NULL) == INVALID    # unknown format
-    assert f(NULL, 4, NULL, 256, 0, FAKE, FAKE, NULL) == INVALID
-    assert f(FAKE, 4, NULL, 256, 0, FAKE, NULL, NULL) == INVALID
-    assert f(NULL, 0, NULL, 256, 0, NULL, NULL, NULL) == OK         # nothing to do, nothing launched
+    assert f(FAKE, 4, NULL, 100, 0, 0, FAKE, FAKE, NULL) == INVALID    # hidden not a multiple of 128
+    assert f(FAKE, 4, NULL, 256, 3, 0, FAKE, FAKE, NULL) == INVALID    # unknown format
+    assert f(FAKE, 4, NULL, 256, 0, 2, FAKE, FAKE, NULL) == INVALID    # unknown rounding
+    assert f(NULL, 4, NULL, 256, 0, 0, FAKE, FAKE, NULL) == INVALID
+    assert f(FAKE, 4, NULL, 256, 0, 1, FAKE, NULL, NULL) == INVALID
+    assert f(NULL, 0, NULL, 256, 0, 1, NULL, NULL, NULL) == OK         # nothing to do, nothing launched
 
 
 def test_gemm_validation(lib):
@@ -104,14 +105,15 @@ def test_gemm_validation(lib):
 def test_silu_mul_quant_validation(lib):
     f = lib.moe_silu_mul_quant
 
-    def call(inter=256, act=0, lim=7.0, fmt=0, rc=64, gu=FAKE):
-        return f(gu, inter, FAKE, FAKE, 4, rc, act, lim, fmt, FAKE, FAKE, NULL)
+    def call(inter=256, act=0, lim=7.0, fmt=0, rc=64, gu=FAKE, rnd=0):
+        return f(gu, inter, FAKE, FAKE, 4, rc, act, lim, fmt, rnd, FAKE, FAKE, NULL)
     assert call(inter=100) == INVALID
     assert call(act=3) == INVALID
     assert call(act=1, lim=0.0) == INVALID
     assert call(act=2, lim=-1.0) == INVALID
     assert call(act=1, lim=float("nan")) == INVALID
     assert call(fmt=5) == INVALID
+    assert call(rnd=-1) == INVALID
     assert call(gu=NULL) == INVALID
     assert call(rc=1 << 24, inter=1 << 15) == INVALID  # 2^32 groups
     assert call(rc=0, gu=NULL) == OK
@@ -127,7 +129,7 @@ def test_combine_validation(lib):
 
 def _problem(**kw):
     d = dict(num_experts=32, hidden=7168, inter=2048, topk=8, t_cap=4096, align_rows=16,
-             row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"))
+             row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"), rounding=0)
     d.update(kw)
     return B._Problem(**d)
 
@@ -161,6 +163,8 @@ def test_forward_validation(lib):
     assert lib.moe_workspace_plan(ctypes.byref(_problem(num_experts=4096)),
                                   ctypes.byref(lay)) == UNSUPPORTED
     assert lib.moe_workspace_bytes(ctypes.byref(_problem(inter=0))) == 0
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(rounding=2)), ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(rounding=1)), ctypes.byref(lay)) == OK
     # FC2-input groups (row_cap * inter / 128) are indexed in 32 bits
     assert lib.moe_workspace_plan(ctypes.byref(_problem(row_cap=1 << 24, inter=1 << 15)),
                                   ctypes.byref(lay)) == INVALID

@@ -41,9 +41,9 @@ def _sample(n, k, seed):
 
 
 def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_tok=8,
-                  n_rows=16):
+                  n_rows=16, rounding="divide"):
     cfg = synth.get(name)
-    say(f"forward {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act} lim={lim}")
+    say(f"forward {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act} lim={lim} {rounding}")
     E, H, I, K, A = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, cfg.align_rows
     x, ids, w = synth.make_workload(cfg, t_cap, variant)
     (w1q, w1s), (w2q, w2s) = host_weights(name)
@@ -51,11 +51,12 @@ def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_
     lim32 = float(np.float32(lim))
     out = torch.full((t_cap, H), POISON_BF16, dtype=torch.int16, device=dev())
     row_cap = cfg.row_cap or 0
-    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32)
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32, rounding)
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     gave_up = moe.moe_barrier_timeouts()
     moe.moe_forward(up(x), up(ids), up(w), d_w1q, d_w1s, d_w2q, d_w2s, fmt, act, lim32, A,
-                    row_cap, t_live=up(np.array([t_live], np.int32)), out=out, workspace=ws)
+                    row_cap, t_live=up(np.array([t_live], np.int32)), out=out, workspace=ws,
+                    rounding=rounding)
     torch.cuda.synchronize()
     assert moe.moe_barrier_timeouts() == gave_up, "a wait at the decode layer's grid barrier gave up"
     if moe.decode_layer_applies(t_cap, K, H, I):  # the one-launch layer reports per workgroup
@@ -78,7 +79,8 @@ def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_
     # per-token activation quantization: bit-exact
     xq = _ws_view(ws, lay, "xq", np.uint8, (t_cap, H))
     xs = _ws_view(ws, lay, "xs", sdt, (H // 128, t_cap))
-    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt,
+                                    rounding)
     assert np.array_equal(xq[:t_live], rq)
     assert np.array_equal(np.ascontiguousarray(xs[:, :t_live]).view(np.uint8),
                           np.ascontiguousarray(rs).view(np.uint8))
@@ -95,13 +97,13 @@ def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_
         seg = np.arange(al["offsets"][e], al["offsets"][e] + al["counts"][e])
         rows = seg[_sample(len(seg), n_rows, int(e))]
         tok = al["row_to_pair"][rows] // K
-        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e])
+        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e], rounding)
         assert_bf16_close(c1[rows], ref_c1, f"FC1 expert {e}")
-        rhq, rhs = oracle.silu_mul_quant(c1[rows], fmt, act, lim32)
+        rhq, rhs = oracle.silu_mul_quant(c1[rows], fmt, act, lim32, rounding)
         assert np.array_equal(hq[rows], rhq)
         assert np.array_equal(np.ascontiguousarray(hs[:, rows]).view(np.uint8),
                               np.ascontiguousarray(rhs).view(np.uint8))
-        ref_y = oracle.moe.gemm_rows(hq[rows], sa_h[:, rows], w2q[e], w2s[e])
+        ref_y = oracle.moe.gemm_rows(hq[rows], sa_h[:, rows], w2q[e], w2s[e], rounding)
         assert_bf16_close(y[rows], ref_y, f"FC2 expert {e}")
 
     got = down(out)
@@ -114,7 +116,7 @@ def run_and_check(name, t_cap, t_live, fmt, act="swiglu", lim=INF, variant=0, n_
         assert_bf16_close(got[toks], ref_comb, "combine")
         # whole layer against the dense per-token oracle
         ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, t_live, fmt, act, lim32,
-                                   tokens=toks)
+                                   tokens=toks, rounding=rounding)
         err = assert_bf16_close(got[toks], ref, "layer")
         say(f"  layer max err / max|ref| = {err:.3e}")
     return got, ws, lay
@@ -141,10 +143,26 @@ CONFIG_RUNS = [
     ("sweep", 4096, 4096, "pow2", "swiglu", INF),
 ]
 
+# The reciprocal rounding convention on every schedule: the one-launch layer
+# (tiny, decode, sweep at 8 tokens with the 4-deep ring), the general path.
+RECIPROCAL_RUNS = [
+    ("tiny", 8, 8, "fp32", "swiglu", INF),
+    ("decode", 4, 4, "fp32", "swiglu", INF),
+    ("decode", 1, 1, "ue8m0", "swiglu_clamp", 7.0),
+    ("sweep", 8, 8, "pow2", "swiglu", INF),
+    ("padded", 512, 16, "fp32", "swiglu", INF),
+    ("sweep", 1024, 1024, "fp32", "swiglu", INF),
+]
+
 
 @pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim", CONFIG_RUNS)
 def test_forward_matches_oracle(name, t_cap, t_live, fmt, act, lim):
     run_and_check(name, t_cap, t_live, fmt, act, lim)
+
+
+@pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim", RECIPROCAL_RUNS)
+def test_forward_reciprocal_rounding_matches_oracle(name, t_cap, t_live, fmt, act, lim):
+    run_and_check(name, t_cap, t_live, fmt, act, lim, rounding="reciprocal")
 
 
 def test_forward_forced_clamp_on_decode_shape():
@@ -420,32 +438,34 @@ def test_padded_tiles_are_skipped():
 
 
 FC1_DECODE_RUNS = [
-    ("decode", 4, 4, "fp32", "swiglu", INF),
-    ("decode", 4, 3, "ue8m0", "swiglu_clamp", 7.0),
-    ("decode", 1, 1, "pow2", "swiglu_clamp_after_silu", 7.0),
-    ("tiny", 8, 5, "fp32", "swiglu", INF),
-    ("sweep", 1, 1, "fp32", "swiglu", INF),
+    ("decode", 4, 4, "fp32", "swiglu", INF, "divide"),
+    ("decode", 4, 4, "fp32", "swiglu", INF, "reciprocal"),
+    ("decode", 4, 3, "ue8m0", "swiglu_clamp", 7.0, "divide"),
+    ("decode", 1, 1, "pow2", "swiglu_clamp_after_silu", 7.0, "divide"),
+    ("decode", 1, 1, "pow2", "swiglu_clamp_after_silu", 7.0, "reciprocal"),
+    ("tiny", 8, 5, "fp32", "swiglu", INF, "divide"),
+    ("sweep", 1, 1, "fp32", "swiglu", INF, "divide"),
 ]
 
 
-@pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim", FC1_DECODE_RUNS)
-def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
+@pytest.mark.parametrize("name,t_cap,t_live,fmt,act,lim,rounding", FC1_DECODE_RUNS)
+def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim, rounding):
     """The decode path's first launch on its own: alignment and activation codes
     bit-exact, C1 rows within the GEMM tolerance, act = SiLU(gate)*up of the GPU's
     own C1 rows bit for bit, and nothing written outside the live rows."""
     cfg = synth.get(name)
-    say(f"fc1_decode {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act}")
+    say(f"fc1_decode {name} t_cap={t_cap} t_live={t_live} fmt={fmt} act={act} {rounding}")
     E, H, I, K, A = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, cfg.align_rows
     x, ids, w = synth.make_workload(cfg, t_cap)
     (w1q, w1s), _ = host_weights(name)
     d_w1q, d_w1s, _, _ = device_weights(name)
     lim32 = float(np.float32(lim))
     row_cap = cfg.row_cap or 0
-    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32)
+    lay = moe.moe_workspace_plan(E, H, I, K, t_cap, A, row_cap, fmt, act, lim32, rounding)
     assert lay["act"] < lay["status"]
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     moe.moe_fc1_decode(up(x), up(ids), d_w1q, d_w1s, I, fmt, act, lim32, A, row_cap,
-                       t_live=up(np.array([t_live], np.int32)), workspace=ws)
+                       t_live=up(np.array([t_live], np.int32)), workspace=ws, rounding=rounding)
     torch.cuda.synchronize()
     R = lay["row_cap"]
     sdt = np.uint8 if fmt == "ue8m0" else np.float32
@@ -460,7 +480,8 @@ def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
     assert np.array_equal(p2r[:t_live * K], al["pair_to_row"])
     xq = _ws_view(ws, lay, "xq", np.uint8, (t_cap, H))
     xs = _ws_view(ws, lay, "xs", sdt, (H // 128, t_cap))
-    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt,
+                                    rounding)
     assert np.array_equal(xq[:t_live], rq)
     assert np.all(xq[t_live:] == POISON_U8)
     assert np.array_equal(np.ascontiguousarray(xs[:, :t_live]).view(np.uint8),
@@ -472,11 +493,11 @@ def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim):
     for e in np.flatnonzero(al["counts"] > 0):
         seg = np.arange(al["offsets"][e], al["offsets"][e] + al["counts"][e])
         tok = al["row_to_pair"][seg] // K
-        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e])
+        ref_c1 = oracle.moe.gemm_rows(xq[tok], sa_x[:, tok], w1q[e], w1s[e], rounding)
         assert_bf16_close(c1[seg], ref_c1, f"FC1 expert {e}")
         g = oracle.bf16_bits_to_f64(c1[seg][:, :I])
         u = oracle.bf16_bits_to_f64(c1[seg][:, I:])
-        ref_act = oracle.moe.swiglu(g, u, act, lim32)
+        ref_act = oracle.moe.swiglu(g, u, act, lim32, rounding)
         assert np.array_equal(act_rows[seg].view(np.uint32), ref_act.view(np.uint32)), e
     dead = np.setdiff1d(np.arange(R), live_rows)
     assert np.all(c1[dead] == (POISON_U8 << 8 | POISON_U8))

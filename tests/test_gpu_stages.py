@@ -110,6 +110,14 @@ def _tokens(kind, t_cap, h, seed):
         sel[...] = g.choice(np.concatenate([mids, -mids]), sel.shape)
         sel[..., 0] = 448.0
         groups[:, 2::9, :] = sel
+        # groups where the two rounding conventions round midpoints apart:
+        # amax 1.625 with 39/32 and 39/64 (exact quotients 336 and 168), at
+        # random powers of two
+        split = groups[:, 4::10, :]
+        split[...] = g.choice([1.21875, 0.609375, -1.21875, 0.0], split.shape)
+        split[..., 0] = 1.625
+        split *= np.exp2(g.integers(-20, 8, split.shape[:2] + (1,)))
+        groups[:, 4::10, :] = split
         x = groups.reshape(t_cap, h)
     bits = oracle.bf16_from_f64(x)
     if kind == "mixed":
@@ -117,19 +125,21 @@ def _tokens(kind, t_cap, h, seed):
     return bits
 
 
+@pytest.mark.parametrize("rounding", ["divide", "reciprocal"])
 @pytest.mark.parametrize("fmt", ["fp32", "pow2", "ue8m0"])
 @pytest.mark.parametrize("t_cap,t_live,h,seed,kind", [
     (8, 8, 256, 0, "normal"), (37, 30, 4096, 1, "mixed"), (512, 16, 7168, 2, "normal"),
     (300, 300, 6144, 3, "mixed"), (5, 0, 128, 4, "normal")])
-def test_act_quant_bit_exact(fmt, t_cap, t_live, h, seed, kind):
-    say(f"act_quant fmt={fmt} t_cap={t_cap} t_live={t_live} H={h} {kind}")
+def test_act_quant_bit_exact(fmt, t_cap, t_live, h, seed, kind, rounding):
+    say(f"act_quant fmt={fmt} {rounding} t_cap={t_cap} t_live={t_live} H={h} {kind}")
     x = _tokens(kind, t_cap, h, seed)
     sdt = torch.uint8 if fmt == "ue8m0" else torch.float32
     xq = _full((t_cap, h), POISON_U8, torch.uint8)
     xs = _full((h // 128, t_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
-    moe.moe_act_quant(up(x), fmt, t_live=_t_live(t_live), xq=xq, xs=xs)
+    moe.moe_act_quant(up(x), fmt, t_live=_t_live(t_live), xq=xq, xs=xs, rounding=rounding)
     torch.cuda.synchronize()
-    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt)
+    rq, rs = oracle.quantize_groups(oracle.bf16_bits_to_f64(x[:t_live]).astype(np.float32), fmt,
+                                    rounding)
     gq, gs = down(xq), down(xs)
     assert np.array_equal(gq[:t_live], rq)
     assert np.all(gq[t_live:] == POISON_U8)
@@ -156,9 +166,12 @@ def _segments(g, e, max_rows, align, zero_frac=0.3):
                                          ("swiglu_clamp_after_silu", 7.0, 8.0),
                                          ("swiglu_clamp", 0.5, 1.0),
                                          ("swiglu_clamp_after_silu", 0.5, 1.0)])
-@pytest.mark.parametrize("inter,e,seed", [(128, 4, 0), (512, 288, 1), (2048, 32, 2)])
-def test_silu_mul_quant_bit_exact(fmt, act, lim, amp, inter, e, seed):
-    say(f"silu_mul_quant fmt={fmt} act={act} lim={lim} I={inter} E={e}")
+@pytest.mark.parametrize("inter,e,seed,rounding", [(128, 4, 0, "divide"), (512, 288, 1, "divide"),
+                                                   (2048, 32, 2, "divide"),
+                                                   (128, 4, 3, "reciprocal"),
+                                                   (2048, 32, 4, "reciprocal")])
+def test_silu_mul_quant_bit_exact(fmt, act, lim, amp, inter, e, seed, rounding):
+    say(f"silu_mul_quant fmt={fmt} {rounding} act={act} lim={lim} I={inter} E={e}")
     g = np.random.default_rng(seed)
     counts, offsets = _segments(g, e, 40, 16)
     row_cap = int(offsets[-1]) + 16
@@ -171,9 +184,10 @@ def test_silu_mul_quant_bit_exact(fmt, act, lim, amp, inter, e, seed):
     hq = _full((row_cap, inter), POISON_U8, torch.uint8)
     hs = _full((inter // 128, row_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
     lim32 = float(np.float32(lim))
-    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs)
+    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs,
+                           rounding=rounding)
     torch.cuda.synchronize()
-    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32)
+    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32, rounding)
     gq, gs = down(hq), down(hs)
     assert np.array_equal(gq[live], rq)
     assert np.all(gq[~live] == POISON_U8)
@@ -197,11 +211,13 @@ def _gate_specials(g, shape):
     return (bits | (g.integers(0, 2, shape, dtype=np.uint16) << 15)).astype(np.uint16)
 
 
-@pytest.mark.parametrize("fmt,act,lim", [("fp32", "swiglu", float("inf")),
-                                          ("ue8m0", "swiglu_clamp", 7.0),
-                                          ("pow2", "swiglu_clamp", 0.3),
-                                          ("ue8m0", "swiglu_clamp_after_silu", 7.0)])
-def test_silu_mul_quant_table_path(fmt, act, lim):
+@pytest.mark.parametrize("fmt,act,lim,rounding", [("fp32", "swiglu", float("inf"), "divide"),
+                                                   ("ue8m0", "swiglu_clamp", 7.0, "divide"),
+                                                   ("pow2", "swiglu_clamp", 0.3, "divide"),
+                                                   ("ue8m0", "swiglu_clamp_after_silu", 7.0, "divide"),
+                                                   ("fp32", "swiglu", float("inf"), "reciprocal"),
+                                                   ("pow2", "swiglu_clamp", 0.3, "reciprocal")])
+def test_silu_mul_quant_table_path(fmt, act, lim, rounding):
     """Launches large enough that every workgroup takes SiLU from its table of
     BF16 gates (at least 128 groups each with two workgroups per CU): codes
     and scales bit-exact, including gates outside the table's range and a
@@ -230,9 +246,10 @@ def test_silu_mul_quant_table_path(fmt, act, lim):
     hq = _full((row_cap, inter), POISON_U8, torch.uint8)
     hs = _full((inter // 128, row_cap), POISON_U8 if fmt == "ue8m0" else float("nan"), sdt)
     lim32 = float(np.float32(lim))
-    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs)
+    moe.moe_silu_mul_quant(up(gu), up(counts), up(offsets), act, lim32, fmt, hq=hq, hs=hs,
+                           rounding=rounding)
     torch.cuda.synchronize()
-    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32)
+    rq, rs = oracle.silu_mul_quant(gu[live], fmt, act, lim32, rounding)
     gq, gs = down(hq), down(hs)
     bad = np.argwhere(gq[live] != rq)
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
