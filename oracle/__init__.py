@@ -32,7 +32,7 @@ from .fp_formats import (E4M3_MAX, bf16_bits_to_f64, bf16_from_f64,
                          e4m3_decode, e4m3_encode)
 from .quant import (ROUNDINGS, SCALE_FMTS, group_scales, quantize_groups,
                     reciprocal_multiplier, scales_to_f64)
-from .align import align
+from .align import align, align_batched
 from .moe import (ACTS, combine, forward, grouped_gemm, silu_mul_quant,
                   swiglu, token_forward, unquantized_reference)
 
@@ -40,6 +40,6 @@ __all__ = [
     "E4M3_MAX", "bf16_bits_to_f64", "bf16_from_f64", "e4m3_decode",
     "e4m3_encode", "ROUNDINGS", "SCALE_FMTS", "group_scales", "quantize_groups",
     "reciprocal_multiplier",
-    "scales_to_f64", "align", "ACTS", "combine", "forward", "grouped_gemm",
+    "scales_to_f64", "align", "align_batched", "ACTS", "combine", "forward", "grouped_gemm",
     "silu_mul_quant", "swiglu", "token_forward", "unquantized_reference",
 ]

@@ -41,7 +41,7 @@ Stages and the passages they follow:
 
 import numpy as np
 
-from .align import align
+from .align import align, align_batched
 from .fp_formats import bf16_bits_to_f64, bf16_from_f64, e4m3_decode
 from .quant import GROUP, ROUNDINGS, quantize_groups, scales_to_f64
 
@@ -183,7 +183,8 @@ def combine(y_bits, pair_to_row, topk_w, t_live, hidden=None):
 
 
 def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
-            act="swiglu", clamp_limit=np.inf, num_experts=None, rounding="divide"):
+            act="swiglu", clamp_limit=np.inf, num_experts=None, rounding="divide",
+            expert_start=0, expert_cap=0):
     """The whole layer on the aligned, per-expert-contiguous row layout.
 
     ``x_bits`` [t_cap, H] BF16 bits; ``topk_ids``/``topk_w`` [t_cap, K];
@@ -195,14 +196,25 @@ def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
     if num_experts is None:
         num_experts = w1[0].shape[0]
     return forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live,
-                     align_rows, fmt, act, clamp_limit, rounding)
+                     align_rows, fmt, act, clamp_limit, rounding, expert_start, expert_cap)
 
 
 def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
-              fmt, act="swiglu", clamp_limit=np.inf, rounding="divide"):
-    """``forward`` with an explicit expert count (for callable weights)."""
+              fmt, act="swiglu", clamp_limit=np.inf, rounding="divide", expert_start=0,
+              expert_cap=0):
+    """``forward`` with an explicit expert count (for callable weights).
+
+    ``expert_start``: the rank's first expert (local id = id - expert_start;
+    pairs of other ranks' experts are dropped). ``expert_cap`` > 0: the
+    batched masked-M layout with that many rows per expert (align_rows is
+    then unused); 0: the aligned layout.
+    """
     k = np.asarray(topk_ids).shape[1]
-    al = align(topk_ids, t_live, num_experts, align_rows)
+    if expert_cap > 0:
+        al = align_batched(topk_ids, t_live, num_experts, expert_cap, expert_start)
+        al["counts"] = al["masked_m"]
+    else:
+        al = align(topk_ids, t_live, num_experts, align_rows, expert_start)
     x = bf16_bits_to_f64(np.asarray(x_bits)[:t_live]).astype(np.float32)
     xq, xs = quantize_groups(x, fmt, rounding)
     token_of_row = np.where(al["row_to_pair"] >= 0, al["row_to_pair"] // k, 0)
@@ -217,18 +229,21 @@ def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
     y, _ = grouped_gemm(hq_full, hs_full, fmt, w2, al["counts"], al["offsets"], rounding=rounding)
     out = combine(y, al["pair_to_row"], topk_w, t_live, np.asarray(x_bits).shape[1])
     res = dict(al)
+    res.setdefault("overflow", 0)
     res.update(xq=xq, xs=xs, c1=c1, live=live, hq=hq_full, hs=hs_full, y=y, out=out)
     return res
 
 
 def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
-                  act="swiglu", clamp_limit=np.inf, tokens=None, rounding="divide"):
+                  act="swiglu", clamp_limit=np.inf, tokens=None, rounding="divide",
+                  expert_start=0):
     """Dense per-token brute force: no alignment, no row maps, one token at a time.
 
     ``tokens`` selects which tokens to evaluate (default: all t < t_live);
-    returns BF16 bits [len(tokens), H].
+    experts are the local ids id - expert_start in [0, num_experts).
+    Returns BF16 bits [len(tokens), H].
     """
-    ids = np.asarray(topk_ids)
+    ids = np.asarray(topk_ids).astype(np.int64) - int(expert_start)
     topk_w = np.asarray(topk_w, dtype=np.float32)
     tokens = range(t_live) if tokens is None else tokens
     rows = []
