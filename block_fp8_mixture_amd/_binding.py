@@ -50,7 +50,7 @@ class _Problem(ctypes.Structure):
     _fields_ = [("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("topk", _i32),
                 ("t_cap", _i32), ("align_rows", _i32), ("row_cap", _i32),
                 ("scale_fmt", ctypes.c_int), ("act", ctypes.c_int), ("clamp_limit", _f32),
-                ("rounding", ctypes.c_int)]
+                ("rounding", ctypes.c_int), ("expert_start", _i32), ("expert_cap", _i32)]
 
 
 class _Tensors(ctypes.Structure):
@@ -64,14 +64,22 @@ class _Layout(ctypes.Structure):
                 ("row_to_pair", ctypes.c_size_t), ("pair_to_row", ctypes.c_size_t),
                 ("xq", ctypes.c_size_t), ("xs", ctypes.c_size_t), ("c1", ctypes.c_size_t),
                 ("hq", ctypes.c_size_t), ("hs", ctypes.c_size_t), ("y", ctypes.c_size_t),
-                ("act", ctypes.c_size_t), ("status", ctypes.c_size_t), ("total", ctypes.c_size_t),
-                ("row_cap", _i32)]
+                ("act", ctypes.c_size_t), ("status", ctypes.c_size_t),
+                ("overflow", ctypes.c_size_t), ("total", ctypes.c_size_t), ("row_cap", _i32)]
 
 
 _SIGNATURES = {
     "moe_min_row_cap": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "moe_align": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "moe_align": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                 _vp]),
+    "moe_align_batched": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                         _vp, _vp]),
+    "moe_grouped_gemm_fp8_masked": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp,
+                                                   _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                                   _vp]),
+    "moe_silu_mul_quant_masked": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, ctypes.c_int, _f32,
+                                                 ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "moe_act_quant": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.c_int, ctypes.c_int, _vp, _vp,
                                      _vp]),
     "moe_grouped_gemm_fp8": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp, _vp,
@@ -200,8 +208,10 @@ def moe_status_string(status):
     return load_library().moe_status_string(status).decode()
 
 
-def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, out=None):
-    """Routing alignment. Returns dict(counts, offsets, row_to_pair, pair_to_row)."""
+def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, out=None,
+              expert_start=0):
+    """Routing alignment. Returns dict(counts, offsets, row_to_pair, pair_to_row).
+    Local expert ids are ``topk_ids - expert_start``."""
     lib = load_library()
     ids = _need(topk_ids, "topk_ids", torch.int32, ndim=2)
     t_cap, topk = ids.shape
@@ -219,10 +229,35 @@ def moe_align(topk_ids, num_experts, align_rows=16, row_cap=None, t_live=None, o
                  ("row_to_pair", row_cap), ("pair_to_row", t_cap * topk)):
         _min_numel(_need(out[k], k, torch.int32), k, n)
     _same_device(ids, *out.values())
-    st = lib.moe_align(_ptr(ids), t_cap, _live(t_live), topk, num_experts, align_rows, row_cap,
-                       _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["row_to_pair"]),
-                       _ptr(out["pair_to_row"]), _stream())
+    st = lib.moe_align(_ptr(ids), t_cap, _live(t_live), topk, num_experts, expert_start,
+                       align_rows, row_cap, _ptr(out["counts"]), _ptr(out["offsets"]),
+                       _ptr(out["row_to_pair"]), _ptr(out["pair_to_row"]), _stream())
     _check("moe_align", st)
+    return out
+
+
+def moe_align_batched(topk_ids, num_experts, expert_cap, t_live=None, out=None, expert_start=0):
+    """Routing into the batched masked-M layout ([E, expert_cap] rows). Returns
+    dict(masked_m, row_to_pair, pair_to_row, overflow)."""
+    lib = load_library()
+    ids = _need(topk_ids, "topk_ids", torch.int32, ndim=2)
+    t_cap, topk = ids.shape
+    dev = ids.device
+    if out is None:
+        out = {
+            "masked_m": torch.empty(num_experts, dtype=torch.int32, device=dev),
+            "row_to_pair": torch.empty(max(num_experts * expert_cap, 1), dtype=torch.int32, device=dev),
+            "pair_to_row": torch.empty(max(t_cap * topk, 1), dtype=torch.int32, device=dev),
+            "overflow": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    for k, n in (("masked_m", num_experts), ("row_to_pair", num_experts * expert_cap),
+                 ("pair_to_row", t_cap * topk), ("overflow", 1)):
+        _min_numel(_need(out[k], k, torch.int32), k, n)
+    _same_device(ids, *out.values())
+    st = lib.moe_align_batched(_ptr(ids), t_cap, _live(t_live), topk, num_experts, expert_start,
+                               expert_cap, _ptr(out["masked_m"]), _ptr(out["row_to_pair"]),
+                               _ptr(out["pair_to_row"]), _ptr(out["overflow"]), _stream())
+    _check("moe_align_batched", st)
     return out
 
 
@@ -284,6 +319,72 @@ def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap
     return out
 
 
+def moe_grouped_gemm_fp8_masked(a, a_scales, fmt, w, w_scales, masked_m, expert_cap,
+                                a_row_map=None, a_row_div=1, out=None, tiles_visited=None):
+    """Grouped FP8 GEMM on the batched masked-M layout: expert e's live rows are
+    [e*cap, e*cap + masked_m[e]). Returns BF16 bits (int16) [E*cap, N]."""
+    lib = load_library()
+    _need(a, "a", torch.uint8, ndim=2)
+    _need(a_scales, "a_scales", _scale_dtype(fmt), ndim=2)
+    _need(w, "w", torch.uint8, ndim=3)
+    _need(w_scales, "w_scales", torch.float32, ndim=3)
+    num_experts, n, k = w.shape
+    rows = num_experts * expert_cap
+    a_rows = a.shape[0]
+    if a.shape[1] != k:
+        raise ValueError("a and w disagree on K")
+    _shape(a_scales, "a_scales", (k // 128, a_rows))
+    _shape(w_scales, "w_scales", (num_experts, n // 128, k // 128))
+    _shape(_need(masked_m, "masked_m", torch.int32), "masked_m", (num_experts,))
+    if out is None:
+        out = torch.empty((max(rows, 1), n), dtype=torch.int16, device=a.device)
+    ob = _bf16_view(out, "out")
+    if ob.dim() != 2 or ob.shape[1] != n or ob.shape[0] < rows:
+        raise ValueError(f"out must be [>= {rows}, {n}], got {tuple(ob.shape)}")
+    if a_row_map is not None:
+        _min_numel(_need(a_row_map, "a_row_map", torch.int32), "a_row_map", rows)
+    elif a_rows < rows:
+        raise ValueError("without a row map, a needs num_experts * expert_cap rows")
+    if tiles_visited is not None:
+        _min_numel(_need(tiles_visited, "tiles_visited", torch.int32), "tiles_visited", 1)
+    _same_device(a, a_scales, w, w_scales, masked_m, ob, a_row_map, tiles_visited)
+    st = lib.moe_grouped_gemm_fp8_masked(_ptr(a), _ptr(a_scales), _fmt(fmt), a_rows,
+                                         _ptr(a_row_map), a_row_div, _ptr(w), _ptr(w_scales),
+                                         _ptr(masked_m), num_experts, expert_cap, n, k, _ptr(ob),
+                                         _ptr(tiles_visited), _stream())
+    _check("moe_grouped_gemm_fp8_masked", st)
+    return out
+
+
+def moe_silu_mul_quant_masked(gate_up, masked_m, expert_cap, act="swiglu",
+                              clamp_limit=float("inf"), fmt="fp32", hq=None, hs=None,
+                              rounding="divide"):
+    """SiLU(gate)*up + 1x128 FP8 quantization on the batched masked-M layout.
+    Returns (hq uint8 [E*cap, I], hs [I/128, E*cap])."""
+    lib = load_library()
+    gu = _bf16_view(gate_up, "gate_up")
+    _need(masked_m, "masked_m", torch.int32, ndim=1)
+    num_experts = masked_m.shape[0]
+    rows = num_experts * expert_cap
+    if gu.dim() != 2 or gu.shape[1] % 2 or gu.shape[0] != rows:
+        raise ValueError(f"gate_up must be [{rows}, 2 * inter], got {tuple(gu.shape)}")
+    inter = gu.shape[1] // 2
+    if hq is None:
+        hq = torch.empty((rows, inter), dtype=torch.uint8, device=gu.device)
+    if hs is None:
+        hs = torch.empty((inter // 128, rows), dtype=_scale_dtype(fmt), device=gu.device)
+    _shape(_need(hq, "hq", torch.uint8), "hq", (rows, inter))
+    _shape(_need(hs, "hs", _scale_dtype(fmt)), "hs", (inter // 128, rows))
+    _same_device(gu, masked_m, hq, hs)
+    if act not in ACTS:
+        raise ValueError(f"act must be one of {list(ACTS)}")
+    st = lib.moe_silu_mul_quant_masked(_ptr(gu), inter, _ptr(masked_m), num_experts, expert_cap,
+                                       ACTS[act], float(clamp_limit), _fmt(fmt),
+                                       _rounding(rounding), _ptr(hq), _ptr(hs), _stream())
+    _check("moe_silu_mul_quant_masked", st)
+    return hq, hs
+
+
 def moe_silu_mul_quant(gate_up, counts, offsets, act="swiglu", clamp_limit=float("inf"),
                        fmt="fp32", hq=None, hs=None, rounding="divide"):
     """SiLU(gate)*up + 1x128 FP8 quantization of live rows.
@@ -334,29 +435,32 @@ def moe_topk_combine(y, pair_to_row, topk_w, t_live=None, out=None):
 
 
 def _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act, clamp_limit,
-             rounding="divide"):
+             rounding="divide", expert_start=0, expert_cap=0):
     if act not in ACTS:
         raise ValueError(f"act must be one of {list(ACTS)}")
     return _Problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap or 0, _fmt(fmt),
-                    ACTS[act], float(clamp_limit), _rounding(rounding))
+                    ACTS[act], float(clamp_limit), _rounding(rounding), int(expert_start),
+                    int(expert_cap))
 
 
 def moe_workspace_plan(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
-                       fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide"):
+                       fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide",
+                       expert_start=0, expert_cap=0):
     """Byte offsets of every intermediate in the forward workspace (dict)."""
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding)
+                    clamp_limit, rounding, expert_start, expert_cap)
     lay = _Layout()
     _check("moe_workspace_plan", lib.moe_workspace_plan(ctypes.byref(prob), ctypes.byref(lay)))
     return {name: getattr(lay, name) for name, _ in _Layout._fields_}
 
 
 def moe_workspace_bytes(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
-                        fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide"):
+                        fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide",
+                        expert_start=0, expert_cap=0):
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding)
+                    clamp_limit, rounding, expert_start, expert_cap)
     return int(lib.moe_workspace_bytes(ctypes.byref(prob)))
 
 
@@ -382,7 +486,7 @@ def _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2=None, w2_scales=None):
 
 def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", act="swiglu",
                 clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None, out=None,
-                workspace=None, rounding="divide"):
+                workspace=None, rounding="divide", expert_start=0, expert_cap=0):
     """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8).
     ``topk_w=None`` weights every routed pair by one."""
     lib = load_library()
@@ -395,7 +499,7 @@ def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", a
         topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
     _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding)
+                    clamp_limit, rounding, expert_start, expert_cap)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if need == 0:
         lay = _Layout()
@@ -424,7 +528,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32",
                         act="swiglu", clamp_limit=float("inf"), align_rows=16, row_cap=0,
-                        t_live=None, out=None, rounding="divide"):
+                        t_live=None, out=None, rounding="divide", expert_start=0, expert_cap=0):
     """moe_forward with the library's static per-device workspace instead of a
     caller buffer (for callers that cannot allocate; the call allocates nothing
     when ``out`` and ``topk_w`` are given). Calls on one device must not overlap.
@@ -445,7 +549,7 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
         _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
     _same_device(xb, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, ob, t_live)
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding)
+                    clamp_limit, rounding, expert_start, expert_cap)
     tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
                     _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
     _check("moe_forward_noalloc", lib.moe_forward_noalloc(ctypes.byref(prob), ctypes.byref(tens),
@@ -455,7 +559,7 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
 
 def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
                    clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None,
-                   workspace=None, rounding="divide"):
+                   workspace=None, rounding="divide", expert_start=0):
     """The decode path's first launch alone (routing, activation quantization and
     FC1 with SiLU(gate)*up), writing moe_forward's workspace. Returns the workspace."""
     lib = load_library()
@@ -467,7 +571,7 @@ def moe_fc1_decode(x, topk_ids, w1, w1_scales, inter, fmt="fp32", act="swiglu",
     if w_inter != inter:
         raise ValueError("w1 shape disagrees with inter")
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap,
-                    fmt, act, clamp_limit, rounding)
+                    fmt, act, clamp_limit, rounding, expert_start)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xb.device)

@@ -6,6 +6,14 @@
 // alignment yields padded expert blocks and sorted token ids, and ids outside
 // the local expert range are dropped.
 //
+// Expert parallelism (TensorRT-LLM PR #21250, review comment: drop pairs of
+// other ranks' experts): ids are read as local ids id - expert_start, and
+// those outside [0, E) are dropped. The batched masked-M layout (vLLM PR
+// #65794, Details, batched experts; batch_cap > 0): expert e owns the fixed
+// rows [e*cap, (e+1)*cap), counts become masked_m = min(count, cap), pairs
+// ranked at or past the capacity are dropped (and counted), and rows past
+// masked_m are left untouched.
+//
 // One launch, no scratch memory. Block b owns pairs [b*kChunk, (b+1)*kChunk).
 // Every block counts all live pairs per expert in LDS (so every block knows
 // the endpoints) and, separately, the pairs before its chunk (so it knows
@@ -33,7 +41,8 @@ __device__ __forceinline__ void align_block(
     int block, const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
-    int32_t* __restrict__ pair_to_row) {
+    int32_t* __restrict__ pair_to_row, int expert_start, int batch_cap,
+    int32_t* __restrict__ overflow) {
   // Per expert: live pairs (low word) and live pairs before the chunk (high).
   __shared__ unsigned long long s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
@@ -57,7 +66,7 @@ __device__ __forceinline__ void align_block(
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int p = p0 + i * kThreads + tid;
-      ev[i] = p < cap_pairs ? ids[p] : -1;
+      ev[i] = p < cap_pairs ? ids[p] - expert_start : -1;
     }
   };
   load_batch(0);
@@ -87,9 +96,13 @@ __device__ __forceinline__ void align_block(
   __syncthreads();
   auto total = [&](int e) { return static_cast<int>(static_cast<uint32_t>(s_cnt[e])); };
 
-  // Phase 2: endpoints = exclusive prefix sum of counts rounded up to align_rows.
-  // Thread t owns experts [t*per, t*per + per).
-  {
+  // Phase 2: endpoints = exclusive prefix sum of counts rounded up to
+  // align_rows (thread t owns experts [t*per, t*per + per)), or the fixed
+  // segments e*cap of the batched layout.
+  if (batch_cap > 0) {
+    for (int e = tid; e <= E; e += kThreads) s_off[e] = e * batch_cap;
+    __syncthreads();
+  } else {
     const int per = (E + kThreads - 1) / kThreads;
     const int b = tid * per;
     int local = 0;
@@ -116,12 +129,28 @@ __device__ __forceinline__ void align_block(
   }
 
   if (block == 0) {
-    for (int e = tid; e < E; e += kThreads) {
-      counts[e] = total(e);
-      offsets[e] = s_off[e];
-      for (int r = s_off[e] + total(e); r < s_off[e + 1]; ++r) row_to_pair[r] = -1;
+    if (batch_cap > 0) {
+      int over = 0;
+      for (int e = tid; e < E; e += kThreads) {
+        counts[e] = min(total(e), batch_cap);
+        if (offsets) offsets[e] = s_off[e];  // implicit in the batched layout: optional
+        over += max(total(e) - batch_cap, 0);
+      }
+      if (overflow) {
+        if (tid == 0) s_wsum[0] = 0;
+        __syncthreads();
+        if (over) atomicAdd(&s_wsum[0], over);
+        __syncthreads();
+        if (tid == 0) *overflow = s_wsum[0];
+      }
+    } else {
+      for (int e = tid; e < E; e += kThreads) {
+        counts[e] = total(e);
+        offsets[e] = s_off[e];
+        for (int r = s_off[e] + total(e); r < s_off[e + 1]; ++r) row_to_pair[r] = -1;
+      }
     }
-    if (tid == 0) offsets[E] = s_off[E];
+    if (tid == 0 && offsets) offsets[E] = s_off[E];
   }
 
   // Phase 3: stable ranks inside the chunk (kChunk == kThreads: one pair per
@@ -166,8 +195,9 @@ __device__ __forceinline__ void align_block(
       for (int w = 0; w < kWaves; ++w) prior += w < wave ? cnt[w * kMaxExperts + e] : 0;
     }
   }
-  if (ok) {
-    const int row = s_off[e] + static_cast<int>(s_cnt[e] >> 32) + prior + rank;
+  const int within = ok ? static_cast<int>(s_cnt[e] >> 32) + prior + rank : 0;
+  if (ok && (batch_cap == 0 || within < batch_cap)) {
+    const int row = s_off[e] + within;
     row_to_pair[row] = p;
     pair_to_row[p] = row;
   } else if (in_range) {
@@ -179,9 +209,10 @@ __global__ __launch_bounds__(kThreads) void align_kernel(
     const int32_t* __restrict__ ids, int t_cap, const int32_t* __restrict__ t_live_dev,
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
-    int32_t* __restrict__ pair_to_row) {
+    int32_t* __restrict__ pair_to_row, int expert_start, int batch_cap,
+    int32_t* __restrict__ overflow) {
   align_block(blockIdx.x, ids, t_cap, t_live_dev, topk, num_experts, align_rows, counts, offsets,
-              row_to_pair, pair_to_row);
+              row_to_pair, pair_to_row, expert_start, batch_cap, overflow);
 }
 
 // Routing alignment and the activation quantization in one launch, for the
@@ -194,10 +225,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     int topk, int num_experts, int align_rows, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_pair,
     int32_t* __restrict__ pair_to_row, int n_align, const uint16_t* __restrict__ x, int hidden,
-    uint8_t* __restrict__ xq, void* __restrict__ xs, int rnd) {
+    uint8_t* __restrict__ xq, void* __restrict__ xs, int rnd, AlignMode mode) {
   if (static_cast<int>(blockIdx.x) < n_align) {
     align_block(blockIdx.x, ids, t_cap, t_live_dev, topk, num_experts, align_rows, counts,
-                offsets, row_to_pair, pair_to_row);
+                offsets, row_to_pair, pair_to_row, mode.expert_start, mode.batch_cap,
+                mode.overflow);
     return;
   }
   const int64_t gid = static_cast<int64_t>(blockIdx.x - n_align) * (kThreads / 16) + (threadIdx.x >> 4);
@@ -213,18 +245,20 @@ int align_blocks(int t_cap, int topk) {
 
 hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                         int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
-                        int32_t* row_to_pair, int32_t* pair_to_row, hipStream_t stream) {
+                        int32_t* row_to_pair, int32_t* pair_to_row, AlignMode mode,
+                        hipStream_t stream) {
   const int blocks = align_blocks(t_cap, topk);
   hipLaunchKernelGGL(align_kernel, dim3(blocks), dim3(kThreads), 0, stream, ids, t_cap,
                      t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
-                     pair_to_row);
+                     pair_to_row, mode.expert_start, mode.batch_cap, mode.overflow);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                        int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                        int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
-                       int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream) {
+                       int fmt, int rounding, uint8_t* xq, void* xs, AlignMode mode,
+                       hipStream_t stream) {
   const int n_align = align_blocks(t_cap, topk);
   const int64_t groups = static_cast<int64_t>(t_cap) * (hidden / kGroup);
   const int64_t n_quant = (groups + kThreads / 16 - 1) / (kThreads / 16);
@@ -233,15 +267,15 @@ hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev,
   if (fmt == kFp32)
     hipLaunchKernelGGL(prep_kernel<kFp32>, grid, dim3(kThreads), 0, stream, ids, t_cap, t_live_dev,
                        topk, num_experts, align_rows, counts, offsets, row_to_pair, pair_to_row,
-                       n_align, x, hidden, xq, xs, rounding);
+                       n_align, x, hidden, xq, xs, rounding, mode);
   else if (fmt == kFp32Pow2)
     hipLaunchKernelGGL(prep_kernel<kFp32Pow2>, grid, dim3(kThreads), 0, stream, ids, t_cap,
                        t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
-                       pair_to_row, n_align, x, hidden, xq, xs, rounding);
+                       pair_to_row, n_align, x, hidden, xq, xs, rounding, mode);
   else
     hipLaunchKernelGGL(prep_kernel<kUe8m0>, grid, dim3(kThreads), 0, stream, ids, t_cap,
                        t_live_dev, topk, num_experts, align_rows, counts, offsets, row_to_pair,
-                       pair_to_row, n_align, x, hidden, xq, xs, rounding);
+                       pair_to_row, n_align, x, hidden, xq, xs, rounding, mode);
   return hipGetLastError();
 }
 

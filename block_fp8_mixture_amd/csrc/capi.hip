@@ -108,9 +108,9 @@ const char* moe_status_string(moe_status s) {
 }
 
 moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
-                     int32_t topk, int32_t num_experts, int32_t align_rows, int32_t row_cap,
-                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_pair,
-                     int32_t* pair_to_row, void* stream) {
+                     int32_t topk, int32_t num_experts, int32_t expert_start, int32_t align_rows,
+                     int32_t row_cap, int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* row_to_pair, int32_t* pair_to_row, void* stream) {
   if (t_cap < 0 || topk < 1 || topk > kMaxTopk || num_experts < 1 || align_rows < 1 || row_cap < 0)
     return MOE_ERR_INVALID_ARG;
   if (num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -118,9 +118,32 @@ moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_li
   if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (t_cap > 0 && (!topk_ids || !row_to_pair || !pair_to_row)) return MOE_ERR_INVALID_ARG;
   if (row_cap < min_row_cap64(t_cap, topk, num_experts, align_rows)) return MOE_ERR_CAPACITY;
+  moe::AlignMode mode;
+  mode.expert_start = expert_start;
   return from_hip(moe::launch_align(topk_ids, t_cap, t_live_dev, topk, num_experts, align_rows,
-                                    expert_counts, expert_offsets, row_to_pair, pair_to_row,
+                                    expert_counts, expert_offsets, row_to_pair, pair_to_row, mode,
                                     as_stream(stream)));
+}
+
+moe_status moe_align_batched(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
+                             int32_t topk, int32_t num_experts, int32_t expert_start,
+                             int32_t expert_cap, int32_t* masked_m, int32_t* row_to_pair,
+                             int32_t* pair_to_row, int32_t* overflow, void* stream) {
+  if (t_cap < 0 || topk < 1 || topk > kMaxTopk || num_experts < 1 || expert_cap < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(t_cap) * topk > INT32_MAX / 2 ||
+      static_cast<int64_t>(num_experts) * expert_cap > INT32_MAX / 2)
+    return MOE_ERR_INVALID_ARG;
+  if (!masked_m) return MOE_ERR_INVALID_ARG;
+  if (t_cap > 0 && (!topk_ids || !row_to_pair || !pair_to_row)) return MOE_ERR_INVALID_ARG;
+  moe::AlignMode mode;
+  mode.expert_start = expert_start;
+  mode.batch_cap = expert_cap;
+  mode.overflow = overflow;
+  // The fixed segments' endpoints e*cap are implicit: no offsets output.
+  return from_hip(moe::launch_align(topk_ids, t_cap, t_live_dev, topk, num_experts, 1, masked_m,
+                                    nullptr, row_to_pair, pair_to_row, mode, as_stream(stream)));
 }
 
 moe_status moe_act_quant(const uint16_t* x, int32_t t_cap, const int32_t* t_live_dev,
@@ -141,7 +164,7 @@ static moe_status gemm_checked(const moe::GemmArgs& g, void* stream) {
     return MOE_ERR_INVALID_ARG;
   if (g.num_experts > moe::kMaxExperts || !gemm_shape_ok(g.a_rows, g.n, g.k))
     return MOE_ERR_UNSUPPORTED;
-  if (!g.counts || !g.offsets || !g.w || !g.w_scales) return MOE_ERR_INVALID_ARG;
+  if (!g.counts || (!g.offsets && g.seg_cap == 0) || !g.w || !g.w_scales) return MOE_ERR_INVALID_ARG;
   if (g.row_cap > 0 && (!g.c || !g.a || !g.a_scales)) return MOE_ERR_INVALID_ARG;
   if (g.row_cap == 0) return MOE_OK;
   return from_hip(moe::launch_grouped_gemm(g, as_stream(stream)));
@@ -178,6 +201,38 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
   return gemm_checked(g, stream);
 }
 
+moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                       int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                       const uint8_t* w, const float* w_scales,
+                                       const int32_t* masked_m, int32_t num_experts,
+                                       int32_t expert_cap, int32_t n, int32_t k, uint16_t* c,
+                                       int32_t* tiles_visited, void* stream) {
+  if (expert_cap < 1 || num_experts < 1) return MOE_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_experts) * expert_cap > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
+  const int32_t rows = num_experts * expert_cap;
+  moe::GemmArgs g;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.fmt = fmt;
+  g.a_rows = a_rows;
+  g.a_row_map = a_row_map;
+  g.a_row_div = a_row_div;
+  g.w = w;
+  g.w_scales = w_scales;
+  g.counts = masked_m;
+  g.offsets = nullptr;
+  g.seg_cap = expert_cap;
+  g.num_experts = num_experts;
+  g.row_cap = rows;
+  g.max_rows_per_expert = expert_cap;
+  g.max_live_experts = num_experts;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  g.tiles_visited = tiles_visited;
+  return gemm_checked(g, stream);
+}
+
 moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               const int32_t* expert_counts, const int32_t* expert_offsets,
                               int32_t num_experts, int32_t row_cap, moe_act act,
@@ -187,13 +242,32 @@ moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
       !rounding_ok(rounding))
     return MOE_ERR_INVALID_ARG;
   if (act != MOE_ACT_SWIGLU && !(clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;  // the kernel's LDS endpoint table
   if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
   if (row_cap > 0 && (!gate_up || !hq || !hs)) return MOE_ERR_INVALID_ARG;
   if (static_cast<int64_t>(row_cap) * (inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (row_cap == 0) return MOE_OK;
   return from_hip(moe::launch_silu_mul_quant(gate_up, inter, expert_counts, expert_offsets,
                                              num_experts, row_cap, act, clamp_limit, fmt,
-                                             rounding, hq, hs, as_stream(stream)));
+                                             rounding, hq, hs, 0, as_stream(stream)));
+}
+
+moe_status moe_silu_mul_quant_masked(const uint16_t* gate_up, int32_t inter,
+                                     const int32_t* masked_m, int32_t num_experts,
+                                     int32_t expert_cap, moe_act act, float clamp_limit,
+                                     moe_scale_fmt fmt, moe_rounding rounding, uint8_t* hq,
+                                     void* hs, void* stream) {
+  if (!dim128(inter) || num_experts < 1 || expert_cap < 1 || !fmt_ok(fmt) || !act_ok(act) ||
+      !rounding_ok(rounding))
+    return MOE_ERR_INVALID_ARG;
+  if (num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (act != MOE_ACT_SWIGLU && !(clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
+  const int64_t rows = static_cast<int64_t>(num_experts) * expert_cap;
+  if (rows > INT32_MAX / 2 || rows * (inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!masked_m || !gate_up || !hq || !hs) return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_silu_mul_quant(gate_up, inter, masked_m, nullptr, num_experts,
+                                             static_cast<int>(rows), act, clamp_limit, fmt,
+                                             rounding, hq, hs, expert_cap, as_stream(stream)));
 }
 
 moe_status moe_topk_combine(const uint16_t* y, int32_t row_cap, const int32_t* pair_to_row,
@@ -216,9 +290,14 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
     return MOE_ERR_INVALID_ARG;
   if (p->act != MOE_ACT_SWIGLU && !(p->clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (p->num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
-  const int64_t need = min_row_cap64(p->t_cap, p->topk, p->num_experts, p->align_rows);
+  if (p->expert_cap < 0) return MOE_ERR_INVALID_ARG;
+  const bool batched = p->expert_cap > 0;
+  // Rows: any aligned routing's need, or the batched layout's E * cap.
+  const int64_t need = batched ? static_cast<int64_t>(p->num_experts) * p->expert_cap
+                               : min_row_cap64(p->t_cap, p->topk, p->num_experts, p->align_rows);
   if (need > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
   const int64_t rc = p->row_cap == 0 ? need : p->row_cap;
+  if (batched && rc != need) return MOE_ERR_INVALID_ARG;  // the batched layout fixes its rows
   if (rc < need) return MOE_ERR_CAPACITY;
   if (rc * (p->inter / 128) > INT32_MAX) return MOE_ERR_INVALID_ARG;  // as moe_silu_mul_quant
   if (!gemm_shape_ok(p->t_cap, 2 * static_cast<int64_t>(p->inter), p->hidden) ||
@@ -242,9 +321,11 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   L->hq = take(R * I);
   L->hs = take((I / 128) * R * sb);
   L->y = take(R * H * 2);
-  const bool decode = moe::down_combine_fits(p->t_cap, p->topk, p->inter);
+  // The decode path serves the aligned layout only.
+  const bool decode = !batched && moe::down_combine_fits(p->t_cap, p->topk, p->inter);
   L->act = decode ? take(R * I * 4) : 0;
   L->status = take(static_cast<size_t>(moe::kDlMaxGrid) * 4);
+  L->overflow = take(4);
   L->total = off;
   if (!decode) L->act = L->status;
   L->row_cap = static_cast<int32_t>(rc);
@@ -297,6 +378,7 @@ moe::DecodeFc1Args fc1_decode_args(const moe_problem* p, const moe_tensors* t,
   f.num_experts = p->num_experts;
   f.align_rows = p->align_rows;
   f.row_cap = L.row_cap;
+  f.expert_start = p->expert_start;
   f.x = t->x;
   f.hidden = p->hidden;
   f.inter = p->inter;
@@ -413,9 +495,13 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
     return from_hip(e);
   }
   // Alignment and activation quantization share one launch (independent work).
+  moe::AlignMode mode;
+  mode.expert_start = p->expert_start;
+  mode.batch_cap = p->expert_cap;
+  mode.overflow = p->expert_cap > 0 ? reinterpret_cast<int32_t*>(ws + L.overflow) : nullptr;
   e = moe::launch_prep(t->topk_ids, p->t_cap, t->t_live_dev, p->topk, p->num_experts,
                        p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden, p->scale_fmt,
-                       p->rounding, xq, xs, s);
+                       p->rounding, xq, xs, mode, s);
 
   moe::GemmArgs g;
   g.fmt = p->scale_fmt;
@@ -424,6 +510,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   g.num_experts = p->num_experts;
   g.row_cap = R;
   g.max_rows_per_expert = pairs < R ? pairs : R;
+  if (p->expert_cap > 0 && p->expert_cap < g.max_rows_per_expert) g.max_rows_per_expert = p->expert_cap;
   g.max_live_experts = pairs < p->num_experts ? pairs : p->num_experts;
   g.tiles_visited = nullptr;
   g.rounding = p->rounding;
@@ -452,7 +539,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   }
   if (e == hipSuccess)
     e = moe::launch_silu_mul_quant(c1, p->inter, counts, offsets, p->num_experts, R, p->act,
-                                   p->clamp_limit, p->scale_fmt, p->rounding, hq, hs, s);
+                                   p->clamp_limit, p->scale_fmt, p->rounding, hq, hs, 0, s);
   if (e == hipSuccess) {  // FC2
     g.a = hq;
     g.a_scales = hs;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const int gpr = H / kGroup;   // activation groups per token
 
   // ---- 1. everything the prologue reads, issued together
-  const int my_id = tid < PQ ? p.ids[tid] : -1;
+  const int my_id = tid < PQ ? p.ids[tid] - p.expert_start : -1;  // local expert id
   const float my_tw = FUSED && tid < PQ ? q.topk_w[tid] : 0.0f;
   // This launch's epoch at the grid barrier.
   const unsigned epoch = FUSED ? flag_load(&g_dl_flag[blockIdx.x]) + 1u : 0u;

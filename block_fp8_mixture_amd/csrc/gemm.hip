@@ -43,8 +43,17 @@ namespace {
 constexpr int kThreads = 256;
 
 
+// Segment of expert e: from the endpoints, or the batched layout's fixed
+// rows [e*seg_cap, (e+1)*seg_cap).
+__device__ __forceinline__ int seg_start(const GemmArgs& p, int e) {
+  return p.seg_cap > 0 ? e * p.seg_cap : p.offsets[e];
+}
+__device__ __forceinline__ int seg_end(const GemmArgs& p, int e) {
+  return p.seg_cap > 0 ? (e + 1) * p.seg_cap : p.offsets[e + 1];
+}
+
 __device__ __forceinline__ int expert_rows(const GemmArgs& p, int e) {
-  return segment_rows(p.offsets[e], p.offsets[e + 1], p.counts[e], p.row_cap);
+  return segment_rows(seg_start(p, e), seg_end(p, e), p.counts[e], p.row_cap);
 }
 
 // A row feeding output row r, or -1 when the map points outside A. GATHER
@@ -77,8 +86,8 @@ __device__ int build_expert_list(const GemmArgs& p, Want want, Units units, int*
 #pragma unroll
   for (int c = 0; c < kC; ++c) {
     const int e = c * NT + tid < num_experts ? c * NT + tid : num_experts - 1;
-    row0s[c] = p.offsets[e];
-    cnts[c] = p.offsets[e + 1];
+    row0s[c] = seg_start(p, e);
+    cnts[c] = seg_end(p, e);
     cnts[c] = segment_rows(row0s[c], cnts[c], p.counts[e], p.row_cap);
     if (c * NT + tid >= num_experts) cnts[c] = 0;
   }
@@ -681,7 +690,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     tile_coords(tile - s_pref[lo] * nt, mt_e, nt, &mt, &ntile);
     const int cnt = __builtin_amdgcn_readfirstlane(expert_rows(p, e));
     const int rows_here = min(TM, cnt - mt * TM);
-    const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]) + mt * TM;
+    const int row0 = __builtin_amdgcn_readfirstlane(seg_start(p, e)) + mt * TM;
     const int n0 = ntile * TNT;
     const bool wave_on = wm * 64 < rows_here && n0 + wn * WN < N;
     const uint8_t* wbase = p.w + static_cast<int64_t>(e) * N * K;

@@ -12,24 +12,38 @@ constexpr int kStreamMaxRows = 64;    // experts with at most this many rows str
 constexpr int kTiledTileM = 256;      // row tile of the MFMA-tiled GEMM
 constexpr int kColTile = 128;         // column tile (= weight block rows)
 
+// How routed ids become rows: local ids id - expert_start (other ids are
+// dropped); batch_cap > 0 selects the batched layout of batch_cap rows per
+// expert, whose pairs past the capacity are dropped and counted into
+// *overflow (when given).
+struct AlignMode {
+  int expert_start = 0;
+  int batch_cap = 0;
+  int32_t* overflow = nullptr;
+};
+
 hipError_t launch_align(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                         int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
-                        int32_t* row_to_pair, int32_t* pair_to_row, hipStream_t stream);
+                        int32_t* row_to_pair, int32_t* pair_to_row, AlignMode mode,
+                        hipStream_t stream);
 
 // moe_align and moe_act_quant of one layer in a single launch.
 // `rounding` below is the quantizers' convention (Rounding in device_common.h).
 hipError_t launch_prep(const int32_t* ids, int t_cap, const int32_t* t_live_dev, int topk,
                        int num_experts, int align_rows, int32_t* counts, int32_t* offsets,
                        int32_t* row_to_pair, int32_t* pair_to_row, const uint16_t* x, int hidden,
-                       int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream);
+                       int fmt, int rounding, uint8_t* xq, void* xs, AlignMode mode,
+                       hipStream_t stream);
 
 hipError_t launch_act_quant(const uint16_t* x, int t_cap, const int32_t* t_live_dev, int hidden,
                             int fmt, int rounding, uint8_t* xq, void* xs, hipStream_t stream);
 
+// seg_cap > 0: the batched layout, expert e's rows starting at e*seg_cap
+// (offsets is then not read).
 hipError_t launch_silu_mul_quant(const uint16_t* gate_up, int inter, const int32_t* counts,
                                  const int32_t* offsets, int num_experts, int row_cap, int act,
                                  float clamp_limit, int fmt, int rounding, uint8_t* hq, void* hs,
-                                 hipStream_t stream);
+                                 int seg_cap, hipStream_t stream);
 
 hipError_t launch_topk_combine(const uint16_t* y, int row_cap, const int32_t* pair_to_row,
                                const float* topk_w, int t_cap, const int32_t* t_live_dev,
@@ -45,7 +59,7 @@ struct GemmArgs {
   const uint8_t* w;
   const float* w_scales;
   const int32_t* counts;
-  const int32_t* offsets;
+  const int32_t* offsets;   // not read when seg_cap > 0
   int num_experts;
   int row_cap;
   int max_rows_per_expert;  // host bound on counts[e]
@@ -64,6 +78,9 @@ struct GemmArgs {
   int act = 0;
   float act_limit = 0.0f;
   int rounding = 0;  // act_out is BF16-rounded under the reciprocal convention
+  // The batched layout: expert e's segment is rows [e*seg_cap, (e+1)*seg_cap)
+  // (0: the segments come from offsets).
+  int seg_cap = 0;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
@@ -129,6 +146,7 @@ struct DecodeFc1Args {
   int num_experts;
   int align_rows;
   int row_cap;
+  int expert_start;           // local ids are ids - expert_start
   const uint16_t* x;          // [t_cap, H] BF16
   int hidden;
   int inter;

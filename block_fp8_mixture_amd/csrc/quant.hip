@@ -48,7 +48,7 @@ template <int FMT, int ACT>
 __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
     const uint16_t* __restrict__ gate_up, int inter, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int num_experts, int row_cap, float clamp_limit,
-    uint8_t* __restrict__ hq, void* __restrict__ hs, int rnd) {
+    uint8_t* __restrict__ hq, void* __restrict__ hs, int rnd, int seg_cap) {
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_cnt[kMaxExperts];
   __shared__ double s_lut[kSiluLutSize];
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kSmqThreads) void silu_mul_quant_kernel(
   const int l16 = threadIdx.x & 15;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kSmqGroupsPerBlock;
   for (int e = threadIdx.x; e <= num_experts; e += kSmqThreads) {
-    s_off[e] = offsets[e];
+    s_off[e] = seg_cap > 0 ? e * seg_cap : offsets[e];  // the batched layout's fixed segments
     if (e < num_experts) s_cnt[e] = counts[e];
   }
   __syncthreads();
@@ -127,7 +127,7 @@ hipError_t act_quant_fmt(const uint16_t* x, int t_cap, const int32_t* t_live_dev
 template <int FMT, int ACT>
 hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
                       const int32_t* offsets, int num_experts, int row_cap, float clamp_limit,
-                      uint8_t* hq, void* hs, int rnd, hipStream_t stream) {
+                      uint8_t* hq, void* hs, int rnd, int seg_cap, hipStream_t stream) {
   const int64_t groups = static_cast<int64_t>(row_cap) * (inter / kGroup);
   if (groups > INT32_MAX) return hipErrorInvalidValue;  // the kernel divides 32-bit group indices
   const int64_t need = (groups + 2 * kSmqGroupsPerBlock - 1) / (2 * kSmqGroupsPerBlock);
@@ -135,25 +135,27 @@ hipError_t smq_launch(const uint16_t* gate_up, int inter, const int32_t* counts,
   const int blocks = static_cast<int>(need < cap ? need : cap);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((silu_mul_quant_kernel<FMT, ACT>), dim3(blocks), dim3(kSmqThreads), 0, stream,
-                     gate_up, inter, counts, offsets, num_experts, row_cap, clamp_limit, hq, hs, rnd);
+                     gate_up, inter, counts, offsets, num_experts, row_cap, clamp_limit, hq, hs, rnd,
+                     seg_cap);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t smq_fmt(const uint16_t* gate_up, int inter, const int32_t* counts,
                    const int32_t* offsets, int num_experts, int row_cap, int act,
-                   float clamp_limit, uint8_t* hq, void* hs, int rnd, hipStream_t stream) {
+                   float clamp_limit, uint8_t* hq, void* hs, int rnd, int seg_cap,
+                   hipStream_t stream) {
   switch (act) {
     case kSwiglu:
       return smq_launch<FMT, kSwiglu>(gate_up, inter, counts, offsets, num_experts, row_cap,
-                                      clamp_limit, hq, hs, rnd, stream);
+                                      clamp_limit, hq, hs, rnd, seg_cap, stream);
     case kSwigluClamp:
       return smq_launch<FMT, kSwigluClamp>(gate_up, inter, counts, offsets, num_experts,
-                                           row_cap, clamp_limit, hq, hs, rnd, stream);
+                                           row_cap, clamp_limit, hq, hs, rnd, seg_cap, stream);
     default:
       return smq_launch<FMT, kSwigluClampAfterSilu>(gate_up, inter, counts, offsets,
                                                     num_experts, row_cap, clamp_limit, hq, hs,
-                                                    rnd, stream);
+                                                    rnd, seg_cap, stream);
   }
 }
 
@@ -172,18 +174,18 @@ hipError_t launch_act_quant(const uint16_t* x, int t_cap, const int32_t* t_live_
 hipError_t launch_silu_mul_quant(const uint16_t* gate_up, int inter, const int32_t* counts,
                                  const int32_t* offsets, int num_experts, int row_cap, int act,
                                  float clamp_limit, int fmt, int rounding, uint8_t* hq, void* hs,
-                                 hipStream_t stream) {
+                                 int seg_cap, hipStream_t stream) {
   const int rnd = rounding;
   switch (fmt) {
     case kFp32:
       return smq_fmt<kFp32>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                            clamp_limit, hq, hs, rnd, stream);
+                            clamp_limit, hq, hs, rnd, seg_cap, stream);
     case kFp32Pow2:
       return smq_fmt<kFp32Pow2>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                                clamp_limit, hq, hs, rnd, stream);
+                                clamp_limit, hq, hs, rnd, seg_cap, stream);
     default:
       return smq_fmt<kUe8m0>(gate_up, inter, counts, offsets, num_experts, row_cap, act,
-                             clamp_limit, hq, hs, rnd, stream);
+                             clamp_limit, hq, hs, rnd, seg_cap, stream);
   }
 }
 

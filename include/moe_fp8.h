@@ -110,8 +110,13 @@ int32_t moe_min_row_cap(int32_t t_cap, int32_t topk, int32_t num_experts, int32_
  * sorted token ids; review comment on expert parallelism: ids outside the
  * local range are dropped).
  *
- *   topk_ids      device int32 [t_cap, topk]; ids outside [0, num_experts)
- *                 are dropped (their pair maps to row -1)
+ *   topk_ids      device int32 [t_cap, topk]; local ids id - expert_start
+ *                 outside [0, num_experts) are dropped (their pair maps to
+ *                 row -1)
+ *   expert_start  the first expert this caller owns (expert parallelism:
+ *                 TensorRT-LLM PR #21250, For MoE owners and review comment:
+ *                 pairs of other ranks' experts are dropped, not clamped);
+ *                 0 without expert parallelism
  *   t_live_dev    device int32 scalar or NULL (see conventions)
  *   align_rows    >= 1; each expert's row count is rounded up to a multiple
  *   row_cap       rows available; must be >= moe_min_row_cap(...)
@@ -126,9 +131,31 @@ int32_t moe_min_row_cap(int32_t t_cap, int32_t topk, int32_t num_experts, int32_
  *                            dropped; entries of tokens >= t_live untouched
  * Errors: INVALID_ARG (sizes, null pointers), CAPACITY (row_cap too small). */
 moe_status moe_align(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
-                     int32_t topk, int32_t num_experts, int32_t align_rows, int32_t row_cap,
-                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* row_to_pair,
-                     int32_t* pair_to_row, void* stream);
+                     int32_t topk, int32_t num_experts, int32_t expert_start, int32_t align_rows,
+                     int32_t row_cap, int32_t* expert_counts, int32_t* expert_offsets,
+                     int32_t* row_to_pair, int32_t* pair_to_row, void* stream);
+
+/* Routing into the batched masked-M layout (vLLM PR #65794, Details, batched
+ * experts: a fixed capacity per expert with a per-expert valid count, the
+ * layout persistent_masked_m_silu_mul_quant consumes): expert e owns rows
+ * [e*expert_cap, (e+1)*expert_cap), the first masked_m[e] of which hold its
+ * pairs in ascending pair order. Pairs ranked at or past the capacity are
+ * dropped (pair_to_row -1) and counted: the pages leave the overflow open,
+ * and this library's reading is to drop and report it.
+ *
+ *   topk_ids, t_cap, t_live_dev, topk, expert_start  as moe_align
+ *   expert_cap    rows per expert, >= 1; num_experts * expert_cap <= 2^30
+ * Outputs (device int32):
+ *   masked_m      [num_experts]  min(pairs of expert e, expert_cap)
+ *   row_to_pair   [num_experts * expert_cap]  pair of each live row; rows
+ *                 past masked_m[e] of each expert untouched
+ *   pair_to_row   [t_cap*topk]  as moe_align (-1 also for overflow)
+ *   overflow      one int32 or NULL: the number of pairs dropped for capacity
+ * Errors: INVALID_ARG, UNSUPPORTED (num_experts above 1024). */
+moe_status moe_align_batched(const int32_t* topk_ids, int32_t t_cap, const int32_t* t_live_dev,
+                             int32_t topk, int32_t num_experts, int32_t expert_start,
+                             int32_t expert_cap, int32_t* masked_m, int32_t* row_to_pair,
+                             int32_t* pair_to_row, int32_t* overflow, void* stream);
 
 /* Per-1x128 FP8 E4M3 activation quantization of the live tokens (vLLM PR
  * #65794, Details: scale = max(amax / 448, 1 / (448 * 512)), then x / scale,
@@ -180,6 +207,18 @@ moe_status moe_grouped_gemm_fp8(const uint8_t* a, const void* a_scales, moe_scal
                                 int32_t n, int32_t k, uint16_t* c, int32_t* tiles_visited,
                                 void* stream);
 
+/* moe_grouped_gemm_fp8 on the batched masked-M layout (see moe_align_batched;
+ * vLLM PR #65794, Details, batched experts): expert e's live rows are
+ * [e*expert_cap, e*expert_cap + min(masked_m[e], expert_cap)), and C is
+ * [num_experts * expert_cap, n]; rows past the mask are untouched. Other
+ * arguments and errors as moe_grouped_gemm_fp8, whose kernels it runs. */
+moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                       int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                       const uint8_t* w, const float* w_scales,
+                                       const int32_t* masked_m, int32_t num_experts,
+                                       int32_t expert_cap, int32_t n, int32_t k, uint16_t* c,
+                                       int32_t* tiles_visited, void* stream);
+
 /* Row-tile heights of the two GEMM kernels, for interpreting tiles_visited:
  * experts with at most MOE_GEMM_STREAM_MAX_ROWS live rows are computed by
  * the weight-streaming kernel in row tiles of MOE_GEMM_STREAM_TILE_M, larger
@@ -210,6 +249,17 @@ moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               float clamp_limit, moe_scale_fmt fmt, moe_rounding rounding,
                               uint8_t* hq, void* hs, void* stream);
 
+/* moe_silu_mul_quant on the batched masked-M layout (vLLM PR #65794,
+ * Details: persistent_masked_m_silu_mul_quant): gate_up is
+ * [num_experts * expert_cap, 2*inter], hq [num_experts * expert_cap, inter],
+ * hs [inter/128][num_experts * expert_cap]; only the first masked_m[e] rows
+ * of each expert are read and written. Errors as moe_silu_mul_quant. */
+moe_status moe_silu_mul_quant_masked(const uint16_t* gate_up, int32_t inter,
+                                     const int32_t* masked_m, int32_t num_experts,
+                                     int32_t expert_cap, moe_act act, float clamp_limit,
+                                     moe_scale_fmt fmt, moe_rounding rounding, uint8_t* hq,
+                                     void* hs, void* stream);
+
 /* Top-k weighted unpermute/sum (TensorRT-LLM PR #21250, rounding-fix commit:
  * the routing weights scale the BF16 expert outputs in fp32 in the top-k sum,
  * not the FC2 accumulators). For each live token t:
@@ -239,6 +289,11 @@ typedef struct {
   moe_act act;
   float clamp_limit;
   moe_rounding rounding; /* quantizer convention of both activation quantizations */
+  int32_t expert_start;  /* first expert owned (local id = id - expert_start), see moe_align */
+  int32_t expert_cap;    /* 0: the aligned layout; > 0: the batched masked-M layout with this
+                            many rows per expert (row_cap is then 0 or num_experts *
+                            expert_cap, align_rows is unused, and the decode path's
+                            fused schedules do not apply) */
 } moe_problem;
 
 typedef struct {
@@ -276,6 +331,7 @@ typedef struct {
                             and workgroup b wrote NaN (0x7FC0) to its output columns
                             16*(b + grid*j) .. +15 of the live tokens instead of computing
                             them. Other paths do not write it. */
+  size_t overflow;       /* int32: pairs dropped for capacity (batched layout only) */
   size_t total;          /* bytes required */
   int32_t row_cap;       /* effective row capacity */
 } moe_workspace_layout;

@@ -62,8 +62,8 @@ def test_align_validation(lib):
 
     def call(**kw):
         a = dict(args, **kw)
-        return f(a["ids"], a["t_cap"], a["live"], a["k"], a["e"], a["a"], a["rc"], FAKE, FAKE, FAKE,
-                 FAKE, NULL)
+        return f(a["ids"], a["t_cap"], a["live"], a["k"], a["e"], 0, a["a"], a["rc"], FAKE, FAKE,
+                 FAKE, FAKE, NULL)
     assert call(k=0) == INVALID
     assert call(k=65) == INVALID
     assert call(a=0) == INVALID
@@ -72,7 +72,7 @@ def test_align_validation(lib):
     assert call(e=1025) == UNSUPPORTED
     assert call(rc=511) == CAPACITY
     assert call(ids=NULL) == INVALID
-    assert f(FAKE, 4, NULL, 8, 288, 16, 512, NULL, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert f(FAKE, 4, NULL, 8, 288, 0, 16, 512, NULL, FAKE, FAKE, FAKE, NULL) == INVALID
 
 
 def test_act_quant_validation(lib):
@@ -129,7 +129,8 @@ def test_combine_validation(lib):
 
 def _problem(**kw):
     d = dict(num_experts=32, hidden=7168, inter=2048, topk=8, t_cap=4096, align_rows=16,
-             row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"), rounding=0)
+             row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"), rounding=0, expert_start=0,
+             expert_cap=0)
     d.update(kw)
     return B._Problem(**d)
 
@@ -246,3 +247,37 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
     assert lib.moe_forward_noalloc(ctypes.byref(_problem(hidden=100)), ctypes.byref(t), NULL) == INVALID
     assert lib.moe_forward_noalloc(ctypes.byref(_problem(t_cap=4)), None, NULL) == INVALID
     assert moe.NOALLOC_SCRATCH_BYTES == _header_macros("MOE_NOALLOC_")["MOE_NOALLOC_SCRATCH_BYTES"]
+
+
+def test_batched_layout_validation(lib):
+    lay = B._Layout()
+    p = _problem(t_cap=512, expert_cap=64)
+    assert lib.moe_workspace_plan(ctypes.byref(p), ctypes.byref(lay)) == OK
+    assert lay.row_cap == 32 * 64
+    assert lay.act == lay.status  # no decode path on the batched layout
+    assert lay.overflow % 256 == 0 and lay.overflow + 4 <= lay.total
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(t_cap=512, expert_cap=64, row_cap=2047)),
+                                  ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(t_cap=512, expert_cap=-1)),
+                                  ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(expert_cap=1 << 26)), ctypes.byref(lay)) == INVALID
+    # a decode-sized batched problem takes no decode path either
+    pd = _problem(num_experts=288, hidden=4096, inter=512, t_cap=4, expert_cap=4)
+    assert lib.moe_workspace_plan(ctypes.byref(pd), ctypes.byref(lay)) == OK and lay.act == lay.status
+    fa = lib.moe_align_batched
+    assert fa(FAKE, 4, NULL, 8, 32, 0, 0, FAKE, FAKE, FAKE, NULL, NULL) == INVALID   # cap 0
+    assert fa(FAKE, 4, NULL, 8, 2000, 0, 4, FAKE, FAKE, FAKE, NULL, NULL) == UNSUPPORTED
+    assert fa(FAKE, 4, NULL, 8, 32, 0, 4, NULL, FAKE, FAKE, NULL, NULL) == INVALID
+    fg = lib.moe_grouped_gemm_fp8_masked
+    assert fg(FAKE, FAKE, 0, 64, NULL, 1, FAKE, FAKE, FAKE, 4, 0, 256, 256, FAKE, NULL, NULL) == INVALID
+    assert fg(FAKE, FAKE, 0, 64, NULL, 1, FAKE, FAKE, NULL, 4, 16, 256, 256, FAKE, NULL, NULL) == INVALID
+    assert fg(FAKE, FAKE, 0, 64, NULL, 1, FAKE, FAKE, FAKE, 4, 16, 200, 256, FAKE, NULL, NULL) == INVALID
+    fs = lib.moe_silu_mul_quant_masked
+    assert fs(FAKE, 256, FAKE, 4, 0, 0, 7.0, 0, 0, FAKE, FAKE, NULL) == INVALID
+    assert fs(FAKE, 256, FAKE, 2000, 4, 0, 7.0, 0, 0, FAKE, FAKE, NULL) == UNSUPPORTED
+    assert fs(FAKE, 256, NULL, 4, 4, 0, 7.0, 0, 0, FAKE, FAKE, NULL) == INVALID
+
+
+def test_silu_mul_quant_rejects_more_experts_than_its_table(lib):
+    f = lib.moe_silu_mul_quant
+    assert f(FAKE, 256, FAKE, FAKE, 1025, 64, 0, 7.0, 0, 0, FAKE, FAKE, NULL) == UNSUPPORTED
