@@ -272,7 +272,7 @@ def _gemm_case(seed, e, n, k, counts, exact, fmt, gather_k=0):
     row_cap = int(offsets[-1]) + 32
     kb = k // 128
     if exact:
-        w = g.choice(EXACT_CODES, (e, n, k))
+        w = EXACT_CODES[g.integers(0, len(EXACT_CODES), (e, n, k), dtype=np.uint8)]
         ws = g.choice(np.array([0.5, 1.0, 2.0], np.float32), (e, n // 128, kb))
     else:
         w = np.empty((e, n, k), np.uint8)
@@ -348,7 +348,14 @@ GEMM_SHAPES = [
     (10, 8, 2048, 256, [300] * 8, 0),               # 128-wide weight tiles
     (11, 12, 1024, 512, [400] * 12, 8),             # 128-wide, gathered
     (12, 8, 8320, 256, [300] * 7 + [211], 8),       # 256-wide, output staged in LDS; N % 256 = 128
+    (13, 8, 8192, 2048, [300] * 7 + [271], 0),      # 256-wide at K = 2048 (the full layer's FC2)
 ]
+
+# The 256-wide staged-output kernel at the full layer's FC1 depth, K = 7168
+# (56 scale blocks of accumulator rescaling), gathered: 16 experts of about
+# 300 rows on N = 4096 give 35 x 16 tiles, past the 2 x CU bound of the
+# narrow kernels.
+LONG_K_SHAPE = (14, 16, 4096, 7168, [300] * 15 + [270], 8)
 
 
 @pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
@@ -378,6 +385,24 @@ def test_gemm_tolerance(fmt, seed, e, n, k, counts, gk):
     assert_bf16_close(got[:total][live], ref[live], "gemm")
     assert np.all(got[:total][~live] == POISON_BF16)
     assert np.all(got[total:] == POISON_BF16)
+
+
+@pytest.mark.parametrize("fmt,exact", [("fp32", True), ("ue8m0", True), ("fp32", False),
+                                       ("pow2", False)])
+def test_gemm_wide_tiles_at_long_k(fmt, exact):
+    seed, e, n, k, counts, gk = LONG_K_SHAPE
+    say(f"gemm 256-wide K={k} fmt={fmt} exact={exact}")
+    c = _gemm_case(seed + (0 if exact else 100), e, n, k, counts, exact, fmt, gk)
+    got, tiles = _run_gemm(c)
+    ref, live = _ref_gemm(c)
+    total = int(c["offsets"][-1])
+    if exact:
+        assert np.array_equal(got[:total][live], ref[live])
+    else:
+        assert_bf16_close(got[:total][live], ref[live], "gemm K=7168")
+    assert np.all(got[:total][~live] == POISON_BF16)
+    assert np.all(got[total:] == POISON_BF16)
+    assert tiles == _expected_tiles(c["counts"], n)
 
 
 def test_gemm_empty_experts_write_nothing():
