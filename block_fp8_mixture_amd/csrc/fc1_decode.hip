@@ -215,6 +215,12 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   __syncthreads();
   const int n_live = __builtin_amdgcn_readfirstlane(s_nlive);
   const int total_rows = __builtin_amdgcn_readfirstlane(s_total);
+  // Lane j's copies of entry j's tile prefix and expert (j <= n_live; the
+  // prefix past the last entry is tp_end), so that decoding a task is one
+  // ballot and a few lane reads instead of a search through LDS.
+  const int tp_lane = s_tp[min(lane, n_live)];
+  const int tp_end = __builtin_amdgcn_readfirstlane(s_tp[n_live]);
+  const int e_lane = lane < n_live ? s_e[lane] : 0;
   // The first entry whose expert is >= e (n_live if none).
   auto entry_ge = [&](int e) {
     int lo = 0, hi = n_live;
@@ -225,8 +231,11 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     return lo;
   };
 
-  // ---- the alignment to the workspace (workgroup 0), as moe_align writes it
-  if (blockIdx.x == 0) {
+  // ---- the alignment to the workspace (workgroup 0), as moe_align writes
+  // it; nothing in this launch reads it, so it is written once workgroup 0
+  // is off the critical path (after its FC1 stream, or after releasing the
+  // grid barrier)
+  auto write_alignment = [&]() {
     for (int e = tid; e <= E; e += kF1Threads) {
       const int i = entry_ge(e);
       if (e < E) p.counts[e] = i < n_live && s_e[i] == e ? s_cnt[i] : 0;
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
       p.row_to_pair[r] = j < s_cnt[lo] ? s_cpair[s_c0[lo] + j] : -1;
     }
     if (tid < min(t_live * TK, PQ)) p.pair_to_row[tid] = s_prow[tid];
-  }
+  };
 
   // ---- per-wave task stream. A workgroup takes a contiguous block of the
   // tasks (neighbouring row blocks of an expert stay on one CU, which streams
@@ -254,17 +263,19 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const int n_rb = I / 8;  // 16-row blocks (8 gate + 8 up rows)
   const int n_tasks = s_tp[n_live] * n_rb;
   const int G1 = gridDim.x;
-  const int t_lo = static_cast<int>(static_cast<int64_t>(blockIdx.x) * n_tasks / G1);
-  const int t_hi = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * n_tasks / G1);
+  // (blockIdx.x + 1) * n_tasks < 2^32: n_tasks <= 64 tiles x I / 8.
+  const int t_lo = static_cast<int>(blockIdx.x * static_cast<uint32_t>(n_tasks) / static_cast<uint32_t>(G1));
+  const int t_hi = static_cast<int>((blockIdx.x + 1) * static_cast<uint32_t>(n_tasks) / static_cast<uint32_t>(G1));
   const int wg_max = (n_tasks + G1 - 1) / G1;  // tasks of the fullest workgroup
-  int S = 1;
-  while (S < kF1Waves && wg_max * (2 * S) <= kF1Waves && KB % (2 * S) == 0) S *= 2;
-  S = __builtin_amdgcn_readfirstlane(S);
-  const int NG = kF1Waves / S;  // groups of S waves in a workgroup
-  const int gl = wave / S;      // this wave's group
-  const int kbs = KB / S;       // K blocks of a share
-  const int kb_lo = (wave % S) * kbs, kb_hi = kb_lo + kbs;
-  const int my_tasks = gl < t_hi - t_lo ? (t_hi - t_lo - 1 - gl) / NG + 1 : 0;
+  int lgS = 0;  // S = 2^lgS
+  while (lgS < 3 && (wg_max << (lgS + 1)) <= kF1Waves && (KB & ((2 << lgS) - 1)) == 0) ++lgS;
+  lgS = __builtin_amdgcn_readfirstlane(lgS);
+  const int S = 1 << lgS;
+  const int NG = kF1Waves >> lgS;  // groups of S waves in a workgroup
+  const int gl = wave >> lgS;      // this wave's group
+  const int kbs = KB >> lgS;       // K blocks of a share
+  const int kb_lo = (wave & (S - 1)) * kbs, kb_hi = kb_lo + kbs;
+  const int my_tasks = gl < t_hi - t_lo ? ((t_hi - t_lo - 1 - gl) >> (3 - lgS)) + 1 : 0;
   const int total = my_tasks * kbs;  // stages of this wave
   uint8_t* ring = s_ring + wave * (DEPTH * kF1Stage);
   const int grow = lane >> 3;
@@ -273,19 +284,26 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   struct Task {
     int ent, rb, mt;
   };
+  // Quotient of non-negative integers a < 2^24 and b > 0 with a / b < 2^16:
+  // the float estimate is off by less than one.
+  auto small_div = [](int a, int b) {
+    int q = static_cast<int>(static_cast<float>(a) * __builtin_amdgcn_rcpf(static_cast<float>(b)));
+    if (q * b > a) --q;
+    if ((q + 1) * b <= a) ++q;
+    return q;
+  };
   auto decode_task = [&](int t) {
-    const int key = t / n_rb;
-    int lo = 0, hi = n_live - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
-    }
+    const int key = small_div(t, n_rb);
+    // Entries whose tile prefix is <= key: a prefix of the entries (the
+    // prefixes do not decrease), entry 0's is 0.
     Task k;
-    k.ent = __builtin_amdgcn_readfirstlane(lo);
-    const int tiles = __builtin_amdgcn_readfirstlane(s_tp[lo + 1] - s_tp[lo]);
-    const int local = t - __builtin_amdgcn_readfirstlane(s_tp[lo]) * n_rb;
-    k.rb = local / tiles;
-    k.mt = local % tiles;
+    k.ent = static_cast<int>(__popcll(__ballot(lane < n_live && tp_lane <= key))) - 1;
+    const int base = __builtin_amdgcn_readlane(tp_lane, k.ent);
+    const int next = k.ent + 1 < 64 ? __builtin_amdgcn_readlane(tp_lane, (k.ent + 1) & 63) : tp_end;
+    const int tiles = next - base;
+    const int local = t - base * n_rb;
+    k.rb = small_div(local, tiles);
+    k.mt = local - k.rb * tiles;
     return k;
   };
   // Issue side: stage pointers of the current task. Stand-ins (valid
@@ -297,7 +315,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const uint8_t* i_s = reinterpret_cast<const uint8_t*>(p.w_scales);
   auto i_set = [&]() {
     const Task k = decode_task(i_task);
-    const int e = __builtin_amdgcn_readfirstlane(s_e[k.ent]);
+    const int e = __builtin_amdgcn_readlane(e_lane, k.ent);
     const int jg = k.rb * 8;  // first gate column
     const uint8_t* we = p.w + static_cast<int64_t>(e) * N * H;
     i_w0 = we + static_cast<int64_t>(jg + grow) * H + chunk_lo;
@@ -446,6 +464,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     slot = slot == DEPTH - 1 ? 0 : slot + 1;
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // stand-in stages of a wave with few stages
+  if (!FUSED && blockIdx.x == 0) write_alignment();
   if constexpr (FUSED) {
     // ---- 4. FC2 and the top-k combine in the same launch (fc2_decode.h). A
     // workgroup owns 16 output columns of every live expert (column blocks
@@ -502,6 +521,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
       if (!flag_wait(&g_dl_release, epoch, limit, kDlEpochMask) || (flag_load(&g_dl_release) & kDlFailBit))
         s_failed = 1;
     }
+    if (blockIdx.x == 0) write_alignment();
     for (int x = tid; x < PQ * 16; x += kF1Threads) s_slot[x] = 0.0f;  // the K-split partials are done
     lds_barrier();
     const bool failed = s_failed != 0;  // uniform
