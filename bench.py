@@ -59,6 +59,13 @@ MALL_BYTES = 256 << 20       # MI355X Infinity Cache
 CAL_BYTES = 256 << 20        # calibration copy for the HBM traffic counters
 
 
+# SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD's matrix core
+# (256 CUs x 4 SIMDs); GRBM_GUI_ACTIVE sums the active cycles of the 8 XCDs.
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT",
+                 "GRBM_GUI_ACTIVE")
+N_SIMDS, N_XCDS = 1024, 8
+
+
 def traffic_file(workload_key):
     """profiles/ file of the dominant kernel's traffic summary of a workload,
     e.g. roofline_kernel_decode_t4_fp32_traffic.json for decode:T4:fp32."""
@@ -87,6 +94,10 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this command (FETCH_SIZE, then "
                          "WRITE_SIZE) into the FC1 traffic file under profiles/, then exit")
+    ap.add_argument("--counters-from", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of this command with "
+                         f"{' '.join(MFMA_COUNTERS)} into the grouped GEMMs' MFMA utilisation "
+                         "file under profiles/, then exit")
     return ap.parse_args()
 
 
@@ -230,6 +241,60 @@ def traffic_from(args, fetch_dir, write_dir):
     print(json.dumps(res))
 
 
+def counters_from(args, pmc_dir):
+    """MFMA utilisation of the grouped GEMMs from one rocprofv3 --pmc run with
+    MFMA_COUNTERS: per kernel, the medians over its dispatches of the matrix
+    cores' busy fraction (busy cycles per SIMD over active cycles), the clock
+    those cycles imply, FP8 MFMA ops and LDS bank-conflict cycles."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {pmc_dir}")
+    per = {}
+    for row in csv.DictReader(open(files[0])):
+        key = int(row["Dispatch_Id"])
+        d = per.setdefault(key, {"name": row["Kernel_Name"],
+                                 "us": (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3})
+        d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    fmt = args.fmt or __import__("synth").get(args.config).scale_fmts[0]
+    t_cap, t_live = DEFAULT_TOKENS[args.config]
+    if args.tokens is not None:
+        t_cap = t_live = args.tokens
+    kernels = {}
+    for d in per.values():
+        n = d["name"]
+        if "gemm_tiled_kernel" not in n and "gemm_stream_kernel" not in n and "fc1_decode_kernel" not in n:
+            continue
+        cyc = d.get("GRBM_GUI_ACTIVE", 0.0) / N_XCDS
+        if cyc <= 0 or d["us"] <= 0:
+            continue
+        m = re.search(r"(\w+_kernel<[^()]*?>)\(", n)
+        k = kernels.setdefault(m.group(1) if m else n, {"dispatches": 0, "us": [], "busy": [], "ghz": [],
+                                                   "mops_f8": [], "lds_bank_conflict_cycles": []})
+        k["dispatches"] += 1
+        k["us"].append(d["us"])
+        k["busy"].append(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / N_SIMDS / cyc)
+        k["ghz"].append(cyc / d["us"] / 1e3)
+        k["mops_f8"].append(d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0))
+        k["lds_bank_conflict_cycles"].append(d.get("SQ_LDS_BANK_CONFLICT", 0.0))
+    out = {}
+    for n, k in kernels.items():
+        med = {m: statistics.median(k[m]) for m in ("us", "busy", "ghz", "mops_f8", "lds_bank_conflict_cycles")}
+        out[n] = {"dispatches": k["dispatches"], "median_us": round(med["us"], 2),
+                  "mfma_busy": round(med["busy"], 4), "clock_ghz": round(med["ghz"], 3),
+                  "busy_x_clock_over_peak_clock": round(med["busy"] * med["ghz"] / 2.4, 4),
+                  "mfma_mops_f8": med["mops_f8"], "lds_bank_conflict_cycles": med["lds_bank_conflict_cycles"]}
+    res = {"workload": f"{args.config}:T{t_live}:{fmt}", "gemm_source_sha256_16": kernel_source_hash(),
+           "counters": list(MFMA_COUNTERS), "kernels": out}
+    path = os.path.join(ROOT, "profiles", "mfma_counters_" + res["workload"].replace(":", "_").lower() + ".json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res))
+
+
 def cpu_baseline(cfg, x, ids, w, t_live, fmt, act, lim, weights):
     """The oracle on a bounded sample of the workload, on the host's cores.
 
@@ -348,6 +413,8 @@ def pct(v, q):
 
 # Entries of the per-config table: (workload, token capacity, live tokens,
 # activation scale format, activation, clamp limit).
+# (workload, token capacity, live tokens, activation scales, activation,
+# clamp limit[, rows per expert of the batched masked-M layout])
 PER_CONFIG = [
     ("tiny", 8, 8, "fp32", "swiglu", float("inf")),
     ("decode", 1, 1, "fp32", "swiglu", float("inf")),
@@ -358,13 +425,22 @@ PER_CONFIG = [
     ("full", 4096, 4096, "fp32", "swiglu", float("inf")),
     ("full", 4096, 4096, "ue8m0", "swiglu", float("inf")),
 ] + [("sweep", m, m, f, "swiglu", float("inf"))
-     for m in (1, 8, 64, 256, 1024, 4096) for f in ("fp32", "pow2")]
+     for m in (1, 8, 64, 256, 1024, 4096) for f in ("fp32", "pow2")] + [
+    # the batched masked-M layout ([E, cap] rows, masked_m live; vLLM PR
+    # #65794, Details, batched experts): a low-latency dispatch's capacity
+    # and the fully occupied layer with room for 1.5x the mean expert load
+    ("padded", 512, 16, "fp32", "swiglu", float("inf"), 64),
+    ("full", 4096, 4096, "fp32", "swiglu", float("inf"), 1536),
+]
 
 
 def main():
     args = parse()
     if args.traffic_from:
         traffic_from(args, *args.traffic_from)
+        return
+    if args.counters_from:
+        counters_from(args, args.counters_from)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
@@ -401,12 +477,13 @@ def main():
             weights_cache[name] = (host, [up(a) for a in (host[0][0], host[0][1], host[1][0], host[1][1])])
         return weights_cache[name]
 
-    def layer_inputs(name, t_cap, t_live, fmt, act, lim):
+    def layer_inputs(name, t_cap, t_live, fmt, act, lim, expert_cap=0):
         cfg_l = synth.get(name)
         x_l, ids_l, w_l = synth.make_workload(cfg_l, t_cap)
         _, d_w_l = weights_for(name)
         E_l, H_l, I_l, K_l = cfg_l.num_experts, cfg_l.hidden, cfg_l.inter, cfg_l.topk
-        lay_l = moe.moe_workspace_plan(E_l, H_l, I_l, K_l, t_cap, cfg_l.align_rows, 0, fmt, act, lim)
+        lay_l = moe.moe_workspace_plan(E_l, H_l, I_l, K_l, t_cap, cfg_l.align_rows, 0, fmt, act, lim,
+                                       expert_cap=expert_cap)
         ws_l = torch.zeros(lay_l["total"], dtype=torch.uint8, device=dev)
         out_l = torch.zeros((t_cap, H_l), dtype=torch.int16, device=dev)
         dx_l, dids_l, dw_l = up(x_l), up(ids_l), up(w_l)
@@ -414,7 +491,7 @@ def main():
 
         def fwd():
             moe.moe_forward(dx_l, dids_l, dw_l, *d_w_l, fmt, act, lim, cfg_l.align_rows, 0,
-                            t_live=dlive_l, out=out_l, workspace=ws_l)
+                            t_live=dlive_l, out=out_l, workspace=ws_l, expert_cap=expert_cap)
         return cfg_l, (x_l, ids_l, w_l), fwd, lay_l, ws_l, (dx_l, dids_l, dw_l, dlive_l), out_l
 
     def rates(cfg_l, ids_l, t_live, span_us):
@@ -578,15 +655,21 @@ def main():
     # ---- every workload and variant, the same protocol with fewer replays
     if not args.no_per_config:
         table = []
-        for name, tc, tl, f, ac, li in PER_CONFIG:
-            cfg_l, (xl, idsl, wl), fwd_l, _, ws_l, _, out_l = layer_inputs(name, tc, tl, f, ac, li)
+        for name, tc, tl, f, ac, li, *cap in PER_CONFIG:
+            cap = cap[0] if cap else 0
+            cfg_l, (xl, idsl, wl), fwd_l, lay_l, ws_l, _, out_l = layer_inputs(name, tc, tl, f, ac, li, cap)
             spans, evs, _ = time_layer(torch, fwd_l, args.config_steps, 3, flush_caches)
             m = statistics.median(spans)
             ent = {"workload": name, "tokens": tl, "token_capacity": tc, "act_scale_fmt": f,
                    "activation": ac, "span_us": round(m, 2), "p10_us": round(pct(spans, 0.1), 2),
                    "p90_us": round(pct(spans, 0.9), 2), "events_us": round(statistics.median(evs), 2),
-                   "path": ("one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter)
+                   "path": ("batched masked-M" if cap else
+                            "one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter)
                             else "general")}
+            if cap:
+                ent["expert_cap"] = cap
+                ovf = int(ws_l[lay_l["overflow"]:lay_l["overflow"] + 4].view(torch.int32).item())
+                ent["pairs_dropped"] = ovf
             ent.update(rates(cfg_l, idsl, tl, m))
             # the bars: HBM at <= 32 tokens, FP8 MFMA at the fully occupied
             # layer; the tiny layer is launch-bound and reported only
@@ -596,7 +679,7 @@ def main():
             if c:
                 ent["pages_context_us"] = c
             table.append(ent)
-            print(f"# per-config {name} T={tl}/{tc} {f} {ac}: {m:.1f} us, "
+            print(f"# per-config {name} T={tl}/{tc} {f} {ac}{f' cap {cap}' if cap else ''}: {m:.1f} us, "
                   f"{ent['frac_fp8_peak']:.3f} FP8, {ent['frac_hbm_peak']:.3f} HBM",
                   file=sys.stderr, flush=True)
             del fwd_l, ws_l, out_l
