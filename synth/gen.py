@@ -61,14 +61,15 @@ def make_routing(cfg, t_cap, variant=0):
 def quantize_weight_blocks(w):
     """Checkpoint-style 128x128 block FP8 weights from float32 [N, K].
 
-    Per block: scale = amax / 448 (float32, not a power of two), codes =
-    torch's float8_e4m3fn cast of w / scale. Returns (codes uint8 [N, K],
-    scales float32 [N/128, K/128]).
+    Per block: scale = max(amax / 448, 1 / (448 * 512)) in float32, the
+    activation rule's scale and floor (vLLM PR #65794, Details) applied to a
+    128x128 block (not a power of two); codes = torch's float8_e4m3fn cast of
+    w / scale. Returns (codes uint8 [N, K], scales float32 [N/128, K/128]).
     """
     n, k = w.shape
     blocks = w.reshape(n // BLOCK, BLOCK, k // BLOCK, BLOCK)
     amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)
-    scale = np.maximum(amax / np.float32(448.0), np.float32(2.0 ** -30))
+    scale = np.maximum(amax / np.float32(448.0), np.float32(1.0) / np.float32(229376.0))
     ratio = blocks / scale[:, None, :, None]
     codes = torch.from_numpy(np.ascontiguousarray(ratio.reshape(n, k))).to(
         torch.float8_e4m3fn).view(torch.uint8).numpy()
