@@ -15,6 +15,8 @@ Sources (three web pages, cited by title and section):
   Purpose; SM100 on B200; SM90 on H200.
 * vLLM PR #65794 (per-layer activation-scale format, fused SiLU+quant) --
   Overview; Claims; Details (fused-kernel and sorted-A bullets).
+* vLLM PR #59128's description names FP4 weights (prefix sums on SM10.x);
+  their format is read as OCP MXFP4 (``fp_formats``).
 * TensorRT-LLM PR #21250 "Triton FP8-activation MoE for decode-sized
   batches on Hopper" -- description; rounding-fix commit message (the
   ``reciprocal`` rounding convention); review comments on expert-parallel
@@ -28,17 +30,19 @@ pinned only against their own defining formula plus invariants, because the
 pages name the variants without giving a formula (see ``moe.swiglu``).
 """
 
-from .fp_formats import (E4M3_MAX, bf16_bits_to_f64, bf16_from_f64,
-                         e4m3_decode, e4m3_encode)
+from .fp_formats import (E4M3_MAX, bf16_bits_to_f64, bf16_from_f64, e2m1_decode,
+                         e4m3_decode, e4m3_encode, e8m0_decode, fp4_unpack)
 from .quant import (ROUNDINGS, SCALE_FMTS, group_scales, quantize_groups,
                     reciprocal_multiplier, scales_to_f64)
 from .align import align, align_batched
-from .moe import (ACTS, combine, forward, grouped_gemm, silu_mul_quant,
-                  swiglu, token_forward, unquantized_reference)
+from .moe import (ACTS, MX_BLOCK, WEIGHT_FMTS, combine, forward, gemm_rows_mxfp4,
+                  grouped_gemm, mxfp4_dequant, silu_mul_quant, swiglu, token_forward,
+                  unquantized_reference)
 
 __all__ = [
-    "E4M3_MAX", "bf16_bits_to_f64", "bf16_from_f64", "e4m3_decode",
-    "e4m3_encode", "ROUNDINGS", "SCALE_FMTS", "group_scales", "quantize_groups",
+    "E4M3_MAX", "bf16_bits_to_f64", "bf16_from_f64", "e2m1_decode", "e4m3_decode",
+    "e4m3_encode", "e8m0_decode", "fp4_unpack", "MX_BLOCK", "WEIGHT_FMTS", "gemm_rows_mxfp4",
+    "mxfp4_dequant", "ROUNDINGS", "SCALE_FMTS", "group_scales", "quantize_groups",
     "reciprocal_multiplier",
     "scales_to_f64", "align", "align_batched", "ACTS", "combine", "forward", "grouped_gemm",
     "silu_mul_quant", "swiglu", "token_forward", "unquantized_reference",

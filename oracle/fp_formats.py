@@ -1,4 +1,5 @@
-"""Number formats used by the layer: OCP FP8 E4M3 (the "FN" variant) and BF16.
+"""Number formats used by the layer: OCP FP8 E4M3 (the "FN" variant), BF16,
+and the MXFP4 weight format (E2M1 elements with E8M0 block scales).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -11,6 +12,14 @@ saturation or negative zero; the reading taken here is round to nearest with
 ties to the even code, saturation to +-448, and a sign-preserving zero.
 
 BF16 is held as uint16 bit patterns because numpy has no bfloat16 type.
+
+MXFP4: the pages name FP4 weights only (vLLM PR #59128, description: prefix
+sums for FP4 weights on SM10.x) and give no encoding. The reading taken is
+the OCP Microscaling (MX) v1.0 format: E2M1 elements (1 sign bit, 2 exponent
+bits with bias 1, 1 mantissa bit; exponent 0 holds the subnormal m * 0.5;
+magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities or NaN) sharing one
+E8M0 scale (2**(b - 127), byte 255 = NaN) per 32 consecutive elements along
+K. Two elements share a byte, the even-K element in the low nibble.
 """
 
 import numpy as np
@@ -93,3 +102,30 @@ def bf16_from_f64(x):
     f = y.astype(np.float32)  # exact: y is on the BF16 grid (or inf)
     top = (f.view(np.uint32) >> 16).astype(np.uint32)
     return (top | (sign << 15)).astype(np.uint16)
+
+
+def e2m1_decode(nibbles):
+    """Decode E2M1 4-bit codes (0..15) to float64, straight from the field layout."""
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = (c >> 3) & 1
+    exp = (c >> 1) & 0x3
+    man = c & 0x1
+    subnormal = man * 0.5
+    normal = (1.0 + man / 2.0) * np.exp2(exp.astype(np.float64) - 1.0)
+    mag = np.where(exp == 0, subnormal, normal)
+    return np.where(sign == 1, -mag, mag)
+
+
+def e8m0_decode(codes):
+    """Decode E8M0 scale bytes to float64: 2**(b - 127); 255 is NaN."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b.astype(np.float64) - 127.0))
+
+
+def fp4_unpack(packed):
+    """[..., K/2] bytes -> [..., K] E2M1 codes; element 2j is the low nibble of byte j."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out

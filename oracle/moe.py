@@ -27,6 +27,15 @@ Stages and the passages they follow:
   quantization, and each K block's scale is the float32 product
   fl32(sa * sw), formed before it multiplies the block's dot product. The
   default ``divide`` is vLLM PR #65794's arithmetic described above.
+* ``weight_fmt="mxfp4"`` -- FP4 weights (vLLM PR #59128, description, names
+  FP4 weights only; the format read as OCP MXFP4, see ``fp_formats``): each
+  weight is e2m1(code) * 2**(b - 127) with one E8M0 byte b per 32 weights
+  along K, so the weight scale sits inside the 128-wide K block instead of
+  multiplying it. Per 128-wide K block the partial dot product of the E4M3
+  activations with the dequantized weights is formed in fp64 (exact when the
+  block's four weight scales lie within 20 binades of each other, as in every
+  test input), multiplied by the activation scale and accumulated; the
+  rounding conventions only differ upstream, in the quantizers.
 * ``combine`` -- the routing weights scale the BF16 expert outputs, in top-k
   order, not the FC2 accumulators (TensorRT-LLM PR #21250, rounding-fix
   commit message). Accumulated in fp64, rounded once to BF16. A token with
@@ -42,10 +51,13 @@ Stages and the passages they follow:
 import numpy as np
 
 from .align import align, align_batched
-from .fp_formats import bf16_bits_to_f64, bf16_from_f64, e4m3_decode
+from .fp_formats import (bf16_bits_to_f64, bf16_from_f64, e2m1_decode, e4m3_decode,
+                         e8m0_decode, fp4_unpack)
 from .quant import GROUP, ROUNDINGS, quantize_groups, scales_to_f64
 
 ACTS = ("swiglu", "swiglu_clamp", "swiglu_clamp_after_silu")
+WEIGHT_FMTS = ("e4m3", "mxfp4")
+MX_BLOCK = 32  # weights per E8M0 scale along K
 
 _DECODE_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
 
@@ -82,18 +94,51 @@ def gemm_rows(a_codes, a_scales, w_codes, w_scales, rounding="divide"):
     return bf16_from_f64(acc)
 
 
+def mxfp4_dequant(w_packed, w_scales):
+    """[N, Kd/2] packed E2M1 codes and [N, Kd/32] E8M0 bytes -> float64 [N, Kd]."""
+    w = e2m1_decode(fp4_unpack(w_packed))
+    s = np.repeat(e8m0_decode(w_scales), MX_BLOCK, axis=1)
+    return w * s
+
+
+def gemm_rows_mxfp4(a_codes, a_scales, w_packed, w_scales):
+    """C[m, n] = bf16( sum_kb sa[kb, m] * sum_{j<128} a * w ) with MXFP4 weights.
+
+    ``a_codes`` [m, Kd] uint8 E4M3, ``a_scales`` [Kd/128, m] float64 (decoded),
+    ``w_packed`` [N, Kd/2] uint8, ``w_scales`` [N, Kd/32] uint8 (E8M0).
+    Returns BF16 bits [m, N].
+    """
+    a = _dec(a_codes)
+    w = mxfp4_dequant(w_packed, w_scales)
+    m, kd = a.shape
+    acc = np.zeros((m, w.shape[0]), dtype=np.float64)
+    for kb in range(kd // GROUP):
+        cols = slice(kb * GROUP, (kb + 1) * GROUP)
+        acc = acc + a_scales[kb][:, None] * (a[:, cols] @ w[:, cols].T)
+    return bf16_from_f64(acc)
+
+
+def _gemm(a_codes, a_scales, w, rounding, weight_fmt):
+    if weight_fmt == "mxfp4":
+        return gemm_rows_mxfp4(a_codes, a_scales, w[0], w[1])
+    if weight_fmt != "e4m3":
+        raise ValueError(weight_fmt)
+    return gemm_rows(a_codes, a_scales, w[0], w[1], rounding)
+
+
 def _expert(weights, e):
     return weights(e) if callable(weights) else (weights[0][e], weights[1][e])
 
 
 def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=None,
-                 rounding="divide"):
+                 rounding="divide", weight_fmt="e4m3"):
     """Grouped FP8 GEMM over the live rows of every expert segment.
 
     ``a_codes``/``a_scales`` are indexed by A row; row r of the output reads
     A row ``row_index[r]`` (or r itself when ``row_index`` is None).
     ``weights`` is ``(w_codes [E, N, Kd], w_scales [E, N/128, Kd/128])`` or a
-    callable e -> (w_codes[e], w_scales[e]).
+    callable e -> (w_codes[e], w_scales[e]); under ``weight_fmt="mxfp4"``
+    ``(w_packed [E, N, Kd/2], w_scales [E, N, Kd/32] E8M0 bytes)``.
     Returns ``(c bits [offsets[E], N], live mask [offsets[E]])``; pad rows are
     zero in ``c`` and False in the mask.
     """
@@ -106,10 +151,9 @@ def grouped_gemm(a_codes, a_scales, fmt, weights, counts, offsets, row_index=Non
         cnt = int(counts[e])
         if cnt == 0:
             continue
-        w_codes, w_scales = _expert(weights, e)
         rows = np.arange(int(offsets[e]), int(offsets[e]) + cnt)
         src = rows if row_index is None else np.asarray(row_index)[rows]
-        out = gemm_rows(a_codes[src], sa_all[:, src], w_codes, w_scales, rounding)
+        out = _gemm(a_codes[src], sa_all[:, src], _expert(weights, e), rounding, weight_fmt)
         if c is None:
             c = np.zeros((total, out.shape[1]), dtype=np.uint16)
         c[rows] = out
@@ -184,7 +228,7 @@ def combine(y_bits, pair_to_row, topk_w, t_live, hidden=None):
 
 def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
             act="swiglu", clamp_limit=np.inf, num_experts=None, rounding="divide",
-            expert_start=0, expert_cap=0):
+            expert_start=0, expert_cap=0, weight_fmt="e4m3"):
     """The whole layer on the aligned, per-expert-contiguous row layout.
 
     ``x_bits`` [t_cap, H] BF16 bits; ``topk_ids``/``topk_w`` [t_cap, K];
@@ -196,12 +240,13 @@ def forward(x_bits, topk_ids, topk_w, w1, w2, t_live, align_rows, fmt,
     if num_experts is None:
         num_experts = w1[0].shape[0]
     return forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live,
-                     align_rows, fmt, act, clamp_limit, rounding, expert_start, expert_cap)
+                     align_rows, fmt, act, clamp_limit, rounding, expert_start, expert_cap,
+                     weight_fmt)
 
 
 def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
               fmt, act="swiglu", clamp_limit=np.inf, rounding="divide", expert_start=0,
-              expert_cap=0):
+              expert_cap=0, weight_fmt="e4m3"):
     """``forward`` with an explicit expert count (for callable weights).
 
     ``expert_start``: the rank's first expert (local id = id - expert_start;
@@ -218,7 +263,8 @@ def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
     x = bf16_bits_to_f64(np.asarray(x_bits)[:t_live]).astype(np.float32)
     xq, xs = quantize_groups(x, fmt, rounding)
     token_of_row = np.where(al["row_to_pair"] >= 0, al["row_to_pair"] // k, 0)
-    c1, live = grouped_gemm(xq, xs, fmt, w1, al["counts"], al["offsets"], token_of_row, rounding)
+    c1, live = grouped_gemm(xq, xs, fmt, w1, al["counts"], al["offsets"], token_of_row, rounding,
+                            weight_fmt)
     hq, hs = silu_mul_quant(c1[live], fmt, act, clamp_limit, rounding)
     total = int(al["offsets"][-1])
     inter = c1.shape[1] // 2
@@ -226,7 +272,8 @@ def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
     hq_full[live] = hq
     hs_full = np.zeros((inter // GROUP, total), dtype=hs.dtype)
     hs_full[:, live] = hs
-    y, _ = grouped_gemm(hq_full, hs_full, fmt, w2, al["counts"], al["offsets"], rounding=rounding)
+    y, _ = grouped_gemm(hq_full, hs_full, fmt, w2, al["counts"], al["offsets"], rounding=rounding,
+                        weight_fmt=weight_fmt)
     out = combine(y, al["pair_to_row"], topk_w, t_live, np.asarray(x_bits).shape[1])
     res = dict(al)
     res.setdefault("overflow", 0)
@@ -236,7 +283,7 @@ def forward_e(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, align_rows,
 
 def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
                   act="swiglu", clamp_limit=np.inf, tokens=None, rounding="divide",
-                  expert_start=0):
+                  expert_start=0, weight_fmt="e4m3"):
     """Dense per-token brute force: no alignment, no row maps, one token at a time.
 
     ``tokens`` selects which tokens to evaluate (default: all t < t_live);
@@ -256,11 +303,9 @@ def token_forward(x_bits, topk_ids, topk_w, w1, w2, num_experts, t_live, fmt,
             e = int(ids[t, kk])
             if not 0 <= e < num_experts:
                 continue
-            w1c, w1s = _expert(w1, e)
-            w2c, w2s = _expert(w2, e)
-            c1 = gemm_rows(xq, scales_to_f64(xs, fmt), w1c, w1s, rounding)
+            c1 = _gemm(xq, scales_to_f64(xs, fmt), _expert(w1, e), rounding, weight_fmt)
             hq, hs = silu_mul_quant(c1, fmt, act, clamp_limit, rounding)
-            y = gemm_rows(hq, scales_to_f64(hs, fmt), w2c, w2s, rounding)
+            y = _gemm(hq, scales_to_f64(hs, fmt), _expert(w2, e), rounding, weight_fmt)
             acc = acc + np.float64(topk_w[t, kk]) * bf16_bits_to_f64(y[0])
         rows.append(bf16_from_f64(acc))
     hidden = np.asarray(x_bits).shape[1]

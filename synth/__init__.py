@@ -3,7 +3,8 @@
 This module is shared by the oracle tests, the GPU tests and the benchmark,
 and holds none of the layer's own arithmetic: it draws activations, router
 logits and weights, turns logits into top-k routing (the router is upstream
-of the layer), and produces FP8 weight checkpoints. Weight quantization here
+of the layer), and produces FP8 weight checkpoints (and MXFP4 ones, drawn
+directly as codes and scale bytes). Weight quantization here
 stands in for the checkpoint producer; it uses torch's float8_e4m3fn cast, a
 library routine, and never the layer's activation quantizer.
 
@@ -23,8 +24,8 @@ Workloads (sizes from the pages' benchmarks and tests):
 """
 
 from .configs import CONFIGS, Workload, get
-from .gen import (ExpertWeights, make_routing, make_tokens, make_workload,
-                  quantize_weight_blocks)
+from .gen import (ExpertWeights, ExpertWeightsMxfp4, make_routing, make_tokens,
+                  make_workload, quantize_weight_blocks)
 
-__all__ = ["CONFIGS", "Workload", "get", "ExpertWeights", "make_routing",
+__all__ = ["CONFIGS", "Workload", "get", "ExpertWeights", "ExpertWeightsMxfp4", "make_routing",
            "make_tokens", "make_workload", "quantize_weight_blocks"]

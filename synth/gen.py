@@ -129,6 +129,55 @@ class ExpertWeights:
         return (w1q, w1s), (w2q, w2s)
 
 
+MX_BLOCK = 32
+MX_SCALE_BYTES = (117, 118, 119, 120, 121)  # E8M0 scales 2**-10 .. 2**-6
+
+
+class ExpertWeightsMxfp4:
+    """Seeded MXFP4 expert weights: FC1 [2I, H] and FC2 [H, I] as packed
+    E2M1 codes [rows, cols/2] (even column in the low nibble) and E8M0 scale
+    bytes [rows, cols/32]. Codes are drawn uniformly from all 16 (both zeros
+    included) and scale bytes uniformly from MX_SCALE_BYTES, which gives an
+    RMS weight of about 0.02 like the FP8 checkpoints; there is nothing to
+    quantize, the draws are the checkpoint."""
+
+    def __init__(self, cfg, variant=0):
+        self.cfg = cfg
+        self.variant = variant
+
+    def _make(self, e, which):
+        c = self.cfg
+        rows, cols = (2 * c.inter, c.hidden) if which == 1 else (c.hidden, c.inter)
+        g = _rng(WEIGHT_SEED + c.index, self.variant, e, 10 + which)
+        packed = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+        scales = np.asarray(MX_SCALE_BYTES, np.uint8)[g.integers(0, len(MX_SCALE_BYTES),
+                                                                   size=(rows, cols // MX_BLOCK))]
+        return packed, scales
+
+    def fc1(self, e):
+        return self._make(e, 1)
+
+    def fc2(self, e):
+        return self._make(e, 2)
+
+    def stacked(self, threads=8):
+        """All experts as ((w1p, w1s), (w2p, w2s)) with a leading E axis."""
+        c = self.cfg
+        e_n = c.num_experts
+        w1p = np.empty((e_n, 2 * c.inter, c.hidden // 2), np.uint8)
+        w1s = np.empty((e_n, 2 * c.inter, c.hidden // MX_BLOCK), np.uint8)
+        w2p = np.empty((e_n, c.hidden, c.inter // 2), np.uint8)
+        w2s = np.empty((e_n, c.hidden, c.inter // MX_BLOCK), np.uint8)
+
+        def one(e):
+            w1p[e], w1s[e] = self._make(e, 1)
+            w2p[e], w2s[e] = self._make(e, 2)
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(e_n)))
+        return (w1p, w1s), (w2p, w2s)
+
+
 def make_workload(cfg, t_cap, variant=0):
     """(x bits, ids, weights) for ``t_cap`` tokens of a workload."""
     x = make_tokens(cfg, t_cap, variant)
