@@ -12,19 +12,21 @@ is missing, importing the binding's functions raises -- there is no fallback.
 """
 
 from ._binding import (ACTS, DECODE_LIMITS, GEMM_TILES, NOALLOC_SCRATCH_BYTES, ROUNDINGS, SCALE_FMTS,
-                       MoeError,
+                       WEIGHT_FMTS, MoeError,
                        decode_layer_applies, library_path, load_library, moe_act_quant,
                        moe_align, moe_align_batched, moe_barrier_spin_limit, moe_barrier_timeouts, moe_fc1_decode,
                        moe_forward, moe_forward_noalloc, moe_grouped_gemm_fp8,
-                       moe_grouped_gemm_fp8_masked, moe_silu_mul_quant_masked, moe_min_row_cap, moe_silu_mul_quant,
+                       moe_grouped_gemm_fp8_masked, moe_grouped_gemm_mxfp4, moe_silu_mul_quant_masked, moe_min_row_cap, moe_silu_mul_quant,
                        moe_status_string, moe_topk_combine, moe_workspace_bytes,
                        moe_workspace_plan)
 
 __all__ = [
-    "ACTS", "DECODE_LIMITS", "GEMM_TILES", "NOALLOC_SCRATCH_BYTES", "ROUNDINGS", "SCALE_FMTS", "MoeError", "decode_layer_applies",
+    "ACTS", "DECODE_LIMITS", "GEMM_TILES", "NOALLOC_SCRATCH_BYTES", "ROUNDINGS", "SCALE_FMTS",
+    "WEIGHT_FMTS", "MoeError", "decode_layer_applies",
     "library_path", "load_library", "moe_act_quant", "moe_align", "moe_align_batched", "moe_barrier_spin_limit",
     "moe_barrier_timeouts", "moe_fc1_decode", "moe_forward", "moe_forward_noalloc",
-    "moe_grouped_gemm_fp8", "moe_grouped_gemm_fp8_masked", "moe_silu_mul_quant_masked",
+    "moe_grouped_gemm_fp8", "moe_grouped_gemm_fp8_masked", "moe_grouped_gemm_mxfp4",
+    "moe_silu_mul_quant_masked",
     "moe_min_row_cap", "moe_silu_mul_quant", "moe_status_string", "moe_topk_combine",
     "moe_workspace_bytes", "moe_workspace_plan",
 ]

@@ -12,6 +12,7 @@ _LIB_NAME = "libmoefp8.so"
 SCALE_FMTS = {"fp32": 0, "pow2": 1, "ue8m0": 2}
 ROUNDINGS = {"divide": 0, "reciprocal": 1}
 ACTS = {"swiglu": 0, "swiglu_clamp": 1, "swiglu_clamp_after_silu": 2}
+WEIGHT_FMTS = {"e4m3": 0, "mxfp4": 1}
 # Row-tile geometry of the grouped GEMM (mirrors the header's macros), used to
 # interpret the tiles_visited counter.
 GEMM_TILES = {"stream_tile_m": 16, "stream_max_rows": 64, "tiled_tile_m": 256, "col_tile": 128}
@@ -50,7 +51,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("num_experts", _i32), ("hidden", _i32), ("inter", _i32), ("topk", _i32),
                 ("t_cap", _i32), ("align_rows", _i32), ("row_cap", _i32),
                 ("scale_fmt", ctypes.c_int), ("act", ctypes.c_int), ("clamp_limit", _f32),
-                ("rounding", ctypes.c_int), ("expert_start", _i32), ("expert_cap", _i32)]
+                ("rounding", ctypes.c_int), ("expert_start", _i32), ("expert_cap", _i32),
+                ("weight_fmt", ctypes.c_int)]
 
 
 class _Tensors(ctypes.Structure):
@@ -75,6 +77,8 @@ _SIGNATURES = {
                                  _vp]),
     "moe_align_batched": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                          _vp, _vp]),
+    "moe_grouped_gemm_mxfp4": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp, _vp,
+                                              _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "moe_grouped_gemm_fp8_masked": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp,
                                                    _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                                    _vp]),
@@ -319,6 +323,50 @@ def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap
     return out
 
 
+def moe_grouped_gemm_mxfp4(a, a_scales, fmt, w, w_scales, counts, offsets=None, row_cap=None,
+                           a_row_map=None, a_row_div=1, expert_cap=0, out=None):
+    """Grouped GEMM with MXFP4 weights over live rows. ``w`` is uint8 [E, N, K/2]
+    packed E2M1 codes, ``w_scales`` uint8 [E, N, K/32] E8M0 bytes. With
+    ``expert_cap`` > 0 the batched layout (``counts`` = masked_m, no offsets,
+    row_cap = E * expert_cap). Returns BF16 bits (int16) [row_cap, N]."""
+    lib = load_library()
+    _need(a, "a", torch.uint8, ndim=2)
+    _need(a_scales, "a_scales", _scale_dtype(fmt), ndim=2)
+    _need(w, "w", torch.uint8, ndim=3)
+    _need(w_scales, "w_scales", torch.uint8, ndim=3)
+    num_experts, n, k2 = w.shape
+    k = 2 * k2
+    a_rows = a.shape[0]
+    if a.shape[1] != k:
+        raise ValueError("a and w disagree on K")
+    _shape(a_scales, "a_scales", (k // 128, a_rows))
+    _shape(w_scales, "w_scales", (num_experts, n, k // 32))
+    _shape(_need(counts, "counts", torch.int32), "counts", (num_experts,))
+    if expert_cap > 0:
+        row_cap = num_experts * expert_cap if row_cap is None else row_cap
+        offsets = None
+    else:
+        if offsets is None or row_cap is None:
+            raise ValueError("the aligned layout needs offsets and row_cap")
+        _shape(_need(offsets, "offsets", torch.int32), "offsets", (num_experts + 1,))
+    if out is None:
+        out = torch.empty((max(row_cap, 1), n), dtype=torch.int16, device=a.device)
+    ob = _bf16_view(out, "out")
+    if ob.dim() != 2 or ob.shape[1] != n or ob.shape[0] < row_cap:
+        raise ValueError(f"out must be [>= {row_cap}, {n}], got {tuple(ob.shape)}")
+    if a_row_map is not None:
+        _min_numel(_need(a_row_map, "a_row_map", torch.int32), "a_row_map", row_cap)
+    elif a_rows < row_cap:
+        raise ValueError("without a row map, a needs row_cap rows")
+    _same_device(a, a_scales, w, w_scales, counts, offsets, ob, a_row_map)
+    st = lib.moe_grouped_gemm_mxfp4(_ptr(a), _ptr(a_scales), _fmt(fmt), a_rows, _ptr(a_row_map),
+                                    a_row_div, _ptr(w), _ptr(w_scales), _ptr(counts),
+                                    _ptr(offsets), int(expert_cap), num_experts, row_cap, n, k,
+                                    _ptr(ob), _stream())
+    _check("moe_grouped_gemm_mxfp4", st)
+    return out
+
+
 def moe_grouped_gemm_fp8_masked(a, a_scales, fmt, w, w_scales, masked_m, expert_cap,
                                 a_row_map=None, a_row_div=1, out=None, tiles_visited=None):
     """Grouped FP8 GEMM on the batched masked-M layout: expert e's live rows are
@@ -434,22 +482,28 @@ def moe_topk_combine(y, pair_to_row, topk_w, t_live=None, out=None):
     return out
 
 
+def _weight_fmt(weight_fmt):
+    if weight_fmt not in WEIGHT_FMTS:
+        raise ValueError(f"weight_fmt must be one of {list(WEIGHT_FMTS)}")
+    return WEIGHT_FMTS[weight_fmt]
+
+
 def _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act, clamp_limit,
-             rounding="divide", expert_start=0, expert_cap=0):
+             rounding="divide", expert_start=0, expert_cap=0, weight_fmt="e4m3"):
     if act not in ACTS:
         raise ValueError(f"act must be one of {list(ACTS)}")
     return _Problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap or 0, _fmt(fmt),
                     ACTS[act], float(clamp_limit), _rounding(rounding), int(expert_start),
-                    int(expert_cap))
+                    int(expert_cap), _weight_fmt(weight_fmt))
 
 
 def moe_workspace_plan(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
                        fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide",
-                       expert_start=0, expert_cap=0):
+                       expert_start=0, expert_cap=0, weight_fmt="e4m3"):
     """Byte offsets of every intermediate in the forward workspace (dict)."""
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding, expert_start, expert_cap)
+                    clamp_limit, rounding, expert_start, expert_cap, weight_fmt)
     lay = _Layout()
     _check("moe_workspace_plan", lib.moe_workspace_plan(ctypes.byref(prob), ctypes.byref(lay)))
     return {name: getattr(lay, name) for name, _ in _Layout._fields_}
@@ -457,49 +511,63 @@ def moe_workspace_plan(num_experts, hidden, inter, topk, t_cap, align_rows=16, r
 
 def moe_workspace_bytes(num_experts, hidden, inter, topk, t_cap, align_rows=16, row_cap=0,
                         fmt="fp32", act="swiglu", clamp_limit=float("inf"), rounding="divide",
-                        expert_start=0, expert_cap=0):
+                        expert_start=0, expert_cap=0, weight_fmt="e4m3"):
     lib = load_library()
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding, expert_start, expert_cap)
+                    clamp_limit, rounding, expert_start, expert_cap, weight_fmt)
     return int(lib.moe_workspace_bytes(ctypes.byref(prob)))
 
 
-def _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2=None, w2_scales=None):
+def _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2=None, w2_scales=None, weight_fmt="e4m3"):
     """Shapes and devices of the layer's inputs; returns (num_experts, inter, topk)."""
     t_cap, hidden = xb.shape
+    _weight_fmt(weight_fmt)
+    mx = weight_fmt == "mxfp4"
     _need(topk_ids, "topk_ids", torch.int32, ndim=2)
     if topk_ids.shape[0] != t_cap:
         raise ValueError(f"topk_ids has {topk_ids.shape[0]} rows, x has {t_cap}")
     _need(w1, "w1", torch.uint8, ndim=3)
     num_experts, two_i, h1 = w1.shape
-    if h1 != hidden or two_i % 256:
-        raise ValueError(f"w1 must be [E, 2*inter, {hidden}], got {tuple(w1.shape)}")
+    if h1 != (hidden // 2 if mx else hidden) or two_i % 256:
+        raise ValueError(f"w1 must be [E, 2*inter, {hidden // 2 if mx else hidden}], got {tuple(w1.shape)}")
     inter = two_i // 2
-    _shape(_need(w1_scales, "w1_scales", torch.float32), "w1_scales",
-           (num_experts, two_i // 128, hidden // 128))
+    if mx:
+        _shape(_need(w1_scales, "w1_scales", torch.uint8), "w1_scales", (num_experts, two_i, hidden // 32))
+    else:
+        _shape(_need(w1_scales, "w1_scales", torch.float32), "w1_scales",
+               (num_experts, two_i // 128, hidden // 128))
     if w2 is not None:
-        _shape(_need(w2, "w2", torch.uint8), "w2", (num_experts, hidden, inter))
-        _shape(_need(w2_scales, "w2_scales", torch.float32), "w2_scales",
-               (num_experts, hidden // 128, inter // 128))
+        if mx:
+            _shape(_need(w2, "w2", torch.uint8), "w2", (num_experts, hidden, inter // 2))
+            _shape(_need(w2_scales, "w2_scales", torch.uint8), "w2_scales",
+                   (num_experts, hidden, inter // 32))
+        else:
+            _shape(_need(w2, "w2", torch.uint8), "w2", (num_experts, hidden, inter))
+            _shape(_need(w2_scales, "w2_scales", torch.float32), "w2_scales",
+                   (num_experts, hidden // 128, inter // 128))
     return num_experts, inter, topk_ids.shape[1]
 
 
 def moe_forward(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32", act="swiglu",
                 clamp_limit=float("inf"), align_rows=16, row_cap=0, t_live=None, out=None,
-                workspace=None, rounding="divide", expert_start=0, expert_cap=0):
+                workspace=None, rounding="divide", expert_start=0, expert_cap=0,
+                weight_fmt="e4m3"):
     """The whole expert layer. Returns (out BF16 bits int16 [t_cap, H], workspace uint8).
-    ``topk_w=None`` weights every routed pair by one."""
+    ``topk_w=None`` weights every routed pair by one. ``weight_fmt="mxfp4"``:
+    w1/w2 are packed E2M1 codes [E, rows, cols/2] with E8M0 scale bytes
+    [E, rows, cols/32]."""
     lib = load_library()
     xb = _bf16_view(x, "x")
     if xb.dim() != 2:
         raise ValueError("x must be [t_cap, hidden]")
     t_cap, hidden = xb.shape
-    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales)
+    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales,
+                                                    weight_fmt)
     if topk_w is None:
         topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
     _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding, expert_start, expert_cap)
+                    clamp_limit, rounding, expert_start, expert_cap, weight_fmt)
     need = int(lib.moe_workspace_bytes(ctypes.byref(prob)))
     if need == 0:
         lay = _Layout()
@@ -528,7 +596,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="fp32",
                         act="swiglu", clamp_limit=float("inf"), align_rows=16, row_cap=0,
-                        t_live=None, out=None, rounding="divide", expert_start=0, expert_cap=0):
+                        t_live=None, out=None, rounding="divide", expert_start=0, expert_cap=0,
+                        weight_fmt="e4m3"):
     """moe_forward with the library's static per-device workspace instead of a
     caller buffer (for callers that cannot allocate; the call allocates nothing
     when ``out`` and ``topk_w`` are given). Calls on one device must not overlap.
@@ -538,7 +607,8 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
     if xb.dim() != 2:
         raise ValueError("x must be [t_cap, hidden]")
     t_cap, hidden = xb.shape
-    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales)
+    num_experts, inter, topk = _check_layer_tensors(xb, topk_ids, w1, w1_scales, w2, w2_scales,
+                                                    weight_fmt)
     if topk_w is None:
         topk_w = torch.ones((t_cap, topk), dtype=torch.float32, device=xb.device)
     _shape(_need(topk_w, "topk_w", torch.float32), "topk_w", (t_cap, topk))
@@ -549,7 +619,7 @@ def moe_forward_noalloc(x, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, fmt="
         _shape(_need(t_live, "t_live", torch.int32), "t_live", (1,))
     _same_device(xb, topk_ids, topk_w, w1, w1_scales, w2, w2_scales, ob, t_live)
     prob = _problem(num_experts, hidden, inter, topk, t_cap, align_rows, row_cap, fmt, act,
-                    clamp_limit, rounding, expert_start, expert_cap)
+                    clamp_limit, rounding, expert_start, expert_cap, weight_fmt)
     tens = _Tensors(_ptr(xb), _ptr(topk_ids), _ptr(topk_w), _live(t_live), _ptr(w1),
                     _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(ob))
     _check("moe_forward_noalloc", lib.moe_forward_noalloc(ctypes.byref(prob), ctypes.byref(tens),

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmoefp8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["align.hip", "quant.hip", "gemm.hip", "fc1_decode.hip", "down_combine.hip", "combine.hip", "capi.hip"]
+SOURCES = ["align.hip", "quant.hip", "gemm.hip", "gemm_w4.hip", "fc1_decode.hip", "down_combine.hip", "combine.hip", "capi.hip"]
 # Benchmark-only device-clock marks, a library of their own.
 BENCH_SOURCES = ["bench_clock.hip"]
 BENCH_LIB = os.path.join(HERE, "libmoebench.so")

@@ -233,6 +233,46 @@ moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, m
   return gemm_checked(g, stream);
 }
 
+static moe_status gemm_w4_checked(const moe::W4Args& g, void* stream) {
+  if (!dim128(g.n) || !dim128(g.k) || !fmt_ok(g.fmt) || g.a_rows < 0 || g.a_row_div < 1 ||
+      g.num_experts < 1 || g.row_cap < 0 || g.seg_cap < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (g.seg_cap > 0 && static_cast<int64_t>(g.seg_cap) * g.num_experts != g.row_cap)
+    return MOE_ERR_INVALID_ARG;
+  if (g.num_experts > moe::kMaxExperts || !gemm_shape_ok(g.a_rows, g.n, g.k))
+    return MOE_ERR_UNSUPPORTED;
+  if (!g.counts || (!g.offsets && g.seg_cap == 0) || !g.w || !g.w_scales) return MOE_ERR_INVALID_ARG;
+  if (g.row_cap > 0 && (!g.c || !g.a || !g.a_scales || g.a_rows < 1)) return MOE_ERR_INVALID_ARG;
+  if (g.row_cap == 0) return MOE_OK;
+  return from_hip(moe::launch_grouped_gemm_w4(g, as_stream(stream)));
+}
+
+moe_status moe_grouped_gemm_mxfp4(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                  int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                  const uint8_t* w, const uint8_t* w_scales,
+                                  const int32_t* expert_counts, const int32_t* expert_offsets,
+                                  int32_t expert_cap, int32_t num_experts, int32_t row_cap,
+                                  int32_t n, int32_t k, uint16_t* c, void* stream) {
+  moe::W4Args g;
+  g.a = a;
+  g.a_scales = a_scales;
+  g.fmt = fmt;
+  g.a_rows = a_rows;
+  g.a_row_map = a_row_map;
+  g.a_row_div = a_row_div;
+  g.w = w;
+  g.w_scales = w_scales;
+  g.counts = expert_counts;
+  g.offsets = expert_offsets;
+  g.seg_cap = expert_cap;
+  g.num_experts = num_experts;
+  g.row_cap = row_cap;
+  g.n = n;
+  g.k = k;
+  g.c = c;
+  return gemm_w4_checked(g, stream);
+}
+
 moe_status moe_silu_mul_quant(const uint16_t* gate_up, int32_t inter,
                               const int32_t* expert_counts, const int32_t* expert_offsets,
                               int32_t num_experts, int32_t row_cap, moe_act act,
@@ -286,7 +326,8 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   if (!p || !L) return MOE_ERR_INVALID_ARG;
   if (p->num_experts < 1 || !dim128(p->hidden) || !dim128(p->inter) || p->topk < 1 ||
       p->topk > kMaxTopk || p->t_cap < 0 || p->align_rows < 1 || p->row_cap < 0 ||
-      !fmt_ok(p->scale_fmt) || !act_ok(p->act) || !rounding_ok(p->rounding))
+      !fmt_ok(p->scale_fmt) || !act_ok(p->act) || !rounding_ok(p->rounding) ||
+      (p->weight_fmt != MOE_WEIGHT_E4M3 && p->weight_fmt != MOE_WEIGHT_MXFP4))
     return MOE_ERR_INVALID_ARG;
   if (p->act != MOE_ACT_SWIGLU && !(p->clamp_limit > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (p->num_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -321,8 +362,9 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   L->hq = take(R * I);
   L->hs = take((I / 128) * R * sb);
   L->y = take(R * H * 2);
-  // The decode path serves the aligned layout only.
-  const bool decode = !batched && moe::down_combine_fits(p->t_cap, p->topk, p->inter);
+  // The decode path serves the aligned layout and FP8 weights only.
+  const bool decode = !batched && p->weight_fmt == MOE_WEIGHT_E4M3 &&
+                      moe::down_combine_fits(p->t_cap, p->topk, p->inter);
   L->act = decode ? take(R * I * 4) : 0;
   L->status = take(static_cast<size_t>(moe::kDlMaxGrid) * 4);
   L->overflow = take(4);
@@ -346,7 +388,7 @@ moe::DownCombineArgs down_combine_args(const moe_problem* p, const moe_tensors* 
   d.act = reinterpret_cast<const float*>(ws + L.act);
   d.fmt = p->scale_fmt;
   d.w = t->w2;
-  d.w_scales = t->w2_scales;
+  d.w_scales = static_cast<const float*>(t->w2_scales);
   d.counts = reinterpret_cast<const int32_t*>(ws + L.expert_counts);
   d.offsets = reinterpret_cast<const int32_t*>(ws + L.expert_offsets);
   d.row_to_pair = reinterpret_cast<const int32_t*>(ws + L.row_to_pair);
@@ -384,7 +426,7 @@ moe::DecodeFc1Args fc1_decode_args(const moe_problem* p, const moe_tensors* t,
   f.inter = p->inter;
   f.fmt = p->scale_fmt;
   f.w = t->w1;
-  f.w_scales = t->w1_scales;
+  f.w_scales = static_cast<const float*>(t->w1_scales);
   f.act = p->act;
   f.act_limit = p->clamp_limit;
   f.counts = reinterpret_cast<int32_t*>(ws + L.expert_counts);
@@ -503,6 +545,50 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
                        p->align_rows, counts, offsets, r2p, p2r, t->x, p->hidden, p->scale_fmt,
                        p->rounding, xq, xs, mode, s);
 
+  if (p->weight_fmt == MOE_WEIGHT_MXFP4) {
+    // FC1 and FC2 with MXFP4 weights; the rest as the general path.
+    moe::W4Args w;
+    w.fmt = p->scale_fmt;
+    w.counts = counts;
+    w.offsets = offsets;
+    w.seg_cap = 0;  // the batched layout's offsets are e * cap, written by the alignment
+    w.num_experts = p->num_experts;
+    w.row_cap = R;
+    if (e == hipSuccess) {
+      w.a = xq;
+      w.a_scales = xs;
+      w.a_rows = p->t_cap;
+      w.a_row_map = r2p;
+      w.a_row_div = p->topk;
+      w.w = t->w1;
+      w.w_scales = static_cast<const uint8_t*>(t->w1_scales);
+      w.n = 2 * p->inter;
+      w.k = p->hidden;
+      w.c = c1;
+      e = moe::launch_grouped_gemm_w4(w, s);
+    }
+    if (e == hipSuccess)
+      e = moe::launch_silu_mul_quant(c1, p->inter, counts, offsets, p->num_experts, R, p->act,
+                                     p->clamp_limit, p->scale_fmt, p->rounding, hq, hs, 0, s);
+    if (e == hipSuccess) {
+      w.a = hq;
+      w.a_scales = hs;
+      w.a_rows = R;
+      w.a_row_map = nullptr;
+      w.a_row_div = 1;
+      w.w = t->w2;
+      w.w_scales = static_cast<const uint8_t*>(t->w2_scales);
+      w.n = p->hidden;
+      w.k = p->inter;
+      w.c = y;
+      e = moe::launch_grouped_gemm_w4(w, s);
+    }
+    if (e == hipSuccess)
+      e = moe::launch_topk_combine(y, R, p2r, t->topk_w, p->t_cap, t->t_live_dev, p->topk,
+                                   p->hidden, t->out, s);
+    return from_hip(e);
+  }
+
   moe::GemmArgs g;
   g.fmt = p->scale_fmt;
   g.counts = counts;
@@ -521,7 +607,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
     g.a_row_map = r2p;
     g.a_row_div = p->topk;
     g.w = t->w1;
-    g.w_scales = t->w1_scales;
+    g.w_scales = static_cast<const float*>(t->w1_scales);
     g.n = 2 * p->inter;
     g.k = p->hidden;
     g.c = c1;
@@ -547,7 +633,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
     g.a_row_map = nullptr;
     g.a_row_div = 1;
     g.w = t->w2;
-    g.w_scales = t->w2_scales;
+    g.w_scales = static_cast<const float*>(t->w2_scales);
     g.n = p->hidden;
     g.k = p->inter;
     g.c = y;

@@ -85,6 +85,30 @@ struct GemmArgs {
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
 
+// The grouped GEMM with MXFP4 weights: w [num_experts, n, k/2] packed E2M1
+// codes (the even K element in the low nibble), w_scales [num_experts, n,
+// k/32] E8M0 bytes; everything else as GemmArgs.
+constexpr int kMxBlock = 32;  // weights per E8M0 scale along K
+struct W4Args {
+  const uint8_t* a;
+  const void* a_scales;
+  int fmt;
+  int a_rows;
+  const int32_t* a_row_map;
+  int a_row_div;
+  const uint8_t* w;
+  const uint8_t* w_scales;
+  const int32_t* counts;
+  const int32_t* offsets;  // not read when seg_cap > 0
+  int seg_cap;
+  int num_experts;
+  int row_cap;
+  int n;
+  int k;
+  uint16_t* c;
+};
+hipError_t launch_grouped_gemm_w4(const W4Args& g, hipStream_t stream);
+
 // FC2 and the top-k combine of a decode-sized layer in one launch: a
 // workgroup owns 16 output columns of every live expert. Limits of its LDS
 // tables: at most kDcMaxPairs routed pairs of capacity, their quantized

@@ -92,6 +92,22 @@ typedef enum {
  *   SWIGLU                   y = silu(g) * u
  *   SWIGLU_CLAMP             y = silu(min(g, L)) * clamp(u, -L, L)
  *   SWIGLU_CLAMP_AFTER_SILU  y = min(silu(g), L) * clamp(u, -L, L)          */
+/* Expert weight formats.
+ *   MOE_WEIGHT_E4M3   FP8 E4M3 codes [E, rows, cols] with float32 scales per
+ *                     128x128 block [E, rows/128, cols/128] (vLLM PR #59128,
+ *                     Purpose; TensorRT-LLM PR #21250, description).
+ *   MOE_WEIGHT_MXFP4  FP4 weights (vLLM PR #59128's description names them;
+ *                     the pages give no format, read here as OCP MXFP4):
+ *                     E2M1 codes packed two per byte, [E, rows, cols/2], the
+ *                     even column in the low nibble (magnitudes 0, 0.5, 1,
+ *                     1.5, 2, 3, 4, 6; bit 3 the sign), and one E8M0 scale
+ *                     byte b (2^(b-127); 255 is NaN) per 32 consecutive
+ *                     columns, [E, rows, cols/32]. */
+typedef enum {
+  MOE_WEIGHT_E4M3 = 0,
+  MOE_WEIGHT_MXFP4 = 1
+} moe_weight_fmt;
+
 typedef enum {
   MOE_ACT_SWIGLU = 0,
   MOE_ACT_SWIGLU_CLAMP = 1,
@@ -219,6 +235,34 @@ moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, m
                                        int32_t expert_cap, int32_t n, int32_t k, uint16_t* c,
                                        int32_t* tiles_visited, void* stream);
 
+/* Grouped GEMM with FP8 E4M3 activations and MXFP4 weights (vLLM PR #59128,
+ * description: FP4 weights on the same prefix-sum expert endpoints; the
+ * format is MOE_WEIGHT_MXFP4's). For every expert e and live row r:
+ *   C[r, n] = bf16( sum_kb sa[kb, ar] * sum_{j<128} A[ar, kb*128+j] * w(e, n, kb*128+j) )
+ *   w(e, n, k) = e2m1(code of column k of row n) * 2^(w_scales[e, n, k/32] - 127)
+ * with ar as in moe_grouped_gemm_fp8, accumulated in fp32 (the weight scales
+ * applied inside the matrix cores, the activation scale once per 128-wide
+ * block) and rounded to nearest even BF16.
+ *
+ *   a, a_scales, fmt, a_rows, a_row_map, a_row_div   as moe_grouped_gemm_fp8
+ *   w          device uint8 [num_experts, n, k/2] packed E2M1 codes
+ *   w_scales   device uint8 [num_experts, n, k/32] E8M0 bytes
+ *   expert_cap 0: the aligned layout, expert_counts/expert_offsets as
+ *              moe_align produces them; > 0: the batched masked-M layout
+ *              (expert_counts is masked_m, expert_offsets is not read, expert
+ *              e's rows start at e*expert_cap, row_cap = num_experts*expert_cap)
+ *   c          device BF16 [row_cap, n]; only live rows written
+ * Errors: INVALID_ARG (n or k not positive multiples of 128, null pointers,
+ * a_row_div < 1, unknown fmt, a_rows < 1 with rows to compute, a batched
+ * row_cap other than num_experts*expert_cap); UNSUPPORTED (num_experts above
+ * 1024, a_rows * k or n * k at or above 2^32). */
+moe_status moe_grouped_gemm_mxfp4(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
+                                  int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
+                                  const uint8_t* w, const uint8_t* w_scales,
+                                  const int32_t* expert_counts, const int32_t* expert_offsets,
+                                  int32_t expert_cap, int32_t num_experts, int32_t row_cap,
+                                  int32_t n, int32_t k, uint16_t* c, void* stream);
+
 /* Row-tile heights of the two GEMM kernels, for interpreting tiles_visited:
  * experts with at most MOE_GEMM_STREAM_MAX_ROWS live rows are computed by
  * the weight-streaming kernel in row tiles of MOE_GEMM_STREAM_TILE_M, larger
@@ -294,6 +338,9 @@ typedef struct {
                             many rows per expert (row_cap is then 0 or num_experts *
                             expert_cap, align_rows is unused, and the decode path's
                             fused schedules do not apply) */
+  moe_weight_fmt weight_fmt; /* format of w1/w2 and their scales; MXFP4 weights take the
+                                general six-launch schedule with moe_grouped_gemm_mxfp4 as
+                                both GEMMs (the decode path's fused schedules are FP8-only) */
 } moe_problem;
 
 typedef struct {
@@ -301,10 +348,10 @@ typedef struct {
   const int32_t* topk_ids;    /* [t_cap, topk] */
   const float* topk_w;        /* [t_cap, topk] */
   const int32_t* t_live_dev;  /* scalar or NULL */
-  const uint8_t* w1;          /* [E, 2I, H]: gate rows [0, I), up rows [I, 2I) */
-  const float* w1_scales;     /* [E, 2I/128, H/128] */
-  const uint8_t* w2;          /* [E, H, I] */
-  const float* w2_scales;     /* [E, H/128, I/128] */
+  const uint8_t* w1;          /* [E, 2I, H] (MXFP4: [E, 2I, H/2]): gate rows [0, I), up rows [I, 2I) */
+  const void* w1_scales;      /* float [E, 2I/128, H/128] (MXFP4: E8M0 bytes [E, 2I, H/32]) */
+  const uint8_t* w2;          /* [E, H, I] (MXFP4: [E, H, I/2]) */
+  const void* w2_scales;      /* float [E, H/128, I/128] (MXFP4: E8M0 bytes [E, H, I/32]) */
   uint16_t* out;              /* BF16 [t_cap, H]; rows >= t_live untouched */
 } moe_tensors;
 

@@ -138,3 +138,63 @@ def test_spin_limit_round_trips():
     finally:
         moe.moe_barrier_spin_limit(old)
     assert old == 1 << 21
+
+
+def _mx_layer(**over):
+    t = dict(
+        w1=torch.zeros((E, 2 * I, H // 2), dtype=torch.uint8),
+        w1_scales=torch.full((E, 2 * I, H // 32), 127, dtype=torch.uint8),
+        w2=torch.zeros((E, H, I // 2), dtype=torch.uint8),
+        w2_scales=torch.full((E, H, I // 32), 127, dtype=torch.uint8),
+    )
+    t.update(over)
+    return _layer(**t)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("w1", torch.zeros((E, 2 * I, H), dtype=torch.uint8)),              # FP8 width
+    ("w1_scales", torch.ones((E, 2 * I // 128, H // 128), dtype=torch.float32)),
+    ("w2", torch.zeros((E, H, I), dtype=torch.uint8)),
+    ("w2_scales", torch.full((E, H, I // 32 + 1), 127, dtype=torch.uint8)),
+])
+def test_mxfp4_forward_rejects_mismatched_shapes(name, bad):
+    t = _mx_layer(**{name: bad})
+    with pytest.raises((ValueError, TypeError)):  # a wrong dtype is a TypeError
+        moe.moe_forward(t["x"], t["topk_ids"], t["topk_w"], t["w1"], t["w1_scales"], t["w2"],
+                        t["w2_scales"], weight_fmt="mxfp4")
+
+
+def test_mxfp4_forward_shapes_pass_and_then_require_gpu_tensors():
+    t = _mx_layer()
+    with pytest.raises(ValueError, match="GPU"):
+        moe.moe_forward(t["x"], t["topk_ids"], t["topk_w"], t["w1"], t["w1_scales"], t["w2"],
+                        t["w2_scales"], weight_fmt="mxfp4")
+    with pytest.raises(ValueError, match="weight_fmt"):
+        moe.moe_forward(t["x"], t["topk_ids"], t["topk_w"], t["w1"], t["w1_scales"], t["w2"],
+                        t["w2_scales"], weight_fmt="fp4")
+
+
+def test_mxfp4_gemm_rejects_mismatched_shapes():
+    a = torch.zeros((64, 256), dtype=torch.uint8)
+    sa = torch.ones((2, 64), dtype=torch.float32)
+    w = torch.zeros((3, 128, 128), dtype=torch.uint8)
+    ws = torch.full((3, 128, 8), 127, dtype=torch.uint8)
+    cnt = torch.zeros(3, dtype=torch.int32)
+    off = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="K"):
+        moe.moe_grouped_gemm_mxfp4(torch.zeros((64, 128), dtype=torch.uint8), sa, "fp32", w, ws,
+                                   cnt, off, 64)
+    with pytest.raises(ValueError, match="w_scales"):
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, torch.full((3, 128, 2), 127, dtype=torch.uint8),
+                                   cnt, off, 64)
+    with pytest.raises(TypeError, match="w_scales"):
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, ws.float(), cnt, off, 64)
+    with pytest.raises(ValueError, match="offsets"):
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, ws, cnt, None, 64)
+    with pytest.raises(ValueError, match="out"):
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, ws, cnt, off, 64,
+                                   out=torch.zeros((64, 127), dtype=torch.int16))
+    with pytest.raises(ValueError, match="GPU"):
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, ws, cnt, off, 64)
+    with pytest.raises(ValueError, match="GPU"):  # batched: counts = masked_m, no offsets
+        moe.moe_grouped_gemm_mxfp4(a, sa, "fp32", w, ws, cnt, expert_cap=16)

@@ -130,7 +130,7 @@ def test_combine_validation(lib):
 def _problem(**kw):
     d = dict(num_experts=32, hidden=7168, inter=2048, topk=8, t_cap=4096, align_rows=16,
              row_cap=0, scale_fmt=0, act=0, clamp_limit=float("inf"), rounding=0, expert_start=0,
-             expert_cap=0)
+             expert_cap=0, weight_fmt=0)
     d.update(kw)
     return B._Problem(**d)
 
@@ -281,3 +281,37 @@ def test_batched_layout_validation(lib):
 def test_silu_mul_quant_rejects_more_experts_than_its_table(lib):
     f = lib.moe_silu_mul_quant
     assert f(FAKE, 256, FAKE, FAKE, 1025, 64, 0, 7.0, 0, 0, FAKE, FAKE, NULL) == UNSUPPORTED
+
+
+def test_mxfp4_gemm_validation(lib):
+    f = lib.moe_grouped_gemm_mxfp4
+
+    def call(n=256, k=256, fmt=0, div=1, e=4, rc=64, cap=0, a=FAKE, c=FAKE, w=FAKE, ws=FAKE,
+             counts=FAKE, offsets=FAKE, a_rows=64):
+        return f(a, FAKE, fmt, a_rows, NULL, div, w, ws, counts, offsets, cap, e, rc, n, k, c, NULL)
+    assert call(n=200) == INVALID
+    assert call(k=64) == INVALID
+    assert call(fmt=7) == INVALID
+    assert call(div=0) == INVALID
+    assert call(e=0) == INVALID
+    assert call(e=2000) == UNSUPPORTED
+    assert call(a=NULL) == INVALID
+    assert call(w=NULL) == INVALID
+    assert call(ws=NULL) == INVALID
+    assert call(counts=NULL) == INVALID
+    assert call(offsets=NULL) == INVALID          # the aligned layout reads offsets
+    assert call(a_rows=0) == INVALID              # rows to compute but no A rows
+    assert call(cap=16, rc=63) == INVALID         # batched: row_cap must be E * cap
+    assert call(cap=-1) == INVALID
+    assert call(rc=0, a=NULL, c=NULL) == OK
+
+
+def test_forward_weight_format_field(lib):
+    lay = B._Layout()
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(weight_fmt=2)), ctypes.byref(lay)) == INVALID
+    assert lib.moe_workspace_plan(ctypes.byref(_problem(weight_fmt=1)), ctypes.byref(lay)) == OK
+    # MXFP4 weights never take the decode path's fused schedules
+    pd = _problem(num_experts=288, hidden=4096, inter=512, t_cap=4, weight_fmt=1)
+    assert lib.moe_workspace_plan(ctypes.byref(pd), ctypes.byref(lay)) == OK and lay.act == lay.status
+    pd8 = _problem(num_experts=288, hidden=4096, inter=512, t_cap=4, weight_fmt=0)
+    assert lib.moe_workspace_plan(ctypes.byref(pd8), ctypes.byref(lay)) == OK and lay.act < lay.status
