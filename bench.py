@@ -112,15 +112,19 @@ def live_stats(ids, t_live, num_experts):
     return len(np.unique(flat)), len(flat)
 
 
-def algorithmic(cfg, n_live_experts, pairs, t_live):
+def algorithmic(cfg, n_live_experts, pairs, t_live, weight_fmt="e4m3"):
     """Bytes the layer must move at least, and FLOPs on live rows only.
 
     Per expert: FC1 codes 2I*H + fp32 block scales (2I/128)(H/128)*4, FC2
-    codes H*I + (H/128)(I/128)*4. Plus BF16 x in and BF16 out (2*T*H each).
+    codes H*I + (H/128)(I/128)*4 (MXFP4: half a byte per weight and one
+    scale byte per 32). Plus BF16 x in and BF16 out (2*T*H each).
     FLOPs: FC1 2*P*2I*H + FC2 2*P*H*I = 6*P*H*I.
     """
     H, I = cfg.hidden, cfg.inter
-    per_expert = 2 * I * H + (2 * I // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4
+    if weight_fmt == "mxfp4":
+        per_expert = 3 * I * H // 2 + 3 * I * H // 32
+    else:
+        per_expert = 2 * I * H + (2 * I // 128) * (H // 128) * 4 + H * I + (H // 128) * (I // 128) * 4
     bmin = n_live_experts * per_expert + 2 * t_live * H * 2
     flops = 6 * pairs * H * I
     return bmin, flops
@@ -431,6 +435,11 @@ PER_CONFIG = [
     # and the fully occupied layer with room for 1.5x the mean expert load
     ("padded", 512, 16, "fp32", "swiglu", float("inf"), 64),
     ("full", 4096, 4096, "fp32", "swiglu", float("inf"), 1536),
+    # MXFP4 weights (E2M1 codes, E8M0 scales per 32 along K) with FP8 activations
+    ("decode", 1, 1, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
+    ("decode", 4, 4, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
+    ("padded", 512, 16, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
+    ("full", 4096, 4096, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
 ]
 
 
@@ -468,22 +477,24 @@ def main():
 
     weights_cache = {}
 
-    def weights_for(name):
-        if name not in weights_cache:
+    def weights_for(name, weight_fmt="e4m3"):
+        key = (name, weight_fmt)
+        if key not in weights_cache:
             weights_cache.clear()
             torch.cuda.empty_cache()
             cfg_w = synth.get(name)
-            host = synth.ExpertWeights(cfg_w).stacked(threads=min(16, len(os.sched_getaffinity(0))))
-            weights_cache[name] = (host, [up(a) for a in (host[0][0], host[0][1], host[1][0], host[1][1])])
-        return weights_cache[name]
+            gen = synth.ExpertWeightsMxfp4 if weight_fmt == "mxfp4" else synth.ExpertWeights
+            host = gen(cfg_w).stacked(threads=min(16, len(os.sched_getaffinity(0))))
+            weights_cache[key] = (host, [up(a) for a in (host[0][0], host[0][1], host[1][0], host[1][1])])
+        return weights_cache[key]
 
-    def layer_inputs(name, t_cap, t_live, fmt, act, lim, expert_cap=0):
+    def layer_inputs(name, t_cap, t_live, fmt, act, lim, expert_cap=0, weight_fmt="e4m3"):
         cfg_l = synth.get(name)
         x_l, ids_l, w_l = synth.make_workload(cfg_l, t_cap)
-        _, d_w_l = weights_for(name)
+        _, d_w_l = weights_for(name, weight_fmt)
         E_l, H_l, I_l, K_l = cfg_l.num_experts, cfg_l.hidden, cfg_l.inter, cfg_l.topk
         lay_l = moe.moe_workspace_plan(E_l, H_l, I_l, K_l, t_cap, cfg_l.align_rows, 0, fmt, act, lim,
-                                       expert_cap=expert_cap)
+                                       expert_cap=expert_cap, weight_fmt=weight_fmt)
         ws_l = torch.zeros(lay_l["total"], dtype=torch.uint8, device=dev)
         out_l = torch.zeros((t_cap, H_l), dtype=torch.int16, device=dev)
         dx_l, dids_l, dw_l = up(x_l), up(ids_l), up(w_l)
@@ -491,12 +502,13 @@ def main():
 
         def fwd():
             moe.moe_forward(dx_l, dids_l, dw_l, *d_w_l, fmt, act, lim, cfg_l.align_rows, 0,
-                            t_live=dlive_l, out=out_l, workspace=ws_l, expert_cap=expert_cap)
+                            t_live=dlive_l, out=out_l, workspace=ws_l, expert_cap=expert_cap,
+                            weight_fmt=weight_fmt)
         return cfg_l, (x_l, ids_l, w_l), fwd, lay_l, ws_l, (dx_l, dids_l, dw_l, dlive_l), out_l
 
-    def rates(cfg_l, ids_l, t_live, span_us):
+    def rates(cfg_l, ids_l, t_live, span_us, weight_fmt="e4m3"):
         n_e, pairs_l = live_stats(ids_l, t_live, cfg_l.num_experts)
-        bmin_l, flops_l = algorithmic(cfg_l, n_e, pairs_l, t_live)
+        bmin_l, flops_l = algorithmic(cfg_l, n_e, pairs_l, t_live, weight_fmt)
         return {"live_experts": n_e, "live_pairs": pairs_l,
                 "live_tflops": round(flops_l / (span_us * 1e-6) / 1e12, 3),
                 "frac_fp8_peak": round(flops_l / (span_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4),
@@ -655,22 +667,25 @@ def main():
     # ---- every workload and variant, the same protocol with fewer replays
     if not args.no_per_config:
         table = []
-        for name, tc, tl, f, ac, li, *cap in PER_CONFIG:
-            cap = cap[0] if cap else 0
-            cfg_l, (xl, idsl, wl), fwd_l, lay_l, ws_l, _, out_l = layer_inputs(name, tc, tl, f, ac, li, cap)
+        for name, tc, tl, f, ac, li, *extra in PER_CONFIG:
+            cap = extra[0] if extra else 0
+            wfmt = extra[1] if len(extra) > 1 else "e4m3"
+            cfg_l, (xl, idsl, wl), fwd_l, lay_l, ws_l, _, out_l = layer_inputs(name, tc, tl, f, ac, li,
+                                                                               cap, wfmt)
             spans, evs, _ = time_layer(torch, fwd_l, args.config_steps, 3, flush_caches)
             m = statistics.median(spans)
             ent = {"workload": name, "tokens": tl, "token_capacity": tc, "act_scale_fmt": f,
                    "activation": ac, "span_us": round(m, 2), "p10_us": round(pct(spans, 0.1), 2),
                    "p90_us": round(pct(spans, 0.9), 2), "events_us": round(statistics.median(evs), 2),
-                   "path": ("batched masked-M" if cap else
+                   "weights": wfmt,
+                   "path": ("batched masked-M" if cap else "general" if wfmt != "e4m3" else
                             "one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter)
                             else "general")}
             if cap:
                 ent["expert_cap"] = cap
                 ovf = int(ws_l[lay_l["overflow"]:lay_l["overflow"] + 4].view(torch.int32).item())
                 ent["pairs_dropped"] = ovf
-            ent.update(rates(cfg_l, idsl, tl, m))
+            ent.update(rates(cfg_l, idsl, tl, m, wfmt))
             # the bars: HBM at <= 32 tokens, FP8 MFMA at the fully occupied
             # layer; the tiny layer is launch-bound and reported only
             bar = None if name == "tiny" else ("hbm" if tl <= 32 else ("mfma" if name == "full" else None))
@@ -679,7 +694,8 @@ def main():
             if c:
                 ent["pages_context_us"] = c
             table.append(ent)
-            print(f"# per-config {name} T={tl}/{tc} {f} {ac}{f' cap {cap}' if cap else ''}: {m:.1f} us, "
+            print(f"# per-config {name} T={tl}/{tc} {f} {ac}{f' cap {cap}' if cap else ''}"
+                  f"{' ' + wfmt + ' weights' if wfmt != 'e4m3' else ''}: {m:.1f} us, "
                   f"{ent['frac_fp8_peak']:.3f} FP8, {ent['frac_hbm_peak']:.3f} HBM",
                   file=sys.stderr, flush=True)
             del fwd_l, ws_l, out_l

@@ -78,7 +78,8 @@ _SIGNATURES = {
     "moe_align_batched": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                          _vp, _vp]),
     "moe_grouped_gemm_mxfp4": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp, _vp,
-                                              _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+                                              _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                              _vp]),
     "moe_grouped_gemm_fp8_masked": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i32, _vp, _i32, _vp,
                                                    _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                                    _vp]),
@@ -324,7 +325,8 @@ def moe_grouped_gemm_fp8(a, a_scales, fmt, w, w_scales, counts, offsets, row_cap
 
 
 def moe_grouped_gemm_mxfp4(a, a_scales, fmt, w, w_scales, counts, offsets=None, row_cap=None,
-                           a_row_map=None, a_row_div=1, expert_cap=0, out=None):
+                           a_row_map=None, a_row_div=1, expert_cap=0, max_rows_per_expert=0,
+                           out=None):
     """Grouped GEMM with MXFP4 weights over live rows. ``w`` is uint8 [E, N, K/2]
     packed E2M1 codes, ``w_scales`` uint8 [E, N, K/32] E8M0 bytes. With
     ``expert_cap`` > 0 the batched layout (``counts`` = masked_m, no offsets,
@@ -361,8 +363,8 @@ def moe_grouped_gemm_mxfp4(a, a_scales, fmt, w, w_scales, counts, offsets=None, 
     _same_device(a, a_scales, w, w_scales, counts, offsets, ob, a_row_map)
     st = lib.moe_grouped_gemm_mxfp4(_ptr(a), _ptr(a_scales), _fmt(fmt), a_rows, _ptr(a_row_map),
                                     a_row_div, _ptr(w), _ptr(w_scales), _ptr(counts),
-                                    _ptr(offsets), int(expert_cap), num_experts, row_cap, n, k,
-                                    _ptr(ob), _stream())
+                                    _ptr(offsets), int(expert_cap), num_experts, row_cap,
+                                    int(max_rows_per_expert), n, k, _ptr(ob), _stream())
     _check("moe_grouped_gemm_mxfp4", st)
     return out
 

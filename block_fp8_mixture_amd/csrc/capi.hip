@@ -252,7 +252,9 @@ moe_status moe_grouped_gemm_mxfp4(const uint8_t* a, const void* a_scales, moe_sc
                                   const uint8_t* w, const uint8_t* w_scales,
                                   const int32_t* expert_counts, const int32_t* expert_offsets,
                                   int32_t expert_cap, int32_t num_experts, int32_t row_cap,
-                                  int32_t n, int32_t k, uint16_t* c, void* stream) {
+                                  int32_t max_rows_per_expert, int32_t n, int32_t k, uint16_t* c,
+                                  void* stream) {
+  if (max_rows_per_expert < 0) return MOE_ERR_INVALID_ARG;
   moe::W4Args g;
   g.a = a;
   g.a_scales = a_scales;
@@ -267,6 +269,8 @@ moe_status moe_grouped_gemm_mxfp4(const uint8_t* a, const void* a_scales, moe_sc
   g.seg_cap = expert_cap;
   g.num_experts = num_experts;
   g.row_cap = row_cap;
+  const int32_t seg = expert_cap > 0 ? expert_cap : row_cap;
+  g.max_rows_per_expert = (max_rows_per_expert == 0 || max_rows_per_expert > seg) ? seg : max_rows_per_expert;
   g.n = n;
   g.k = k;
   g.c = c;
@@ -554,6 +558,8 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
     w.seg_cap = 0;  // the batched layout's offsets are e * cap, written by the alignment
     w.num_experts = p->num_experts;
     w.row_cap = R;
+    w.max_rows_per_expert = pairs < R ? pairs : R;
+    if (p->expert_cap > 0 && p->expert_cap < w.max_rows_per_expert) w.max_rows_per_expert = p->expert_cap;
     if (e == hipSuccess) {
       w.a = xq;
       w.a_scales = xs;

@@ -25,14 +25,24 @@
 // into the accumulator (16 FMAs per lane): the oracle's order, one
 // activation block at a time.
 //
-// Work: a wave task is (expert, 32 token rows, 32 weight rows, 1/S of K).
-// A 4-wave workgroup runs 4/S tasks at once; the S waves of a task add their
-// partial sums in LDS in wave order, so the result does not depend on which
-// finishes first. S (1, 2 or 4) is picked on the device so that the tasks
-// fill the grid's waves. Tasks run expert by expert, token tile by token
-// tile, and the weight tiles fastest, so neighbouring tasks share their
-// token rows in L2. Weights and tokens go straight from global memory into
-// the MFMA registers, two K steps ahead.
+// Two kernels split the experts by their live rows, as the FP8 GEMM does:
+//  - gemm_w4_kernel (experts with at most kW4SmallMax rows, or every expert
+//    when the launch's bound says none is larger): a wave task is (expert,
+//    32 token rows, 32 weight rows, 1/S of K). A 4-wave workgroup runs 4/S
+//    tasks at once; the S waves of a task add their partial sums in LDS in
+//    wave order, so the result does not depend on which finishes first. S
+//    (1, 2 or 4) is picked on the device so that the tasks fill the grid's
+//    waves. Weights and tokens go straight from global memory into the MFMA
+//    registers, two K steps ahead.
+//  - gemm_w4_tiled_kernel (larger experts): a workgroup tile is 64 token
+//    rows x 128 weight rows; the tile's token rows pass through LDS by
+//    direct-to-LDS loads (double buffered, one K step ahead, 128-byte rows
+//    XOR-swizzled by row pair so the fragment reads are conflict-free) and
+//    each wave streams its 32 weight rows from global memory one K step
+//    ahead, for the 2 token sub-tiles (4 sub-tiles held twice the registers
+//    the accumulators and operands fit in).
+// Tasks run expert by expert, token tile by token tile, and the weight tiles
+// fastest, so neighbouring tasks share their token rows in L2.
 #include "device_common.h"
 #include "gemm_device.h"
 #include "kernels.h"
@@ -42,7 +52,11 @@ namespace {
 
 constexpr int kW4Threads = 256;
 constexpr int kW4Waves = kW4Threads / 64;
-constexpr int kW4Tile = 32;  // token rows and weight rows of a wave task
+constexpr int kW4Tile = 32;       // token rows and weight rows of a wave task
+constexpr int kW4TiledM = 64;     // token rows of a tiled workgroup
+constexpr int kW4Subs = kW4TiledM / 32;  // its 32-row token sub-tiles
+constexpr int kW4TiledN = 128;    // weight rows of a tiled workgroup (32 per wave)
+constexpr int kW4SmallMax = 64;   // experts with more live rows go to the tiled kernel
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -63,25 +77,19 @@ struct W4Step {
   float sa;     // the token's activation scale of the step
 };
 
-template <bool UE8M0, bool GATHER>
-__global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_kernel(W4Args p) {
-  __shared__ int s_pref[kMaxExperts + 1];  // exclusive prefix of 32-row token tiles over experts
-  __shared__ int s_wsum[kW4Waves];
-  __shared__ __attribute__((aligned(16))) float s_red[kW4Waves][64 * 16];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
+// Exclusive prefix over the experts of units(rows) for the experts `want`
+// keeps (0 for the others), into s_pref[0..E]; all threads call it.
+template <typename Want, typename Units>
+__device__ void w4_prefix(const W4Args& p, Want want, Units units, int* s_pref, int* s_wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.num_experts;
-
-  // ---- token tiles per expert and their prefix (every workgroup, in LDS)
   constexpr int kPer = (kMaxExperts + kW4Threads - 1) / kW4Threads;
   int tiles[kPer], run = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = tid * kPer + i;
-    tiles[i] = e < E ? (w4_rows(p, e) + kW4Tile - 1) / kW4Tile : 0;
+    const int rows = e < E ? w4_rows(p, e) : 0;
+    tiles[i] = want(rows) ? units(rows) : 0;
     run += tiles[i];
   }
   int incl = run;
@@ -102,6 +110,49 @@ __global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_kernel(W4Args p) {
   }
   if (tid == kW4Threads - 1) s_pref[E] = base;
   __syncthreads();
+}
+
+// The expert whose units hold unit u (s_pref ascending, s_pref[0] = 0).
+__device__ __forceinline__ int w4_expert_of(const int* s_pref, int E, int u) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pref[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct W4Any {
+  __device__ bool operator()(int rows) const { return rows > 0; }
+};
+struct W4SmallRows {
+  __device__ bool operator()(int rows) const { return rows > 0 && rows <= kW4SmallMax; }
+};
+struct W4LargeRows {
+  __device__ bool operator()(int rows) const { return rows > kW4SmallMax; }
+};
+template <int M>
+struct W4TilesOf {
+  __device__ int operator()(int rows) const { return (rows + M - 1) / M; }
+};
+
+template <bool UE8M0, bool GATHER, bool SMALL_ONLY>
+__global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_kernel(W4Args p) {
+  __shared__ int s_pref[kMaxExperts + 1];  // exclusive prefix of 32-row token tiles over experts
+  __shared__ int s_wsum[kW4Waves];
+  __shared__ __attribute__((aligned(16))) float s_red[kW4Waves][64 * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int E = p.num_experts;
+
+  // ---- token tiles per expert and their prefix (every workgroup, in LDS)
+  if constexpr (SMALL_ONLY)
+    w4_prefix(p, W4SmallRows(), W4TilesOf<kW4Tile>(), s_pref, s_wsum);
+  else
+    w4_prefix(p, W4Any(), W4TilesOf<kW4Tile>(), s_pref, s_wsum);
 
   const int N = p.n, K = p.k, KB = K / kGroup;
   const int nt = N / kW4Tile;
@@ -125,12 +176,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_kernel(W4Args p) {
     if (live) {
       const int tm_all = t / nt;
       n0 = (t - tm_all * nt) * kW4Tile;
-      int lo = 0, hi = E - 1;  // the expert whose token tiles hold tm_all
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] <= tm_all) lo = mid; else hi = mid - 1;
-      }
-      e = lo;
+      e = w4_expert_of(s_pref, E, tm_all);
       const int mt = tm_all - s_pref[e];
       rows_here = min(kW4Tile, w4_rows(p, e) - mt * kW4Tile);
       row0 = w4_seg_start(p, e) + mt * kW4Tile;
@@ -230,15 +276,191 @@ __global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_kernel(W4Args p) {
   }
 }
 
+
+// The loads of one K step of a tiled wave: its weight rows' codes and scale
+// bytes, and the activation scale of its token in each sub-tile.
+constexpr int kW4StepLoads = 3 + kW4Subs;  // vector loads of load_w: 2 code, 1 scale, 1 per sub
+struct W4TStep {
+  uint4 w[2];
+  uint32_t ws;
+  float sa[kW4Subs];
+};
+
+template <bool UE8M0, bool GATHER>
+__global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_tiled_kernel(W4Args p) {
+  __shared__ int s_pref[kMaxExperts + 1];  // exclusive prefix of the token tiles over experts
+  __shared__ int s_wsum[kW4Waves];
+  __shared__ int s_src[kW4TiledM];         // A row of each token row of the tile (-1: none)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_tok[2][kW4TiledM * kGroup];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int E = p.num_experts;
+  w4_prefix(p, W4LargeRows(), W4TilesOf<kW4TiledM>(), s_pref, s_wsum);
+
+  const int N = p.n, K = p.k, KB = K / kGroup;
+  const int ntn = N / kW4TiledN;
+  const int total = s_pref[E] * ntn;
+  const v16f zero = {};
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int tm_all = tile / ntn;
+    const int n0 = (tile - tm_all * ntn) * kW4TiledN;
+    const int e = w4_expert_of(s_pref, E, tm_all);
+    const int mt = tm_all - s_pref[e];
+    const int rows_here = min(kW4TiledM, w4_rows(p, e) - mt * kW4TiledM);
+    const int row0 = w4_seg_start(p, e) + mt * kW4TiledM;
+
+    __syncthreads();  // the previous tile is done with s_src and s_tok
+    if (tid < kW4TiledM) {
+      int src = -1;
+      if (tid < rows_here) {
+        const int r = row0 + tid;
+        src = GATHER ? p.a_row_map[r] / p.a_row_div : r;
+        if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = -1;
+      }
+      s_src[tid] = src;
+    }
+    __syncthreads();
+
+    // Token staging by direct-to-LDS loads: instruction q of wave w fills the
+    // 1 KB at slot (4 q + w) * 64 of a stage (16-byte slots), so lane l lands
+    // in row 32 q + 8 w + l / 8, slot l % 8, and fetches the chunk that the
+    // row-pair swizzle keeps there. Rows without a source load row 0 of A
+    // (never stored).
+    const uint8_t* tsrc[kW4Subs];
+#pragma unroll
+    for (int q = 0; q < kW4Subs; ++q) {
+      const int row = 32 * q + 8 * wave + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+      const int src = s_src[row];
+      tsrc[q] = p.a + static_cast<int64_t>(src < 0 ? 0 : src) * K + chunk * 16;
+    }
+    auto load_tok = [&](int kb, int buf) {
+#pragma unroll
+      for (int q = 0; q < kW4Subs; ++q)
+        __builtin_amdgcn_global_load_lds(tsrc[q] + kb * kGroup,
+                                         (lds_void*)(s_tok[buf] + (4 * q + wave) * 1024), 16, 0, 0);
+    };
+
+    // This wave's weight rows and its tokens' scales.
+    const int64_t wrow = static_cast<int64_t>(e) * N + n0 + 32 * wave + (lane & 31);
+    const uint8_t* wp = p.w + wrow * (K / 2) + 16 * h;
+    const uint8_t* sp = p.w_scales + wrow * (K / kMxBlock);
+    int tsrc_lane[kW4Subs];
+#pragma unroll
+    for (int sub = 0; sub < kW4Subs; ++sub) tsrc_lane[sub] = s_src[32 * sub + (lane & 31)];
+    auto load_w = [&](int kb, W4TStep& st) {
+      st.w[0] = *reinterpret_cast<const uint4*>(wp + kb * 64);
+      st.w[1] = *reinterpret_cast<const uint4*>(wp + kb * 64 + 32);
+      st.ws = *reinterpret_cast<const uint32_t*>(sp + kb * 4);
+#pragma unroll
+      for (int sub = 0; sub < kW4Subs; ++sub) {
+        const int src = tsrc_lane[sub] < 0 ? 0 : tsrc_lane[sub];
+        const int64_t si = static_cast<int64_t>(kb) * p.a_rows + src;
+        if constexpr (UE8M0)
+          st.sa[sub] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint8_t*>(p.a_scales)[si]) << 23);
+        else
+          st.sa[sub] = static_cast<const float*>(p.a_scales)[si];
+        if (tsrc_lane[sub] < 0) st.sa[sub] = 0.0f;
+      }
+    };
+    v16f acc[kW4Subs];
+#pragma unroll
+    for (int sub = 0; sub < kW4Subs; ++sub) acc[sub] = zero;
+    auto compute = [&](int kb, const W4TStep& st) {
+      const uint8_t* buf = s_tok[kb & 1];
+#pragma unroll
+      for (int sub = 0; sub < kW4Subs; ++sub) {
+        const int row = 32 * sub + (lane & 31);
+        v16f part = zero;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint4 b0 = *reinterpret_cast<const uint4*>(buf + swz128(row, 4 * kk + h));
+          const uint4 b1 = *reinterpret_cast<const uint4*>(buf + swz128(row, 4 * kk + 2 + h));
+          const v8i wa = {static_cast<int>(st.w[kk].x), static_cast<int>(st.w[kk].y),
+                          static_cast<int>(st.w[kk].z), static_cast<int>(st.w[kk].w), 0, 0, 0, 0};
+          const v8i tb = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
+                          static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
+                          static_cast<int>(b1.z), static_cast<int>(b1.w)};
+          const int sc = static_cast<int>((st.ws >> (8 * (2 * kk + h))) & 0xFFu);
+          part = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, tb, part, 4, 0, 0, sc, 0, 127);
+        }
+        acc[sub] += part * st.sa[sub];
+        // One sub-tile's fragments at a time: reads of the next are not
+        // hoisted above this one's MFMAs (that would hold 32 fragments).
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // One K step: the next step's tokens (direct to the other LDS buffer,
+    // free since the last barrier) and weights (to registers), this step's
+    // MFMAs, then a wait for this wave's token loads (the weight and scale
+    // loads issued after them, kW4StepLoads, may stay in flight) and a barrier.
+    auto step = [&](int kb, const W4TStep& cur, W4TStep& nxt) {
+      const bool more = kb + 1 < KB;
+      if (more) load_tok(kb + 1, (kb + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_w(kb + 1, nxt);
+      compute(kb, cur);
+      if (more)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kW4StepLoads));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);  // no scheduling across steps (registers)
+    };
+
+    W4TStep s0, s1;
+    load_tok(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(0, s0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kW4StepLoads));
+    lds_barrier();
+    int kb = 0;
+    for (; kb + 1 < KB; kb += 2) {
+      step(kb, s0, s1);
+      step(kb + 1, s1, s0);
+    }
+    if (kb < KB) step(kb, s0, s1);
+
+#pragma unroll
+    for (int sub = 0; sub < kW4Subs; ++sub) {
+      const int j = 32 * sub + (lane & 31);
+      if (j < rows_here) {
+        uint16_t* crow = p.c + static_cast<int64_t>(row0 + j) * N + n0 + 32 * wave + 4 * h;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const v4f v = {acc[sub][4 * g], acc[sub][4 * g + 1], acc[sub][4 * g + 2], acc[sub][4 * g + 3]};
+          *reinterpret_cast<uint2*>(crow + 8 * g) = pack_bf16x4(v);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
+template <bool U, bool M>
+static void launch_w4(const W4Args& g, bool large, hipStream_t stream) {
+  const int cus = device_cu_count();
+  if (!large) {  // every expert to the wave-task kernel
+    hipLaunchKernelGGL((gemm_w4_kernel<U, M, false>), dim3(4 * cus), dim3(kW4Threads), 0, stream, g);
+    return;
+  }
+  hipLaunchKernelGGL((gemm_w4_kernel<U, M, true>), dim3(4 * cus), dim3(kW4Threads), 0, stream, g);
+  hipLaunchKernelGGL((gemm_w4_tiled_kernel<U, M>), dim3(2 * cus), dim3(kW4Threads), 0, stream, g);
+}
+
 hipError_t launch_grouped_gemm_w4(const W4Args& g, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(4 * device_cu_count()));
+  // The tiled kernel only when some expert can hold more than kW4SmallMax rows.
+  const bool large = g.max_rows_per_expert > kW4SmallMax;
   const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
-  if (u && m) hipLaunchKernelGGL((gemm_w4_kernel<true, true>), grid, dim3(kW4Threads), 0, stream, g);
-  else if (u) hipLaunchKernelGGL((gemm_w4_kernel<true, false>), grid, dim3(kW4Threads), 0, stream, g);
-  else if (m) hipLaunchKernelGGL((gemm_w4_kernel<false, true>), grid, dim3(kW4Threads), 0, stream, g);
-  else hipLaunchKernelGGL((gemm_w4_kernel<false, false>), grid, dim3(kW4Threads), 0, stream, g);
+  if (u && m) launch_w4<true, true>(g, large, stream);
+  else if (u) launch_w4<true, false>(g, large, stream);
+  else if (m) launch_w4<false, true>(g, large, stream);
+  else launch_w4<false, false>(g, large, stream);
   return hipGetLastError();
 }
 

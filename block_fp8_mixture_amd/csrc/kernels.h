@@ -103,6 +103,7 @@ struct W4Args {
   int seg_cap;
   int num_experts;
   int row_cap;
+  int max_rows_per_expert;  // host bound on counts[e]: selects the kernels, never the result
   int n;
   int k;
   uint16_t* c;

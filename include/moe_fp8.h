@@ -251,17 +251,20 @@ moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, m
  *              moe_align produces them; > 0: the batched masked-M layout
  *              (expert_counts is masked_m, expert_offsets is not read, expert
  *              e's rows start at e*expert_cap, row_cap = num_experts*expert_cap)
+ *   max_rows_per_expert  host-side bound on any counts[e] (0 = row_cap); it
+ *              only selects which kernels are launched, never the result
  *   c          device BF16 [row_cap, n]; only live rows written
  * Errors: INVALID_ARG (n or k not positive multiples of 128, null pointers,
  * a_row_div < 1, unknown fmt, a_rows < 1 with rows to compute, a batched
- * row_cap other than num_experts*expert_cap); UNSUPPORTED (num_experts above
+ * row_cap other than num_experts*expert_cap, max_rows_per_expert < 0); UNSUPPORTED (num_experts above
  * 1024, a_rows * k or n * k at or above 2^32). */
 moe_status moe_grouped_gemm_mxfp4(const uint8_t* a, const void* a_scales, moe_scale_fmt fmt,
                                   int32_t a_rows, const int32_t* a_row_map, int32_t a_row_div,
                                   const uint8_t* w, const uint8_t* w_scales,
                                   const int32_t* expert_counts, const int32_t* expert_offsets,
                                   int32_t expert_cap, int32_t num_experts, int32_t row_cap,
-                                  int32_t n, int32_t k, uint16_t* c, void* stream);
+                                  int32_t max_rows_per_expert, int32_t n, int32_t k, uint16_t* c,
+                                  void* stream);
 
 /* Row-tile heights of the two GEMM kernels, for interpreting tiles_visited:
  * experts with at most MOE_GEMM_STREAM_MAX_ROWS live rows are computed by

@@ -287,8 +287,8 @@ def test_mxfp4_gemm_validation(lib):
     f = lib.moe_grouped_gemm_mxfp4
 
     def call(n=256, k=256, fmt=0, div=1, e=4, rc=64, cap=0, a=FAKE, c=FAKE, w=FAKE, ws=FAKE,
-             counts=FAKE, offsets=FAKE, a_rows=64):
-        return f(a, FAKE, fmt, a_rows, NULL, div, w, ws, counts, offsets, cap, e, rc, n, k, c, NULL)
+             counts=FAKE, offsets=FAKE, a_rows=64, mr=0):
+        return f(a, FAKE, fmt, a_rows, NULL, div, w, ws, counts, offsets, cap, e, rc, mr, n, k, c, NULL)
     assert call(n=200) == INVALID
     assert call(k=64) == INVALID
     assert call(fmt=7) == INVALID
@@ -303,6 +303,7 @@ def test_mxfp4_gemm_validation(lib):
     assert call(a_rows=0) == INVALID              # rows to compute but no A rows
     assert call(cap=16, rc=63) == INVALID         # batched: row_cap must be E * cap
     assert call(cap=-1) == INVALID
+    assert call(mr=-1) == INVALID
     assert call(rc=0, a=NULL, c=NULL) == OK
 
 
