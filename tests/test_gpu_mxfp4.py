@@ -190,3 +190,47 @@ def test_mxfp4_layer_matches_oracle(run):
                                rounding=rounding, weight_fmt="mxfp4")
     err = assert_bf16_close(got[toks], ref, "layer")
     say(f"  layer max err / max|ref| = {err:.3e}")
+
+
+@pytest.mark.parametrize("gather", [False, True])
+def test_mxfp4_gemm_full_size_sampled(gather):
+    # The 4096-token layer's FC1 shape (32 experts of about 1024 rows, N 4096,
+    # K 7168) through the tiled kernel, checked on whole 64 x 128 tiles of
+    # several experts, row tiles and column tiles (the first, the last and a
+    # ragged one) against the oracle.
+    g = np.random.default_rng(21)
+    e_n, n, k = 32, 4096, 7168
+    cnt = g.integers(900, 1150, e_n)
+    counts, offsets = _routing_layout(cnt)
+    row_cap = int(offsets[-1])
+    a_rows = 4096 if gather else row_cap
+    x = g.standard_normal((a_rows, k)).astype(np.float32)
+    aq, asc = oracle.quantize_groups(x, "fp32")
+    wp = g.integers(0, 256, size=(e_n, n, k // 2), dtype=np.uint8)
+    ws = g.integers(117, 122, size=(e_n, n, k // 32)).astype(np.uint8)
+    row_map = None
+    if gather:
+        row_map = np.full(row_cap, -1, np.int32)
+        for e in range(e_n):
+            row_map[offsets[e]:offsets[e] + counts[e]] = g.integers(0, a_rows * 8, counts[e])
+    say(f"mxfp4 gemm full size gather={gather} row_cap={row_cap}")
+    out = torch.full((row_cap, n), POISON_BF16, dtype=torch.int16, device=dev())
+    moe.moe_grouped_gemm_mxfp4(up(aq), up(asc), "fp32", up(wp), up(ws), up(counts), up(offsets),
+                               row_cap, a_row_map=None if row_map is None else up(row_map),
+                               a_row_div=8, out=out)
+    torch.cuda.synchronize()
+    got = down(out)
+    for e in (0, 13, e_n - 1):
+        c = int(counts[e])
+        for mt in sorted({0, (c - 1) // 64, c // 128}):
+            r0 = int(offsets[e]) + 64 * mt
+            rows = np.arange(r0, min(r0 + 64, int(offsets[e]) + c))
+            src = rows if row_map is None else row_map[rows] // 8
+            for n0 in (0, 2048, n - 128):
+                ref = oracle.gemm_rows_mxfp4(aq[src], oracle.scales_to_f64(asc[:, src], "fp32"),
+                                             wp[e, n0:n0 + 128], ws[e, n0:n0 + 128])
+                assert_bf16_close(got[rows, n0:n0 + 128], ref, f"expert {e} rows {r0} cols {n0}")
+    # rows past each expert's count stay untouched
+    for e in (0, e_n - 1):
+        pad = np.arange(int(offsets[e]) + int(counts[e]), int(offsets[e + 1]))
+        assert np.all(got[pad] == POISON_BF16)
