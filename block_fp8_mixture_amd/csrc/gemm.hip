@@ -853,11 +853,132 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     // loads clamped, unused data and skips its compute, so every path issues
     // the same vector-memory sequence). Stage j uses buffer j % 4; block
     // kb's token scales use buffer kb % 2.
+    if constexpr (TNT == 256) {
+      // Ping-pong. The two waves that share a SIMD (w and w + 4) take turns:
+      // while one issues the MFMAs of its stage (raised issue priority), the
+      // other reads its next stage's fragments from LDS and issues the
+      // direct-to-LDS loads, so the matrix core is not left idle while a wave
+      // waits on LDS or on the address unit. Every phase ends at a workgroup
+      // barrier; group 1 (waves 4..7) runs one phase behind group 0, which
+      // costs each group one extra barrier (before the loop for group 1,
+      // after it for group 0).
+      //
+      // L(j): stage j's fragments into registers; at a block start the
+      // block's scale ratios; the loads of stage j+3 (+ its token scales when
+      // it starts a block); then this wave's loads of stage j+1 (and the
+      // scales issued with it) have landed once 9 loads remain (stages j+2
+      // and j+3, one of which starts a block); at j odd, group 0 publishes
+      // the token ratios of block (j+1)/2.
+      // M(j): the 8 MFMAs of stage j, at a block start each accumulator
+      // rescaled just before its MFMA (16 multiplies between MFMAs).
+      //
+      // Buffers: stage j's slot j % 4 is refilled with stage j+4 by L(j+1);
+      // its last reader, group 1's L(j), ended one phase earlier. Block kb's
+      // ratios (slot kb % 2) are written in L(2kb-1) by group 0 and read in
+      // L(2kb) by both groups; the next writer of the slot is L(2kb+3).
+      const bool grp1 = wave >= 4;
+      Frag af[2], wf[WT];
+      float ratio0 = 1.0f, ratio1 = 1.0f;
+      auto lphase = [&](int j, const uint8_t* cur, uint8_t* fill, const float* rt_cur,
+                        uint32_t* sr_fill, const uint32_t* sr_next, float* rt_next, auto even_t) {
+        constexpr bool even = decltype(even_t)::value;
+        if (wave_on && j < NS) {
+          const int c0 = 2 * (lane >> 5);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int r = wm * 64 + tt * 32 + (lane & 31);
+            af[tt].u[0] = *reinterpret_cast<const uint4*>(cur + swz(r, c0));
+            af[tt].u[1] = *reinterpret_cast<const uint4*>(cur + swz(r, c0 + 1));
+          }
+#pragma unroll
+          for (int wt = 0; wt < WT; ++wt) {
+            const int r = wn * WN + wt * 32 + (lane & 31);
+            wf[wt].u[0] = *reinterpret_cast<const uint4*>(cur + kStageA + swz(r, c0));
+            wf[wt].u[1] = *reinterpret_cast<const uint4*>(cur + kStageA + swz(r, c0 + 1));
+          }
+          if constexpr (even) {
+            const int kb = j >> 1;
+            const float sw = fmaxf(s_ws[(wn * WN) / kGroup][kb], kScaleFloor);
+            const float q = sw_norm * __builtin_amdgcn_rcpf(sw);
+            sw_norm = sw;
+            const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
+            ratio0 = r2.x * q;
+            ratio1 = r2.y * q;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(j + 3, fill);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!even) issue_s((j + 3) >> 1, sr_fill);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS + 1));
+        if constexpr (!even) {
+          if (!grp1) {
+            const int kb_next = (j + 1) >> 1;
+            const float t = decode_sa(sr_next[tok]);
+            const float r = tok_prev * __builtin_amdgcn_rcpf(t);
+            if (kb_next < KB) {
+              rt_next[(tok & 31) * 8 + (tok >> 5)] = r;
+              if (kb_next == KB - 1) s_sl[(tok & 31) * 8 + (tok >> 5)] = t;
+            }
+            tok_prev = t;
+          }
+        }
+      };
+      auto mphase = [&](int j, auto even_t) {
+        constexpr bool even = decltype(even_t)::value;
+        if (!wave_on || j >= NS) return;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            if constexpr (even) acc[wt][tt] = acc[wt][tt] * (tt == 0 ? ratio0 : ratio1);
+            acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[wt].v, af[tt].v, acc[wt][tt],
+                                                                           0, 0, 0, 0, 0, 0);
+          }
+        if constexpr (even) {
+#pragma unroll
+          for (int i = 0; i < 2 * WT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU: one accumulator's rescale
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // its MFMA
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      const std::true_type ev;
+      const std::false_type od;
+      if (grp1) lds_barrier();
+      for (int j = 0; j < NS; j += 4) {
+        lphase(j, s_st0, s_st3, s_rt[0], s_sr1, s_sr0, s_rt[0], ev);
+        lds_barrier();
+        mphase(j, ev);
+        lds_barrier();
+        lphase(j + 1, s_st1, s_st0, s_rt[0], s_sr0, s_sr1, s_rt[1], od);
+        lds_barrier();
+        mphase(j + 1, od);
+        lds_barrier();
+        lphase(j + 2, s_st2, s_st1, s_rt[1], s_sr0, s_sr1, s_rt[1], ev);
+        lds_barrier();
+        mphase(j + 2, ev);
+        lds_barrier();
+        lphase(j + 3, s_st3, s_st2, s_rt[1], s_sr1, s_sr0, s_rt[0], od);
+        lds_barrier();
+        mphase(j + 3, od);
+        lds_barrier();
+      }
+      if (!grp1) lds_barrier();
+    } else {
     for (int j = 0; j < NS; j += 4) {
       stage(j, s_st0, s_st3, s_sr0, s_rt[0], s_rt[0], s_sr1, false, true, false);
       stage(j + 1, s_st1, s_st0, s_sr1, s_rt[1], s_rt[0], s_sr0, true, false, true);
       stage(j + 2, s_st2, s_st1, s_sr1, s_rt[1], s_rt[1], s_sr0, false, true, false);
       stage(j + 3, s_st3, s_st2, s_sr0, s_rt[0], s_rt[1], s_sr1, true, false, true);
+    }
     }
     __builtin_amdgcn_s_waitcnt(0);  // trailing loads of this tile done before any stage is reused
     __syncthreads();
