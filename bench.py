@@ -678,8 +678,8 @@ def main():
                    "activation": ac, "span_us": round(m, 2), "p10_us": round(pct(spans, 0.1), 2),
                    "p90_us": round(pct(spans, 0.9), 2), "events_us": round(statistics.median(evs), 2),
                    "weights": wfmt,
-                   "path": ("batched masked-M" if cap else "general" if wfmt != "e4m3" else
-                            "one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter)
+                   "path": ("batched masked-M" if cap else
+                            "one launch" if moe.decode_layer_applies(tc, cfg_l.topk, cfg_l.hidden, cfg_l.inter, wfmt)
                             else "general")}
             if cap:
                 ent["expert_cap"] = cap

@@ -22,9 +22,12 @@ DECODE_LIMITS = {"max_pairs": 64, "fc2_row_bytes": 24576, "fc2_max_scales": 256,
                  "layer_token_bytes": 61440, "layer_max_scales": 512}
 
 
-def decode_layer_applies(t_cap, topk, hidden, inter):
-    """Whether moe_forward runs this problem as its one-launch decode layer."""
+def decode_layer_applies(t_cap, topk, hidden, inter, weight_fmt="e4m3"):
+    """Whether moe_forward runs this problem (aligned layout) as its one-launch
+    decode layer; with MXFP4 weights H and I must also be multiples of 256."""
     d, p = DECODE_LIMITS, t_cap * topk
+    if _weight_fmt(weight_fmt) == 1 and (hidden % 256 or inter % 256):
+        return False
     return (1 <= p <= d["max_pairs"] and p * (inter + 16) <= d["fc2_row_bytes"]
             and p * (inter // 128) <= d["fc2_max_scales"] and hidden % 16 == 0
             and t_cap * (hidden + 16) <= d["layer_token_bytes"]

@@ -366,9 +366,11 @@ moe_status moe_workspace_plan(const moe_problem* p, moe_workspace_layout* L) {
   L->hq = take(R * I);
   L->hs = take((I / 128) * R * sb);
   L->y = take(R * H * 2);
-  // The decode path serves the aligned layout and FP8 weights only.
-  const bool decode = !batched && p->weight_fmt == MOE_WEIGHT_E4M3 &&
-                      moe::down_combine_fits(p->t_cap, p->topk, p->inter);
+  // The decode path serves the aligned layout; MXFP4 weights take only its
+  // one-launch layer, whose stages need H and I multiples of 256.
+  const bool decode = !batched && moe::down_combine_fits(p->t_cap, p->topk, p->inter) &&
+                      (p->weight_fmt == MOE_WEIGHT_E4M3 ||
+                       moe::decode_layer_fits_fmt(p->t_cap, p->topk, p->hidden, p->inter, p->weight_fmt));
   L->act = decode ? take(R * I * 4) : 0;
   L->status = take(static_cast<size_t>(moe::kDlMaxGrid) * 4);
   L->overflow = take(4);
@@ -392,7 +394,7 @@ moe::DownCombineArgs down_combine_args(const moe_problem* p, const moe_tensors* 
   d.act = reinterpret_cast<const float*>(ws + L.act);
   d.fmt = p->scale_fmt;
   d.w = t->w2;
-  d.w_scales = static_cast<const float*>(t->w2_scales);
+  d.w_scales = t->w2_scales;
   d.counts = reinterpret_cast<const int32_t*>(ws + L.expert_counts);
   d.offsets = reinterpret_cast<const int32_t*>(ws + L.expert_offsets);
   d.row_to_pair = reinterpret_cast<const int32_t*>(ws + L.row_to_pair);
@@ -430,7 +432,8 @@ moe::DecodeFc1Args fc1_decode_args(const moe_problem* p, const moe_tensors* t,
   f.inter = p->inter;
   f.fmt = p->scale_fmt;
   f.w = t->w1;
-  f.w_scales = static_cast<const float*>(t->w1_scales);
+  f.w_scales = t->w1_scales;
+  f.weight_fmt = p->weight_fmt;
   f.act = p->act;
   f.act_limit = p->clamp_limit;
   f.counts = reinterpret_cast<int32_t*>(ws + L.expert_counts);
@@ -452,7 +455,8 @@ moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* work
   moe_workspace_layout L;
   const moe_status st = moe_workspace_plan(p, &L);
   if (st != MOE_OK) return st;
-  if (!(L.act < L.status) || !moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter))
+  if (!(L.act < L.status) || p->weight_fmt != MOE_WEIGHT_E4M3 ||
+      !moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter))
     return MOE_ERR_UNSUPPORTED;
   if (!t || !workspace) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < L.total) return MOE_ERR_CAPACITY;
@@ -523,7 +527,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
   const int pairs = static_cast<int>(pairs64);
 
   hipError_t e = hipSuccess;
-  if (decode && moe::decode_layer_fits(p->t_cap, p->topk, p->hidden, p->inter) &&
+  if (decode && moe::decode_layer_fits_fmt(p->t_cap, p->topk, p->hidden, p->inter, p->weight_fmt) &&
       moe::decode_layer_grid(moe::decode_layer_wide(p->t_cap, p->hidden)) > 0) {
     // The whole layer in one launch.
     moe::DecodeLayerArgs a;
@@ -533,7 +537,7 @@ static moe_status forward_impl(const moe_problem* p, const moe_workspace_layout&
     a.spin_limit = moe::decode_layer_spin_limit();
     return from_hip(moe::launch_decode_layer(a, s));
   }
-  if (decode && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {
+  if (decode && p->weight_fmt == MOE_WEIGHT_E4M3 && moe::fc1_decode_fits(p->t_cap, p->topk, p->hidden, p->inter)) {
     // Routing, activation quantization and FC1 with SiLU(gate) * up in one
     // launch, then FC2 with the combine.
     e = moe::launch_fc1_decode(fc1_decode_args(p, t, L, ws), s);

@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kThreads = 128;
 constexpr int kCols = kThreads * 8;  // output columns per block
-constexpr int kMaxTopk = 64;
 constexpr int kKChunk = 8;           // top-k rows whose loads are in flight together
 
 // Block b computes columns [cb * kCols, cb * kCols + kCols) of token t, with

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void down_combine_kernel(DownCombin
   t.n_rows = __builtin_amdgcn_readfirstlane(s_nrows);
   t.n_pairs = PQ;
 
-  Fc2Stream st;
+  Fc2Stream<false> st;
   st.init(p.w, p.w_scales, t, s_ring + wave * (kDecDepth * kDecStage), N, I, wave, lane);
   int cb = blockIdx.x;  // < n_cb: the grid has at most n_cb workgroups
   st.start(cb * 16, 0, kDecPreStages);

@@ -21,6 +21,9 @@
 //     tasks' 2 KB weight stages and their two weight block scales through a
 //     private LDS ring by direct-to-LDS loads (whole 128-byte lines); a wave
 //     only waits for its own loads, so the loop has no workgroup barrier.
+//     With MXFP4 weights (one-launch layer, W4) a stage is the same 16 rows x
+//     128 packed bytes, i.e. two K blocks, with the rows' E8M0 scale bytes
+//     as its third load (fc2_decode.h).
 //     Token fragments come from the resident LDS copy. The ring is 6 stages
 //     deep, or 4 in the one-launch layer's variant for up to 60 KB of token
 //     codes (the LDS the two stages free holds them).
@@ -90,10 +93,12 @@ __device__ __forceinline__ bool flag_wait(const unsigned* a, unsigned v, int lim
 
 // DEPTH: stages in a wave's ring, kDecDepth; or 4 in the wide variant of the
 // one-launch layer, whose LDS then holds kF1TokBytesWide of token codes.
-template <int FMT, bool FUSED, int DEPTH>
+// W4: MXFP4 weights (one-launch layer only).
+template <int FMT, bool FUSED, int DEPTH, bool W4>
 __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerArgs a) {
   constexpr bool kWide = DEPTH != kDecDepth;
   static_assert(!kWide || (DEPTH == 4 && FUSED), "the wide variant: one-launch layer, 4 stages");
+  static_assert(!W4 || FUSED, "MXFP4 weights: one-launch layer only");
   constexpr int kTokBytes = kWide ? kF1TokBytesWide : kF1TokBytes;
   constexpr int kMaxScales = kWide ? kF1MaxScalesWide : kF1MaxScales;
   constexpr int kXLoads = kTokBytes / 8 / kF1Threads;  // 16-byte (8-value) activation loads per thread
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const DownCombineArgs& q = a.f2;
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kF1Waves * DEPTH * kF1Stage];
   __shared__ __attribute__((aligned(16))) uint8_t s_x[kTokBytes];  // codes, row stride H + 16
-  __shared__ float s_xs[kMaxScales];    // token scale of (token, K block) at t * KB + kb
+  __shared__ __attribute__((aligned(16))) float s_xs[kMaxScales];  // token scale of (token, K block) at t * KB + kb
   __shared__ int s_e[kDcMaxPairs];        // live entry (in expert order) -> expert
   __shared__ int s_cnt[kDcMaxPairs];      //   its live rows
   __shared__ int s_c0[kDcMaxPairs];       //   its first compact row
@@ -261,6 +266,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   // K; S is the largest power of two up to 8 that still leaves at most one
   // task per group of S waves and divides the K blocks.
   const int n_rb = I / 8;  // 16-row blocks (8 gate + 8 up rows)
+  const int KS = W4 ? KB / 2 : KB;  // weight stages per task (MXFP4: two K blocks each)
   const int n_tasks = s_tp[n_live] * n_rb;
   const int G1 = gridDim.x;
   // (blockIdx.x + 1) * n_tasks < 2^32: n_tasks <= 64 tiles x I / 8.
@@ -268,12 +274,12 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   const int t_hi = static_cast<int>((blockIdx.x + 1) * static_cast<uint32_t>(n_tasks) / static_cast<uint32_t>(G1));
   const int wg_max = (n_tasks + G1 - 1) / G1;  // tasks of the fullest workgroup
   int lgS = 0;  // S = 2^lgS
-  while (lgS < 3 && (wg_max << (lgS + 1)) <= kF1Waves && (KB & ((2 << lgS) - 1)) == 0) ++lgS;
+  while (lgS < 3 && (wg_max << (lgS + 1)) <= kF1Waves && (KS & ((2 << lgS) - 1)) == 0) ++lgS;
   lgS = __builtin_amdgcn_readfirstlane(lgS);
   const int S = 1 << lgS;
   const int NG = kF1Waves >> lgS;  // groups of S waves in a workgroup
   const int gl = wave >> lgS;      // this wave's group
-  const int kbs = KB >> lgS;       // K blocks of a share
+  const int kbs = KS >> lgS;       // weight stages of a share
   const int kb_lo = (wave & (S - 1)) * kbs, kb_hi = kb_lo + kbs;
   const int my_tasks = gl < t_hi - t_lo ? ((t_hi - t_lo - 1 - gl) >> (3 - lgS)) + 1 : 0;
   const int total = my_tasks * kbs;  // stages of this wave
@@ -312,22 +318,32 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
   int i_task = t_lo + gl, i_kb = kb_lo;
   const uint8_t* i_w0 = p.w + lane * 16;
   const uint8_t* i_w1 = p.w + lane * 16;
-  const uint8_t* i_s = reinterpret_cast<const uint8_t*>(p.w_scales);
+  const uint8_t* i_s = static_cast<const uint8_t*>(p.w_scales);
   auto i_set = [&]() {
     const Task k = decode_task(i_task);
     const int e = __builtin_amdgcn_readlane(e_lane, k.ent);
     const int jg = k.rb * 8;  // first gate column
-    const uint8_t* we = p.w + static_cast<int64_t>(e) * N * H;
-    i_w0 = we + static_cast<int64_t>(jg + grow) * H + chunk_lo;
-    i_w1 = we + static_cast<int64_t>(I + jg + grow) * H + chunk_hi;
-    // Lane 1 loads the up rows' block scale, every other lane the gate rows'.
-    const int sb = lane == 1 ? (I + jg) / kGroup : jg / kGroup;
-    i_s = reinterpret_cast<const uint8_t*>(p.w_scales + (static_cast<int64_t>(e) * (N / kGroup) + sb) * KB);
+    const int64_t rs = W4 ? H / 2 : H;  // bytes per weight row
+    const uint8_t* we = p.w + static_cast<int64_t>(e) * N * rs;
+    i_w0 = we + static_cast<int64_t>(jg + grow) * rs + chunk_lo;
+    i_w1 = we + static_cast<int64_t>(I + jg + grow) * rs + chunk_hi;
+    if constexpr (W4) {
+      // Lane 2r + h (and 32 + 2r + h) loads scale bytes 4h..4h+3 of slab row
+      // r: gate rows 0..7, up rows 8..15.
+      const int r = (lane & 31) >> 1;
+      const int wr = r < 8 ? jg + r : I + jg + r - 8;
+      i_s = static_cast<const uint8_t*>(p.w_scales) + (static_cast<int64_t>(e) * N + wr) * (H / kMxBlock) + (lane & 1) * 4;
+    } else {
+      // Lane 1 loads the up rows' block scale, every other lane the gate rows'.
+      const int sb = lane == 1 ? (I + jg) / kGroup : jg / kGroup;
+      i_s = reinterpret_cast<const uint8_t*>(static_cast<const float*>(p.w_scales) +
+                                             (static_cast<int64_t>(e) * (N / kGroup) + sb) * KB);
+    }
   };
   auto issue_stage = [&](uint8_t* st) {
     __builtin_amdgcn_global_load_lds(i_w0 + i_kb * kGroup, (lds_void*)(st), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(i_w1 + i_kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(i_s + i_kb * 4, (lds_void*)(st + kF1StageW), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(i_s + i_kb * (W4 ? 8 : 4), (lds_void*)(st + kF1StageW), 4, 0, 0);
   };
   auto advance = [&]() {
     if (++i_kb == kb_hi) {
@@ -368,7 +384,8 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
 
   // ---- 3. stream: wait for stage s, refill the slot of stage s - 1, compute s
   const int tok = lane & 15;
-  const int c0f = 2 * (lane >> 4);  // fragment chunks c0f, c0f + 1 of a 128-byte K block
+  // fragment chunks c0f, c0f + 1 of a 128-byte K block (MXFP4: token chunks g, g + 4)
+  const int c0f = W4 ? (lane >> 4) : 2 * (lane >> 4);
   const uint32_t x_base = lds_addr(s_x) + c0f * 16;
   const uint32_t xs_base = lds_addr(s_xs);
   int c_task = t_lo + gl, c_kb = kb_lo, slot = 0, c_iter = 0;
@@ -398,16 +415,24 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
       advance();
     }
     const uint32_t st = lds_addr(ring + slot * kF1Stage);
-    union {
-      uint4 u[2];
-      v8i v;
-    } wf, af;
-    float sa, sw;
-    const uint32_t ta = x_base + c_t * XS + c_kb * kGroup;
-    lds_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
-                  xs_base + (c_t * KB + c_kb) * 4, st + kF1StageW + ((lane >> 5) << 2), wf.u[0],
-                  wf.u[1], af.u[0], af.u[1], sa, sw);
-    acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
+    if constexpr (W4) {
+      // stage c_kb holds K blocks 2 c_kb and 2 c_kb + 1
+      W4Frags f;
+      lds_read_stage_w4(st + swz128(tok, c0f), st + swz128(tok, 4 + c0f), st + kF1StageW + 8 * tok + c0f,
+                        x_base + c_t * XS + c_kb * 2 * kGroup, xs_base + (c_t * KB + 2 * c_kb) * 4, f);
+      acc = w4_stage_step(f, acc);
+    } else {
+      union {
+        uint4 u[2];
+        v8i v;
+      } wf, af;
+      float sa, sw;
+      const uint32_t ta = x_base + c_t * XS + c_kb * kGroup;
+      lds_read_stage(st + swz128(tok, c0f), st + swz128(tok, c0f + 1), ta, ta + 16,
+                    xs_base + (c_t * KB + c_kb) * 4, st + kF1StageW + ((lane >> 5) << 2), wf.u[0],
+                    wf.u[1], af.u[0], af.u[1], sa, sw);
+      acc = fma4(mfma_fp8(wf.v, af.v), sa * sw, acc);
+    }
     if (++c_kb == kb_hi) {
       // This wave's share of the task is done. With S > 1 the partial goes to
       // LDS and the last share of the group to arrive adds the S partials in
@@ -487,7 +512,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void fc1_decode_kernel(DecodeLayerAr
     uint8_t* const s_tok = s_x;                             // FC2 input codes, row stride I + 16
     float* const s_sa = s_xs;                               // their scales
     float* const s_slot = reinterpret_cast<float*>(s_part);  // pair q's 16 columns
-    Fc2Stream st;
+    Fc2Stream<W4> st;
     st.init(q.w, q.w_scales, t, ring, H, I, wave, lane);
     int cb = blockIdx.x;
     const bool has_cb = cb < n_cb;  // uniform
@@ -569,12 +594,13 @@ hipError_t launch_fc1_decode(const DecodeFc1Args& a, hipStream_t stream) {
   DecodeLayerArgs l{};
   l.f1 = a;
   const dim3 grid(static_cast<unsigned>(device_cu_count()));
+  if (a.weight_fmt != kWeightE4m3) return hipErrorInvalidValue;  // FC1 alone: FP8 weights
   if (a.fmt == kFp32)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32, false, kDecDepth, false>), grid, dim3(kF1Threads), 0, stream, l);
   else if (a.fmt == kFp32Pow2)
-    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, false, kDecDepth, false>), grid, dim3(kF1Threads), 0, stream, l);
   else
-    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, false, kDecDepth>), grid, dim3(kF1Threads), 0, stream, l);
+    hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, false, kDecDepth, false>), grid, dim3(kF1Threads), 0, stream, l);
   return hipGetLastError();
 }
 
@@ -589,8 +615,8 @@ int decode_layer_grid(bool wide) {
   if (v != 0) return v > 0 ? v : 0;
   int cus = 0, occ = 0;
   const hipError_t e =
-      wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, 4>, kF1Threads, 0)
-           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, kDecDepth>, kF1Threads, 0);
+      wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, 4, false>, kF1Threads, 0)
+           : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fc1_decode_kernel<kFp32, true, kDecDepth, false>, kF1Threads, 0);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       e != hipSuccess || cus < 1 || cus > kDlMaxGrid || occ < 1)
     v = -1;
@@ -604,22 +630,29 @@ hipError_t launch_decode_layer(const DecodeLayerArgs& a, hipStream_t stream) {
   if (a.f1.t_cap == 0) return hipSuccess;
   const bool wide = decode_layer_wide(a.f1.t_cap, a.f1.hidden);
   const int grid = decode_layer_grid(wide);
-  if (!decode_layer_fits(a.f1.t_cap, a.f1.topk, a.f1.hidden, a.f1.inter) || grid < 1 ||
-      a.f1.num_experts > kMaxExperts || a.f1.num_experts < 1 || a.f1.align_rows < 1)
+  if (!decode_layer_fits_fmt(a.f1.t_cap, a.f1.topk, a.f1.hidden, a.f1.inter, a.f1.weight_fmt) ||
+      grid < 1 || a.f1.num_experts > kMaxExperts || a.f1.num_experts < 1 || a.f1.align_rows < 1)
     return hipErrorInvalidValue;
-  auto launch = [&](auto depth) {
+  auto launch = [&](auto depth, auto w4) {
     constexpr int D = decltype(depth)::value;
+    constexpr bool W = decltype(w4)::value;
     if (a.f1.fmt == kFp32)
-      hipLaunchKernelGGL((fc1_decode_kernel<kFp32, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+      hipLaunchKernelGGL((fc1_decode_kernel<kFp32, true, D, W>), dim3(grid), dim3(kF1Threads), 0, stream, a);
     else if (a.f1.fmt == kFp32Pow2)
-      hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+      hipLaunchKernelGGL((fc1_decode_kernel<kFp32Pow2, true, D, W>), dim3(grid), dim3(kF1Threads), 0, stream, a);
     else
-      hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, true, D>), dim3(grid), dim3(kF1Threads), 0, stream, a);
+      hipLaunchKernelGGL((fc1_decode_kernel<kUe8m0, true, D, W>), dim3(grid), dim3(kF1Threads), 0, stream, a);
   };
-  if (wide)
-    launch(std::integral_constant<int, 4>{});
+  auto by_depth = [&](auto w4) {
+    if (wide)
+      launch(std::integral_constant<int, 4>{}, w4);
+    else
+      launch(std::integral_constant<int, kDecDepth>{}, w4);
+  };
+  if (a.f1.weight_fmt == kWeightMxfp4)
+    by_depth(std::true_type{});
   else
-    launch(std::integral_constant<int, kDecDepth>{});
+    by_depth(std::false_type{});
   return hipGetLastError();
 }
 

@@ -21,6 +21,14 @@
 //    goes to the LDS slot of its (token, k) pair.
 // Then out[t, cols] = BF16(sum over ascending k of w[t, k] * slot), with
 // fp32 FMAs in the arithmetic and order of moe_topk_combine.
+//
+// MXFP4 weights (vLLM PR #59128's description names FP4 weights; read as
+// OCP MXFP4: E2M1 codes, two per byte with the even K element in the low
+// nibble, one E8M0 scale byte per 32 along K) keep the stage geometry: 16
+// weight rows x 128 packed bytes are two 128-wide K blocks, and the third
+// load brings the rows' 8 scale bytes of those 256 K values. Per K block one
+// v_mfma_scale_f32_16x16x128_f8f6f4 applies the weight scales in the matrix
+// core; then acc += t * sa.
 #pragma once
 
 #include "device_common.h"
@@ -37,6 +45,71 @@ constexpr int kDecStage = kDecStageW + 256;            // + block scale(s): 64 x
 constexpr int kDecLoads = 3;                           // direct-to-LDS loads per wave and stage
 constexpr int kDecTiles = kDcMaxPairs / kStreamTileM;  // 16-token tiles of one expert, at most
 constexpr int kDecPreStages = 2;  // stream-start stages issued before the FC2 input rows are loaded
+
+// One 128-wide K block with MXFP4 weights on v_mfma_scale_f32_16x16x128_f8f6f4
+// (operand layout measured on gfx950 with in-bounds probes): the E2M1 weights
+// are operand A (format 4): lane l holds weight row l % 16 and the K values
+// [32 g, 32 g + 32) of the block (g = l / 16), i.e. 16-byte chunk g of the
+// row's 64 packed bytes, with that MX block's scale byte as its A scale. The
+// E4M3 tokens are operand B: lane l holds token l % 16 and, in that K order,
+// the block's values [16 g, 16 g + 16) and [64 + 16 g, 80 + 16 g): 16-byte
+// chunks g and 4 + g of its 128 codes (not the chunks 2g, 2g + 1 that the
+// FP8 x FP8 instruction pairs). The B scale is 1.0 (E8M0 127). The output
+// layout is the FP8 instruction's: token l % 16, weight row 4 (l / 16) + v.
+__device__ __forceinline__ v4f mfma_w4(uint4 w, uint4 x0, uint4 x1, uint32_t sc) {
+  const v8i a = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                 static_cast<int>(w.w), 0, 0, 0, 0};
+  const v8i b = {static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z),
+                 static_cast<int>(x0.w), static_cast<int>(x1.x), static_cast<int>(x1.y),
+                 static_cast<int>(x1.z), static_cast<int>(x1.w)};
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 0, 0, static_cast<int>(sc), 0, 127);
+}
+
+// Reads of an MXFP4 stage for one token tile, all under one wait (assembly,
+// as lds_read_stage): per K block h = 0, 1 of the stage the weight fragment
+// (at w0, w1) and its scale byte (at sb + 4 h), the token fragments (at t,
+// t + 64 for h = 0; t + 128, t + 192 for h = 1) and the two token scales
+// (adjacent floats at sa, 8-byte aligned).
+struct W4Frags {
+  uint4 w0, w1, x00, x01, x10, x11;
+  uint32_t s0, s1;
+  uint2 sa;  // the two token scales' bits
+};
+__device__ __forceinline__ void lds_read_stage_w4(uint32_t w0, uint32_t w1, uint32_t sb, uint32_t t,
+                                                  uint32_t sa, W4Frags& f) {
+  asm volatile(
+      "ds_read_b128 %0, %9\n\t"
+      "ds_read_b128 %1, %10\n\t"
+      "ds_read_u8 %2, %11\n\t"
+      "ds_read_u8 %3, %11 offset:4\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %12 offset:64\n\t"
+      "ds_read_b128 %6, %12 offset:128\n\t"
+      "ds_read_b128 %7, %12 offset:192\n\t"
+      "ds_read_b64 %8, %13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.w0), "=&v"(f.w1), "=&v"(f.s0), "=&v"(f.s1), "=&v"(f.x00), "=&v"(f.x01), "=&v"(f.x10),
+        "=&v"(f.x11), "=&v"(f.sa)
+      : "v"(w0), "v"(w1), "v"(sb), "v"(t), "v"(sa));
+}
+// Token fragments and scales of a further token tile of an MXFP4 stage.
+__device__ __forceinline__ void lds_read_tile_w4(uint32_t t, uint32_t sa, W4Frags& f) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:64\n\t"
+      "ds_read_b128 %2, %5 offset:128\n\t"
+      "ds_read_b128 %3, %5 offset:192\n\t"
+      "ds_read_b64 %4, %6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.x00), "=&v"(f.x01), "=&v"(f.x10), "=&v"(f.x11), "=&v"(f.sa)
+      : "v"(t), "v"(sa));
+}
+// The two K blocks of an MXFP4 stage, ascending, into acc.
+__device__ __forceinline__ v4f w4_stage_step(const W4Frags& f, v4f acc) {
+  acc = fma4(mfma_w4(f.w0, f.x00, f.x01, f.s0), __uint_as_float(f.sa.x), acc);
+  return fma4(mfma_w4(f.w1, f.x10, f.x11, f.s1), __uint_as_float(f.sa.y), acc);
+}
 
 // A workgroup's live experts ("entries", in expert order) and their rows
 // ("compact rows", entry after entry), in LDS.
@@ -55,22 +128,25 @@ struct DecodeTables {
 };
 
 // One wave's FC2 weight stream over a column block: the 16 x I slab of every
-// kDecWaves-th entry, one stage per 128-wide K block. Stand-ins (valid
-// addresses) fill the stages past the wave's last one that the stream start
-// issues, so that it always issues (ring depth) - 1 stages.
+// kDecWaves-th entry, one stage per 128-wide K block (per two with MXFP4
+// weights, W4). Stand-ins (valid addresses) fill the stages past the wave's
+// last one that the stream start issues, so that it always issues (ring
+// depth) - 1 stages.
+template <bool W4>
 struct Fc2Stream {
-  const uint8_t* w;       // [E, H, I] E4M3
-  const float* w_scales;  // [E, H/128, I/128]
+  const uint8_t* w;       // [E, H, I] E4M3, or [E, H, I/2] MXFP4
+  const void* w_scales;   // fp32 [E, H/128, I/128], or E8M0 bytes [E, H, I/32]
   const int* list_e;
   uint8_t* ring;
-  int H, I, KB, n_list, wave, total;
+  int H, I, KB, n_list, wave, total;  // KB: stages per entry
   int grow, chunk_lo, chunk_hi;
+  int srow, shalf;  // MXFP4: slab row and half of this lane's 4 scale bytes (lanes 32..63 repeat 0..31)
   int ent, kb;
   const uint8_t* w0;
   const uint8_t* w1;
   const uint8_t* s;
 
-  __device__ __forceinline__ void init(const uint8_t* w_, const float* ws_, const DecodeTables& t,
+  __device__ __forceinline__ void init(const uint8_t* w_, const void* ws_, const DecodeTables& t,
                                        uint8_t* ring_, int H_, int I_, int wave_, int lane) {
     w = w_;
     w_scales = ws_;
@@ -78,7 +154,9 @@ struct Fc2Stream {
     ring = ring_;
     H = H_;
     I = I_;
-    KB = I_ / kGroup;
+    KB = W4 ? I_ / (2 * kGroup) : I_ / kGroup;
+    srow = (lane & 31) >> 1;
+    shalf = lane & 1;
     n_list = t.n_list;
     wave = wave_;
     const int my_n = wave < n_list ? (n_list - 1 - wave) / kDecWaves + 1 : 0;
@@ -94,15 +172,23 @@ struct Fc2Stream {
   }
   __device__ __forceinline__ void set(int n0) {
     const int e = __builtin_amdgcn_readfirstlane(list_e[ent]);
-    const uint8_t* wb = w + (static_cast<int64_t>(e) * H + n0) * I;
-    w0 = wb + static_cast<int64_t>(grow) * I + chunk_lo;
-    w1 = wb + static_cast<int64_t>(grow + 8) * I + chunk_hi;
-    s = reinterpret_cast<const uint8_t*>(w_scales + (static_cast<int64_t>(e) * (H / kGroup) + n0 / kGroup) * KB);
+    const int64_t rs = W4 ? I / 2 : I;  // bytes per weight row
+    const uint8_t* wb = w + (static_cast<int64_t>(e) * H + n0) * rs;
+    w0 = wb + static_cast<int64_t>(grow) * rs + chunk_lo;
+    w1 = wb + static_cast<int64_t>(grow + 8) * rs + chunk_hi;
+    if constexpr (W4)
+      s = static_cast<const uint8_t*>(w_scales) + (static_cast<int64_t>(e) * H + n0 + srow) * (I / kMxBlock) + shalf * 4;
+    else
+      s = reinterpret_cast<const uint8_t*>(static_cast<const float*>(w_scales) +
+                                           (static_cast<int64_t>(e) * (H / kGroup) + n0 / kGroup) * (I / kGroup));
   }
+  // A stage: two loads of 8 rows x 128 bytes and the scales (FP8: the block
+  // scale, every lane; MXFP4: the 16 rows' 8 scale bytes, lane 2r + h
+  // bringing bytes 4h..4h+3 of row r to slot 2r + h).
   __device__ __forceinline__ void issue(uint8_t* st) {
     __builtin_amdgcn_global_load_lds(w0 + kb * kGroup, (lds_void*)(st), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(w1 + kb * kGroup, (lds_void*)(st + 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(s + kb * 4, (lds_void*)(st + kDecStageW), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(s + kb * (W4 ? 8 : 4), (lds_void*)(st + kDecStageW), 4, 0, 0);
   }
   __device__ __forceinline__ void advance(int n0) {
     if (++kb == KB) {
@@ -228,13 +314,15 @@ __device__ __forceinline__ void fc2_quant_rows(const DecodeTables& t, int wave, 
 // stage s, refill the slot of stage s - 1, compute s; after an entry's last
 // K block its live rows' BF16-rounded results go to their pairs' slots.
 // Ends with the wave's loads drained.
-template <int DEPTH>
-__device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const DecodeTables& t,
+template <int DEPTH, bool W4>
+__device__ __forceinline__ void fc2_stream_block(Fc2Stream<W4>& st, int n0, const DecodeTables& t,
                                                  const uint8_t* tok, const float* sa, float* slot,
                                                  int lane) {
   const int KB = st.KB, TS = st.I + 16;
+  const int KG = st.I / kGroup;  // token scales per row
   const int tok16 = lane & 15;
-  const int cf = 2 * (lane >> 4);  // fragment chunks cf, cf + 1 of a 128-byte K block
+  // fragment chunks cf, cf + 1 of a 128-byte K block (MXFP4: token chunks g, g + 4)
+  const int cf = W4 ? (lane >> 4) : 2 * (lane >> 4);
   const uint32_t tok_base = lds_addr(tok) + cf * 16;
   const uint32_t sa_base = lds_addr(sa);
   int e_ent = st.wave, e_kb = 0, slotn = 0;
@@ -262,11 +350,30 @@ __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const De
       st.advance(n0);
     }
     const uint32_t stg = lds_addr(st.ring + slotn * kDecStage);
+    const int n_mt = (e_cnt + kStreamTileM - 1) / kStreamTileM;
+    if constexpr (W4) {
+      // stage e_kb holds K blocks 2 e_kb and 2 e_kb + 1
+      W4Frags f;
+      {
+        const int row = min(e_c0 + tok16, t.n_rows - 1);
+        lds_read_stage_w4(stg + swz128(tok16, cf), stg + swz128(tok16, 4 + cf),
+                          stg + kDecStageW + 8 * tok16 + cf, tok_base + row * TS + e_kb * 2 * kGroup,
+                          sa_base + (row * KG + 2 * e_kb) * 4, f);
+        acc[0] = w4_stage_step(f, acc[0]);
+      }
+#pragma unroll
+      for (int m = 1; m < kDecTiles; ++m) {
+        if (m < n_mt) {
+          const int row = min(e_c0 + m * kStreamTileM + tok16, t.n_rows - 1);
+          lds_read_tile_w4(tok_base + row * TS + e_kb * 2 * kGroup, sa_base + (row * KG + 2 * e_kb) * 4, f);
+          acc[m] = w4_stage_step(f, acc[m]);
+        }
+      }
+    } else {
     union {
       uint4 u[2];
       v8i v;
     } wf, af;
-    const int n_mt = (e_cnt + kStreamTileM - 1) / kStreamTileM;
     float fsa, fsw;
     {
       const int row = min(e_c0 + tok16, t.n_rows - 1);
@@ -284,6 +391,7 @@ __device__ __forceinline__ void fc2_stream_block(Fc2Stream& st, int n0, const De
         lds_read_tile(ta, ta + 16, sa_base + (row * KB + e_kb) * 4, af.u[0], af.u[1], fsa);
         acc[m] = fma4(mfma_fp8(wf.v, af.v), fsa * fsw, acc[m]);
       }
+    }
     }
     if (++e_kb == KB) {  // entry done: BF16-rounded rows to their pairs' slots
 #pragma unroll

@@ -89,6 +89,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
 // codes (the even K element in the low nibble), w_scales [num_experts, n,
 // k/32] E8M0 bytes; everything else as GemmArgs.
 constexpr int kMxBlock = 32;  // weights per E8M0 scale along K
+enum WeightFmt : int { kWeightE4m3 = 0, kWeightMxfp4 = 1 };  // the values of moe_weight_fmt
 struct W4Args {
   const uint8_t* a;
   const void* a_scales;
@@ -128,8 +129,8 @@ inline bool down_combine_fits(int64_t t_cap, int64_t topk, int64_t inter) {
 struct DownCombineArgs {
   const float* act;           // [row_cap, I] fp32 FC2 input before quantization
   int fmt;
-  const uint8_t* w;           // [E, H, I] E4M3
-  const float* w_scales;      // [E, H/128, I/128]
+  const uint8_t* w;           // [E, H, I] E4M3, or [E, H, I/2] MXFP4 (decode layer only)
+  const void* w_scales;       // fp32 [E, H/128, I/128], or E8M0 bytes [E, H, I/32]
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* row_to_pair;
@@ -176,8 +177,9 @@ struct DecodeFc1Args {
   int hidden;
   int inter;
   int fmt;
-  const uint8_t* w;           // [E, 2I, H] E4M3: gate rows [0, I), up rows [I, 2I)
-  const float* w_scales;      // [E, 2I/128, H/128]
+  const uint8_t* w;           // [E, 2I, H] E4M3: gate rows [0, I), up rows [I, 2I); MXFP4: [E, 2I, H/2]
+  const void* w_scales;       // fp32 [E, 2I/128, H/128], or E8M0 bytes [E, 2I, H/32]
+  int weight_fmt;             // kWeightE4m3, or kWeightMxfp4 (one-launch layer only; both halves)
   int act;
   float act_limit;
   int32_t* counts;            // workspace copies, as moe_align writes them
@@ -214,6 +216,14 @@ inline bool decode_layer_wide(int64_t t_cap, int64_t hidden) {
 inline bool decode_layer_fits(int64_t t_cap, int64_t topk, int64_t hidden, int64_t inter) {
   return down_combine_fits(t_cap, topk, inter) && hidden % 16 == 0 &&
          t_cap * (hidden + 16) <= kF1TokBytesWide && t_cap * (hidden / 128) <= kF1MaxScalesWide;
+}
+// With MXFP4 weights a weight stage holds two 128-wide K blocks (16 rows x
+// 128 packed bytes), so both K dimensions must be multiples of 256.
+inline bool decode_layer_fits_fmt(int64_t t_cap, int64_t topk, int64_t hidden, int64_t inter,
+                                  int weight_fmt) {
+  if (weight_fmt == kWeightMxfp4 && (hidden % 256 != 0 || inter % 256 != 0)) return false;
+  return (weight_fmt == kWeightE4m3 || weight_fmt == kWeightMxfp4) &&
+         decode_layer_fits(t_cap, topk, hidden, inter);
 }
 
 struct DecodeLayerArgs {

@@ -234,6 +234,14 @@ def test_decode_layer_applies_matches_the_workspace_plan(lib):
     assert moe.decode_layer_applies(8, 8, 6144, 256)       # 49 KB of token codes
     assert not moe.decode_layer_applies(9, 7, 7168, 256)   # 64.6 KB
     assert not moe.decode_layer_applies(4, 8, 4096, 2048)  # FC2 input rows too large
+    # MXFP4 weights: the one-launch layer (and with it the act buffer) exactly
+    # when the FP8 conditions hold and H and I are multiples of 256
+    for t_cap, k, h, i in [(4, 8, 4096, 512), (1, 8, 6144, 256), (8, 8, 6144, 256), (4, 8, 4224, 512),
+                           (4, 8, 4096, 384), (32, 2, 512, 128), (8, 8, 7168, 256), (4, 8, 4096, 2048)]:
+        lay = moe.moe_workspace_plan(288, h, i, k, t_cap, weight_fmt="mxfp4")
+        applies = moe.decode_layer_applies(t_cap, k, h, i, "mxfp4")
+        assert applies == (moe.decode_layer_applies(t_cap, k, h, i) and h % 256 == 0 and i % 256 == 0)
+        assert applies == (lay["act"] < lay["status"]), (t_cap, k, h, i)
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch(lib):
@@ -311,8 +319,19 @@ def test_forward_weight_format_field(lib):
     lay = B._Layout()
     assert lib.moe_workspace_plan(ctypes.byref(_problem(weight_fmt=2)), ctypes.byref(lay)) == INVALID
     assert lib.moe_workspace_plan(ctypes.byref(_problem(weight_fmt=1)), ctypes.byref(lay)) == OK
-    # MXFP4 weights never take the decode path's fused schedules
+    # MXFP4 weights take the decode path's one-launch layer (the act rows are
+    # laid out) when H and I are multiples of 256 (a stage is two K blocks),
+    # and the general schedule otherwise
     pd = _problem(num_experts=288, hidden=4096, inter=512, t_cap=4, weight_fmt=1)
-    assert lib.moe_workspace_plan(ctypes.byref(pd), ctypes.byref(lay)) == OK and lay.act == lay.status
+    assert lib.moe_workspace_plan(ctypes.byref(pd), ctypes.byref(lay)) == OK and lay.act < lay.status
     pd8 = _problem(num_experts=288, hidden=4096, inter=512, t_cap=4, weight_fmt=0)
     assert lib.moe_workspace_plan(ctypes.byref(pd8), ctypes.byref(lay)) == OK and lay.act < lay.status
+    for h, i in ((4096 + 128, 512), (4096, 384), (256, 128)):
+        pn = _problem(num_experts=64, hidden=h, inter=i, t_cap=4, weight_fmt=1)
+        assert lib.moe_workspace_plan(ctypes.byref(pn), ctypes.byref(lay)) == OK and lay.act == lay.status, (h, i)
+        pn8 = _problem(num_experts=64, hidden=h, inter=i, t_cap=4, weight_fmt=0)
+        assert lib.moe_workspace_plan(ctypes.byref(pn8), ctypes.byref(lay)) == OK and lay.act < lay.status, (h, i)
+    # FC1 of the decode path on its own serves FP8 weights only
+    t = B._Tensors(*([FAKE.value] * 9))
+    assert lib.moe_workspace_plan(ctypes.byref(pd), ctypes.byref(lay)) == OK
+    assert lib.moe_fc1_decode(ctypes.byref(pd), ctypes.byref(t), FAKE, lay.total, NULL) == UNSUPPORTED

@@ -128,10 +128,15 @@ def test_mxfp4_gemm_batched_layout(fmt):
 
 
 LAYER_RUNS = [
-    ("tiny", 8, 8, "fp32", "divide", 0),
+    ("tiny", 8, 8, "fp32", "divide", 0),    # general schedule (I = 128)
     ("tiny", 8, 6, "ue8m0", "reciprocal", 0),
-    ("decode", 1, 1, "fp32", "divide", 0),
+    ("decode", 1, 1, "fp32", "divide", 0),  # the one-launch layer from here to sweep 8
     ("decode", 4, 4, "fp32", "divide", 0),
+    ("decode", 1, 1, "ue8m0", "reciprocal", 0),
+    ("decode", 4, 3, "pow2", "divide", 0),
+    ("sweep", 1, 1, "fp32", "divide", 0),   # H 6144 (1.5 column blocks per CU), I 256 (one stage)
+    ("sweep", 8, 8, "fp32", "divide", 0),   # 4-deep ring for the wider token codes
+    ("sweep", 8, 5, "ue8m0", "divide", 0),
     ("sweep", 64, 64, "pow2", "divide", 0),
     ("tiny", 8, 8, "fp32", "divide", 16),   # batched masked-M layout
 ]
@@ -155,9 +160,14 @@ def test_mxfp4_layer_matches_oracle(run):
     torch.cuda.synchronize()
     got = down(out)
     assert np.all(got[t_live:] == POISON_BF16)
+    R = lay["row_cap"]
+    one_launch = lay["act"] < lay["status"]  # the plan lays out act rows for the one-launch layer only
+    assert one_launch == (name in ("decode", "sweep") and t_cap <= 8 and cap == 0), (name, t_cap)
+    if one_launch:  # it ran: the first live row's fp32 act values were written
+        act0 = ws[lay["act"]:lay["act"] + 4 * I].cpu().numpy().view(np.uint32)
+        assert not np.all(act0 == np.uint32(POISON_U8 * 0x01010101))
     # stage by stage on the GPU's own inputs: FC1 rows, the FC2 input codes
     # (bit-exact), FC2 rows
-    R = lay["row_cap"]
     sdt = np.uint8 if fmt == "ue8m0" else np.float32
 
     def view(name_, dtype, shape):
