@@ -341,9 +341,12 @@ typedef struct {
                             many rows per expert (row_cap is then 0 or num_experts *
                             expert_cap, align_rows is unused, and the decode path's
                             fused schedules do not apply) */
-  moe_weight_fmt weight_fmt; /* format of w1/w2 and their scales; MXFP4 weights take the
-                                general six-launch schedule with moe_grouped_gemm_mxfp4 as
-                                both GEMMs (the decode path's fused schedules are FP8-only) */
+  moe_weight_fmt weight_fmt; /* format of w1/w2 and their scales. MXFP4 weights take the
+                                one-launch decode layer where it applies and H and I are
+                                multiples of 256 (a weight stage is two 128-wide K blocks),
+                                otherwise the general six-launch schedule with
+                                moe_grouped_gemm_mxfp4 as both GEMMs; the decode path's
+                                other fused schedules and moe_fc1_decode are FP8-only */
 } moe_problem;
 
 typedef struct {
@@ -400,8 +403,9 @@ size_t moe_workspace_bytes(const moe_problem* p);
  * P*I/128 <= MOE_DECODE_FC2_MAX_SCALES (the quantized FC2 input rows in
  * LDS); the one launch also needs t_cap*(H+16) <= MOE_DECODE_LAYER_TOKEN_BYTES,
  * t_cap*H/128 <= MOE_DECODE_LAYER_MAX_SCALES (all tokens' codes and scales in
- * LDS) and H a multiple of 16. moe_fc1_decode's token limits are 24576 bytes
- * and 256 scales. */
+ * LDS) and H a multiple of 16 (with MXFP4 weights H and I multiples of 256,
+ * and the decode path is then the one launch alone). moe_fc1_decode's token
+ * limits are 24576 bytes and 256 scales. */
 #define MOE_DECODE_MAX_PAIRS 64
 #define MOE_DECODE_FC2_ROW_BYTES 24576
 #define MOE_DECODE_FC2_MAX_SCALES 256
@@ -470,7 +474,7 @@ moe_status moe_forward_noalloc(const moe_problem* p, const moe_tensors* t, void*
  * expert_counts, expert_offsets, row_to_pair, pair_to_row, xq and xs. It
  * also writes c1 for the live rows and act (fp32 SiLU(gate)*up). The arguments
  * are those of moe_forward: t->w2, t->w2_scales, t->topk_w and t->out are
- * not read.
+ * not read. FP8 weights only (UNSUPPORTED for MXFP4).
  * Errors: UNSUPPORTED (not such a problem), INVALID_ARG, CAPACITY, HIP. */
 moe_status moe_fc1_decode(const moe_problem* p, const moe_tensors* t, void* workspace,
                           size_t workspace_bytes, void* stream);
