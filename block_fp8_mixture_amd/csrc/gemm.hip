@@ -624,13 +624,26 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
 // Output (SOUT): the 256-wide kernel stages the BF16 tile in LDS and stores
 // whole 16-byte row chunks; the narrow kernels store each lane's 8-byte
 // pieces straight from the accumulators.
-template <bool UE8M0, bool GATHER, int TNT, bool PICK, bool SOUT>
+//
+// W4: MXFP4 weights (E2M1 codes two per byte, one E8M0 byte per 32 along K;
+// p.w_mx holds the bytes, [E, N, K/32]), 256-wide tiles only. A stage's
+// weight slab is then 256 rows x 32 bytes (one load per wave; 16-byte
+// chunks XOR-swizzled by bit 3 of the row, which keeps the fragment reads
+// conflict-free), and at each block start waves 4..7 load the tile rows' 4
+// scale bytes of the block in place of the sink load. The MFMA is the scaled
+// one with the E2M1 weights as operand A (a lane holds K values [32 h, 32 h +
+// 32) of its row, h = lane / 32, and that MX block's byte as its scale) and
+// the tokens as operand B (16-byte chunks h and 2 + h of the stage's 64, the
+// order the matrix core pairs with E2M1, as measured); the accumulator's
+// normalizer is the token scale alone.
+template <bool UE8M0, bool GATHER, int TNT, bool PICK, bool SOUT, bool W4 = false>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
   static_assert(TNT == 256 || TNT == 128 || TNT == 64, "tile widths");
   static_assert(!PICK || TNT != 256, "the pick is between 64 and 128");
+  static_assert(!W4 || (TNT == 256 && !PICK), "MXFP4 weights: the 256-wide kernel");
   constexpr int WN = TNT / 2;   // weight rows of a wave
   constexpr int WT = WN / 32;   // its 32-row MFMA tiles
-  constexpr int LPS = TNT == 256 ? 4 : 3;  // direct-to-LDS loads per wave and stage
+  constexpr int LPS = W4 ? 3 : TNT == 256 ? 4 : 3;  // direct-to-LDS loads per wave and stage
   // Four stages and two token-scale buffers, all distinct objects, so the
   // compiler can tell that a read never aliases a direct-to-LDS load in
   // flight and does not wait for the prefetch.
@@ -641,6 +654,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   __shared__ uint32_t s_sr0[TM];  // raw token scales of even / odd scale blocks
   __shared__ uint32_t s_sr1[TM];  // (UE8M0 bytes arrive zero-extended)
   __shared__ uint32_t s_srx[TM];  // sink of waves 4..7's copy of the scale loads
+  __shared__ uint32_t s_wsc[W4 ? 2 * TM : 1];  // W4: rows' scale bytes of even / odd blocks
   __shared__ __attribute__((aligned(16))) float s_rt[2][TM];  // token scale ratio of a block
   __shared__ float s_sl[TM];                                  // token scale of the last block
   __shared__ float s_ws[2][kMaxKBlocks];                      // weight block scales of the tile
@@ -695,9 +709,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     const bool wave_on = wm * 64 < rows_here && n0 + wn * WN < N;
     const uint8_t* wbase = p.w + static_cast<int64_t>(e) * N * K;
 
-    for (int i = tid; i < 2 * KB; i += kTiledThreads) {
-      const int blk = i / KB, kb = i % KB, nb = n0 / kGroup + blk;
-      s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
+    const uint8_t* wbase4 = p.w + static_cast<int64_t>(e) * N * (K / 2);  // W4
+    if constexpr (!W4) {
+      for (int i = tid; i < 2 * KB; i += kTiledThreads) {
+        const int blk = i / KB, kb = i % KB, nb = n0 / kGroup + blk;
+        s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
+      }
     }
     // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
     // instructions of 16 rows each (128 weight rows: rows [16 w, 16 w + 16)
@@ -717,6 +734,13 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       const int wr = n0 + wrow < N ? n0 + wrow : n0;
       woff[i] = static_cast<uint32_t>(wr) * K + wchunk;
     }
+    if constexpr (W4) {
+      // wave w: weight rows [32 w, 32 w + 32), two lanes per 32-byte row
+      const int wrow = wave * 32 + (lane >> 1);
+      const int wchunk = ((lane & 1) ^ ((wrow >> 3) & 1)) << 4;
+      const int wr = n0 + wrow < N ? n0 + wrow : n0;
+      woff[0] = static_cast<uint32_t>(wr) * (K / 2) + wchunk;
+    }
     const int sa_row = tok < rows_here ? a_source_row<GATHER>(p, row0 + tok) : -1;
     const int my_src = sa_row < 0 ? 0 : sa_row;
 
@@ -725,7 +749,9 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds(p.a + (aoff[i] + s * SK), (lds_void*)(stage + (wave * 32 + 16 * i) * SK), 16, 0, 0);
-      if constexpr (TNT == 256) {
+      if constexpr (W4) {
+        __builtin_amdgcn_global_load_lds(wbase4 + (woff[0] + s * (SK / 2)), (lds_void*)(stage + kStageA + wave * 32 * (SK / 2)), 16, 0, 0);
+      } else if constexpr (TNT == 256) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
@@ -738,9 +764,20 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     // Token scales of block kb. Waves 0..3 load them into `buf`; waves
     // 4..7 load the same values into a sink so that every wave has the same
     // number of loads in flight and one vmcnt immediate fits all of them.
+    // W4: waves 4..7 load the scale bytes of the tile's 256 weight rows
+    // instead (4 bytes per row and block) into s_wsc, by block parity.
     auto issue_s = [&](int kb, uint32_t* buf) {
+      const int kbc = kb < KB ? kb : KB - 1;
+      if constexpr (W4) {
+        if (wave >= TM / 64) {
+          const int row = n0 + (wave & 3) * 64 + lane;
+          const int64_t widx = (static_cast<int64_t>(e) * N + (row < N ? row : n0)) * (K / kMxBlock) + kbc * 4;
+          __builtin_amdgcn_global_load_lds(p.w_mx + widx, (lds_void*)(s_wsc + (kb & 1) * TM + (wave & 3) * 64), 4, 0, 0);
+          return;
+        }
+      }
       uint32_t* dst = (wave < TM / 64 ? buf : s_srx) + (wave & 3) * 64;
-      const int64_t idx = static_cast<int64_t>(kb < KB ? kb : KB - 1) * p.a_rows + my_src;
+      const int64_t idx = static_cast<int64_t>(kbc) * p.a_rows + my_src;
       if constexpr (UE8M0)
         __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.a_scales) + idx, (lds_void*)dst, 1, 0, 0);
       else
@@ -877,12 +914,40 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       // ratios (slot kb % 2) are written in L(2kb-1) by group 0 and read in
       // L(2kb) by both groups; the next writer of the slot is L(2kb+3).
       const bool grp1 = wave >= 4;
-      Frag af[2], wf[WT];
+      Frag af[2], wf[W4 ? 1 : WT];
+      uint4 wf4[W4 ? WT : 1];           // W4: a lane's 32 E2M1 codes of each weight tile
+      uint32_t wsc[W4 ? WT : 1] = {};   // W4: its row's 4 scale bytes of the current block
+      uint32_t scb[W4 ? WT : 1] = {};   // W4: the stage's scale byte (low byte) per weight tile
       float ratio0 = 1.0f, ratio1 = 1.0f;
       auto lphase = [&](int j, const uint8_t* cur, uint8_t* fill, const float* rt_cur,
                         uint32_t* sr_fill, const uint32_t* sr_next, float* rt_next, auto even_t) {
         constexpr bool even = decltype(even_t)::value;
-        if (wave_on && j < NS) {
+        if (W4 && wave_on && j < NS) {
+          const int h = lane >> 5;
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int r = wm * 64 + tt * 32 + (lane & 31);
+            af[tt].u[0] = *reinterpret_cast<const uint4*>(cur + swz(r, h));
+            af[tt].u[1] = *reinterpret_cast<const uint4*>(cur + swz(r, 2 + h));
+          }
+#pragma unroll
+          for (int wt = 0; wt < (W4 ? WT : 1); ++wt) {
+            const int r = wn * WN + wt * 32 + (lane & 31);
+            wf4[wt] = *reinterpret_cast<const uint4*>(cur + kStageA + r * (SK / 2) + ((h ^ ((r >> 3) & 1)) << 4));
+          }
+          if constexpr (even) {
+            const int kb = j >> 1;
+#pragma unroll
+            for (int wt = 0; wt < (W4 ? WT : 1); ++wt)
+              wsc[wt] = s_wsc[W4 ? (kb & 1) * TM + wn * WN + wt * 32 + (lane & 31) : 0];
+            const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
+            ratio0 = r2.x;
+            ratio1 = r2.y;
+          }
+          // MX blocks 2 (j & 1) + h of the 128-wide block: this stage's half of it
+#pragma unroll
+          for (int wt = 0; wt < (W4 ? WT : 1); ++wt) scb[wt] = wsc[wt] >> (8 * (2 * (j & 1) + h));
+        } else if (!W4 && wave_on && j < NS) {
           const int c0 = 2 * (lane >> 5);
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -891,7 +956,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
             af[tt].u[1] = *reinterpret_cast<const uint4*>(cur + swz(r, c0 + 1));
           }
 #pragma unroll
-          for (int wt = 0; wt < WT; ++wt) {
+          for (int wt = 0; wt < (W4 ? 1 : WT); ++wt) {
             const int r = wn * WN + wt * 32 + (lane & 31);
             wf[wt].u[0] = *reinterpret_cast<const uint4*>(cur + kStageA + swz(r, c0));
             wf[wt].u[1] = *reinterpret_cast<const uint4*>(cur + kStageA + swz(r, c0 + 1));
@@ -936,8 +1001,16 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             if constexpr (even) acc[wt][tt] = acc[wt][tt] * (tt == 0 ? ratio0 : ratio1);
-            acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[wt].v, af[tt].v, acc[wt][tt],
-                                                                           0, 0, 0, 0, 0, 0);
+            if constexpr (W4) {
+              const uint4 w = wf4[wt];
+              const v8i wa = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                              static_cast<int>(w.w), 0, 0, 0, 0};
+              acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, af[tt].v, acc[wt][tt], 4, 0, 0,
+                                                                             static_cast<int>(scb[wt]), 0, 127);
+            } else {
+              acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[wt].v, af[tt].v, acc[wt][tt],
+                                                                             0, 0, 0, 0, 0, 0);
+            }
           }
         if constexpr (even) {
 #pragma unroll
@@ -1073,6 +1146,28 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 }
 
 }  // namespace
+
+bool launch_tiled_w4(const GemmArgs& g, hipStream_t stream, hipError_t* err) {
+  const int live_bound = g.max_live_experts < g.num_experts ? g.max_live_experts : g.num_experts;
+  if (live_bound <= 0 || g.max_rows_per_expert <= kStreamMaxRows || !g.w_mx || g.k % kGroup != 0) return false;
+  // The tile bound of launch_grouped_gemm; the 256-wide kernel only where it
+  // keeps the CUs busy (the narrow cases stay with the MXFP4 kernels).
+  const int64_t rows = g.row_cap;
+  const int64_t large = rows / (kStreamMaxRows + 1) < live_bound ? rows / (kStreamMaxRows + 1) : live_bound;
+  const int64_t row_tiles = (rows + TM - 1) / TM + large;
+  const int64_t cap = device_cu_count();
+  const int64_t tiles = row_tiles * ((g.n + TN - 1) / TN);
+  if (tiles < 2 * cap) return false;
+  const int grid = static_cast<int>(tiles < cap ? tiles : cap);
+  const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
+  const dim3 gr(grid), bl(kTiledThreads);
+  if (u && m) hipLaunchKernelGGL((gemm_tiled_kernel<true, true, TN, false, true, true>), gr, bl, 0, stream, g);
+  else if (u) hipLaunchKernelGGL((gemm_tiled_kernel<true, false, TN, false, true, true>), gr, bl, 0, stream, g);
+  else if (m) hipLaunchKernelGGL((gemm_tiled_kernel<false, true, TN, false, true, true>), gr, bl, 0, stream, g);
+  else hipLaunchKernelGGL((gemm_tiled_kernel<false, false, TN, false, true, true>), gr, bl, 0, stream, g);
+  *err = hipGetLastError();
+  return true;
+}
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream) {
   const int live_bound = g.max_live_experts < g.num_experts ? g.max_live_experts : g.num_experts;

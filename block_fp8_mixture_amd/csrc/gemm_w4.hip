@@ -443,25 +443,53 @@ __global__ __launch_bounds__(kW4Threads, 2) void gemm_w4_tiled_kernel(W4Args p) 
 }  // namespace
 
 template <bool U, bool M>
-static void launch_w4(const W4Args& g, bool large, hipStream_t stream) {
+static hipError_t launch_w4(const W4Args& g, bool large, hipStream_t stream) {
   const int cus = device_cu_count();
   if (!large) {  // every expert to the wave-task kernel
     hipLaunchKernelGGL((gemm_w4_kernel<U, M, false>), dim3(4 * cus), dim3(kW4Threads), 0, stream, g);
-    return;
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_w4_kernel<U, M, true>), dim3(4 * cus), dim3(kW4Threads), 0, stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The larger experts: the FP8 kernel's 256 x 256 ping-pong tiles with E2M1
+  // weight slabs when there are enough tiles to fill the CUs, else 64 x 128
+  // tiles here. Both take the experts of more than kW4SmallMax rows.
+  static_assert(kW4SmallMax == kStreamMaxRows, "the two large-expert kernels split experts alike");
+  GemmArgs t{};
+  t.a = g.a;
+  t.a_scales = g.a_scales;
+  t.fmt = g.fmt;
+  t.a_rows = g.a_rows;
+  t.a_row_map = g.a_row_map;
+  t.a_row_div = g.a_row_div;
+  t.w = g.w;
+  t.w_scales = nullptr;
+  t.w_mx = g.w_scales;
+  t.counts = g.counts;
+  t.offsets = g.offsets;
+  t.num_experts = g.num_experts;
+  t.row_cap = g.row_cap;
+  t.max_rows_per_expert = g.max_rows_per_expert;
+  t.max_live_experts = g.num_experts;
+  t.n = g.n;
+  t.k = g.k;
+  t.c = g.c;
+  t.tiles_visited = nullptr;
+  t.seg_cap = g.seg_cap;
+  if (launch_tiled_w4(t, stream, &e)) return e;
   hipLaunchKernelGGL((gemm_w4_tiled_kernel<U, M>), dim3(2 * cus), dim3(kW4Threads), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_w4(const W4Args& g, hipStream_t stream) {
   // The tiled kernel only when some expert can hold more than kW4SmallMax rows.
   const bool large = g.max_rows_per_expert > kW4SmallMax;
   const bool u = g.fmt == kUe8m0, m = g.a_row_map != nullptr;
-  if (u && m) launch_w4<true, true>(g, large, stream);
-  else if (u) launch_w4<true, false>(g, large, stream);
-  else if (m) launch_w4<false, true>(g, large, stream);
-  else launch_w4<false, false>(g, large, stream);
-  return hipGetLastError();
+  if (u && m) return launch_w4<true, true>(g, large, stream);
+  if (u) return launch_w4<true, false>(g, large, stream);
+  if (m) return launch_w4<false, true>(g, large, stream);
+  return launch_w4<false, false>(g, large, stream);
 }
 
 }  // namespace moe

@@ -81,9 +81,18 @@ struct GemmArgs {
   // The batched layout: expert e's segment is rows [e*seg_cap, (e+1)*seg_cap)
   // (0: the segments come from offsets).
   int seg_cap = 0;
+  // MXFP4 weights (launch_tiled_w4 only): w holds [E, n, k/2] E2M1 codes and
+  // w_mx [E, n, k/32] E8M0 bytes; w_scales is not read.
+  const uint8_t* w_mx = nullptr;
 };
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t stream);
+
+// The 256 x 256 tiled kernel with MXFP4 weights for the experts of more than
+// kStreamMaxRows rows, when the launch's bound on its tiles is at least twice
+// the CU count; otherwise launches nothing and returns false (*err
+// untouched). g.w_mx must be set.
+bool launch_tiled_w4(const GemmArgs& g, hipStream_t stream, hipError_t* err);
 
 // The grouped GEMM with MXFP4 weights: w [num_experts, n, k/2] packed E2M1
 // codes (the even K element in the low nibble), w_scales [num_experts, n,

@@ -202,20 +202,26 @@ def test_mxfp4_layer_matches_oracle(run):
     say(f"  layer max err / max|ref| = {err:.3e}")
 
 
-@pytest.mark.parametrize("gather", [False, True])
-def test_mxfp4_gemm_full_size_sampled(gather):
-    # The 4096-token layer's FC1 shape (32 experts of about 1024 rows, N 4096,
-    # K 7168) through the tiled kernel, checked on whole 64 x 128 tiles of
-    # several experts, row tiles and column tiles (the first, the last and a
-    # ragged one) against the oracle.
+FULL_SIZE = [(4096, 7168, False), (4096, 7168, True), (7168, 2048, False)]
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+@pytest.mark.parametrize("shape", FULL_SIZE, ids=[f"n{n}-k{k}-gather{g}" for n, k, g in FULL_SIZE])
+def test_mxfp4_gemm_full_size_sampled(shape, fmt):
+    # The 4096-token layer's FC1 (N 4096, K 7168, gathered and plain) and FC2
+    # (N 7168, K 2048) shapes with 32 experts of about 1024 rows: enough tiles
+    # for the 256 x 256 ping-pong kernel with E2M1 weight slabs. Checked on
+    # whole 64 x 128 blocks of several experts, row and column positions (the
+    # first, a middle and the last, ragged, ones) against the oracle.
+    n, k, gather = shape
     g = np.random.default_rng(21)
-    e_n, n, k = 32, 4096, 7168
+    e_n = 32
     cnt = g.integers(900, 1150, e_n)
     counts, offsets = _routing_layout(cnt)
     row_cap = int(offsets[-1])
     a_rows = 4096 if gather else row_cap
     x = g.standard_normal((a_rows, k)).astype(np.float32)
-    aq, asc = oracle.quantize_groups(x, "fp32")
+    aq, asc = oracle.quantize_groups(x, fmt)
     wp = g.integers(0, 256, size=(e_n, n, k // 2), dtype=np.uint8)
     ws = g.integers(117, 122, size=(e_n, n, k // 32)).astype(np.uint8)
     row_map = None
@@ -223,9 +229,9 @@ def test_mxfp4_gemm_full_size_sampled(gather):
         row_map = np.full(row_cap, -1, np.int32)
         for e in range(e_n):
             row_map[offsets[e]:offsets[e] + counts[e]] = g.integers(0, a_rows * 8, counts[e])
-    say(f"mxfp4 gemm full size gather={gather} row_cap={row_cap}")
+    say(f"mxfp4 gemm full size n={n} k={k} gather={gather} {fmt} row_cap={row_cap}")
     out = torch.full((row_cap, n), POISON_BF16, dtype=torch.int16, device=dev())
-    moe.moe_grouped_gemm_mxfp4(up(aq), up(asc), "fp32", up(wp), up(ws), up(counts), up(offsets),
+    moe.moe_grouped_gemm_mxfp4(up(aq), up(asc), fmt, up(wp), up(ws), up(counts), up(offsets),
                                row_cap, a_row_map=None if row_map is None else up(row_map),
                                a_row_div=8, out=out)
     torch.cuda.synchronize()
@@ -236,8 +242,8 @@ def test_mxfp4_gemm_full_size_sampled(gather):
             r0 = int(offsets[e]) + 64 * mt
             rows = np.arange(r0, min(r0 + 64, int(offsets[e]) + c))
             src = rows if row_map is None else row_map[rows] // 8
-            for n0 in (0, 2048, n - 128):
-                ref = oracle.gemm_rows_mxfp4(aq[src], oracle.scales_to_f64(asc[:, src], "fp32"),
+            for n0 in (0, n // 256 * 128, n - 128):
+                ref = oracle.gemm_rows_mxfp4(aq[src], oracle.scales_to_f64(asc[:, src], fmt),
                                              wp[e, n0:n0 + 128], ws[e, n0:n0 + 128])
                 assert_bf16_close(got[rows, n0:n0 + 128], ref, f"expert {e} rows {r0} cols {n0}")
     # rows past each expert's count stay untouched
