@@ -576,29 +576,34 @@ def test_fc1_decode_alone(name, t_cap, t_live, fmt, act, lim, rounding):
     assert np.all(c1[dead] == (POISON_U8 << 8 | POISON_U8))
 
 
-def test_barrier_timeout_is_reported_in_the_launch_outputs():
+@pytest.mark.parametrize("weights", ["e4m3", "mxfp4"])
+def test_barrier_timeout_is_reported_in_the_launch_outputs(weights):
     """A grid-barrier wait of the one-launch layer that gives up (forced from
     the host: a negative spin limit makes every wait give up at once, and every
     kernel still exits normally) shows in that launch's own outputs: each
     workgroup's status slot says so and its output columns of the live tokens
     are NaN. With the limit restored the next launch is correct again and all
-    slots read 0."""
+    slots read 0. Both weight formats' kernels."""
     name = "decode"
     cfg = synth.get(name)
     E, H, I, K = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk
     x, ids, w = synth.make_workload(cfg, 4, 7)
-    (w1q, w1s), (w2q, w2s) = host_weights(name)
-    d = device_weights(name)
-    assert moe.decode_layer_applies(4, K, H, I)
-    lay = moe.moe_workspace_plan(E, H, I, K, 4)
+    if weights == "mxfp4":
+        (w1q, w1s), (w2q, w2s) = synth.ExpertWeightsMxfp4(cfg).stacked(threads=16)
+        d = (up(w1q), up(w1s), up(w2q), up(w2s))
+    else:
+        (w1q, w1s), (w2q, w2s) = host_weights(name)
+        d = device_weights(name)
+    assert moe.decode_layer_applies(4, K, H, I, weights)
+    lay = moe.moe_workspace_plan(E, H, I, K, 4, weight_fmt=weights)
     ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
     out = torch.full((4, H), POISON_BF16, dtype=torch.int16, device=dev())
     live = up(np.array([3], np.int32))
     before = moe.moe_barrier_timeouts()
     old = moe.moe_barrier_spin_limit(-1)
     try:
-        say("one-launch layer with every barrier wait forced to give up")
-        moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws)
+        say(f"one-launch layer ({weights} weights) with every barrier wait forced to give up")
+        moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws, weight_fmt=weights)
         torch.cuda.synchronize()
     finally:
         moe.moe_barrier_spin_limit(old)
@@ -612,10 +617,10 @@ def test_barrier_timeout_is_reported_in_the_launch_outputs():
     assert moe.moe_barrier_timeouts() >= before + grid
     # the next launch, with the default limit, is whole again
     say("one-launch layer with the default spin limit")
-    moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws)
+    moe.moe_forward(up(x), up(ids), up(w), *d, t_live=live, out=out, workspace=ws, weight_fmt=weights)
     torch.cuda.synchronize()
     assert np.all(_ws_view(ws, lay, "status", np.int32, (1024,))[:grid] == 0)
-    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, 3, "fp32")
+    ref = oracle.token_forward(x, ids, w, (w1q, w1s), (w2q, w2s), E, 3, "fp32", weight_fmt=weights)
     assert_bf16_close(down(out)[:3], ref, "after a forced timeout")
 
 
