@@ -250,3 +250,65 @@ def test_mxfp4_gemm_full_size_sampled(shape, fmt):
     for e in (0, e_n - 1):
         pad = np.arange(int(offsets[e]) + int(counts[e]), int(offsets[e + 1]))
         assert np.all(got[pad] == POISON_BF16)
+
+
+def test_mxfp4_layer_full_size_sampled():
+    # The 4096-token layer with MXFP4 weights through moe_forward (FC1 and
+    # FC2 on the 256 x 256 kernel with E2M1 slabs): alignment bit-exact; on 16
+    # sampled rows of 3 live experts, C1 and Y within tolerance of the oracle
+    # (from the GPU's own inputs of each GEMM) and the FC2 input codes and
+    # scales bit-exact against SiLU+quant of the GPU's C1; 8 sampled tokens
+    # against the combine of the GPU's own Y; one token against the dense
+    # per-token oracle; nothing written outside the live rows.
+    cfg = synth.get("full")
+    E, H, I, K, A = cfg.num_experts, cfg.hidden, cfg.inter, cfg.topk, cfg.align_rows
+    T, fmt = 4096, "fp32"
+    say(f"mxfp4 layer full size T={T}")
+    x, ids, w = synth.make_workload(cfg, T)
+    (w1p, w1s), (w2p, w2s) = synth.ExpertWeightsMxfp4(cfg).stacked(threads=16)
+    lay = moe.moe_workspace_plan(E, H, I, K, T, A, 0, fmt, weight_fmt="mxfp4")
+    ws = torch.full((lay["total"],), POISON_U8, dtype=torch.uint8, device=dev())
+    out = torch.full((T, H), POISON_BF16, dtype=torch.int16, device=dev())
+    moe.moe_forward(up(x), up(ids), up(w), up(w1p), up(w1s), up(w2p), up(w2s), fmt, align_rows=A,
+                    out=out, workspace=ws, weight_fmt="mxfp4")
+    torch.cuda.synchronize()
+    R = lay["row_cap"]
+
+    def view(name_, dtype, shape):
+        nbytes = int(np.prod(shape)) * np.dtype(dtype).itemsize
+        return ws[lay[name_]:lay[name_] + nbytes].cpu().numpy().view(dtype).reshape(shape)
+    al = oracle.align(ids, T, E, A)
+    counts = view("expert_counts", np.int32, (E,))
+    offsets = view("expert_offsets", np.int32, (E + 1,))
+    assert np.array_equal(counts, al["counts"]) and np.array_equal(offsets, al["offsets"])
+    total = int(offsets[-1])
+    assert np.array_equal(view("row_to_pair", np.int32, (R,))[:total], al["row_to_pair"])
+    xq = view("xq", np.uint8, (T, H))
+    xs = view("xs", np.float32, (H // 128, T))
+    c1 = view("c1", np.uint16, (R, 2 * I))
+    hq = view("hq", np.uint8, (R, I))
+    hs = view("hs", np.float32, (I // 128, R))
+    y = view("y", np.uint16, (R, H))
+    g = np.random.default_rng(4)
+    for e in g.permutation(np.flatnonzero(al["counts"] > 0))[:3]:
+        seg = np.arange(al["offsets"][e], al["offsets"][e] + al["counts"][e])
+        rows = np.unique(np.concatenate([seg[[0, -1]], g.choice(seg, 14, replace=False)]))
+        tok = al["row_to_pair"][rows] // K
+        ref_c1 = oracle.gemm_rows_mxfp4(xq[tok], oracle.scales_to_f64(xs[:, tok], fmt), w1p[e], w1s[e])
+        assert_bf16_close(c1[rows], ref_c1, f"FC1 expert {e}")
+        rhq, rhs = oracle.silu_mul_quant(c1[rows], fmt)
+        assert np.array_equal(hq[rows], rhq)
+        assert np.array_equal(np.ascontiguousarray(hs[:, rows]).view(np.uint8),
+                              np.ascontiguousarray(rhs).view(np.uint8))
+        ref_y = oracle.gemm_rows_mxfp4(hq[rows], oracle.scales_to_f64(hs[:, rows], fmt), w2p[e], w2s[e])
+        assert_bf16_close(y[rows], ref_y, f"FC2 expert {e}")
+        pad = np.arange(al["offsets"][e] + al["counts"][e], al["offsets"][e + 1])
+        assert np.all(c1[pad] == (POISON_U8 << 8 | POISON_U8))
+    got = down(out)
+    toks = np.unique(np.concatenate([[0, T - 1], g.choice(T, 6, replace=False)]))
+    p2r_s = al["pair_to_row"].reshape(T, K)[toks].reshape(-1)
+    assert_bf16_close(got[toks], oracle.combine(y, p2r_s, w[toks], len(toks), H), "combine")
+    ref = oracle.token_forward(x, ids, w, (w1p, w1s), (w2p, w2s), E, T, fmt, tokens=toks[:1],
+                               weight_fmt="mxfp4")
+    err = assert_bf16_close(got[toks[:1]], ref, "layer")
+    say(f"  layer max err / max|ref| = {err:.3e}")
