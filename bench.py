@@ -370,6 +370,48 @@ class Marks:
         return sorted(((m[:, 1] - m[:, 0]) * 1e6 / hz).tolist())
 
 
+def attainable_peaks(torch):
+    """This GPU's attainable peaks, measured by the benchmark library's probes
+    (bench_clock.hip): a streaming read of 1 GiB (HBM-resident: larger than
+    L2 and the 256 MB Infinity Cache; 2, 4, 8 or 16 workgroups of 256 threads
+    per CU, eight 16-byte loads in flight per thread, the best of the four) and an FP8 MFMA-only loop (one 8-wave
+    workgroup per CU, four independent 32x32x64 accumulators per wave). Best
+    of three runs each, after one warm-up run."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
+    lib.moe_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    lib.moe_bench_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def best(launch):
+        ts = []
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts[1:])
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(16 * cus * 256 + cus * 512, dtype=torch.int32, device=dev)
+    t_read = min(best(lambda: lib.moe_bench_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), b, stream))
+                 for b in (2 * cus, 4 * cus, 8 * cus, 16 * cus))
+    del src
+    iters = 10000
+    t_mfma = best(lambda: lib.moe_bench_mfma_loop(iters, sink.data_ptr(), cus, stream))
+    mfma_flops = cus * 8 * 4 * iters * 2 * 32 * 32 * 64
+    return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1),
+            "fp8_mfma_tflops": round(mfma_flops / t_mfma / 1e12, 1),
+            "method": "streaming read of 1 GiB (best of 2-16 workgroups per CU); FP8 MFMA-only loop (32x32x64, 4 accumulators per "
+                      "wave, 8 waves per CU); best of 3 runs each (bench_clock.hip)"}
+
+
 def time_layer(torch, fwd, steps, warmup, flush_caches, record_events=True):
     """Captures fwd() between two device-clock marks and replays it `steps`
     times after `warmup` replays, flushing the caches before each. Returns the
@@ -628,6 +670,13 @@ def main():
         cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst, ws_f, out_f, c1
+    att = attainable_peaks(torch)
+    a_peak = att["fp8_mfma_tflops"] if roof["bound"] == "mfma" else att["hbm_read_gbs"]
+    roof["attainable"] = a_peak
+    roof["frac_attainable"] = round(roof["achieved"] / a_peak, 4)
+    print(f"# attainable on this GPU: {att['hbm_read_gbs']} GB/s streaming read, "
+          f"{att['fp8_mfma_tflops']} TFLOP/s FP8 MFMA loop; dominant kernel at "
+          f"{roof['frac_attainable']:.3f} of its attainable peak", file=sys.stderr, flush=True)
 
     head_rates = rates(cfg, ids, t_live, med)
     ctx = PAGES_CONTEXT_US.get(f"{args.config}:{t_live}")
@@ -660,6 +709,7 @@ def main():
         "frac_fp8_peak": head_rates["frac_fp8_peak"],
         "frac_hbm_peak": head_rates["frac_hbm_peak"],
         "roofline": roof,
+        "attainable_peaks": att,
         "pages_context_us": ctx,
     }
     del fwd, ws, out, dx, dids, dw, dlive, d_w
