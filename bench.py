@@ -374,9 +374,10 @@ def attainable_peaks(torch):
     """This GPU's attainable peaks, measured by the benchmark library's probes
     (bench_clock.hip): a streaming read of 1 GiB (HBM-resident: larger than
     L2 and the 256 MB Infinity Cache; 2, 4, 8 or 16 workgroups of 256 threads
-    per CU, eight 16-byte loads in flight per thread, the best of the four) and an FP8 MFMA-only loop (one 8-wave
-    workgroup per CU, four independent 32x32x64 accumulators per wave). Best
-    of three runs each, after one warm-up run."""
+    per CU, eight 16-byte loads in flight per thread, the best of the four)
+    and an FP8 MFMA-only loop (one 8-wave workgroup per CU, four independent
+    32x32x64 accumulators per wave). Best of three runs each, after one
+    warm-up run."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "block_fp8_mixture_amd", "libmoebench.so"))
     lib.moe_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
