@@ -647,7 +647,7 @@ def main():
         f"<{'true' if fmt == 'ue8m0' else 'false'}, true> (FC1)"
     if fused:
         wide = t_cap * (H + 16) > 24576 or t_cap * (H // 128) > 256  # the 4-deep ring variant
-        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true, {4 if wide else 6}> "
+        kname = (f"fc1_decode_kernel<{ {'fp32': 0, 'pow2': 1, 'ue8m0': 2}[fmt] }, true, {4 if wide else 6}, false> "
                  "(the whole decode layer: routing, activation quantization, FC1, SiLU, "
                  "grid barrier, FC2, top-k combine)")
     if tiled:
