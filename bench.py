@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -162,12 +163,21 @@ def decode_layer_bytes(cfg, n_live_experts, pairs, t_live):
             + t_live * H * 2)
 
 
+KERNEL_SOURCES = ("gemm.hip", "fc1_decode.hip", "gemm_device.h", "fc2_decode.h", "device_common.h",
+                  "quant_device.h", "kernels.h")
+
+
 def kernel_source_hash():
-    """Hash of the dominant kernels' sources (the traffic summaries are keyed by it)."""
+    """Hash of the code the dominant kernels compile from (the traffic and
+    counter summaries are keyed by it), with comments and whitespace removed,
+    so that editing a comment does not make a measurement stale."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "fc1_decode.hip", "gemm_device.h", "fc2_decode.h"):
-        with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_fp8_mixture_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,7 +29,10 @@
 //    idle, picked on the device) on v_mfma_f32_32x32x64_f8f6f4, operands
 //    staged through a 4-deep LDS ring of 64-byte K stages by direct-to-LDS
 //    loads, scales applied by rescaling the accumulator once per 128-wide
-//    block (details at the kernel).
+//    block. The 256-wide kernel runs a ping-pong schedule (the two waves of a
+//    SIMD alternate MFMA and load phases) and also serves MXFP4 weights
+//    (launch_tiled_w4: E2M1 weight slabs, the E8M0 scales applied by the
+//    scaled MFMA). Details at the kernel.
 #include <type_traits>
 
 #include "device_common.h"

@@ -34,8 +34,11 @@
 //    (1, 2 or 4) is picked on the device so that the tasks fill the grid's
 //    waves. Weights and tokens go straight from global memory into the MFMA
 //    registers, two K steps ahead.
-//  - gemm_w4_tiled_kernel (larger experts): a workgroup tile is 64 token
-//    rows x 128 weight rows; the tile's token rows pass through LDS by
+//  - larger experts, when the launch's bound on 256 x 256 tiles fills the
+//    CUs twice: the FP8 GEMM's ping-pong kernel with E2M1 weight slabs
+//    (launch_tiled_w4 in gemm.hip);
+//  - gemm_w4_tiled_kernel (larger experts otherwise): a workgroup tile is 64
+//    token rows x 128 weight rows; the tile's token rows pass through LDS by
 //    direct-to-LDS loads (double buffered, one K step ahead, 128-byte rows
 //    XOR-swizzled by row pair so the fragment reads are conflict-free) and
 //    each wave streams its 32 weight rows from global memory one K step
