@@ -32,7 +32,9 @@
 //    block. The 256-wide kernel runs a ping-pong schedule (the two waves of a
 //    SIMD alternate MFMA and load phases) and also serves MXFP4 weights
 //    (launch_tiled_w4: E2M1 weight slabs, the E8M0 scales applied by the
-//    scaled MFMA). Details at the kernel.
+//    scaled MFMA). Between tiles, the next tile's coordinates, row-map
+//    entries and weight scales load during the output staging, and its
+//    first stages go out during the output stores. Details at the kernel.
 #include <type_traits>
 
 #include "device_common.h"
@@ -601,6 +603,25 @@ __device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, i
   }
 }
 
+// A tile of the large-expert GEMM: its expert's weights, first output row,
+// live rows and first weight row, and the per-lane offsets of its operand
+// loads. The kernel prepares the next tile's while one finishes, and the
+// next tile's first stages go out during the output stores. (Namespace
+// scope: as local classes of the kernel template, hipcc's host pass emits
+// no launch stubs for the kernel.)
+struct TiledTile {
+  const uint8_t* wb;
+  int e, row0, rows_here, n0, sa_row;
+  uint32_t aoff[2], woff[2];
+};
+// A tile before its row-map entries have arrived: raw[0..1] are the map
+// entries (or output rows) of the lane's two staged rows, raw[2] its
+// token's.
+struct TiledTileFetch {
+  int e, row0, rows_here, n0;
+  int raw[3];
+};
+
 // Large-expert GEMM. A workgroup computes a 256 token x TNT weight tile
 // (TNT = 256, or 128 or 64 -- picked on the device, see PICK -- when wide
 // tiles would leave CUs idle) with 8 waves as 4 (tokens) x 2 (weights);
@@ -660,13 +681,15 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   __shared__ uint32_t s_wsc[W4 ? 2 * TM : 1];  // W4: rows' scale bytes of even / odd blocks
   __shared__ __attribute__((aligned(16))) float s_rt[2][TM];  // token scale ratio of a block
   __shared__ float s_sl[TM];                                  // token scale of the last block
-  __shared__ float s_ws[2][kMaxKBlocks];                      // weight block scales of the tile
+  __shared__ float s_wsf[2 * kMaxKBlocks];  // weight block scales of the tile, [block][K block] with row stride KB
   __shared__ int s_list[kMaxExperts];
   __shared__ int s_pref[kMaxExperts + 1];
+  __shared__ int s_cnt[kMaxExperts];   // listed expert -> its live rows
+  __shared__ int s_row0[kMaxExperts];  //   and its first row
   __shared__ int s_tmp[2 * kTiledThreads / 64];
 
   const int n_list = build_expert_list<kTiledThreads>(p, WantLarge(), TiledUnits(), s_list,
-                                                      s_pref, s_tmp);
+                                                      s_pref, s_tmp, s_cnt, s_row0);
   if constexpr (PICK) {
     // The 64- and 128-wide kernels are launched together on the same grid;
     // both find the same row tiles and agree on which one runs: the fewer
@@ -694,98 +717,146 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   const int vid = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
   const int tok = tid & (TM - 1);
 
-  for (int tile = vid; tile < total; tile += G) {
+  auto tile_fetch = [&](int tile) {
+    TiledTileFetch f;
     const int tm_all = tile / nt;
     int lo = 0, hi = n_list - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= tm_all) lo = mid; else hi = mid - 1;
     }
-    const int e = s_list[lo];
+    f.e = __builtin_amdgcn_readfirstlane(s_list[lo]);
     const int mt_e = s_pref[lo + 1] - s_pref[lo];
     int mt, ntile;
     tile_coords(tile - s_pref[lo] * nt, mt_e, nt, &mt, &ntile);
-    const int cnt = __builtin_amdgcn_readfirstlane(expert_rows(p, e));
-    const int rows_here = min(TM, cnt - mt * TM);
-    const int row0 = __builtin_amdgcn_readfirstlane(seg_start(p, e)) + mt * TM;
-    const int n0 = ntile * TNT;
-    const bool wave_on = wm * 64 < rows_here && n0 + wn * WN < N;
-    const uint8_t* wbase = p.w + static_cast<int64_t>(e) * N * K;
-
-    const uint8_t* wbase4 = p.w + static_cast<int64_t>(e) * N * (K / 2);  // W4
-    if constexpr (!W4) {
-      for (int i = tid; i < 2 * KB; i += kTiledThreads) {
-        const int blk = i / KB, kb = i % KB, nb = n0 / kGroup + blk;
-        s_ws[blk][kb] = nb < N / kGroup ? p.w_scales[(static_cast<int64_t>(e) * (N / kGroup) + nb) * KB + kb] : 0.0f;
-      }
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[lo]);
+    f.rows_here = min(TM, cnt - mt * TM);
+    f.row0 = __builtin_amdgcn_readfirstlane(s_row0[lo]) + mt * TM;
+    f.n0 = ntile * TNT;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int row = i < 2 ? wave * 32 + 16 * i + (lane >> 2) : tok;
+      f.raw[i] = !GATHER ? f.row0 + row : row < f.rows_here ? p.a_row_map[f.row0 + row] : 0;
     }
-    // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
-    // instructions of 16 rows each (128 weight rows: rows [16 w, 16 w + 16)
-    // as one instruction; 64: rows [8 w, 8 w + 8) as one instruction of 32
-    // lanes); lane l lands in slot
-    // l & 3 of row 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps
-    // there.
-    uint32_t aoff[2], woff[2];
+    return f;
+  };
+  // Stage loads: wave w stages rows [32 w, 32 w + 32) of both slabs as 2
+  // instructions of 16 rows each (128 weight rows: rows [16 w, 16 w + 16)
+  // as one instruction; 64: rows [8 w, 8 w + 8) as one instruction of 32
+  // lanes); lane l lands in slot
+  // l & 3 of row 32 w + 16 i + (l >> 2) and fetches the chunk swz() keeps
+  // there.
+  auto tile_finish = [&](const TiledTileFetch& f) {
+    TiledTile t;
+    t.e = f.e;
+    t.row0 = f.row0;
+    t.rows_here = f.rows_here;
+    t.n0 = f.n0;
+    t.wb = p.w + static_cast<int64_t>(f.e) * N * (W4 ? K / 2 : K);
+    // A row feeding output row row0 + row, or -1 (as a_source_row)
+    auto source = [&](int row, int raw) {
+      if (row >= f.rows_here) return -1;
+      const int ar = GATHER ? raw / p.a_row_div : raw;
+      return static_cast<unsigned>(ar) < static_cast<unsigned>(p.a_rows) ? ar : -1;
+    };
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wave * 32 + 16 * i + (lane >> 2);
       const int chunk = ((lane & 3) ^ ((row >> 2) & 3)) << 4;
-      const int ar = row < rows_here ? a_source_row<GATHER>(p, row0 + row) : -1;
-      aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
+      const int ar = source(row, f.raw[i]);
+      t.aoff[i] = static_cast<uint32_t>(ar < 0 ? 0 : ar) * K + chunk;
       const int wrow = TNT == 256 ? row : TNT == 128 ? wave * 16 + (lane >> 2) : wave * 8 + (lane >> 2) % 8;
       const int wchunk = TNT == 256 ? chunk : ((lane & 3) ^ ((wrow >> 2) & 3)) << 4;
-      const int wr = n0 + wrow < N ? n0 + wrow : n0;
-      woff[i] = static_cast<uint32_t>(wr) * K + wchunk;
+      const int wr = f.n0 + wrow < N ? f.n0 + wrow : f.n0;
+      t.woff[i] = static_cast<uint32_t>(wr) * K + wchunk;
     }
     if constexpr (W4) {
       // wave w: weight rows [32 w, 32 w + 32), two lanes per 32-byte row
       const int wrow = wave * 32 + (lane >> 1);
       const int wchunk = ((lane & 1) ^ ((wrow >> 3) & 1)) << 4;
-      const int wr = n0 + wrow < N ? n0 + wrow : n0;
-      woff[0] = static_cast<uint32_t>(wr) * (K / 2) + wchunk;
+      const int wr = f.n0 + wrow < N ? f.n0 + wrow : f.n0;
+      t.woff[0] = static_cast<uint32_t>(wr) * (K / 2) + wchunk;
     }
-    const int sa_row = tok < rows_here ? a_source_row<GATHER>(p, row0 + tok) : -1;
-    const int my_src = sa_row < 0 ? 0 : sa_row;
-
-    auto issue = [&](int j, uint8_t* stage) {  // operand slabs of stage j
-      const int s = j < NS ? j : NS - 1;
+    t.sa_row = source(tok, f.raw[2]);
+    return t;
+  };
+  // The weight block scales of a tile's two 128-row blocks into s_wsf
+  // (direct-to-LDS, one value per thread: 2 KB <= 512). A block past the
+  // last weight row repeats the last block; no working wave reads it, since
+  // N is a multiple of 128.
+  auto ws_load = [&](const TiledTileFetch& f) {
+    const int i = tid < 2 * KB ? tid : 0;
+    const int kb = i % KB;
+    const int nb = min(f.n0 / kGroup + i / KB, N / kGroup - 1);
+    __builtin_amdgcn_global_load_lds(p.w_scales + (static_cast<int64_t>(f.e) * (N / kGroup) + nb) * KB + kb,
+                                     (lds_void*)(s_wsf + wave * 64), 4, 0, 0);
+  };
+  auto issue_t = [&](const TiledTile& t, int j, uint8_t* stage) {  // operand slabs of stage j
+    const int s = j < NS ? j : NS - 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(p.a + (t.aoff[i] + s * SK), (lds_void*)(stage + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+    if constexpr (W4) {
+      __builtin_amdgcn_global_load_lds(t.wb + (t.woff[0] + s * (SK / 2)), (lds_void*)(stage + kStageA + wave * 32 * (SK / 2)), 16, 0, 0);
+    } else if constexpr (TNT == 256) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds(p.a + (aoff[i] + s * SK), (lds_void*)(stage + (wave * 32 + 16 * i) * SK), 16, 0, 0);
-      if constexpr (W4) {
-        __builtin_amdgcn_global_load_lds(wbase4 + (woff[0] + s * (SK / 2)), (lds_void*)(stage + kStageA + wave * 32 * (SK / 2)), 16, 0, 0);
-      } else if constexpr (TNT == 256) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          __builtin_amdgcn_global_load_lds(wbase + (woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
-      } else if constexpr (TNT == 128) {
-        __builtin_amdgcn_global_load_lds(wbase + (woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 16 * SK), 16, 0, 0);
-      } else if (lane < 32) {
-        __builtin_amdgcn_global_load_lds(wbase + (woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 8 * SK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(t.wb + (t.woff[i] + s * SK), (lds_void*)(stage + kStageA + (wave * 32 + 16 * i) * SK), 16, 0, 0);
+    } else if constexpr (TNT == 128) {
+      __builtin_amdgcn_global_load_lds(t.wb + (t.woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 16 * SK), 16, 0, 0);
+    } else if (lane < 32) {
+      __builtin_amdgcn_global_load_lds(t.wb + (t.woff[0] + s * SK), (lds_void*)(stage + kStageA + wave * 8 * SK), 16, 0, 0);
+    }
+  };
+  // Token scales of block kb. Waves 0..3 load them into `buf`; waves
+  // 4..7 load the same values into a sink so that every wave has the same
+  // number of loads in flight and one vmcnt immediate fits all of them.
+  // W4: waves 4..7 load the scale bytes of the tile's 256 weight rows
+  // instead (4 bytes per row and block) into s_wsc, by block parity.
+  auto issue_s_t = [&](const TiledTile& t, int kb, uint32_t* buf) {
+    const int kbc = kb < KB ? kb : KB - 1;
+    if constexpr (W4) {
+      if (wave >= TM / 64) {
+        const int row = t.n0 + (wave & 3) * 64 + lane;
+        const int64_t widx = (static_cast<int64_t>(t.e) * N + (row < N ? row : t.n0)) * (K / kMxBlock) + kbc * 4;
+        __builtin_amdgcn_global_load_lds(p.w_mx + widx, (lds_void*)(s_wsc + (kb & 1) * TM + (wave & 3) * 64), 4, 0, 0);
+        return;
       }
-    };
-    // Token scales of block kb. Waves 0..3 load them into `buf`; waves
-    // 4..7 load the same values into a sink so that every wave has the same
-    // number of loads in flight and one vmcnt immediate fits all of them.
-    // W4: waves 4..7 load the scale bytes of the tile's 256 weight rows
-    // instead (4 bytes per row and block) into s_wsc, by block parity.
-    auto issue_s = [&](int kb, uint32_t* buf) {
-      const int kbc = kb < KB ? kb : KB - 1;
-      if constexpr (W4) {
-        if (wave >= TM / 64) {
-          const int row = n0 + (wave & 3) * 64 + lane;
-          const int64_t widx = (static_cast<int64_t>(e) * N + (row < N ? row : n0)) * (K / kMxBlock) + kbc * 4;
-          __builtin_amdgcn_global_load_lds(p.w_mx + widx, (lds_void*)(s_wsc + (kb & 1) * TM + (wave & 3) * 64), 4, 0, 0);
-          return;
-        }
-      }
-      uint32_t* dst = (wave < TM / 64 ? buf : s_srx) + (wave & 3) * 64;
-      const int64_t idx = static_cast<int64_t>(kbc) * p.a_rows + my_src;
-      if constexpr (UE8M0)
-        __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.a_scales) + idx, (lds_void*)dst, 1, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(static_cast<const uint32_t*>(p.a_scales) + idx, (lds_void*)dst, 4, 0, 0);
-    };
+    }
+    uint32_t* dst = (wave < TM / 64 ? buf : s_srx) + (wave & 3) * 64;
+    const int64_t idx = static_cast<int64_t>(kbc) * p.a_rows + (t.sa_row < 0 ? 0 : t.sa_row);
+    if constexpr (UE8M0)
+      __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.a_scales) + idx, (lds_void*)dst, 1, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(static_cast<const uint32_t*>(p.a_scales) + idx, (lds_void*)dst, 4, 0, 0);
+  };
+  // A tile's prologue: stages 0..2 and the token scales of blocks 0 and 1;
+  // each stage issues [A x2][W x2] then, when it starts a block, [S]. The
+  // order is pinned so the vmcnt waits can count. prologue_part(t, b) is
+  // what goes after stage buffer b is free.
+  auto prologue_part = [&](const TiledTile& t, int b) {
+    issue_t(t, b, b == 0 ? s_st0 : b == 1 ? s_st1 : s_st2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b == 0) issue_s_t(t, 0, s_sr0);
+    if (b == 2) issue_s_t(t, 1, s_sr1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  TiledTile cur{};
+  if (vid < total) {
+    const TiledTileFetch f = tile_fetch(vid);
+    if constexpr (!W4) ws_load(f);
+    cur = tile_finish(f);
+    prologue_part(cur, 0);
+    prologue_part(cur, 1);
+    prologue_part(cur, 2);
+  }
+
+  for (int tile = vid; tile < total; tile += G) {
+    const int row0 = cur.row0, rows_here = cur.rows_here, n0 = cur.n0, sa_row = cur.sa_row;
+    const bool wave_on = wm * 64 < rows_here && n0 + wn * WN < N;
+    auto issue = [&](int j, uint8_t* stage) { issue_t(cur, j, stage); };
+    auto issue_s = [&](int kb, uint32_t* buf) { issue_s_t(cur, kb, buf); };
     auto decode_sa = [&](uint32_t raw) -> float {
       const float v = sa_row < 0 ? 1.0f : __uint_as_float(UE8M0 ? raw << 23 : raw);
       return v > kScaleFloor ? v : kScaleFloor;
@@ -799,20 +870,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     float tok_prev = 1.0f;  // this thread's token scale of the previous block
     float sw_norm = 1.0f;   // weight part of the accumulator's normalizer
 
-    // Prologue: stages 0..2 (and the token scales of blocks 0 and 1); each
-    // stage issues [A x2][W x2] then, when it starts a block, [S]. The order
-    // is pinned so the vmcnt waits can count.
-    __syncthreads();  // s_ws visible; the previous tile is done with every stage
-    issue(0, s_st0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_s(0, s_sr0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(1, s_st1);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(2, s_st2);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_s(1, s_sr1);
-    __builtin_amdgcn_sched_barrier(0);
+    // The prologue's loads went out before the loop (first tile) or during
+    // the previous tile's output stores; the barrier keeps this tile's
+    // writes of s_rt and s_sl behind the previous tile's last reads.
+    lds_barrier();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS + 1));  // stage 0 and block 0's scales landed
     if (tid < TM) {
       tok_prev = decode_sa(s_sr0[tok]);
@@ -854,7 +915,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       if (!wave_on || j >= NS) return;
       if (cur_starts) {
         const int kb = j >> 1;
-        const float sw = fmaxf(s_ws[(wn * WN) / kGroup][kb], kScaleFloor);
+        const float sw = fmaxf(s_wsf[((wn * WN) / kGroup) * KB + kb], kScaleFloor);
         const float q = sw_norm * __builtin_amdgcn_rcpf(sw);
         sw_norm = sw;
         const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
@@ -966,7 +1027,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
           }
           if constexpr (even) {
             const int kb = j >> 1;
-            const float sw = fmaxf(s_ws[(wn * WN) / kGroup][kb], kScaleFloor);
+            const float sw = fmaxf(s_wsf[((wn * WN) / kGroup) * KB + kb], kScaleFloor);
             const float q = sw_norm * __builtin_amdgcn_rcpf(sw);
             sw_norm = sw;
             const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
@@ -1059,7 +1120,25 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     __builtin_amdgcn_s_waitcnt(0);  // trailing loads of this tile done before any stage is reused
     __syncthreads();
 
+    // The next tile: its coordinates and row-map entries now (loads into
+    // registers, in flight during the output staging); its weight scales
+    // and prologue follow once the staging's LDS writes are done, the
+    // prologue as the stage buffers free up. (A direct-to-LDS load in
+    // flight would make the compiler wait for it before the staging writes,
+    // whose buffer it cannot tell apart.)
+    const bool has_next = tile + G < total;
+    TiledTileFetch nf{};
+    if (has_next) nf = tile_fetch(tile + G);
+    TiledTile nxt = cur;
+
     if constexpr (!SOUT) {
+      if (has_next) {
+        if constexpr (!W4) ws_load(nf);
+        nxt = tile_finish(nf);
+        prologue_part(nxt, 0);
+        prologue_part(nxt, 1);
+        prologue_part(nxt, 2);
+      }
       // Each lane stores its 4-column pieces straight from the accumulator.
       if (wave_on) {
         const float f = sw_norm;
@@ -1122,11 +1201,23 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         }
       }
       __syncthreads();
+      // The next tile's row-map entries have landed (no store is in flight
+      // yet, so this waits for nothing else).
+      __builtin_amdgcn_s_waitcnt(0);
+      if (has_next) {
+        if constexpr (!W4) ws_load(nf);
+        nxt = tile_finish(nf);
+      }
       {
         // Pass `it` stores rows it * RPI + tr; thread (tr, tq) takes chunk tq.
         // RPI is a multiple of 4, so the row's swizzle is tr % 4 in every pass.
+        // Once every wave has read stage buffer b (rows [b, b + 1) *
+        // kRowsPerBuf), the next tile's prologue part for that buffer goes
+        // out; the stores in flight only lengthen its first wait.
         constexpr int RPI = kTiledThreads / kChunks;
+        constexpr int kPasses = kRowsPerBuf / RPI;  // passes per stage buffer
         static_assert(RPI % 4 == 0, "passes start at rows divisible by 4");
+        static_assert(kPasses * RPI == kRowsPerBuf && TM == 4 * kRowsPerBuf, "whole passes over four buffers");
         const int tq = tid % kChunks, tr = tid / kChunks;
         int lb = tr * kRowBytes + ((tq ^ (tr & 3)) << 4);
         asm volatile("" : "+v"(lb));
@@ -1134,17 +1225,27 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         int step = RPI * N;  // opaque, so per-pass offsets are not hoisted
         asm volatile("" : "+s"(step));
         const bool col_ok = n0 + tq * 8 < N;
-#pragma unroll 1  // unrolled, the passes' LDS reads are batched and hold more registers
-        for (int it = 0; it < TM / RPI; ++it, gc += step) {
-          const int j0 = it * RPI;  // first row of the pass
-          const uint8_t* src = out_row(j0) + lb;
-          if (col_ok && j0 + tr < rows_here)
-            *reinterpret_cast<uint4*>(gc) = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          uint4 v[kPasses];  // a buffer's passes read together, then stored
+#pragma unroll
+          for (int q = 0; q < kPasses; ++q)
+            v[q] = *reinterpret_cast<const uint4*>(out_row((b * kPasses + q) * RPI) + lb);
+#pragma unroll
+          for (int q = 0; q < kPasses; ++q, gc += step) {
+            const int j0 = (b * kPasses + q) * RPI;  // first row of the pass
+            if (col_ok && j0 + tr < rows_here) *reinterpret_cast<uint4*>(gc) = v[q];
+          }
+          if (b < 3 && has_next) {
+            lds_barrier();  // every wave's reads of buffer b have returned
+            prologue_part(nxt, b);
+          }
         }
       }
     }
     if (tid == 0 && p.tiles_visited)  // (row tile, 128-column tile) pairs, each counted once
       atomicAdd(p.tiles_visited, TNT >= kColTile ? min(TNT, N - n0) / kColTile : (n0 % kColTile == 0 ? 1 : 0));
+    cur = nxt;
   }
 }
 

@@ -21,11 +21,14 @@ __device__ __forceinline__ v4f mfma_fp8(v8i w, v8i x) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Four values to BF16 (round to nearest even, as f32_to_bf16 for finite
+// values), two per v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint2 pack_bf16x4(v4f v) {
-  uint2 o;
-  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-  return o;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // Live rows of expert e, or 0 when its endpoints do not describe a segment
