@@ -563,7 +563,6 @@ constexpr int SK = 64;            // K bytes per pipeline stage (half a scale bl
 constexpr int kTiledThreads = 512;
 constexpr int kStageA = TM * SK;              // token part of a stage (16 KB)
 constexpr int kStageBytes = (TM + TN) * SK;   // 32 KB
-constexpr int kGroupN = 8;                    // n-tiles per scheduling group
 constexpr int kMaxKBlocks = 256;              // K <= 32768 on this path
 // Scales below this are treated as this value inside the accumulator's
 // normalizer: a block whose scale is zero then adds 2^-64 times its raw dot
@@ -586,21 +585,15 @@ union Frag {
 };
 
 
-// Tile t of an expert with mt row tiles and nt column tiles, in the order
-// that keeps kGroupN column tiles x all row tiles of an expert together (so
-// the workgroups of one XCD share token and weight slabs in their L2).
-__device__ __forceinline__ void tile_coords(int local, int mt, int nt, int* m, int* n) {
-  const int full = nt / kGroupN;
-  const int gsz = mt * kGroupN;
-  if (local < full * gsz) {
-    const int g = local / gsz, r = local % gsz;
-    *m = r / kGroupN;
-    *n = g * kGroupN + r % kGroupN;
-  } else {
-    const int r = local - full * gsz, gw = nt - full * kGroupN;
-    *m = r / gw;
-    *n = full * kGroupN + r % gw;
-  }
+// Tile `local` of an expert with mt row tiles: weight column tile local / mt,
+// row tile local % mt. Consecutive tiles go to one XCD, so a round of its
+// workgroups covers a few column tiles x all row tiles of an expert, and each
+// weight slab is read by workgroups that share its XCD's L2 at about the
+// same time. (Grouping 4, 8 or 16 column tiles x all row tiles measured
+// 0.2-5% slower at 4096 tokens.)
+__device__ __forceinline__ void tile_coords(int local, int mt, int* m, int* n) {
+  *n = local / mt;
+  *m = local - *n * mt;
 }
 
 // A tile of the large-expert GEMM: its expert's weights, first output row,
@@ -728,7 +721,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
     f.e = __builtin_amdgcn_readfirstlane(s_list[lo]);
     const int mt_e = s_pref[lo + 1] - s_pref[lo];
     int mt, ntile;
-    tile_coords(tile - s_pref[lo] * nt, mt_e, nt, &mt, &ntile);
+    tile_coords(tile - s_pref[lo] * nt, mt_e, &mt, &ntile);
     const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[lo]);
     f.rows_here = min(TM, cnt - mt * TM);
     f.row0 = __builtin_amdgcn_readfirstlane(s_row0[lo]) + mt * TM;
