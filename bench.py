@@ -469,9 +469,8 @@ def pct(v, q):
 
 
 # Entries of the per-config table: (workload, token capacity, live tokens,
-# activation scale format, activation, clamp limit).
-# (workload, token capacity, live tokens, activation scales, activation,
-# clamp limit[, rows per expert of the batched masked-M layout])
+# activation scales, activation, clamp limit[, rows per expert of the
+# batched masked-M layout[, weight format]]).
 PER_CONFIG = [
     ("tiny", 8, 8, "fp32", "swiglu", float("inf")),
     ("decode", 1, 1, "fp32", "swiglu", float("inf")),
@@ -493,6 +492,8 @@ PER_CONFIG = [
     ("decode", 4, 4, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
     ("padded", 512, 16, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
     ("full", 4096, 4096, "fp32", "swiglu", float("inf"), 0, "mxfp4"),
+    # with UE8M0 token scales the matrix cores apply both scales
+    ("full", 4096, 4096, "ue8m0", "swiglu", float("inf"), 0, "mxfp4"),
 ]
 
 

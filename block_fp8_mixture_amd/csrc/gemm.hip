@@ -652,7 +652,9 @@ struct TiledTileFetch {
 // 32) of its row, h = lane / 32, and that MX block's byte as its scale) and
 // the tokens as operand B (16-byte chunks h and 2 + h of the stage's 64, the
 // order the matrix core pairs with E2M1, as measured); the accumulator's
-// normalizer is the token scale alone.
+// normalizer is the token scale alone. With UE8M0 token scales the token's
+// byte is B's scale operand and the accumulator is never rescaled: every
+// factor is a power of two, so the result is bit-identical to rescaling.
 template <bool UE8M0, bool GATHER, int TNT, bool PICK, bool SOUT, bool W4 = false>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p) {
   static_assert(TNT == 256 || TNT == 128 || TNT == 64, "tile widths");
@@ -661,6 +663,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
   constexpr int WN = TNT / 2;   // weight rows of a wave
   constexpr int WT = WN / 32;   // its 32-row MFMA tiles
   constexpr int LPS = W4 ? 3 : TNT == 256 ? 4 : 3;  // direct-to-LDS loads per wave and stage
+  // MXFP4 weights with UE8M0 token scales: both scales are powers of two and
+  // the scaled MFMA applies both (the token's byte as B's scale), so the
+  // accumulator holds the result itself and is never rescaled.
+  constexpr bool kHwScales = W4 && UE8M0;
   // Four stages and two token-scale buffers, all distinct objects, so the
   // compiler can tell that a read never aliases a direct-to-LDS load in
   // flight and does not wait for the prefetch.
@@ -976,6 +982,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       uint32_t wsc[W4 ? WT : 1] = {};   // W4: its row's 4 scale bytes of the current block
       uint32_t scb[W4 ? WT : 1] = {};   // W4: the stage's scale byte (low byte) per weight tile
       float ratio0 = 1.0f, ratio1 = 1.0f;
+      uint32_t tsb0 = 127, tsb1 = 127;  // kHwScales: the lane's two tokens' E8M0 bytes of the block
       auto lphase = [&](int j, const uint8_t* cur, uint8_t* fill, const float* rt_cur,
                         uint32_t* sr_fill, const uint32_t* sr_next, float* rt_next, auto even_t) {
         constexpr bool even = decltype(even_t)::value;
@@ -997,9 +1004,15 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
 #pragma unroll
             for (int wt = 0; wt < (W4 ? WT : 1); ++wt)
               wsc[wt] = s_wsc[W4 ? (kb & 1) * TM + wn * WN + wt * 32 + (lane & 31) : 0];
-            const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
-            ratio0 = r2.x;
-            ratio1 = r2.y;
+            if constexpr (kHwScales) {
+              // the block's raw token bytes (its buffer is refilled one phase later)
+              tsb0 = sr_next[wm * 64 + (lane & 31)];
+              tsb1 = sr_next[wm * 64 + 32 + (lane & 31)];
+            } else {
+              const float2 r2 = *reinterpret_cast<const float2*>(rt_cur + (lane & 31) * 8 + wm * 2);
+              ratio0 = r2.x;
+              ratio1 = r2.y;
+            }
           }
           // MX blocks 2 (j & 1) + h of the 128-wide block: this stage's half of it
 #pragma unroll
@@ -1057,19 +1070,20 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         for (int wt = 0; wt < WT; ++wt)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
-            if constexpr (even) acc[wt][tt] = acc[wt][tt] * (tt == 0 ? ratio0 : ratio1);
+            if constexpr (even && !kHwScales) acc[wt][tt] = acc[wt][tt] * (tt == 0 ? ratio0 : ratio1);
             if constexpr (W4) {
               const uint4 w = wf4[wt];
               const v8i wa = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
                               static_cast<int>(w.w), 0, 0, 0, 0};
+              const int tsb = kHwScales ? static_cast<int>(tt == 0 ? tsb0 : tsb1) : 127;
               acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, af[tt].v, acc[wt][tt], 4, 0, 0,
-                                                                             static_cast<int>(scb[wt]), 0, 127);
+                                                                             static_cast<int>(scb[wt]), 0, tsb);
             } else {
               acc[wt][tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[wt].v, af[tt].v, acc[wt][tt],
                                                                              0, 0, 0, 0, 0, 0);
             }
           }
-        if constexpr (even) {
+        if constexpr (even && !kHwScales) {
 #pragma unroll
           for (int i = 0; i < 2 * WT; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU: one accumulator's rescale
@@ -1136,7 +1150,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       if (wave_on) {
         const float f = sw_norm;
         const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
-        const float fs[2] = {sl.x * f, sl.y * f};
+        const float fs[2] = {kHwScales ? 1.0f : sl.x * f, kHwScales ? 1.0f : sl.y * f};
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int j = wm * 64 + tt * 32 + (lane & 31);
@@ -1171,7 +1185,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
       if (wave_on) {
         const float f = sw_norm;
         const float2 sl = *reinterpret_cast<const float2*>(s_sl + (lane & 31) * 8 + wm * 2);
-        const float fs[2] = {sl.x * f, sl.y * f};
+        const float fs[2] = {kHwScales ? 1.0f : sl.x * f, kHwScales ? 1.0f : sl.y * f};
         // j % 4 equals lane % 4; formed here behind an opaque move so the
         // compiler does not hoist the slot offsets out of the tile loop (they
         // would stay live across it).

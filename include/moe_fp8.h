@@ -242,7 +242,8 @@ moe_status moe_grouped_gemm_fp8_masked(const uint8_t* a, const void* a_scales, m
  *   w(e, n, k) = e2m1(code of column k of row n) * 2^(w_scales[e, n, k/32] - 127)
  * with ar as in moe_grouped_gemm_fp8, accumulated in fp32 (the weight scales
  * applied inside the matrix cores, the activation scale once per 128-wide
- * block) and rounded to nearest even BF16.
+ * block; with UE8M0 activation scales the matrix cores apply both) and
+ * rounded to nearest even BF16.
  *
  *   a, a_scales, fmt, a_rows, a_row_map, a_row_div   as moe_grouped_gemm_fp8
  *   w          device uint8 [num_experts, n, k/2] packed E2M1 codes
