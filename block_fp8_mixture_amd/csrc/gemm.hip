@@ -1216,11 +1216,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(GemmArgs p
         nxt = tile_finish(nf);
       }
       {
-        // Pass `it` stores rows it * RPI + tr; thread (tr, tq) takes chunk tq.
-        // RPI is a multiple of 4, so the row's swizzle is tr % 4 in every pass.
-        // Once every wave has read stage buffer b (rows [b, b + 1) *
-        // kRowsPerBuf), the next tile's prologue part for that buffer goes
-        // out; the stores in flight only lengthen its first wait.
+        // Pass it = b * kPasses + q stores rows it * RPI + tr; thread (tr, tq)
+        // takes chunk tq. RPI is a multiple of 4, so the row's swizzle is
+        // tr % 4 in every pass. Once every wave has read stage buffer b (rows
+        // [b * kRowsPerBuf, (b + 1) * kRowsPerBuf)), the next tile's prologue
+        // part for that buffer goes out; the stores in flight only lengthen
+        // its first wait.
         constexpr int RPI = kTiledThreads / kChunks;
         constexpr int kPasses = kRowsPerBuf / RPI;  // passes per stage buffer
         static_assert(RPI % 4 == 0, "passes start at rows divisible by 4");
