@@ -252,6 +252,41 @@ def test_mxfp4_gemm_full_size_sampled(shape, fmt):
         assert np.all(got[pad] == POISON_BF16)
 
 
+
+def test_mxfp4_gemm_ue8m0_equals_fp32_powers_of_two():
+    # With UE8M0 activation scales the 256 x 256 kernel passes each token's
+    # byte to the matrix cores as B's scale and never rescales the
+    # accumulator; with fp32 scales it rescales by the ratio of consecutive
+    # blocks' scales. For the same powers of two every factor is exact, so
+    # both must give the same bits on every live row (FC2's shape at 4096
+    # tokens: enough tiles for that kernel).
+    n, k = 7168, 2048
+    g = np.random.default_rng(22)
+    e_n = 32
+    counts, offsets = _routing_layout(g.integers(900, 1150, e_n))
+    row_cap = int(offsets[-1])
+    codes = g.integers(0, 0x7F, size=(row_cap, k), dtype=np.uint8)  # E4M3 codes without NaN
+    codes |= (g.integers(0, 2, size=(row_cap, k)) << 7).astype(np.uint8)
+    sb = g.integers(110, 135, size=(k // 128, row_cap)).astype(np.uint8)
+    sf = np.ldexp(np.float32(1.0), sb.astype(np.int32) - 127).astype(np.float32)
+    wp = g.integers(0, 256, size=(e_n, n, k // 2), dtype=np.uint8)
+    ws = g.integers(117, 122, size=(e_n, n, k // 32)).astype(np.uint8)
+    say(f"mxfp4 gemm ue8m0 vs fp32 powers of two n={n} k={k} row_cap={row_cap}")
+    outs = {}
+    for fmt, sc in (("ue8m0", sb), ("fp32", sf)):
+        out = torch.full((row_cap, n), POISON_BF16, dtype=torch.int16, device=dev())
+        moe.moe_grouped_gemm_mxfp4(up(codes), up(sc), fmt, up(wp), up(ws), up(counts), up(offsets),
+                                   row_cap, out=out)
+        torch.cuda.synchronize()
+        outs[fmt] = down(out)
+    live = np.zeros(row_cap, bool)
+    for e in range(e_n):
+        live[offsets[e]:offsets[e] + counts[e]] = True
+    diff = int((outs["ue8m0"][live] != outs["fp32"][live]).sum())
+    assert diff == 0, f"{diff} outputs differ"
+    assert np.all(outs["ue8m0"][~live] == POISON_BF16)
+
+
 def test_mxfp4_layer_full_size_sampled():
     # The 4096-token layer with MXFP4 weights through moe_forward (FC1 and
     # FC2 on the 256 x 256 kernel with E2M1 slabs): alignment bit-exact; on 16
